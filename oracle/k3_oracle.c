@@ -1,0 +1,270 @@
+/*
+ * k3_oracle.c -- the oracle: a plain CPU implementation of the MoE decode
+ * layer's token-side compute, used to check the GPU library.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this code. The GPU library
+ * never links, loads or calls it, and the two share no source.
+ *
+ * Plain, slow and obviously correct. Every output element is its definition
+ * written out: weights are bf16 bit patterns widened exactly to fp64,
+ * activations arrive as fp64, and every sum runs sequentially in fp64 in
+ * index order. OpenMP splits only independent output elements, so results
+ * are bitwise identical for any thread count.
+ *
+ * What is computed, after "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and
+ * Responsibly" (the post gives no formulas; the readings below are the
+ * plainest ones the rest of it supports):
+ *  - Part 1, section 3 "Improve MoE scheduling and overlap": router scores
+ *    and the latent input projection are computed from the same input, before
+ *    the routed experts run; the shared expert runs beside routing, so it
+ *    takes the layer input, not the latent.
+ *  - Part 1, section 1 "Tune shapes for the workload": the attention input
+ *    projection, a plain linear map.
+ *  - Part 1, section 2 "Overlap computation and communication": the attention
+ *    output projection followed by the attention residual add; the RMSNorm
+ *    that follows it (eps inside the square root, mean over the width) is the
+ *    workload's definition.
+ * Readings where the post is silent: router logits are scored by softmax and
+ * the top-k weights renormalised to sum to 1; ties on equal logits go to the
+ * lower expert index; a SwiGLU expert stacks its gate rows [0, I) over its up
+ * rows [I, 2I) and computes down( silu(gate) * up ) with silu(g) = g/(1+e^-g);
+ * the layer output is the shared expert's output plus the weighted sum of the
+ * routed experts' outputs.
+ *
+ * The selection decision is taken on fp32 logits (the fp64 sum rounded to
+ * fp32, then the fp32 bias added in fp32), the precision the GPU kernel
+ * decides in; everything else stays in fp64.
+ *
+ * Matrices are [out x in], row-major, input index contiguous.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* dst[i] = exact value of the bf16 pattern src[i]. */
+void orc_bf16_to_f64(const uint16_t *src, int64_t n, double *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = bf16_value(src[i]);
+}
+
+/* Linear map: y[t][n] = sum_{i<K} x[t][i] * W[n][i], W is [N x K]. */
+void orc_linear(const double *x, int64_t ldx, int b, int K,
+                const uint16_t *W, int N, double *y, int64_t ldy)
+{
+    int64_t total = (int64_t)b * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < total; ++o) {
+        int t = (int)(o / N);
+        int n = (int)(o % N);
+        const double *xt = x + (int64_t)t * ldx;
+        const uint16_t *wn = W + (int64_t)n * K;
+        double s = 0.0;
+        for (int i = 0; i < K; ++i)
+            s += xt[i] * bf16_value(wn[i]);
+        y[(int64_t)t * ldy + n] = s;
+    }
+}
+
+/* Router scores: logits[t][e] = fp32(x_t . Wr[e]) (+ bias[e], added in fp32).
+ * Wr is [E x d]; bias may be NULL. */
+void orc_router_logits(const double *x, int64_t ldx, int b, int d,
+                       const uint16_t *Wr, const float *bias, int E, float *logits)
+{
+    int64_t total = (int64_t)b * E;
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < total; ++o) {
+        int t = (int)(o / E);
+        int e = (int)(o % E);
+        const double *xt = x + (int64_t)t * ldx;
+        const uint16_t *we = Wr + (int64_t)e * d;
+        double s = 0.0;
+        for (int i = 0; i < d; ++i)
+            s += xt[i] * bf16_value(we[i]);
+        float l = (float)s;
+        if (bias)
+            l = l + bias[e];
+        logits[o] = l;
+    }
+}
+
+/* True when expert a ranks before expert b: higher logit first, and on equal
+ * logits the lower index first. */
+static int ranks_before(const float *l, int a, int b)
+{
+    if (l[a] != l[b])
+        return l[a] > l[b];
+    return a < b;
+}
+
+/* Top-k selection and renormalised softmax weights, per token.
+ * ids[t][j] is the j-th expert in (logit desc, index asc) order, j < k.
+ * w[t][j] = p(ids[t][j]) / sum_{j'<k} p(ids[t][j']), where p is the softmax
+ * over all E logits of token t. */
+void orc_topk_softmax(const float *logits, int b, int E, int k,
+                      int32_t *ids, double *w)
+{
+    int *order = (int *)malloc(sizeof(int) * (size_t)E);
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    for (int t = 0; t < b; ++t) {
+        const float *l = logits + (int64_t)t * E;
+        /* full insertion sort of the expert indices */
+        for (int e = 0; e < E; ++e) {
+            int j = e;
+            while (j > 0 && ranks_before(l, e, order[j - 1])) {
+                order[j] = order[j - 1];
+                --j;
+            }
+            order[j] = e;
+        }
+        /* softmax over all E experts */
+        double m = (double)l[0];
+        for (int e = 1; e < E; ++e)
+            if ((double)l[e] > m)
+                m = (double)l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - m);
+            z += p[e];
+        }
+        for (int e = 0; e < E; ++e)
+            p[e] /= z;
+        /* renormalise over the selected k */
+        double sel = 0.0;
+        for (int j = 0; j < k; ++j)
+            sel += p[order[j]];
+        for (int j = 0; j < k; ++j) {
+            ids[(int64_t)t * k + j] = order[j];
+            w[(int64_t)t * k + j] = p[order[j]] / sel;
+        }
+    }
+    free(order);
+    free(p);
+}
+
+static double silu(double g)
+{
+    return g / (1.0 + exp(-g));
+}
+
+/* One SwiGLU expert applied to one input vector z (length din):
+ *   gate_j = W13[j] . z,  up_j = W13[I + j] . z          (j < I)
+ *   h_j    = silu(gate_j) * up_j
+ *   out[r] = W2[r] . h                                    (r < dout)
+ * W13 is [2I x din], W2 is [dout x I]. h is caller scratch of length I. */
+static void swiglu_expert(const double *z, int din, const uint16_t *W13,
+                          const uint16_t *W2, int I, int dout,
+                          double *h, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int j = 0; j < I; ++j) {
+        const uint16_t *wg = W13 + (int64_t)j * din;
+        const uint16_t *wu = W13 + (int64_t)(I + j) * din;
+        double g = 0.0, u = 0.0;
+        for (int i = 0; i < din; ++i) {
+            g += z[i] * bf16_value(wg[i]);
+            u += z[i] * bf16_value(wu[i]);
+        }
+        h[j] = silu(g) * u;
+    }
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < dout; ++r) {
+        const uint16_t *wr = W2 + (int64_t)r * I;
+        double s = 0.0;
+        for (int j = 0; j < I; ++j)
+            s += bf16_value(wr[j]) * h[j];
+        out[r] = s;
+    }
+}
+
+/* Shared expert: y_s[t] = SwiGLU_shared(x_t), x is [b x din] with row stride ldx. */
+void orc_shared_expert(const double *x, int64_t ldx, int b, int din,
+                       const uint16_t *W13, const uint16_t *W2, int I, int dout,
+                       double *y_s)
+{
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int t = 0; t < b; ++t)
+        swiglu_expert(x + (int64_t)t * ldx, din, W13, W2, I, dout, h,
+                      y_s + (int64_t)t * dout);
+    free(h);
+}
+
+/* Routed experts and combine:
+ *   y[t] = y_add[t] + sum_{j<k} w[t][j] * Expert_{ids[t][j]}(z_t)
+ * summed in slot order j = 0..k-1 after y_add (y_add may be NULL = 0).
+ * w13[e] / w2[e] point at expert e's [2I x din] / [dout x I] weights; only
+ * the experts that ids name are read. Returns 0, or -1 when an id is out of
+ * range or names an expert whose weights are NULL. */
+int orc_moe_experts(const double *z, int64_t ldz, int b, int din,
+                    const int32_t *ids, const double *w, int k,
+                    const uint16_t *const *w13, const uint16_t *const *w2,
+                    int E, int I, int dout, const double *y_add, double *y)
+{
+    for (int64_t i = 0; i < (int64_t)b * k; ++i)
+        if (ids[i] < 0 || ids[i] >= E || !w13[ids[i]] || !w2[ids[i]])
+            return -1;
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    double *o = (double *)malloc(sizeof(double) * (size_t)dout);
+    for (int t = 0; t < b; ++t) {
+        double *yt = y + (int64_t)t * dout;
+        for (int r = 0; r < dout; ++r)
+            yt[r] = y_add ? y_add[(int64_t)t * dout + r] : 0.0;
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(int64_t)t * k + j];
+            swiglu_expert(z + (int64_t)t * ldz, din, w13[e], w2[e], I, dout, h, o);
+            double wj = w[(int64_t)t * k + j];
+            for (int r = 0; r < dout; ++r)
+                yt[r] += wj * o[r];
+        }
+    }
+    free(h);
+    free(o);
+    return 0;
+}
+
+/* Output projection, residual and RMSNorm:
+ *   h[t][n] = r[t][n] + sum_{i<K} a[t][i] * Wo[n][i]          (Wo is [d x K])
+ *   y[t][n] = h[t][n] / sqrt( (1/d) sum_m h[t][m]^2 + eps ) * gamma[n] */
+void orc_oproj_residual_rmsnorm(const double *a, int64_t lda, int b, int K,
+                                const uint16_t *Wo, int d, const double *r,
+                                const double *gamma, double eps,
+                                double *h, double *y)
+{
+    orc_linear(a, lda, b, K, Wo, d, h, d);
+    for (int t = 0; t < b; ++t) {
+        double *ht = h + (int64_t)t * d;
+        const double *rt = r + (int64_t)t * d;
+        double ss = 0.0;
+        for (int n = 0; n < d; ++n) {
+            ht[n] += rt[n];
+            ss += ht[n] * ht[n];
+        }
+        double inv = 1.0 / sqrt(ss / d + eps);
+        for (int n = 0; n < d; ++n)
+            y[(int64_t)t * d + n] = ht[n] * inv * gamma[n];
+    }
+}
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of threads the parallel loops above use. */
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
