@@ -1,0 +1,228 @@
+/*
+ * k3dec.h -- C ABI of libk3dec, the MoE decode-layer hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library computes one MoE transformer layer's token-side work at decode
+ * batch sizes 1-64, as described in "Hyper Optimizing Kimi K3 in vLLM: Moving
+ * Fast and Responsibly" (Part 1): router scoring with top-k expert selection,
+ * the latent input projection, the routed-expert SwiGLU, the shared expert on
+ * its own stream, the attention input projection, the attention output
+ * projection with residual add and RMSNorm, and a side-stream weight
+ * prefetch. The attention core itself is not part of the library.
+ *
+ * Conventions, common to every entry point:
+ *  - Pointers marked "device" are device (HBM) addresses; the caller owns
+ *    every buffer, including the workspace. The library never allocates,
+ *    never synchronises the host and never prints.
+ *  - Matrices are [out x in], row-major, with the input index contiguous
+ *    (a weight row is one output's input vector). bf16 values travel as
+ *    uint16_t bit patterns. Activation rows may have a leading dimension
+ *    (ld*, in elements) larger than their width.
+ *  - Every device pointer must be 16-byte aligned, every leading dimension
+ *    and every contracted width (d, K, I) a multiple of 8 elements.
+ *  - All calls are asynchronous on the given stream (a hipStream_t passed as
+ *    void*; NULL means the default stream) and keep the order of their
+ *    kernels on it. Inputs must stay valid and unmodified until that work
+ *    completes.
+ *  - Weights are read with non-temporal loads and must not change while a
+ *    call that reads them is in flight; activations are read with ordinary
+ *    loads after the stream ordering makes them visible.
+ *  - Every fp32 -> bf16 store rounds to nearest even.
+ *  - Return value: K3_OK, or a negative K3_ERR_* code. On any error other
+ *    than K3_ERR_HIP nothing has been launched. Unsupported shapes fail with
+ *    K3_ERR_UNSUPPORTED; there is no silent fallback to another path.
+ *  - Results are deterministic: the same inputs on the same device give the
+ *    same output bits, whatever the scheduling.
+ */
+#ifndef K3DEC_H
+#define K3DEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status */
+#define K3_OK 0
+#define K3_ERR_INVALID_ARG (-1)  /* NULL pointer, non-positive size, bad ld */
+#define K3_ERR_UNSUPPORTED (-2)  /* shape outside the supported range, or misaligned */
+#define K3_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than the size query says */
+#define K3_ERR_HIP (-4)          /* the HIP runtime reported an error at launch */
+
+/* Limits of this build. */
+#define K3_MAX_BATCH 64      /* tokens per call */
+#define K3_MAX_EXPERTS 1024  /* routed experts E */
+#define K3_MAX_TOPK 32       /* experts per token k */
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *k3_status_string(int status);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int k3_version(void);
+
+/* ------------------------------------------------------------ dispatch record
+ * Each entry point records which kernel variant it launched, so tests can
+ * check that a given shape really ran the path it claims (a test that runs a
+ * different path proves nothing about the one it names).
+ */
+#define K3_OP_ROUTER_TOPK 0
+#define K3_OP_PROJ_SKINNY 1
+#define K3_OP_MOE_EXPERTS 2
+#define K3_OP_SHARED_EXPERT 3
+#define K3_OP_OPROJ_RESIDUAL 4
+#define K3_OP_PREFETCH 5
+
+#define K3_VARIANT_NONE 0
+#define K3_VARIANT_DOT2 1    /* VALU dot2 GEMV: whole weight rows per wave */
+#define K3_VARIANT_MFMA 2    /* bf16 MFMA 16x16x32 tiles, K split inside the workgroup */
+#define K3_VARIANT_GROUPED 3 /* permutation + grouped expert tiles */
+#define K3_VARIANT_STREAM 4  /* plain streaming kernel */
+
+/* Variant the last successful call of `op` on this process launched. */
+int k3_get_last_dispatch(int op);
+
+/* Force a variant for `op` (K3_VARIANT_NONE restores the automatic choice).
+ * A forced variant that cannot run a shape makes that call fail with
+ * K3_ERR_UNSUPPORTED. For tests and measurements only. */
+int k3_force_variant(int op, int variant);
+
+/* ------------------------------------------------------------ workspace sizes
+ * Bytes of device workspace each entry point needs for the given shape.
+ * The workspace is caller-owned scratch with no state kept between calls;
+ * its contents need no initialisation.
+ */
+size_t k3_router_topk_workspace_size(int b, int E);
+size_t k3_proj_skinny_workspace_size(int b, int K, int N);
+size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I);
+size_t k3_shared_expert_workspace_size(int b, int d, int I);
+size_t k3_oproj_residual_workspace_size(int b, int K, int d);
+
+/* ------------------------------------------------------------ entry points */
+
+/* Router scores and top-k selection.
+ * "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 3 ("Improve MoE
+ * scheduling and overlap"): the router scores every expert from the layer
+ * input before the routed experts run.
+ *
+ *   logits[t][e] = sum_i x[t][i] * w_router[e][i]  (+ bias[e])      fp32
+ *   topk_ids[t]  = the k experts of highest logit, in descending logit
+ *                  order; equal logits rank the lower expert index first
+ *   topk_w[t][j] = softmax over the k selected logits (equivalently, the
+ *                  softmax over all E renormalised over the selection);
+ *                  the k weights of a token sum to 1
+ *
+ * x        device, [b x d] bf16, row stride ldx
+ * w_router device, [E x d] bf16
+ * bias     device, [E] fp32, or NULL for none
+ * topk_ids device, [b x k] int32 (output)
+ * topk_w   device, [b x k] fp32 (output)
+ * workspace device, >= k3_router_topk_workspace_size(b, E) bytes
+ * Limits: 1 <= b <= 64, 1 <= k <= min(E, 32), E <= 1024.
+ */
+int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
+                   const uint16_t *w_router, const float *bias, int E, int k,
+                   int32_t *topk_ids, float *topk_w,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Skinny projection y = x . W^T, for the latent input projection
+ * (Part 1 section 3) and the attention input projection (Part 1 section 1,
+ * "Tune shapes for the workload": small-matrix kernels at batch 1-2,
+ * work-splitting kernels above that).
+ *
+ *   y[t][n] = bf16( sum_i x[t][i] * w[n][i] ),  fp32 accumulation
+ *
+ * x device, [b x K] bf16, row stride ldx;  w device, [N x K] bf16;
+ * y device, [b x N] bf16 (output), row stride ldy; y must not overlap x.
+ * Variant: K3_VARIANT_DOT2 for b <= 8, K3_VARIANT_MFMA above.
+ * Limits: 1 <= b <= 64.
+ */
+int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K,
+                   const uint16_t *w, int N, uint16_t *y, int64_t ldy,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Routed experts: token-to-expert permutation, grouped SwiGLU gate/up, down
+ * projection and weighted combine (Part 1 section 3; the routed experts run
+ * after router and latent projection).
+ *
+ *   for each token t and slot j < k, with e = topk_ids[t][j]:
+ *     g = w13[e][0:I]  . z_t,   u = w13[e][I:2I] . z_t     (gate rows, then up rows)
+ *     h = silu(g) * u,          silu(g) = g / (1 + exp(-g))
+ *     o = w2[e] . h
+ *   y[t] = bf16( y_add[t] + sum_j topk_w[t][j] * o_(t,j) )
+ *
+ * z        device, [b x d_in] bf16, row stride ldz (the latent projection)
+ * topk_ids device, [b x k] int32, each in [0, E), distinct within a token
+ * topk_w   device, [b x k] fp32
+ * w13      device, [E x 2I x d_in] bf16;  w2 device, [E x d_out x I] bf16
+ * y_add    device, [b x d_out] fp32 added before the routed sum (the shared
+ *          expert's output), or NULL for none
+ * y_add_ready a hipEvent_t (as void*) that the stream waits on before the
+ *          kernel that reads y_add, or NULL (then y_add must already be
+ *          ordered before this call on `stream`)
+ * y        device, [b x d_out] bf16 (output)
+ * cu_budget upper bound on the compute units the call's kernels occupy
+ *          (grid size); 0 = the whole device
+ * Intermediates (h in bf16, the permutation) live in the workspace.
+ * Limits: 1 <= b <= 64, 1 <= k <= 32, E <= 1024, I % 32 == 0,
+ * d_in % 128 == 0, d_out % 16 == 0.
+ */
+int k3_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in,
+                   const int32_t *topk_ids, const float *topk_w, int k,
+                   const uint16_t *w13, const uint16_t *w2, int E, int I, int d_out,
+                   const float *y_add, void *y_add_ready, uint16_t *y, int cu_budget,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Shared expert (Part 1 section 3: it runs on a separate stream, beside
+ * routing or the routed experts, so it reads the layer input x).
+ *
+ *   y_s[t] = w2 . ( silu(w13[0:I] . x_t) * (w13[I:2I] . x_t) )      fp32
+ *
+ * x device, [b x d] bf16, row stride ldx;  w13 device, [2I x d] bf16;
+ * w2 device, [d x I] bf16;  y_s device, [b x d] fp32 (output).
+ * cu_budget as for k3_moe_experts. Limits: 1 <= b <= 64, I % 32 == 0,
+ * d % 128 == 0.
+ */
+int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d,
+                     const uint16_t *w13, const uint16_t *w2, int I,
+                     float *y_s, int cu_budget,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* Attention output projection with residual add and RMSNorm (Part 1
+ * section 2, "Overlap computation and communication": the output
+ * projection is fused with the attention residual that follows it).
+ *
+ *   h[t][n] = r[t][n] + sum_i a[t][i] * w_o[n][i]
+ *   y[t][n] = bf16( h[t][n] / sqrt( (1/d) sum_m h[t][m]^2 + eps ) * gamma[n] )
+ *
+ * a        device, [b x K] bf16, row stride lda (may be a column slice of a
+ *          wider projection output)
+ * w_o      device, [d x K] bf16
+ * residual device, [b x d] bf16, row stride d: read as r, overwritten with
+ *          bf16(h) (in place)
+ * gamma    device, [d] bf16
+ * y_norm   device, [b x d] bf16 (output); must not overlap residual or a
+ * The norm is taken over fp32 h, before h is rounded for the store.
+ * Limits: 1 <= b <= 64, d % 8 == 0, eps >= 0.
+ */
+int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
+                      const uint16_t *w_o, int d, uint16_t *residual,
+                      const uint16_t *gamma, float eps, uint16_t *y_norm,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/* Weight prefetch (Part 1 section 4, "Prefetching upcoming weights into
+ * cache"): reads [p, p + bytes) once, so the next operator that reads those
+ * weights finds them in the device's last-level cache (the MALL) instead of
+ * HBM. Meant for a side stream while the main stream is in a phase that
+ * leaves HBM bandwidth unused. Writes nothing the caller can observe.
+ *
+ * p device, 16-byte aligned; bytes a multiple of 16 (0 is a no-op).
+ * cu_budget as for k3_moe_experts.
+ */
+int k3_prefetch(const void *p, size_t bytes, int cu_budget, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* K3DEC_H */

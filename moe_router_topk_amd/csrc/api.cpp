@@ -1,0 +1,134 @@
+// api.cpp -- status strings, version, dispatch record, launch sizing and
+// workspace layouts of libk3dec.
+#include <atomic>
+#include <mutex>
+
+#include "k3_internal.h"
+
+namespace k3 {
+
+namespace {
+std::atomic<int> g_last_variant[8];
+std::atomic<int> g_forced_variant[8];
+std::mutex g_cu_mutex;
+int g_cu_count[64];
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (g_cu_count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        g_cu_count[dev] = n;
+    }
+    return g_cu_count[dev];
+}
+
+int budget_grid(int want, int cu_budget, int per_cu) {
+    int cus = device_cu_count();
+    if (cu_budget > 0 && cu_budget < cus)
+        cus = cu_budget;
+    long cap = (long)cus * per_cu;
+    long g = want < cap ? want : cap;
+    return g < 1 ? 1 : (int)g;
+}
+
+void record_dispatch(int op, int variant) {
+    if (op >= 0 && op < 8)
+        g_last_variant[op].store(variant);
+}
+
+int forced_variant(int op) {
+    return (op >= 0 && op < 8) ? g_forced_variant[op].load() : K3_VARIANT_NONE;
+}
+
+MoeWorkspace moe_workspace_layout(int b, int E, int k, int I) {
+    const size_t A = 256;
+    size_t P = (size_t)b * k;
+    size_t cap = P < (size_t)E ? P : (size_t)E;
+    MoeWorkspace w;
+    size_t o = 0;
+    w.n_active = o;
+    o = align_up(o + sizeof(int), A);
+    w.active_expert = o;
+    o = align_up(o + cap * sizeof(int), A);
+    w.active_start = o;
+    o = align_up(o + (cap + 1) * sizeof(int), A);
+    w.sorted_token = o;
+    o = align_up(o + P * sizeof(int), A);
+    w.sorted_w = o;
+    o = align_up(o + P * sizeof(float), A);
+    w.hbuf = o;
+    o = align_up(o + P * (size_t)I * sizeof(uint16_t), A);
+    w.total = o;
+    return w;
+}
+
+}  // namespace k3
+
+extern "C" {
+
+const char *k3_status_string(int status) {
+    switch (status) {
+    case K3_OK: return "K3_OK: success";
+    case K3_ERR_INVALID_ARG: return "K3_ERR_INVALID_ARG: NULL pointer, non-positive size or bad leading dimension";
+    case K3_ERR_UNSUPPORTED: return "K3_ERR_UNSUPPORTED: shape outside the supported range, misaligned pointer, or forced variant that cannot run the shape";
+    case K3_ERR_WORKSPACE: return "K3_ERR_WORKSPACE: workspace NULL or smaller than the size query requires";
+    case K3_ERR_HIP: return "K3_ERR_HIP: the HIP runtime reported an error at launch";
+    default: return "unknown k3 status";
+    }
+}
+
+int k3_version(void) { return 10000; }
+
+int k3_get_last_dispatch(int op) {
+    return (op >= 0 && op < 8) ? k3::g_last_variant[op].load() : K3_VARIANT_NONE;
+}
+
+int k3_force_variant(int op, int variant) {
+    if (op < 0 || op > K3_OP_PREFETCH || variant < K3_VARIANT_NONE || variant > K3_VARIANT_STREAM)
+        return K3_ERR_INVALID_ARG;
+    k3::g_forced_variant[op].store(variant);
+    return K3_OK;
+}
+
+size_t k3_router_topk_workspace_size(int b, int E) {
+    if (b <= 0 || E <= 0)
+        return 0;
+    return k3::align_up((size_t)b * E * sizeof(float), 256);
+}
+
+size_t k3_proj_skinny_workspace_size(int b, int K, int N) {
+    (void)b;
+    (void)K;
+    (void)N;
+    return 0;
+}
+
+size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I) {
+    (void)d_in;
+    if (b <= 0 || E <= 0 || k <= 0 || I <= 0)
+        return 0;
+    return k3::moe_workspace_layout(b, E, k, I).total;
+}
+
+size_t k3_shared_expert_workspace_size(int b, int d, int I) {
+    (void)d;
+    if (b <= 0 || I <= 0)
+        return 0;
+    return k3::align_up((size_t)b * I * sizeof(uint16_t), 256);
+}
+
+size_t k3_oproj_residual_workspace_size(int b, int K, int d) {
+    (void)K;
+    if (b <= 0 || d <= 0)
+        return 0;
+    return k3::align_up((size_t)b * d * sizeof(float), 256);
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// k3_internal.h -- host-side helpers shared by the libk3dec entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/k3dec.h"
+
+namespace k3 {
+
+// Compute units on the current device (cached per device).
+int device_cu_count();
+
+// Grid size for a kernel that wants `want` workgroups of 256 threads, at most
+// `per_cu` resident per compute unit, on min(cu_budget, all) compute units.
+int budget_grid(int want, int cu_budget, int per_cu);
+
+// Variant bookkeeping for k3_get_last_dispatch / k3_force_variant.
+void record_dispatch(int op, int variant);
+int forced_variant(int op);
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline int launch_status() {
+    return hipGetLastError() == hipSuccess ? K3_OK : K3_ERR_HIP;
+}
+
+// Workspace layout of k3_moe_experts (offsets in bytes, 256-byte aligned).
+struct MoeWorkspace {
+    size_t n_active, active_expert, active_start, sorted_token, sorted_w, hbuf, total;
+};
+MoeWorkspace moe_workspace_layout(int b, int E, int k, int I);
+
+}  // namespace k3

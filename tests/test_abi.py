@@ -1,0 +1,200 @@
+"""Host-side checks of the C ABI (no GPU needed): libk3dec loads, exports
+every function include/k3dec.h declares, and each entry point rejects bad
+arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "k3dec.h")
+
+K3_OK, INVALID, UNSUP, WORKSPACE = 0, -1, -2, -3
+P = 1 << 20           # a fake, 16-byte aligned address (never dereferenced)
+MIS = (1 << 20) + 8   # a fake misaligned address
+
+
+@pytest.fixture(scope="module")
+def L():
+    import moe_router_topk_amd as k3
+    return k3.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(k3_\w+)\s*\(", text)))
+
+
+def test_header_compiles_as_c():
+    src = f'#include "{HEADER}"\nint main(void) {{ return K3_OK; }}\n'
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-x", "c", "-fsyntax-only", "-"],
+                   input=src, text=True, check=True)
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 15
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    import moe_router_topk_amd as k3
+    assert set(k3.EXPORTED_SYMBOLS) == set(names)
+
+
+def test_exports_no_cxx_or_torch_types():
+    """nm: the dynamic symbols named k3_* are plain C names."""
+    import moe_router_topk_amd as k3
+    out = subprocess.run(["nm", "-D", "--defined-only", k3.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    k3_syms = [ln.split()[-1] for ln in out.splitlines() if " k3_" in ln]
+    assert k3_syms and all(re.fullmatch(r"k3_\w+", s) for s in k3_syms)
+
+
+def test_status_strings(L):
+    L.k3_status_string.restype = ctypes.c_char_p
+    for code in (0, -1, -2, -3, -4):
+        s = L.k3_status_string(code).decode()
+        assert s.startswith("K3_"), s
+    assert L.k3_status_string(-99).decode() == "unknown k3 status"
+    assert L.k3_version() == 10000
+
+
+def test_force_variant_validation(L):
+    assert L.k3_force_variant(1, 2) == K3_OK
+    assert L.k3_force_variant(1, 0) == K3_OK
+    assert L.k3_force_variant(9, 0) == INVALID
+    assert L.k3_force_variant(1, 17) == INVALID
+
+
+def test_workspace_sizes(L):
+    import moe_router_topk_amd as k3
+    assert k3.workspace_size("router_topk", b=64, E=384) >= 64 * 384 * 4
+    assert k3.workspace_size("proj_skinny", b=64, K=7168, N=12288) == 0
+    assert k3.workspace_size("moe_experts", b=64, d_in=7168, E=384, k=8, I=2048) >= 512 * 2048 * 2
+    assert k3.workspace_size("shared_expert", b=64, d=7168, I=2048) >= 64 * 2048 * 2
+    assert k3.workspace_size("oproj_residual", b=64, K=8192, d=7168) >= 64 * 7168 * 4
+    assert k3.workspace_size("router_topk", b=0, E=384) == 0
+
+
+def _router(L, **kw):
+    a = dict(x=P, ldx=256, b=1, d=256, w=P, bias=None, E=8, k=2, ids=P, wts=P, ws=P,
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    return L.k3_router_topk(a["x"], a["ldx"], a["b"], a["d"], a["w"], a["bias"], a["E"], a["k"],
+                            a["ids"], a["wts"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_router_topk_validation(L):
+    assert _router(L, x=None) == INVALID
+    assert _router(L, b=0) == INVALID
+    assert _router(L, ldx=128) == INVALID
+    assert _router(L, b=65) == UNSUP
+    assert _router(L, k=9) == UNSUP
+    assert _router(L, E=1025, k=2) == UNSUP
+    assert _router(L, k=33, E=64) == UNSUP
+    assert _router(L, d=250, ldx=256) == UNSUP
+    assert _router(L, x=MIS) == UNSUP
+    assert _router(L, ws=None) == WORKSPACE
+    assert _router(L, wsb=16) == WORKSPACE
+
+
+def _proj(L, **kw):
+    a = dict(x=P, ldx=256, b=1, K=256, w=P, N=64, y=P, ldy=64)
+    a.update(kw)
+    return L.k3_proj_skinny(a["x"], a["ldx"], a["b"], a["K"], a["w"], a["N"], a["y"], a["ldy"],
+                            None, 0, None)
+
+
+def test_proj_skinny_validation(L):
+    assert _proj(L, w=None) == INVALID
+    assert _proj(L, N=0) == INVALID
+    assert _proj(L, ldy=32) == INVALID
+    assert _proj(L, b=65) == UNSUP
+    assert _proj(L, K=252, ldx=256) == UNSUP
+    assert _proj(L, w=MIS) == UNSUP
+    # MFMA needs K % 128 == 0 above 8 tokens; dot2 stops at 8 tokens
+    assert _proj(L, b=16, K=264, ldx=264) == UNSUP
+    assert L.k3_force_variant(1, 1) == K3_OK
+    try:
+        assert _proj(L, b=9) == UNSUP
+    finally:
+        L.k3_force_variant(1, 0)
+
+
+def _moe(L, **kw):
+    a = dict(z=P, ldz=256, b=1, d_in=256, ids=P, w=P, k=2, w13=P, w2=P, E=8, I=128, d_out=256,
+             y_add=None, ev=None, y=P, cu=0, ws=P, wsb=1 << 24)
+    a.update(kw)
+    return L.k3_moe_experts(a["z"], a["ldz"], a["b"], a["d_in"], a["ids"], a["w"], a["k"],
+                            a["w13"], a["w2"], a["E"], a["I"], a["d_out"], a["y_add"], a["ev"],
+                            a["y"], a["cu"], a["ws"], a["wsb"], None)
+
+
+def test_moe_experts_validation(L):
+    assert _moe(L, y=None) == INVALID
+    assert _moe(L, cu=-1) == INVALID
+    assert _moe(L, ldz=8) == INVALID
+    assert _moe(L, b=65) == UNSUP
+    assert _moe(L, k=33) == UNSUP
+    assert _moe(L, I=96) == UNSUP
+    assert _moe(L, d_in=200, ldz=256) == UNSUP
+    assert _moe(L, d_out=250) == UNSUP
+    assert _moe(L, w2=MIS) == UNSUP
+    assert _moe(L, ws=None) == WORKSPACE
+    assert _moe(L, wsb=1024) == WORKSPACE
+
+
+def _shared(L, **kw):
+    a = dict(x=P, ldx=256, b=1, d=256, w13=P, w2=P, I=128, y=P, cu=0, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return L.k3_shared_expert(a["x"], a["ldx"], a["b"], a["d"], a["w13"], a["w2"], a["I"],
+                              a["y"], a["cu"], a["ws"], a["wsb"], None)
+
+
+def test_shared_expert_validation(L):
+    assert _shared(L, w13=None) == INVALID
+    assert _shared(L, I=0) == INVALID
+    assert _shared(L, b=65) == UNSUP
+    assert _shared(L, d=192, ldx=256) == UNSUP
+    assert _shared(L, x=MIS) == UNSUP
+    assert _shared(L, wsb=8) == WORKSPACE
+
+
+def _oproj(L, **kw):
+    a = dict(a=P, lda=512, b=1, K=256, w=P, d=256, r=P, g=P, eps=1e-6, y=P, ws=P, wsb=1 << 20)
+    a.update(kw)
+    L.k3_oproj_residual.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    return L.k3_oproj_residual(a["a"], a["lda"], a["b"], a["K"], a["w"], a["d"], a["r"], a["g"],
+                               a["eps"], a["y"], a["ws"], a["wsb"], None)
+
+
+def test_oproj_residual_validation(L):
+    assert _oproj(L, g=None) == INVALID
+    assert _oproj(L, eps=-1.0) == INVALID
+    assert _oproj(L, eps=float("nan")) == INVALID
+    assert _oproj(L, lda=128) == INVALID
+    assert _oproj(L, b=65) == UNSUP
+    assert _oproj(L, d=250) == UNSUP
+    assert _oproj(L, a=MIS) == UNSUP
+    assert _oproj(L, ws=None) == WORKSPACE
+
+
+def test_prefetch_validation(L):
+    assert L.k3_prefetch(P, 0, 0, None) == K3_OK  # nothing to read: no launch
+    assert L.k3_prefetch(None, 16, 0, None) == INVALID
+    assert L.k3_prefetch(P, 16, -1, None) == INVALID
+    assert L.k3_prefetch(MIS, 16, 0, None) == UNSUP
+    assert L.k3_prefetch(P, 24, 0, None) == UNSUP
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import moe_router_topk_amd as k3
+    monkeypatch.setattr(k3, "_lib", None)
+    monkeypatch.setattr(k3, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        k3.lib()

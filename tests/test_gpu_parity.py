@@ -1,0 +1,351 @@
+"""GPU parity: every libk3dec entry point against the oracle, on the same
+seeded bf16 inputs, at the tiny workload and at full size (d = 7168,
+E = 384, top-8, I = 2048; projection chain 7168 -> 12288, 8192 -> 7168).
+
+Bars: ids by the gap rule, outputs within 2e-2 * max|ref| (tests/_parity.py).
+Large cases compare sampled outputs (the oracle computes them one by one).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _parity import assert_rel_close, check_ids, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _lib():
+    import moe_router_topk_amd as k3
+    k3.lib()
+    return k3
+
+
+@pytest.fixture(scope="module")
+def k3():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need one")
+    return _lib()
+
+
+@pytest.fixture(scope="module")
+def full(k3):
+    """Full-size MoE weights (about 34 GB of experts) on the GPU, once."""
+    cfg = synth.MOE_CONFIGS["b1"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    torch.cuda.synchronize()
+    return cfg, w
+
+
+@pytest.fixture(scope="module")
+def chain_w(k3):
+    w = synth.make_chain_weights(synth.CHAIN_CONFIG, device=DEV)
+    torch.cuda.synchronize()
+    return w
+
+
+def _experts_on_host(w):
+    cache = {}
+
+    def fetch(e):
+        if e not in cache:
+            cache[e] = (w["w13"][e].cpu(), w["w2"][e].cpu())
+        return cache[e]
+    return fetch
+
+
+# ---------------------------------------------------------------- router + top-k
+@pytest.mark.parametrize("b,zipf", [(1, 0.0), (2, 0.0), (3, 0.0), (16, 0.0), (64, 1.1),
+                                    (64, 0.0)])
+def test_router_topk_full(k3, full, b, zipf):
+    cfg, w = full
+    bias = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
+    x = synth.make_tokens(cfg, device=DEV, index=100 + b, b=b)
+    ids, wts = k3.k3_router_topk(x, w["w_router"], bias, cfg.k)
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(x.cpu(), w["w_router"].cpu(), bias.cpu() if bias is not None else None)
+    ref_ids, ref_w = oracle.topk_softmax(logits, cfg.k)
+    differ = check_ids(ids, ref_ids, logits, cfg.k)
+    g = wts.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(g.sum(axis=1), 1.0, atol=1e-5)
+    keep = [t for t in range(b) if t not in differ]
+    assert_rel_close(g[keep], ref_w[keep], "topk_w")
+    assert (np.diff(g, axis=1) <= 1e-6).all(), "weights not in descending order"
+    want = "dot2" if b <= 8 else "mfma"
+    assert k3.k3_get_last_dispatch("router_topk") == want
+
+
+def test_router_topk_ties(k3):
+    """x = 0 makes every logit 0: ids 0..k-1 and weights 1/k."""
+    x = torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV)
+    wr = synth.uniform_bf16((8, 256), 0.1, 0, "tie", device=DEV)
+    ids, wts = k3.k3_router_topk(x, wr, None, 3)
+    torch.cuda.synchronize()
+    assert ids.cpu().tolist() == [[0, 1, 2], [0, 1, 2]]
+    np.testing.assert_allclose(wts.cpu().numpy(), 1 / 3, rtol=1e-6)
+
+
+def test_router_topk_k_equals_E(k3):
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    x = synth.make_tokens(cfg, device=DEV, b=4)
+    ids, wts = k3.k3_router_topk(x, w["w_router"], None, cfg.E)
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(x.cpu(), w["w_router"].cpu())
+    ref_ids, ref_w = oracle.topk_softmax(logits, cfg.E)
+    check_ids(ids, ref_ids, logits, cfg.E)
+    assert_rel_close(wts.cpu(), ref_w, "topk_w")
+
+
+# ---------------------------------------------------------------- skinny projection
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 8, 9, 16, 33, 64])
+def test_proj_skinny_latent(k3, full, b):
+    cfg, w = full
+    x = synth.make_tokens(cfg, device=DEV, index=200 + b, b=b)
+    y = k3.k3_proj_skinny(x, w["w_lat"])
+    torch.cuda.synchronize()
+    rows = torch.arange(0, cfg.d_lat, 7)  # sampled output columns, every 7th
+    ref = oracle.linear(x.cpu(), w["w_lat"][rows].cpu())
+    assert_rel_close(y[:, rows].cpu(), ref, "z")
+    assert k3.k3_get_last_dispatch("proj_skinny") == ("dot2" if b <= 8 else "mfma")
+
+
+@pytest.mark.parametrize("variant", ["dot2", "mfma"])
+@pytest.mark.parametrize("b,K,N", [(1, 256, 256), (2, 128, 40), (8, 1024, 1000), (7, 896, 33)])
+def test_proj_skinny_ragged(k3, variant, b, K, N):
+    """Both engines on small ragged shapes (N not a multiple of 16, few rows)."""
+    if variant == "mfma" and K % 128:
+        pytest.skip("MFMA engine needs K % 128 == 0")
+    x = synth.randn_bf16((b, K), 1.0, 7, "rag_x", K * 100 + N, device=DEV)
+    W = synth.randn_bf16((N, K), 1 / math.sqrt(K), 7, "rag_w", K * 100 + N, device=DEV)
+    k3.k3_force_variant("proj_skinny", variant)
+    try:
+        y = k3.k3_proj_skinny(x, W)
+        torch.cuda.synchronize()
+        assert k3.k3_get_last_dispatch("proj_skinny") == variant
+    finally:
+        k3.k3_force_variant("proj_skinny", "none")
+    assert_rel_close(y.cpu(), oracle.linear(x.cpu(), W.cpu()), "y")
+
+
+def test_proj_skinny_strided_output(k3, chain_w):
+    """x and y as column slices of wider buffers (row strides > width)."""
+    w = chain_w
+    xb = synth.randn_bf16((3, 7168 + 64), 1.0, 0, "strided_x", device=DEV)
+    x = xb[:, 64:]
+    yb = torch.zeros((3, 12288 + 128), dtype=torch.bfloat16, device=DEV)
+    y = yb[:, :12288]
+    k3.k3_proj_skinny(x, w["w_in"], y=y)
+    torch.cuda.synchronize()
+    rows = torch.arange(0, 12288, 11)
+    ref = oracle.linear(x.cpu(), w["w_in"][rows].cpu())
+    assert_rel_close(y[:, rows].cpu(), ref, "q")
+    assert (yb[:, 12288:] == 0).all()
+
+
+# ---------------------------------------------------------------- shared expert
+@pytest.mark.parametrize("b", [1, 2, 16, 64])
+def test_shared_expert_full(k3, full, b):
+    cfg, w = full
+    x = synth.make_tokens(cfg, device=DEV, index=300 + b, b=b)
+    y_s = k3.k3_shared_expert(x, w["w13_s"], w["w2_s"])
+    torch.cuda.synchronize()
+    ts = list(range(b)) if b <= 4 else [0, 5, b // 2, b - 1]
+    ref = oracle.shared_expert(x[ts].cpu(), w["w13_s"].cpu(), w["w2_s"].cpu())
+    assert_rel_close(y_s[ts].cpu(), ref, "y_s")
+
+
+@pytest.mark.parametrize("cu_budget", [1, 8, 32])
+def test_shared_expert_cu_budget(k3, full, cu_budget):
+    """A CU budget changes the grid, not the result bits."""
+    cfg, w = full
+    x = synth.make_tokens(cfg, device=DEV, index=77, b=3)
+    a = k3.k3_shared_expert(x, w["w13_s"], w["w2_s"]).clone()
+    bb = k3.k3_shared_expert(x, w["w13_s"], w["w2_s"], cu_budget=cu_budget)
+    torch.cuda.synchronize()
+    assert torch.equal(a, bb)
+
+
+# ---------------------------------------------------------------- routed experts
+def _routed_case(k3, cfg, w, b, zipf, index, ids_override=None):
+    bias = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
+    x = synth.make_tokens(cfg, device=DEV, index=index, b=b)
+    ids, wts = k3.k3_router_topk(x, w["w_router"], bias, cfg.k)
+    if ids_override is not None:
+        ids = ids_override
+    z = k3.k3_proj_skinny(x, w["w_lat"])
+    y_add = synth.randn_bf16((b, cfg.d), 0.05, 9, "y_add", index, device=DEV).float()
+    y = k3.k3_moe_experts(z, ids, wts, w["w13"], w["w2"], y_add=y_add)
+    torch.cuda.synchronize()
+    return x, z, ids, wts, y_add, y
+
+
+@pytest.mark.parametrize("b,zipf", [(1, 0.0), (2, 0.0), (16, 0.0), (64, 1.1)])
+def test_moe_experts_full(k3, full, b, zipf):
+    cfg, w = full
+    x, z, ids, wts, y_add, y = _routed_case(k3, cfg, w, b, zipf, 400 + b)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=cfg.E)
+    print(f"b={b} zipf={zipf}: active experts {int((counts > 0).sum())}, "
+          f"max tokens/expert {int(counts.max())}", flush=True)
+    ts = list(range(b)) if b <= 2 else sorted(set([0, 1, b // 3, b // 2, b - 2, b - 1]))
+    ref = oracle.moe_experts(z[ts].cpu(), ids[ts].cpu().numpy(), wts[ts].cpu().numpy(),
+                             _experts_on_host(w), cfg.E, y_add=y_add[ts].cpu())
+    assert_rel_close(y[ts].cpu(), ref, "y")
+    assert k3.k3_get_last_dispatch("moe_experts") == "grouped"
+
+
+def test_moe_experts_hot_expert_tiles(k3, full):
+    """All 64 tokens on the same 8 experts: four 16-token MFMA tiles each."""
+    cfg, w = full
+    b = 64
+    ids = torch.tensor([[3, 17, 42, 99, 100, 255, 300, 383]] * b, dtype=torch.int32, device=DEV)
+    ids = ids[:, torch.randperm(8, generator=torch.Generator().manual_seed(1))].contiguous()
+    x, z, _, wts, y_add, y = _routed_case(k3, cfg, w, b, 0.0, 500, ids_override=ids)
+    ts = [0, 15, 16, 31, 32, 47, 48, 63]
+    ref = oracle.moe_experts(z[ts].cpu(), ids[ts].cpu().numpy(), wts[ts].cpu().numpy(),
+                             _experts_on_host(w), cfg.E, y_add=y_add[ts].cpu())
+    assert_rel_close(y[ts].cpu(), ref, "y")
+
+
+def test_moe_experts_deterministic(k3, full):
+    cfg, w = full
+    a = _routed_case(k3, cfg, w, 16, 0.0, 600)[-1].clone()
+    bb = _routed_case(k3, cfg, w, 16, 0.0, 600)[-1]
+    assert torch.equal(a, bb)
+
+
+def test_moe_experts_invalid_ids_dropped(k3):
+    """Ids outside [0, E) contribute nothing (and read no memory)."""
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    x = synth.make_tokens(cfg, device=DEV, b=2)
+    z = k3.k3_proj_skinny(x, w["w_lat"])
+    ids = torch.tensor([[1, -1], [8, 5]], dtype=torch.int32, device=DEV)
+    wts = torch.tensor([[0.5, 0.5], [0.25, 0.75]], dtype=torch.float32, device=DEV)
+    y = k3.k3_moe_experts(z, ids, wts, w["w13"], w["w2"])
+    torch.cuda.synchronize()
+    ref = oracle.moe_experts(z.cpu(), np.array([[1, 1], [5, 5]], np.int32),
+                             np.array([[0.5, 0.0], [0.0, 0.75]]), _experts_on_host(w), cfg.E)
+    assert_rel_close(y.cpu(), ref, "y")
+
+
+# ---------------------------------------------------------------- o-proj + residual + norm
+@pytest.mark.parametrize("b", [1, 2, 3, 8, 16, 64])
+def test_oproj_residual_full(k3, chain_w, b):
+    w = chain_w
+    cc = synth.CHAIN_CONFIG
+    a_full = synth.randn_bf16((b, cc.n_in), 1.0, 0, "oproj_a", b, device=DEV)
+    a = a_full[:, :cc.k_o]
+    r = synth.randn_bf16((b, cc.d), 1.0, 0, "oproj_r", b, device=DEV)
+    r_in = r.clone()
+    y = k3.k3_oproj_residual(a, w["w_o"], r, w["gamma"], cc.eps)
+    torch.cuda.synchronize()
+    ts = list(range(b)) if b <= 4 else [0, b // 2, b - 1]
+    h_ref, y_ref = oracle.oproj_residual_rmsnorm(a[ts].cpu(), w["w_o"].cpu(), r_in[ts].cpu(),
+                                                 w["gamma"].cpu(), cc.eps)
+    assert_rel_close(r[ts].cpu(), h_ref, "h")
+    assert_rel_close(y[ts].cpu(), y_ref, "y_norm")
+
+
+def test_oproj_residual_identity_norm(k3):
+    """W_o = 0: h = r bit for bit, and y = RMSNorm(r) * gamma."""
+    d, K = 256, 128
+    a = synth.randn_bf16((3, K), 1.0, 1, "idn_a", device=DEV)
+    wo = torch.zeros((d, K), dtype=torch.bfloat16, device=DEV)
+    r = synth.randn_bf16((3, d), 1.0, 1, "idn_r", device=DEV)
+    g = synth.randn_bf16((d,), 0.1, 1, "idn_g", device=DEV) + 1
+    r0 = r.clone()
+    y = k3.k3_oproj_residual(a, wo, r, g.to(torch.bfloat16), 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(r, r0)
+    _, yr = oracle.oproj_residual_rmsnorm(a.cpu(), wo.cpu(), r0.cpu(), g.to(torch.bfloat16).cpu(),
+                                          1e-6)
+    assert_rel_close(y.cpu(), yr, "y_norm")
+
+
+# ---------------------------------------------------------------- prefetch
+def test_prefetch_reads_only(k3):
+    t = synth.randn_bf16((1 << 20,), 1.0, 0, "pf", device=DEV)
+    t0 = t.clone()
+    k3.k3_prefetch(t, cu_budget=16)
+    k3.k3_prefetch(t, nbytes=16)
+    k3.k3_prefetch(t, nbytes=0)
+    torch.cuda.synchronize()
+    assert torch.equal(t, t0)
+    assert k3.k3_get_last_dispatch("prefetch") == "stream"
+
+
+# ---------------------------------------------------------------- whole block / layer
+def test_tiny_layer_end_to_end(k3):
+    from moe_router_topk_amd.layer import DecodeLayer
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    layer = DecodeLayer(w, cfg.k, b_max=4)
+    for b in (1, 4):
+        x = synth.make_tokens(cfg, device=DEV, index=b, b=b)
+        y = layer.moe_block(x)
+        torch.cuda.synchronize()
+        wc = {key: (v.cpu() if v is not None else None) for key, v in w.items()}
+        ref = oracle.moe_block(x.cpu(), wc, cfg.k)
+        check_ids(layer.ids[:b], ref["ids"], ref["logits"], cfg.k)
+        assert_rel_close(layer.z[:b].cpu(), ref["z"], "z")
+        assert_rel_close(layer.y_s[:b].cpu(), ref["y_s"], "y_s")
+        assert_rel_close(y.cpu(), ref["y"], "y")
+
+
+@pytest.mark.parametrize("b,zipf", [(1, 0.0), (64, 1.1)])
+def test_moe_block_end_to_end_full(k3, full, b, zipf):
+    """The block as the benchmark runs it (two streams), against the oracle
+    carrying fp64 intermediates; sampled tokens."""
+    from moe_router_topk_amd.layer import DecodeLayer
+    cfg, w = full
+    w = dict(w)
+    w["bias"] = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
+    layer = DecodeLayer(w, cfg.k, b_max=b)
+    x = synth.make_tokens(cfg, device=DEV, index=700 + b, b=b)
+    y = layer.moe_block(x)
+    torch.cuda.synchronize()
+    ts = [0] if b == 1 else [0, 21, 42, 63]
+    xs = x[ts].cpu()
+    logits = oracle.router_logits(xs, w["w_router"].cpu(), w["bias"].cpu() if zipf else None)
+    ref_ids, ref_w = oracle.topk_softmax(logits, cfg.k)
+    differ = check_ids(layer.ids[ts], ref_ids, logits, cfg.k)
+    for i in differ:  # tie band: continue from the GPU's selection
+        g = layer.ids[ts[i]].cpu().numpy()
+        l = logits[i][g].astype(np.float64)
+        p = np.exp(l - l.max())
+        ref_ids[i], ref_w[i] = g, p / p.sum()
+    z = oracle.linear(xs, w["w_lat"].cpu())
+    y_s = oracle.shared_expert(xs, w["w13_s"].cpu(), w["w2_s"].cpu())
+    ref = oracle.moe_experts(z, ref_ids, ref_w, _experts_on_host(w), cfg.E, y_add=y_s)
+    assert_rel_close(y[ts].cpu(), ref, "y")
+
+
+def test_layer_step_chain_then_moe(k3, full, chain_w):
+    """Chain + MoE block at b = 1, the benchmark's step, against the oracle."""
+    from moe_router_topk_amd.layer import DecodeLayer
+    cfg, w = full
+    layer = DecodeLayer(w, cfg.k, b_max=1, chain=chain_w)
+    inp = synth.make_chain_inputs(synth.CHAIN_CONFIG, 1, device=DEV)
+    r0 = inp["r"].clone()
+    y = layer.step(inp["x"], inp["r"], prefetch=True)
+    torch.cuda.synchronize()
+    c = oracle.chain(inp["x"].cpu(), r0.cpu(), chain_w["w_in"].cpu(), chain_w["w_o"].cpu(),
+                     chain_w["gamma"].cpu(), 1e-6)
+    assert_rel_close(layer.x_moe[:1].cpu(), c["y"], "x_moe")
+    # the MoE block continues from the bf16 hidden state the GPU produced
+    wc = {key: w[key].cpu() for key in ("w_router", "w_lat", "w13_s", "w2_s")}
+    wc["bias"] = None
+    xm = layer.x_moe[:1].cpu()
+    logits = oracle.router_logits(xm, wc["w_router"])
+    ids, wt = oracle.topk_softmax(logits, cfg.k)
+    check_ids(layer.ids[:1], ids, logits, cfg.k)
+    z = oracle.linear(xm, wc["w_lat"])
+    y_s = oracle.shared_expert(xm, wc["w13_s"], wc["w2_s"])
+    ref = oracle.moe_experts(z, ids, wt, _experts_on_host(w), cfg.E, y_add=y_s)
+    assert_rel_close(y.cpu(), ref, "y")
