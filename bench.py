@@ -1,0 +1,424 @@
+#!/usr/bin/env python3
+"""Decode-layer benchmark on one MI355X: us per layer step and achieved HBM GB/s.
+
+A step is one pass of the whole hot path over one batch of synthetic tokens
+(b = 1 by default, d = 7168): attention input projection 7168 -> 12288,
+output projection 8192 -> 7168 with residual add and RMSNorm, router scores
+over E = 384 experts with top-8 renormalised softmax, latent projection
+7168 -> 7168, the 8 routed SwiGLU experts (I = 2048) behind the token
+permutation, the shared expert on a second stream, and the side-stream
+prefetch. Weights are bf16, synthetic and seeded; they and the inputs are
+resident in HBM before timing starts.
+
+Cold-cache discipline: steps rotate over --layers independent copies of the
+layer's weights (about 35 GB each) and a pool of 16 token batches, so no
+weight a step reads is still in the 256 MB MALL from an earlier step.
+
+Timing: W eager warm-up steps, then a pass of K eager steps with an event
+after each step and trace events around every launch of the dominant kernel
+(the routed gate/up kernel, on the stream it runs on) for its average
+duration; then the timed region proper: exactly K steps captured in one HIP
+graph and replayed once, between events on the replay stream, synchronised on
+both sides. ROCm does not allow timing events inside a captured graph, which
+is why the kernel is timed in the eager pass.
+
+Value = algorithmic bytes per step / time per step (weights touched once plus
+activations in and out), in GB/s; peak = 8 TB/s (MI355X HBM3E).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_expert_gateup_b1_traffic.json")
+DOMINANT_SOURCES = ["moe_router_topk_amd/csrc/experts.hip", "moe_router_topk_amd/csrc/k3_device.h"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ byte accounting
+def moe_bytes(cfg, b: int, n_active: int) -> int:
+    """Algorithmic bytes of one MoE block pass: each weight once, plus the
+    activations each kernel boundary hands over (written once, read once)."""
+    d, E, I, Is, dl, k = cfg.d, cfg.E, cfg.I, cfg.I_s, cfg.d_lat, cfg.k
+    weights = 2 * (E * d + dl * d + 3 * Is * d + n_active * (2 * I * dl + d * I))
+    if cfg.zipf_bias:
+        weights += 4 * E
+    acts = (2 * b * d                      # x
+            + 2 * (4 * b * E)              # logits out and in
+            + 2 * (8 * b * k)              # ids + weights out and in
+            + 2 * (2 * b * dl)             # z out and in
+            + 2 * (2 * b * k * I)          # routed h out and in
+            + 2 * (2 * b * Is)             # shared h out and in
+            + 2 * (4 * b * d)              # y_s out and in
+            + 2 * b * d)                   # y out
+    return weights + acts
+
+
+def chain_bytes(cc, b: int) -> int:
+    weights = 2 * (cc.n_in * cc.d + cc.d * cc.k_o + cc.d)
+    acts = (2 * b * cc.d                   # x
+            + 2 * b * cc.n_in + 2 * b * cc.k_o   # q out, a in
+            + 2 * (2 * b * cc.d)           # residual in and out
+            + 2 * (4 * b * cc.d)           # fp32 h out and in
+            + 2 * b * cc.d)                # normalised hidden state out
+    return weights + acts
+
+
+def gateup_bytes(cfg, b: int, n_active: int) -> int:
+    """Per launch of the routed gate/up kernel: n_active experts' [2I x d]
+    weights, the z rows it reads and the h rows it writes."""
+    return 2 * n_active * 2 * cfg.I * cfg.d_lat + 2 * b * cfg.d_lat + 2 * b * cfg.k * cfg.I
+
+
+def sources_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when it is missing or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sources_digest(DOMINANT_SOURCES):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ timing helpers
+def capture(torch, fn, n: int):
+    """Capture fn(i) for i < n into one graph."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_timed(torch, g, n: int):
+    """One replay of an n-step graph between events on the replay stream,
+    synchronised on both sides: (ms per step, wall seconds)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n, time.perf_counter() - t0
+
+
+def eager_timed(torch, k3, fn, n: int):
+    """n host-launched steps with an event after each and the routed gate/up
+    kernel bracketed by trace events: (ms per step, per-step ms sorted,
+    gate/up ms per launch)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    kb = [k3.HipEvent() for _ in range(n)]
+    ke = [k3.HipEvent() for _ in range(n)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    try:
+        for i in range(n):
+            k3.k3_trace_events("moe_experts", kb[i], ke[i])
+            fn(i)
+            ev[i + 1].record()
+    finally:
+        k3.k3_trace_events("moe_experts", None, None)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    kern = [kb[i].elapsed_ms(ke[i]) for i in range(n)]
+    return ev[0].elapsed_time(ev[n]) / n, per, kern
+
+
+def pct(v, q):
+    return v[min(len(v) - 1, int(q * len(v)))]
+
+
+# ------------------------------------------------------------------ main
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=2, help="weight copies rotated per step")
+    ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--cu-shared", type=int, default=0, help="CU budget of the shared expert")
+    ap.add_argument("--prefetch-cu", type=int, default=32, help="CU budget of the prefetch")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the b = 1..64 sweep")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; there is no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        return 2
+    if not 1 <= args.steps <= 2000:
+        print("bench.py: --steps must be in 1..2000", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    import moe_router_topk_amd as k3
+    from moe_router_topk_amd.layer import DecodeLayer
+
+    k3.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_mb} MiB x3")
+        return 0
+
+    cfg = synth.MOE_CONFIGS["b1"]
+    cc = synth.CHAIN_CONFIG
+    b = args.batch
+    t_gen = time.perf_counter()
+    layers = []
+    for li in range(args.layers):
+        mw = synth.make_moe_weights(cfg, device=dev, layer=li)
+        cw = synth.make_chain_weights(cc, device=dev, layer=li)
+        layers.append(DecodeLayer(mw, cfg.k, b_max=64, chain=cw, eps=cc.eps,
+                                  cu_shared=args.cu_shared, prefetch_cu=args.prefetch_cu))
+        log(f"layer {li}: weights generated")
+    NX = 16
+    pool = [synth.make_chain_inputs(cc, 64, device=dev, index=i) for i in range(NX)]
+    torch.cuda.synchronize()
+    log(f"weights + inputs ready in {time.perf_counter() - t_gen:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    prefetch = not args.no_prefetch
+
+    def step(i, bb=b):
+        lay = layers[i % len(layers)]
+        inp = pool[i % NX]
+        return lay.step(inp["x"][:bb], inp["r"][:bb], prefetch=prefetch)
+
+    # ---- warm-up (eager) and routing statistics
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n_act = []
+    for i in range(NX):
+        step(i)
+        ids = layers[i % len(layers)].ids[:b]
+        n_act.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+    log(f"warm-up done; distinct experts per step: {sorted(set(n_act))}")
+
+    # ---- eager pass: per-step events and the dominant kernel's launches
+    K = args.steps
+    eager_ms, per, kern_ms = eager_timed(torch, k3, step, K)
+    kern_avg = sum(kern_ms) / K
+
+    # ---- timed region: exactly K steps in one graph, one replay
+    g = capture(torch, step, K)
+    ms, wall = replay_timed(torch, g, K)
+    del g
+    mean_act = sum(n_act[i % NX] for i in range(K)) / K
+    bytes_step = moe_bytes(cfg, b, mean_act) + chain_bytes(cc, b)
+    gbs = bytes_step / (ms * 1e-3) / 1e9
+    log(f"layer step b={b}: {ms * 1e3:.1f} us/step in the graph, {gbs:.0f} GB/s "
+        f"({100 * gbs / PEAK_GBS:.1f}% of peak); eager {eager_ms * 1e3:.1f} us/step "
+        f"(median {pct(per, 0.5) * 1e3:.1f}, p90 {pct(per, 0.9) * 1e3:.1f}); "
+        f"wall {wall * 1e3:.1f} ms for {K} steps")
+    gu_bytes = gateup_bytes(cfg, b, mean_act)
+    gu_gbs = gu_bytes / (kern_avg * 1e-3) / 1e9
+    log(f"routed gate/up kernel: {kern_avg * 1e3:.1f} us avg over {K} launches, "
+        f"{gu_gbs:.0f} GB/s")
+
+    # ---- MoE block alone (the block the 70%-of-peak target names)
+    def block(i, bb=b):
+        lay = layers[i % len(layers)]
+        return lay.moe_block(pool[i % NX]["x"][:bb])
+
+    for i in range(4):
+        block(i)
+    g = capture(torch, block, K)
+    moe_ms, _ = replay_timed(torch, g, K)
+    del g
+    moe_gbs = moe_bytes(cfg, b, mean_act) / (moe_ms * 1e-3) / 1e9
+    log(f"MoE block b={b}: {moe_ms * 1e3:.1f} us, {moe_gbs:.0f} GB/s "
+        f"({100 * moe_gbs / PEAK_GBS:.1f}% of peak)")
+
+    extra = {"moe_block_us": round(moe_ms * 1e3, 2), "moe_block_GBps": round(moe_gbs, 1),
+             "moe_block_frac_of_peak": round(moe_gbs / PEAK_GBS, 4),
+             "eager_step_us": round(eager_ms * 1e3, 2),
+             "eager_step_us_median": round(pct(per, 0.5) * 1e3, 2),
+             "eager_step_us_p10": round(pct(per, 0.1) * 1e3, 2),
+             "eager_step_us_p90": round(pct(per, 0.9) * 1e3, 2),
+             "bytes_per_step": int(bytes_step), "n_active_mean": mean_act}
+
+    # ---- sweep: MoE block at b = 16 (uniform) and 64 (Zipf bias); chain b = 1..64
+    if not args.no_sweep:
+        sweep = []
+        S = 40
+        bias = synth.zipf_router_bias(cfg.E, 1.1, cfg.seed).to(dev)
+        for bb, zipf in ((16, False), (64, True)):
+            for lay in layers:
+                lay.moe["bias"] = bias if zipf else None
+            acts = []
+            for i in range(NX):
+                block(i, bb)
+                acts.append(int(torch.unique(layers[i % len(layers)].ids[:bb]).numel()))
+            g = capture(torch, lambda i: block(i, bb), S)
+            ts, _ = replay_timed(torch, g, S)
+            del g
+            us = ts * 1e3
+            na = sum(acts[i % NX] for i in range(S)) / S
+            by = moe_bytes(synth.MOE_CONFIGS["b64zipf" if zipf else "b16"], bb, na)
+            sweep.append({"what": "moe_block", "b": bb, "routing": "zipf1.1" if zipf else "uniform",
+                          "us": round(us, 1), "n_active_mean": na,
+                          "GBps": round(by / us / 1e3, 1),
+                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)})
+            log(f"MoE block b={bb} {'zipf' if zipf else 'uniform'}: {us:.1f} us, "
+                f"n_active {na:.1f}, {by / us / 1e3:.0f} GB/s")
+        for lay in layers:
+            lay.moe["bias"] = None
+
+        def chain(i, bb):
+            lay = layers[i % len(layers)]
+            inp = pool[i % NX]
+            return lay.attn_chain(inp["x"][:bb], inp["r"][:bb])
+
+        for bb in synth.CHAIN_BATCHES:
+            chain(0, bb)
+            g = capture(torch, lambda i: chain(i, bb), S)
+            ts, _ = replay_timed(torch, g, S)
+            del g
+            us = ts * 1e3
+            by = chain_bytes(cc, bb)
+            sweep.append({"what": "chain", "b": bb, "us": round(us, 1),
+                          "GBps": round(by / us / 1e3, 1),
+                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)})
+            log(f"chain b={bb}: {us:.1f} us, {by / us / 1e3:.0f} GB/s")
+        extra["sweep"] = sweep
+
+    # ---- CPU baseline: the oracle, timed on this host's cores
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, layers[0], cfg, cc, pool, b, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE decode layer us/step and achieved HBM GB/s (% of peak), batch 1-64",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "frac_of_peak": round(gbs / PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 weights and tokens, rotated over "
+                f"{args.layers} weight copies and {NX} token batches)",
+        "config": {
+            "workload": ("decode layer step at batch 1: attention in-proj 7168->12288, "
+                         "o-proj 8192->7168 + residual + RMSNorm, router E=384 top-8 "
+                         "renormalised softmax, latent 7168->7168, 8 routed + 1 shared "
+                         "SwiGLU experts I=2048 (gate/up [4096x7168], down [7168x2048]), "
+                         "side-stream prefetch"),
+            "batch": b, "d": cfg.d, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
+            "prefetch": prefetch, "hip_graph": True, "layers_rotated": args.layers,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_expert_gateup (routed gate/up + SwiGLU)",
+            "achieved": round(gu_gbs, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / PEAK_GBS, 4),
+            "traffic": traffic_per_launch(),
+            "bytes_per_launch": int(gu_bytes),
+            "avg_launch_us": round(kern_avg * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(torch, layer, cfg, cc, pool, b, seconds):
+    """Time the oracle (plain fp64 C, all host cores) on whole layer steps at
+    batch b, as many as fit in about `seconds` (at least one)."""
+    import numpy as np
+
+    import oracle
+
+    L = oracle.lib()
+    threads = oracle.threads()
+    host = {k: (v.cpu() if v is not None else None) for k, v in layer.moe.items()
+            if k not in ("w13", "w2")}
+    ch = {k: v.cpu() for k, v in layer.chain_w.items()}
+    experts = {}
+
+    def fetch(e):
+        if e not in experts:
+            experts[e] = (layer.moe["w13"][e].cpu(), layer.moe["w2"][e].cpu())
+        return experts[e]
+
+    done, spent, i, nbytes = 0, 0.0, 0, 0
+    while done < 50 and (done == 0 or spent < seconds):
+        inp = pool[i % len(pool)]
+        x, r = inp["x"][:b].cpu(), inp["r"][:b].cpu()
+        # host copies of what this step reads (outside the timed part)
+        hm = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)["y"]
+        ids, _ = oracle.topk_softmax(oracle.router_logits(hm, host["w_router"]), cfg.k)
+        for e in np.unique(ids):
+            fetch(int(e))
+        t0 = time.perf_counter()
+        c = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)
+        oracle.moe_block(c["y"], host, cfg.k, expert_weights=fetch)
+        dt = time.perf_counter() - t0
+        nbytes += moe_bytes(cfg, b, len(np.unique(ids))) + chain_bytes(cc, b)
+        spent += dt
+        done += 1
+        i += 1
+    sec = spent / done
+    log(f"oracle: {done} steps, {sec * 1e3:.1f} ms/step on {threads} threads")
+    del L
+    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "ms_per_step": round(sec * 1e3, 2),
+            "sample": f"{done} whole layer steps at batch {b} (chain + MoE block, "
+                      f"{cfg.k} routed experts each), fp64 C oracle with OpenMP"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

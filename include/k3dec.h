@@ -88,6 +88,17 @@ int k3_get_last_dispatch(int op);
  * K3_ERR_UNSUPPORTED. For tests and measurements only. */
 int k3_force_variant(int op, int variant);
 
+/* Tracing: while set, every call of `op` records `begin` (a hipEvent_t as
+ * void*) on its stream right before the op's main kernel and `end` right
+ * after it -- k3_moe_experts: the grouped gate/up kernel; k3_shared_expert:
+ * its gate/up kernel; k3_router_topk: the logits kernel; the others: their
+ * only or first kernel. NULL events clear the hook. The records are plain
+ * hipEventRecord calls, so they time eager calls; inside a stream capture
+ * they only mark capture dependencies (ROCm rejects external event nodes).
+ * Process-wide state, for measurement only; not safe against concurrent
+ * calls of the same op. */
+int k3_trace_events(int op, void *begin, void *end);
+
 /* ------------------------------------------------------------ workspace sizes
  * Bytes of device workspace each entry point needs for the given shape.
  * The workspace is caller-owned scratch with no state kept between calls;

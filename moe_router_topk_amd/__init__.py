@@ -18,6 +18,7 @@ __all__ = [
     "K3Error", "lib", "library_path",
     "k3_router_topk", "k3_proj_skinny", "k3_moe_experts", "k3_shared_expert",
     "k3_oproj_residual", "k3_prefetch", "k3_get_last_dispatch", "k3_force_variant",
+    "k3_trace_events", "HipEvent",
     "k3_status_string", "k3_version", "workspace_size",
     "OP", "VARIANT", "EXPORTED_SYMBOLS",
 ]
@@ -33,7 +34,7 @@ VARIANT_NAME = {v: k for k, v in VARIANT.items()}
 
 EXPORTED_SYMBOLS = [
     "k3_status_string", "k3_version", "k3_get_last_dispatch", "k3_force_variant",
-    "k3_router_topk_workspace_size", "k3_proj_skinny_workspace_size",
+    "k3_trace_events", "k3_router_topk_workspace_size", "k3_proj_skinny_workspace_size",
     "k3_moe_experts_workspace_size", "k3_shared_expert_workspace_size",
     "k3_oproj_residual_workspace_size",
     "k3_router_topk", "k3_proj_skinny", "k3_moe_experts", "k3_shared_expert",
@@ -75,6 +76,8 @@ def lib():
     L.k3_get_last_dispatch.restype = _i32
     L.k3_force_variant.argtypes = [_i32, _i32]
     L.k3_force_variant.restype = _i32
+    L.k3_trace_events.argtypes = [_i32, _vp, _vp]
+    L.k3_trace_events.restype = _i32
     L.k3_router_topk_workspace_size.argtypes = [_i32, _i32]
     L.k3_proj_skinny_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_moe_experts_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
@@ -118,6 +121,51 @@ def k3_force_variant(op, variant) -> None:
     o = OP[op] if isinstance(op, str) else op
     v = VARIANT[variant] if isinstance(variant, str) else variant
     _check("k3_force_variant", lib().k3_force_variant(o, v))
+
+
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        _hip.hipEventDestroy.argtypes = [_vp]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+    return _hip
+
+
+class HipEvent:
+    """A raw hipEvent_t with timing enabled, for k3_trace_events (torch only
+    times events it recorded itself)."""
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        rc = _hiprt().hipEventCreate(ctypes.byref(self.handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        rc = _hiprt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipEventDestroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+
+def k3_trace_events(op, begin, end) -> None:
+    """Record the HipEvent pair (begin, end) around the main kernel of every
+    following call of `op`; (None, None) clears."""
+    o = OP[op] if isinstance(op, str) else op
+    b = None if begin is None else begin.handle
+    e = None if end is None else end.handle
+    _check("k3_trace_events", lib().k3_trace_events(o, b, e))
 
 
 def _check(fn: str, status: int) -> None:

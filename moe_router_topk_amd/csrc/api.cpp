@@ -10,6 +10,8 @@ namespace k3 {
 namespace {
 std::atomic<int> g_last_variant[8];
 std::atomic<int> g_forced_variant[8];
+std::atomic<void *> g_trace_begin[8];
+std::atomic<void *> g_trace_end[8];
 std::mutex g_cu_mutex;
 int g_cu_count[64];
 }  // namespace
@@ -41,6 +43,18 @@ int budget_grid(int want, int cu_budget, int per_cu) {
 void record_dispatch(int op, int variant) {
     if (op >= 0 && op < 8)
         g_last_variant[op].store(variant);
+}
+
+void trace_begin(int op, hipStream_t s) {
+    void *ev = g_trace_begin[op].load();
+    if (ev)
+        (void)hipEventRecord((hipEvent_t)ev, s);
+}
+
+void trace_end(int op, hipStream_t s) {
+    void *ev = g_trace_end[op].load();
+    if (ev)
+        (void)hipEventRecord((hipEvent_t)ev, s);
 }
 
 int forced_variant(int op) {
@@ -94,6 +108,14 @@ int k3_force_variant(int op, int variant) {
     if (op < 0 || op > K3_OP_PREFETCH || variant < K3_VARIANT_NONE || variant > K3_VARIANT_STREAM)
         return K3_ERR_INVALID_ARG;
     k3::g_forced_variant[op].store(variant);
+    return K3_OK;
+}
+
+int k3_trace_events(int op, void *begin, void *end) {
+    if (op < 0 || op > K3_OP_PREFETCH || (!begin) != (!end))
+        return K3_ERR_INVALID_ARG;
+    k3::g_trace_begin[op].store(begin);
+    k3::g_trace_end[op].store(end);
     return K3_OK;
 }
 

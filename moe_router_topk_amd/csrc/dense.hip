@@ -351,7 +351,10 @@ extern "C" int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K, cons
     const int variant = pick_dense_variant(K3_OP_PROJ_SKINNY, b, K);
     if (variant < 0)
         return K3_ERR_UNSUPPORTED;
-    launch_dense(variant, x, ldx, b, w, N, K, EpiBf16{y, ldy}, 0, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    trace_begin(K3_OP_PROJ_SKINNY, s);
+    launch_dense(variant, x, ldx, b, w, N, K, EpiBf16{y, ldy}, 0, s);
+    trace_end(K3_OP_PROJ_SKINNY, s);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_PROJ_SKINNY, variant);
@@ -376,7 +379,9 @@ extern "C" int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     float *logits = (float *)workspace;
+    trace_begin(K3_OP_ROUTER_TOPK, s);
     launch_dense(variant, x, ldx, b, w_router, E, d, EpiLogits{logits, E, bias}, 0, s);
+    trace_end(K3_OP_ROUTER_TOPK, s);
     k_topk_softmax<<<b, kWave, 0, s>>>(logits, E, k, topk_ids, topk_w);
     const int st = launch_status();
     if (st == K3_OK)
@@ -401,7 +406,9 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     float *h32 = (float *)workspace;
+    trace_begin(K3_OP_OPROJ_RESIDUAL, s);
     launch_dense(variant, a, lda, b, w_o, d, K, EpiResidual{residual, h32, d}, 0, s);
+    trace_end(K3_OP_OPROJ_RESIDUAL, s);
     k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     const int st = launch_status();
     if (st == K3_OK)

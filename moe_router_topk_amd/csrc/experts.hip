@@ -355,7 +355,9 @@ extern "C" int k3_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in,
                                        (float *)(ws + L.sorted_w));
     const int max_active = b * k < E ? b * k : E;
     const int g1 = budget_grid(max_active * (I / 16), cu_budget, 4);
+    trace_begin(K3_OP_MOE_EXPERTS, s);
     k_expert_gateup<8, Routed><<<g1, kBlock, 0, s>>>(z, ldz, d_in, w13, I, rt, hbuf);
+    trace_end(K3_OP_MOE_EXPERTS, s);
     if (y_add_ready && hipStreamWaitEvent(s, (hipEvent_t)y_add_ready, 0) != hipSuccess)
         return K3_ERR_HIP;
     const int g2 = budget_grid(d_out / 16, cu_budget, 2);
@@ -386,7 +388,9 @@ extern "C" int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d, co
     uint16_t *hbuf = (uint16_t *)workspace;
     Dense rt{b};
     const int g1 = budget_grid(I / 16, cu_budget, 4);
+    trace_begin(K3_OP_SHARED_EXPERT, s);
     k_expert_gateup<8, Dense><<<g1, kBlock, 0, s>>>(x, ldx, d, w13, I, rt, hbuf);
+    trace_end(K3_OP_SHARED_EXPERT, s);
     const int g2 = budget_grid(d / 16, cu_budget, 2);
     k_expert_down<16, Dense, OutF32><<<g2, kBlock, 0, s>>>(hbuf, I, w2, d, rt, b, OutF32{y_s, d});
     const int st = launch_status();

@@ -17,6 +17,10 @@ int budget_grid(int want, int cu_budget, int per_cu);
 
 // Variant bookkeeping for k3_get_last_dispatch / k3_force_variant.
 void record_dispatch(int op, int variant);
+
+// Event pair of k3_trace_events, recorded around an op's main kernel.
+void trace_begin(int op, hipStream_t s);
+void trace_end(int op, hipStream_t s);
 int forced_variant(int op);
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }

@@ -56,7 +56,10 @@ extern "C" int k3_prefetch(const void *p, size_t bytes, int cu_budget, void *str
     const size_t per_block = (size_t)kBlock * 8;
     const size_t want = (n + per_block - 1) / per_block;
     const int grid = budget_grid(want > (1u << 30) ? (1 << 30) : (int)want, cu_budget, 1);
-    k_prefetch<8><<<grid, kBlock, 0, (hipStream_t)stream>>>((const u32x4 *)p, n, 0x9e3779b9u);
+    hipStream_t s = (hipStream_t)stream;
+    trace_begin(K3_OP_PREFETCH, s);
+    k_prefetch<8><<<grid, kBlock, 0, s>>>((const u32x4 *)p, n, 0x9e3779b9u);
+    trace_end(K3_OP_PREFETCH, s);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_PREFETCH, K3_VARIANT_STREAM);
