@@ -171,6 +171,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="time host-launched steps only (no graph, sweep or CPU leg); "
+                         "for profiler counter runs")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -245,9 +248,13 @@ def main() -> int:
     kern_avg = sum(kern_ms) / K
 
     # ---- timed region: exactly K steps in one graph, one replay
-    g = capture(torch, step, K)
-    ms, wall = replay_timed(torch, g, K)
-    del g
+    if args.eager_only:
+        ms, wall = eager_ms, float("nan")
+        args.no_sweep = args.no_cpu_baseline = True
+    else:
+        g = capture(torch, step, K)
+        ms, wall = replay_timed(torch, g, K)
+        del g
     mean_act = sum(n_act[i % NX] for i in range(K)) / K
     bytes_step = moe_bytes(cfg, b, mean_act) + chain_bytes(cc, b)
     gbs = bytes_step / (ms * 1e-3) / 1e9
@@ -267,9 +274,12 @@ def main() -> int:
 
     for i in range(4):
         block(i)
-    g = capture(torch, block, K)
-    moe_ms, _ = replay_timed(torch, g, K)
-    del g
+    if args.eager_only:
+        moe_ms = eager_timed(torch, k3, block, K)[0]
+    else:
+        g = capture(torch, block, K)
+        moe_ms, _ = replay_timed(torch, g, K)
+        del g
     moe_gbs = moe_bytes(cfg, b, mean_act) / (moe_ms * 1e-3) / 1e9
     log(f"MoE block b={b}: {moe_ms * 1e3:.1f} us, {moe_gbs:.0f} GB/s "
         f"({100 * moe_gbs / PEAK_GBS:.1f}% of peak)")
@@ -355,7 +365,8 @@ def main() -> int:
                          "SwiGLU experts I=2048 (gate/up [4096x7168], down [7168x2048]), "
                          "side-stream prefetch"),
             "batch": b, "d": cfg.d, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
-            "prefetch": prefetch, "hip_graph": True, "layers_rotated": args.layers,
+            "prefetch": prefetch, "hip_graph": not args.eager_only,
+            "layers_rotated": args.layers,
         },
         "roofline": {
             "bound": "hbm",

@@ -100,13 +100,18 @@ int k3_force_variant(int op, int variant);
 int k3_trace_events(int op, void *begin, void *end);
 
 /* ------------------------------------------------------------ workspace sizes
- * Bytes of device workspace each entry point needs for the given shape.
- * The workspace is caller-owned scratch with no state kept between calls;
- * its contents need no initialisation.
+ * Bytes of device workspace each entry point needs for the given shape
+ * (16-byte aligned, caller-owned). k3_router_topk and k3_oproj_residual keep
+ * a completion counter in the first 4 bytes of theirs: that workspace must
+ * be zero-filled once before its first use, and every call leaves the
+ * counter at zero again (whatever the shape, so one workspace can serve
+ * calls of different shapes of the same entry point, one at a time).
+ * The other workspaces need no initialisation. A workspace serves one call
+ * at a time: calls that may overlap need workspaces of their own.
  */
 size_t k3_router_topk_workspace_size(int b, int E);
 size_t k3_proj_skinny_workspace_size(int b, int K, int N);
-size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I);
+size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I, int d_out);
 size_t k3_shared_expert_workspace_size(int b, int d, int I);
 size_t k3_oproj_residual_workspace_size(int b, int K, int d);
 
@@ -129,7 +134,8 @@ size_t k3_oproj_residual_workspace_size(int b, int K, int d);
  * bias     device, [E] fp32, or NULL for none
  * topk_ids device, [b x k] int32 (output)
  * topk_w   device, [b x k] fp32 (output)
- * workspace device, >= k3_router_topk_workspace_size(b, E) bytes
+ * workspace device, >= k3_router_topk_workspace_size(b, E) bytes,
+ *          zero-filled before first use (see above)
  * Limits: 1 <= b <= 64, 1 <= k <= min(E, 32), E <= 1024.
  */
 int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
@@ -146,7 +152,8 @@ int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
  *
  * x device, [b x K] bf16, row stride ldx;  w device, [N x K] bf16;
  * y device, [b x N] bf16 (output), row stride ldy; y must not overlap x.
- * Variant: K3_VARIANT_DOT2 for b <= 8, K3_VARIANT_MFMA above.
+ * Variant: K3_VARIANT_DOT2 for b <= 4 and K <= 8192, K3_VARIANT_MFMA
+ * otherwise (which needs K % 128 == 0).
  * Limits: 1 <= b <= 64.
  */
 int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K,
@@ -175,9 +182,12 @@ int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K,
  * y        device, [b x d_out] bf16 (output)
  * cu_budget upper bound on the compute units the call's kernels occupy
  *          (grid size); 0 = the whole device
- * Intermediates (h in bf16, the permutation) live in the workspace.
- * Limits: 1 <= b <= 64, 1 <= k <= 32, E <= 1024, I % 32 == 0,
- * d_in % 128 == 0, d_out % 16 == 0.
+ * Intermediates (h in bf16, per-slot expert outputs in fp32, the
+ * permutation) live in the workspace. Ids outside [0, E) contribute
+ * nothing; an id repeated within a token counts once per slot.
+ * The combine adds y_add first, then the slots in order j = 0..k-1.
+ * Limits: 1 <= b <= 64, 1 <= k <= 32, E <= 1024, I % 128 == 0, I <= 8192,
+ * d_in % 128 == 0, d_in <= 8192, d_out % 16 == 0.
  */
 int k3_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in,
                    const int32_t *topk_ids, const float *topk_w, int k,
@@ -192,8 +202,8 @@ int k3_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in,
  *
  * x device, [b x d] bf16, row stride ldx;  w13 device, [2I x d] bf16;
  * w2 device, [d x I] bf16;  y_s device, [b x d] fp32 (output).
- * cu_budget as for k3_moe_experts. Limits: 1 <= b <= 64, I % 32 == 0,
- * d % 128 == 0.
+ * cu_budget as for k3_moe_experts. Limits: 1 <= b <= 64, I % 128 == 0,
+ * d % 128 == 0, d and I <= 8192.
  */
 int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d,
                      const uint16_t *w13, const uint16_t *w2, int I,
@@ -215,6 +225,8 @@ int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d,
  * gamma    device, [d] bf16
  * y_norm   device, [b x d] bf16 (output); must not overlap residual or a
  * The norm is taken over fp32 h, before h is rounded for the store.
+ * workspace: >= k3_oproj_residual_workspace_size(b, K, d) bytes,
+ *          zero-filled before first use (see above).
  * Limits: 1 <= b <= 64, d % 8 == 0, eps >= 0.
  */
 int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,

@@ -80,7 +80,7 @@ def lib():
     L.k3_trace_events.restype = _i32
     L.k3_router_topk_workspace_size.argtypes = [_i32, _i32]
     L.k3_proj_skinny_workspace_size.argtypes = [_i32, _i32, _i32]
-    L.k3_moe_experts_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    L.k3_moe_experts_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
     L.k3_shared_expert_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_oproj_residual_workspace_size.argtypes = [_i32, _i32, _i32]
     for f in ("k3_router_topk_workspace_size", "k3_proj_skinny_workspace_size",
@@ -209,7 +209,8 @@ def _workspace(device, nbytes: int, tag: str):
     key = (device.index if device.index is not None else torch.cuda.current_device(), tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        # zero-filled: the router and o-proj workspaces hold completion counters
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -221,7 +222,8 @@ def workspace_size(op: str, **kw) -> int:
     if op == "proj_skinny":
         return L.k3_proj_skinny_workspace_size(kw["b"], kw["K"], kw["N"])
     if op == "moe_experts":
-        return L.k3_moe_experts_workspace_size(kw["b"], kw["d_in"], kw["E"], kw["k"], kw["I"])
+        return L.k3_moe_experts_workspace_size(kw["b"], kw["d_in"], kw["E"], kw["k"], kw["I"],
+                                               kw["d_out"])
     if op == "shared_expert":
         return L.k3_shared_expert_workspace_size(kw["b"], kw["d"], kw["I"])
     if op == "oproj_residual":
@@ -274,7 +276,7 @@ def k3_moe_experts(z, topk_ids, topk_w, w13, w2, y_add=None, y_add_ready=None, y
     d_out = w2.shape[1]
     if y is None:
         y = torch.empty((b, d_out), dtype=torch.bfloat16, device=dev)
-    nbytes = lib().k3_moe_experts_workspace_size(b, d_in, E, k, I)
+    nbytes = lib().k3_moe_experts_workspace_size(b, d_in, E, k, I, d_out)
     ws = workspace if workspace is not None else _workspace(dev, nbytes, "moe_experts")
     ev = None
     if y_add_ready is not None:

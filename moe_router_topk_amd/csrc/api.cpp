@@ -61,28 +61,6 @@ int forced_variant(int op) {
     return (op >= 0 && op < 8) ? g_forced_variant[op].load() : K3_VARIANT_NONE;
 }
 
-MoeWorkspace moe_workspace_layout(int b, int E, int k, int I) {
-    const size_t A = 256;
-    size_t P = (size_t)b * k;
-    size_t cap = P < (size_t)E ? P : (size_t)E;
-    MoeWorkspace w;
-    size_t o = 0;
-    w.n_active = o;
-    o = align_up(o + sizeof(int), A);
-    w.active_expert = o;
-    o = align_up(o + cap * sizeof(int), A);
-    w.active_start = o;
-    o = align_up(o + (cap + 1) * sizeof(int), A);
-    w.sorted_token = o;
-    o = align_up(o + P * sizeof(int), A);
-    w.sorted_w = o;
-    o = align_up(o + P * sizeof(float), A);
-    w.hbuf = o;
-    o = align_up(o + P * (size_t)I * sizeof(uint16_t), A);
-    w.total = o;
-    return w;
-}
-
 }  // namespace k3
 
 extern "C" {
@@ -117,40 +95,6 @@ int k3_trace_events(int op, void *begin, void *end) {
     k3::g_trace_begin[op].store(begin);
     k3::g_trace_end[op].store(end);
     return K3_OK;
-}
-
-size_t k3_router_topk_workspace_size(int b, int E) {
-    if (b <= 0 || E <= 0)
-        return 0;
-    return k3::align_up((size_t)b * E * sizeof(float), 256);
-}
-
-size_t k3_proj_skinny_workspace_size(int b, int K, int N) {
-    (void)b;
-    (void)K;
-    (void)N;
-    return 0;
-}
-
-size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I) {
-    (void)d_in;
-    if (b <= 0 || E <= 0 || k <= 0 || I <= 0)
-        return 0;
-    return k3::moe_workspace_layout(b, E, k, I).total;
-}
-
-size_t k3_shared_expert_workspace_size(int b, int d, int I) {
-    (void)d;
-    if (b <= 0 || I <= 0)
-        return 0;
-    return k3::align_up((size_t)b * I * sizeof(uint16_t), 256);
-}
-
-size_t k3_oproj_residual_workspace_size(int b, int K, int d) {
-    (void)K;
-    if (b <= 0 || d <= 0)
-        return 0;
-    return k3::align_up((size_t)b * d * sizeof(float), 256);
 }
 
 }  // extern "C"

@@ -1,24 +1,33 @@
 // dense.hip -- skinny dense projections, router scoring + top-k, and the
 // output projection with residual add and RMSNorm.
 //
-// Two GEMV/GEMM engines serve every dense [N x K] weight read here:
-//  * dot2: each wave owns whole weight rows and streams them with 128-bit
-//    non-temporal loads (up to 16 in flight per lane), multiplying against
-//    the T <= 8 token rows with v_dot2c_f32_bf16 and reducing across the
-//    wave at the end of a row. Small-batch kernels of "Hyper Optimizing Kimi
-//    K3 in vLLM", Part 1 section 1 ("Tune shapes for the workload").
-//  * mfma: one workgroup per 16-row tile of W; its four waves split K into
-//    quarters and run v_mfma_f32_16x16x32_bf16 with the tokens as the A
-//    operand (up to four 16-token tiles) and the weight rows as B, then sum
-//    the four partial tiles in LDS in a fixed order. This is the
-//    work-splitting kernel the same section uses above batch 2; the split
-//    stays inside one workgroup, so no partial sums go through HBM.
+// Two engines serve the dense [N x K] weight reads here:
+//  * dot2 (batch <= 4): the row-streaming engine of k3_device.h -- each wave
+//    owns whole weight rows, reads them 1 KB per load instruction with two
+//    row buffers in flight, and multiplies against the tokens staged in LDS
+//    with v_dot2c_f32_bf16. The small-batch kernels of "Hyper Optimizing
+//    Kimi K3 in vLLM", Part 1 section 1 ("Tune shapes for the workload").
+//  * mfma (batch > 4): one workgroup per 16-row tile of W; its four waves
+//    split K into quarters and run v_mfma_f32_16x16x32_bf16 with the tokens
+//    as the A operand (up to four 16-token tiles) and the weight rows as B,
+//    then sum the four partial tiles in LDS in a fixed order: the
+//    work-splitting kernel the same section uses at larger batch, with the
+//    split kept inside one workgroup so no partial sums go through HBM.
+//
+// Router top-k and RMSNorm need every output of their projection. On the
+// dot2 path they run in the projection kernel itself: each workgroup
+// publishes its results, a device-scope fence orders them before a counter
+// increment, and the workgroup that brings the counter to the grid size
+// (after an acquire fence) finishes the job and resets the counter. All
+// cross-workgroup sums run in a fixed order, so results are deterministic.
 #include <math.h>
 
 #include "k3_device.h"
 #include "k3_internal.h"
 
 namespace k3 {
+
+constexpr int kDot2MaxTokens = 4;
 
 // ------------------------------------------------------------------ epilogues
 struct EpiBf16 {  // y[t][n] = bf16(s)
@@ -42,72 +51,216 @@ struct EpiResidual {  // h = r + s: fp32 copy for the norm, bf16 back into r
     uint16_t *res;
     float *h32;
     int d;
-    __device__ void operator()(int t, int n, float s) const {
+    __device__ float operator()(int t, int n, float s) const {
         const int64_t i = (int64_t)t * d + n;
         const float h = bf16_to_f32(res[i]) + s;
         h32[i] = h;
         res[i] = f32_to_bf16(h);
+        return h;
     }
 };
 
-// ------------------------------------------------------------------ dot2 engine
-// Wave w owns rows [w * rows_per_wave, ...) of W and takes them R at a time;
-// lane l reads 16-byte vectors l, l + 64, ... of each row (U of them in
-// flight per row) and the matching vectors of the T token rows.
-template <int T, int R, int U, class Epi>
+struct EpiResidualStore {  // EpiResidual without the return value
+    EpiResidual r;
+    __device__ void operator()(int t, int n, float s) const { (void)r(t, n, s); }
+};
+
+// Rows per wave so that N rows spread evenly over `waves` waves, rounded up
+// to whole RB-row batches.
+static inline int rows_per_wave(int N, int waves, int RB) {
+    int rpw = (N + waves - 1) / waves;
+    return (rpw + RB - 1) / RB * RB;
+}
+
+// ------------------------------------------------------------------ dot2 dense
+template <int TM, int CB, class Epi>
 __global__ void __launch_bounds__(kBlock)
-k_gemv_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b,
-            const uint16_t *__restrict__ W, int N, int K, int rows_per_wave, Epi epi) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * (kBlock / kWave) + (threadIdx.x / kWave);
-    const int r_begin = wave * rows_per_wave;
-    const int r_end = min(N, r_begin + rows_per_wave);
+k_dense_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, const uint16_t *__restrict__ W,
+             int N, int K, int rpw, Epi epi) {
+    extern __shared__ u32x4 xs[];
     const int nv = K >> 3;
-    for (int r = r_begin; r < r_end; r += R) {
-        float acc[R][T];
+    stage_rows(xs, nv, b, nv, [&](int t) { return x + (int64_t)t * ldx; });
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    const int r0 = wave * rpw, r1 = min(N, r0 + rpw);
+    stream_rows<TM, 16 / CB, CB>(
+        r0, r1, nv, xs, nv, b, [&](int r) { return W + (int64_t)r * K; },
+        [&](int r, int t, float s) {
+            if (lane == 0)
+                epi(t, r, s);
+        });
+}
+
+// ------------------------------------------------------------------ top-k
+// One wave picks token t's k experts: lane l holds logits l, l + 64, ...;
+// k rounds of a wave-wide argmax under the order (logit desc, index asc);
+// lane j keeps the j-th pick. The weights are the softmax over the k picked
+// logits (the full softmax renormalised over the selection).
+__device__ void topk_wave(const float *logits, int E, int k, int32_t *ids, float *wts) {
+    constexpr int PER = K3_MAX_EXPERTS / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    float v[PER];
+    uint32_t taken = 0;
 #pragma unroll
-        for (int i = 0; i < R; ++i)
+    for (int i = 0; i < PER; ++i) {
+        const int e = i * kWave + lane;
+        float l = -INFINITY;
+        if (e < E)
+            l = logits[e];
+        else
+            taken |= 1u << i;
+        v[i] = (l != l) ? -INFINITY : l;  // NaN never outranks a number
+    }
+    float sel_v = 0.0f, top = 0.0f;
+    int sel_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                acc[i][t] = 0.0f;
-        for (int v0 = 0; v0 < nv; v0 += kWave * U) {
-            u32x4 w[R][U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * kWave + lane;
-#pragma unroll
-                for (int i = 0; i < R; ++i)
-                    w[i][u] = (v < nv && r + i < r_end)
-                                  ? ld_weight16(W + (int64_t)(r + i) * K + (int64_t)v * 8)
-                                  : zero16();
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * kWave + lane;
-                if (v < nv) {
-#pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        if (t < b) {
-                            const u32x4 xv = ld_act16(x + (int64_t)t * ldx + (int64_t)v * 8);
-#pragma unroll
-                            for (int i = 0; i < R; ++i)
-                                acc[i][t] = dot8(w[i][u], xv, acc[i][t]);
-                        }
-                    }
-                }
+        for (int i = 0; i < PER; ++i) {
+            const int e = i * kWave + lane;
+            if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
+                bv = v[i];
+                be = e;
             }
         }
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                if (t < b && r + i < r_end) {
-                    const float s = wave_sum(acc[i][t]);
-                    if (lane == 0)
-                        epi(t, r + i, s);
-                }
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, kWave);
+            const int oe = __shfl_xor(be, m, kWave);
+            if (ov > bv || (ov == bv && oe < be)) {
+                bv = ov;
+                be = oe;
             }
+        }
+        if ((be & (kWave - 1)) == lane)
+            taken |= 1u << (be / kWave);
+        if (lane == j) {
+            sel_v = bv;
+            sel_e = be;
+        }
+        if (j == 0)
+            top = bv;
     }
+    const float dl = (sel_v == top) ? 0.0f : sel_v - top;
+    const float p = lane < k ? expf(dl) : 0.0f;
+    const float sum = wave_sum(p);
+    if (lane < k) {
+        ids[lane] = sel_e;
+        wts[lane] = p / sum;
+    }
+}
+
+__global__ void __launch_bounds__(kWave)
+k_topk_softmax(const float *__restrict__ logits, int E, int k, int32_t *__restrict__ ids,
+               float *__restrict__ wts) {
+    const int t = blockIdx.x;
+    topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k);
+}
+
+// Publish this workgroup's results and count it; true in the one workgroup
+// that arrives last, after an acquire fence (all other workgroups' results
+// are then visible to its loads).
+__device__ bool arrive_last(int *counter) {
+    __shared__ int is_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        is_last = atomicAdd(counter, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!is_last)
+        return false;
+    __threadfence();
+    return true;
+}
+
+// Router logits on the dot2 engine; the last workgroup runs the top-k for
+// every token (wave w takes tokens w, w + 4, ...) and resets the counter.
+template <int TM, int CB>
+__global__ void __launch_bounds__(kBlock)
+k_router_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, const uint16_t *__restrict__ W,
+              int E, int d, int rpw, const float *__restrict__ bias, float *logits, int *counter,
+              int k, int32_t *__restrict__ ids, float *__restrict__ wts) {
+    extern __shared__ u32x4 xs[];
+    const int nv = d >> 3;
+    stage_rows(xs, nv, b, nv, [&](int t) { return x + (int64_t)t * ldx; });
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wq = threadIdx.x / kWave;
+    const int wave = blockIdx.x * (kBlock / kWave) + wq;
+    const int r0 = wave * rpw, r1 = min(E, r0 + rpw);
+    stream_rows<TM, 16 / CB, CB>(
+        r0, r1, nv, xs, nv, b, [&](int r) { return W + (int64_t)r * d; },
+        [&](int r, int t, float s) {
+            if (lane == 0)
+                logits[(int64_t)t * E + r] = bias ? s + bias[r] : s;
+        });
+    if (!arrive_last(counter))
+        return;
+    for (int t = wq; t < b; t += kBlock / kWave)
+        topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k);
+    if (threadIdx.x == 0)
+        atomicExch(counter, 0);
+}
+
+// Output projection + residual on the dot2 engine. Lane 0 of each wave keeps
+// the running sum of h^2 per token over its rows; the workgroup's four wave
+// sums are added in order into ss_part[block][t]; the last workgroup adds the
+// ss_part of all workgroups in block order and writes y = h * inv * gamma.
+template <int TM, int CB>
+__global__ void __launch_bounds__(kBlock)
+k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t *__restrict__ Wo,
+             int d, int K, int rpw, uint16_t *res, const uint16_t *__restrict__ gamma, float eps,
+             float *h32, float *ss_part, int *counter, uint16_t *__restrict__ y) {
+    extern __shared__ u32x4 xs[];
+    __shared__ float wss[kBlock / kWave][TM];
+    __shared__ float inv[TM];
+    const int nv = K >> 3;
+    stage_rows(xs, nv, b, nv, [&](int t) { return a + (int64_t)t * lda; });
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wq = threadIdx.x / kWave;
+    const int wave = blockIdx.x * (kBlock / kWave) + wq;
+    const int r0 = wave * rpw, r1 = min(d, r0 + rpw);
+    const EpiResidual er{res, h32, d};
+    float ss[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+        ss[t] = 0.0f;
+    stream_rows<TM, 16 / CB, CB>(
+        r0, r1, nv, xs, nv, b, [&](int r) { return Wo + (int64_t)r * K; },
+        [&](int r, int t, float s) {
+            if (lane == 0) {
+                const float h = er(t, r, s);
+                ss[t] += h * h;
+            }
+        });
+    if (lane == 0)
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            wss[wq][t] = ss[t];
+    __syncthreads();
+    if (threadIdx.x < b)
+        ss_part[(int64_t)blockIdx.x * TM + threadIdx.x] =
+            (wss[0][threadIdx.x] + wss[1][threadIdx.x]) + (wss[2][threadIdx.x] + wss[3][threadIdx.x]);
+    if (!arrive_last(counter))
+        return;
+    if (wq < b) {  // wave t sums token t's partials: lanes take blocks l, l+64, ...
+        float s = 0.0f;
+        for (int g = lane; g < (int)gridDim.x; g += kWave)
+            s += ss_part[(int64_t)g * TM + wq];
+        s = wave_sum(s);
+        if (lane == 0)
+            inv[wq] = 1.0f / sqrtf(s / (float)d + eps);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < b * d; i += kBlock) {
+        const int t = i / d, n = i - t * d;
+        y[i] = f32_to_bf16(h32[i] * inv[t] * bf16_to_f32(gamma[n]));
+    }
+    if (threadIdx.x == 0)
+        atomicExch(counter, 0);
 }
 
 // ------------------------------------------------------------------ mfma engine
@@ -157,8 +310,8 @@ k_gemm_mfma(const uint16_t *__restrict__ x, int64_t ldx, int b,
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
                         if (mt < MT) {
-                            const u32x4 a = aval[mt] ? ld_act16(x + aoff[mt] + k) : zero16();
-                            acc[mt] = mfma16x16x32(a, bfr[u], acc[mt]);
+                            const u32x4 av = aval[mt] ? ld_act16(x + aoff[mt] + k) : zero16();
+                            acc[mt] = mfma16x16x32(av, bfr[u], acc[mt]);
                         }
                     }
                 }
@@ -183,53 +336,97 @@ k_gemm_mfma(const uint16_t *__restrict__ x, int64_t ldx, int b,
     }
 }
 
+// One workgroup per token: y = h / sqrt(mean(h^2) + eps) * gamma, the mean in
+// fp32 with a fixed reduction order; loads are issued in 16-byte vectors so
+// the loop is not latency-bound (d % 4 == 0).
+__global__ void __launch_bounds__(kBlock)
+k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gamma, float eps,
+          uint16_t *__restrict__ y) {
+    __shared__ float part[kBlock / kWave];
+    const int t = blockIdx.x;
+    const f32x4 *h = reinterpret_cast<const f32x4 *>(h32 + (int64_t)t * d);
+    const int n4 = d >> 2;
+    float ss = 0.0f;
+#pragma unroll 8
+    for (int i = threadIdx.x; i < n4; i += kBlock) {
+        const f32x4 v = h[i];
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        part[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)d + eps);
+#pragma unroll 8
+    for (int i = threadIdx.x; i < n4; i += kBlock) {
+        const f32x4 v = h[i];
+        uint16_t *o = y + (int64_t)t * d + 4 * i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = f32_to_bf16(v[j] * inv * bf16_to_f32(gamma[4 * i + j]));
+    }
+}
+
 // ------------------------------------------------------------------ launchers
-template <int T, class Epi>
-static void launch_dot2_t(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
-                          Epi epi, int cu_budget, hipStream_t s) {
-    // Rows per wave: spread N evenly over the waves of one workgroup per CU.
+// Launch geometry of the dot2 engine: one workgroup (four waves) per compute
+// unit by default; each wave streams an even share of the rows.
+struct Dot2Geom {
+    int grid, rpw, cb;
+    size_t lds;
+};
+
+static Dot2Geom dot2_geom(int N, int K, int b, int cu_budget) {
+    Dot2Geom g;
+    g.cb = K > 2048 ? 16 : (K > 512 ? 4 : 1);
+    const int rb = 16 / g.cb;
     const int cus = budget_grid(1 << 30, cu_budget, 1);
-    const int waves = cus * (kBlock / kWave);
-    const int R = K > 4096 ? 1 : (K > 2048 ? 2 : 4);
-    int rpw = (N + waves - 1) / waves;
-    rpw = (rpw + R - 1) / R * R;
-    const int grid = ((N + rpw - 1) / rpw + 3) / 4;
-    if (R == 1)
-        k_gemv_dot2<T, 1, 16, Epi><<<grid, kBlock, 0, s>>>(x, ldx, b, W, N, K, rpw, epi);
-    else if (R == 2)
-        k_gemv_dot2<T, 2, 8, Epi><<<grid, kBlock, 0, s>>>(x, ldx, b, W, N, K, rpw, epi);
+    g.rpw = rows_per_wave(N, cus * (kBlock / kWave), rb);
+    const int waves = (N + g.rpw - 1) / g.rpw;
+    g.grid = (waves + 3) / 4;
+    g.lds = (size_t)b * K * sizeof(uint16_t);
+    return g;
+}
+
+// The dot2 engine keeps a whole row in one register buffer (K <= 8192) and
+// the b token rows in LDS (at most 64 KB).
+static bool dot2_fits(int b, int K) {
+    return b <= kDot2MaxTokens && K <= 16 * 512 && (size_t)b * K * 2 <= 65536;
+}
+
+template <int TM, class Epi>
+static void launch_dense_dot2_t(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N,
+                                int K, Epi epi, hipStream_t s) {
+    const Dot2Geom g = dot2_geom(N, K, b, 0);
+    if (g.cb == 16)
+        k_dense_dot2<TM, 16, Epi><<<g.grid, kBlock, g.lds, s>>>(x, ldx, b, W, N, K, g.rpw, epi);
+    else if (g.cb == 4)
+        k_dense_dot2<TM, 4, Epi><<<g.grid, kBlock, g.lds, s>>>(x, ldx, b, W, N, K, g.rpw, epi);
     else
-        k_gemv_dot2<T, 4, 4, Epi><<<grid, kBlock, 0, s>>>(x, ldx, b, W, N, K, rpw, epi);
+        k_dense_dot2<TM, 1, Epi><<<g.grid, kBlock, g.lds, s>>>(x, ldx, b, W, N, K, g.rpw, epi);
 }
 
 template <class Epi>
-static void launch_dot2(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
-                        Epi epi, int cu_budget, hipStream_t s) {
-    if (b <= 1)
-        launch_dot2_t<1>(x, ldx, b, W, N, K, epi, cu_budget, s);
-    else if (b <= 2)
-        launch_dot2_t<2>(x, ldx, b, W, N, K, epi, cu_budget, s);
-    else if (b <= 4)
-        launch_dot2_t<4>(x, ldx, b, W, N, K, epi, cu_budget, s);
-    else
-        launch_dot2_t<8>(x, ldx, b, W, N, K, epi, cu_budget, s);
+static void launch_dense(int variant, const uint16_t *x, int64_t ldx, int b, const uint16_t *W,
+                         int N, int K, Epi epi, hipStream_t s) {
+    if (variant == K3_VARIANT_DOT2) {
+        if (b == 1)
+            launch_dense_dot2_t<1>(x, ldx, b, W, N, K, epi, s);
+        else
+            launch_dense_dot2_t<kDot2MaxTokens>(x, ldx, b, W, N, K, epi, s);
+    } else {
+        const int grid = budget_grid((N + 15) / 16, 0, 4);
+        k_gemm_mfma<8, Epi><<<grid, kBlock, 0, s>>>(x, ldx, b, W, N, K, epi);
+    }
 }
 
-template <class Epi>
-static void launch_mfma(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
-                        Epi epi, int cu_budget, hipStream_t s) {
-    const int tiles = (N + 15) / 16;
-    const int grid = budget_grid(tiles, cu_budget, 4);
-    k_gemm_mfma<8, Epi><<<grid, kBlock, 0, s>>>(x, ldx, b, W, N, K, epi);
-}
-
-// Variant for a dense [N x K] read at batch b: dot2 up to 8 tokens, MFMA
-// above (MFMA needs K % 128 == 0 so each wave's K quarter is whole steps).
+// Variant for a dense [N x K] read at batch b: dot2 while the tokens fit the
+// engine, MFMA above (MFMA needs K % 128 == 0 so each K quarter is whole
+// 32-wide steps).
 static int pick_dense_variant(int op, int b, int K) {
     int v = forced_variant(op);
     if (v == K3_VARIANT_NONE)
-        v = (b <= 8 || K % 128 != 0) ? K3_VARIANT_DOT2 : K3_VARIANT_MFMA;
-    if (v == K3_VARIANT_DOT2 && b > 8)
+        v = dot2_fits(b, K) ? K3_VARIANT_DOT2 : K3_VARIANT_MFMA;
+    if (v == K3_VARIANT_DOT2 && !dot2_fits(b, K))
         return -1;
     if (v == K3_VARIANT_MFMA && K % 128 != 0)
         return -1;
@@ -238,103 +435,42 @@ static int pick_dense_variant(int op, int b, int K) {
     return v;
 }
 
-template <class Epi>
-static void launch_dense(int variant, const uint16_t *x, int64_t ldx, int b, const uint16_t *W,
-                         int N, int K, Epi epi, int cu_budget, hipStream_t s) {
-    if (variant == K3_VARIANT_DOT2)
-        launch_dot2(x, ldx, b, W, N, K, epi, cu_budget, s);
-    else
-        launch_mfma(x, ldx, b, W, N, K, epi, cu_budget, s);
-}
-
-// ------------------------------------------------------------------ top-k
-// One wave per token. Lane l holds logits l, l + 64, ...; k rounds of a
-// wave-wide argmax under the order (logit desc, index asc) pick the experts;
-// lane j keeps the j-th pick. The weights are the softmax over the k picked
-// logits (the full softmax renormalised over the selection).
-__global__ void __launch_bounds__(kWave)
-k_topk_softmax(const float *__restrict__ logits, int E, int k, int32_t *__restrict__ ids,
-               float *__restrict__ wts) {
-    constexpr int PER = K3_MAX_EXPERTS / kWave;
-    const int t = blockIdx.x;
-    const int lane = threadIdx.x;
-    float v[PER];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = i * kWave + lane;
-        float l = -INFINITY;
-        if (e < E)
-            l = logits[(int64_t)t * E + e];
-        else
-            taken |= 1u << i;
-        v[i] = (l != l) ? -INFINITY : l;  // NaN never outranks a number
-    }
-    float sel_v = 0.0f, top = 0.0f;
-    int sel_e = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = i * kWave + lane;
-            if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-                bv = v[i];
-                be = e;
-            }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, kWave);
-            const int oe = __shfl_xor(be, m, kWave);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & (kWave - 1)) == lane)
-            taken |= 1u << (be / kWave);
-        if (lane == j) {
-            sel_v = bv;
-            sel_e = be;
-        }
-        if (j == 0)
-            top = bv;
-    }
-    const float dl = (sel_v == top) ? 0.0f : sel_v - top;
-    const float p = lane < k ? expf(dl) : 0.0f;
-    const float sum = wave_sum(p);
-    if (lane < k) {
-        ids[(int64_t)t * k + lane] = sel_e;
-        wts[(int64_t)t * k + lane] = p / sum;
-    }
-}
-
-// ------------------------------------------------------------------ RMSNorm
-// One workgroup per token: mean of h^2 over d in fp32 (fixed reduction
-// order), then y = h / sqrt(mean + eps) * gamma.
-__global__ void __launch_bounds__(kBlock)
-k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gamma, float eps,
-          uint16_t *__restrict__ y) {
-    __shared__ float part[kBlock / kWave];
-    const int t = blockIdx.x;
-    const float *h = h32 + (int64_t)t * d;
-    float ss = 0.0f;
-    for (int n = threadIdx.x; n < d; n += kBlock)
-        ss += h[n] * h[n];
-    ss = wave_sum(ss);
-    if ((threadIdx.x & (kWave - 1)) == 0)
-        part[threadIdx.x / kWave] = ss;
-    __syncthreads();
-    const float total = (part[0] + part[1]) + (part[2] + part[3]);
-    const float inv = 1.0f / sqrtf(total / (float)d + eps);
-    for (int n = threadIdx.x; n < d; n += kBlock)
-        y[(int64_t)t * d + n] = f32_to_bf16(h[n] * inv * bf16_to_f32(gamma[n]));
-}
-
 }  // namespace k3
 
 using namespace k3;
+
+// ------------------------------------------------------------------ workspace layouts
+// The completion counter sits at offset 0, where it stays whatever the shape
+// of the call, so a workspace reused for other shapes of the same entry
+// point still finds it at zero.
+namespace {
+constexpr size_t kCounterBytes = 256;
+size_t oproj_h32_offset() { return kCounterBytes; }
+size_t oproj_ss_offset(int b, int d) {
+    return kCounterBytes + align_up((size_t)b * d * sizeof(float), 256);
+}
+size_t router_logits_offset() { return kCounterBytes; }
+}  // namespace
+
+extern "C" size_t k3_router_topk_workspace_size(int b, int E) {
+    if (b <= 0 || E <= 0)
+        return 0;
+    return router_logits_offset() + align_up((size_t)b * E * sizeof(float), 256);
+}
+
+extern "C" size_t k3_oproj_residual_workspace_size(int b, int K, int d) {
+    (void)K;
+    if (b <= 0 || d <= 0)
+        return 0;
+    return oproj_ss_offset(b, d) + align_up((size_t)1024 * kDot2MaxTokens * sizeof(float), 256);
+}
+
+extern "C" size_t k3_proj_skinny_workspace_size(int b, int K, int N) {
+    (void)b;
+    (void)K;
+    (void)N;
+    return 0;
+}
 
 // ------------------------------------------------------------------ entry points
 extern "C" int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K, const uint16_t *w,
@@ -353,7 +489,7 @@ extern "C" int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K, cons
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     trace_begin(K3_OP_PROJ_SKINNY, s);
-    launch_dense(variant, x, ldx, b, w, N, K, EpiBf16{y, ldy}, 0, s);
+    launch_dense(variant, x, ldx, b, w, N, K, EpiBf16{y, ldy}, s);
     trace_end(K3_OP_PROJ_SKINNY, s);
     const int st = launch_status();
     if (st == K3_OK)
@@ -372,17 +508,36 @@ extern "C" int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
     if (b > K3_MAX_BATCH || E > K3_MAX_EXPERTS || k > K3_MAX_TOPK || k > E || d % 8 || ldx % 8 ||
         !aligned16(x) || !aligned16(w_router))
         return K3_ERR_UNSUPPORTED;
-    if (!workspace || ws_bytes < k3_router_topk_workspace_size(b, E))
+    if (!workspace || ws_bytes < k3_router_topk_workspace_size(b, E) || !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     const int variant = pick_dense_variant(K3_OP_ROUTER_TOPK, b, d);
     if (variant < 0)
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    float *logits = (float *)workspace;
+    int *counter = (int *)workspace;
+    float *logits = (float *)((char *)workspace + router_logits_offset());
     trace_begin(K3_OP_ROUTER_TOPK, s);
-    launch_dense(variant, x, ldx, b, w_router, E, d, EpiLogits{logits, E, bias}, 0, s);
-    trace_end(K3_OP_ROUTER_TOPK, s);
-    k_topk_softmax<<<b, kWave, 0, s>>>(logits, E, k, topk_ids, topk_w);
+    if (variant == K3_VARIANT_DOT2) {
+        const Dot2Geom g = dot2_geom(E, d, b, 0);
+        if (g.cb == 16 && b == 1)
+            k_router_dot2<1, 16><<<g.grid, kBlock, g.lds, s>>>(x, ldx, b, w_router, E, d, g.rpw,
+                                                              bias, logits, counter, k, topk_ids,
+                                                              topk_w);
+        else if (g.cb == 16)
+            k_router_dot2<kDot2MaxTokens, 16><<<g.grid, kBlock, g.lds, s>>>(
+                x, ldx, b, w_router, E, d, g.rpw, bias, logits, counter, k, topk_ids, topk_w);
+        else if (g.cb == 4)
+            k_router_dot2<kDot2MaxTokens, 4><<<g.grid, kBlock, g.lds, s>>>(
+                x, ldx, b, w_router, E, d, g.rpw, bias, logits, counter, k, topk_ids, topk_w);
+        else
+            k_router_dot2<kDot2MaxTokens, 1><<<g.grid, kBlock, g.lds, s>>>(
+                x, ldx, b, w_router, E, d, g.rpw, bias, logits, counter, k, topk_ids, topk_w);
+        trace_end(K3_OP_ROUTER_TOPK, s);
+    } else {
+        launch_dense(variant, x, ldx, b, w_router, E, d, EpiLogits{logits, E, bias}, s);
+        trace_end(K3_OP_ROUTER_TOPK, s);
+        k_topk_softmax<<<b, kWave, 0, s>>>(logits, E, k, topk_ids, topk_w);
+    }
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_ROUTER_TOPK, variant);
@@ -397,19 +552,45 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         return K3_ERR_INVALID_ARG;
     if (b <= 0 || K <= 0 || d <= 0 || lda < K || !(eps >= 0.0f))
         return K3_ERR_INVALID_ARG;
-    if (b > K3_MAX_BATCH || K % 8 || lda % 8 || d % 8 || !aligned16(a) || !aligned16(w_o))
+    if (b > K3_MAX_BATCH || K % 8 || lda % 8 || d % 8 || !aligned16(a) || !aligned16(w_o) ||
+        !aligned16(residual))
         return K3_ERR_UNSUPPORTED;
-    if (!workspace || ws_bytes < k3_oproj_residual_workspace_size(b, K, d))
+    if (!workspace || ws_bytes < k3_oproj_residual_workspace_size(b, K, d) ||
+        !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     const int variant = pick_dense_variant(K3_OP_OPROJ_RESIDUAL, b, K);
     if (variant < 0)
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    float *h32 = (float *)workspace;
+    char *ws = (char *)workspace;
+    int *counter = (int *)ws;
+    float *h32 = (float *)(ws + oproj_h32_offset());
+    float *ss_part = (float *)(ws + oproj_ss_offset(b, d));
     trace_begin(K3_OP_OPROJ_RESIDUAL, s);
-    launch_dense(variant, a, lda, b, w_o, d, K, EpiResidual{residual, h32, d}, 0, s);
-    trace_end(K3_OP_OPROJ_RESIDUAL, s);
-    k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
+    if (variant == K3_VARIANT_DOT2) {
+        const Dot2Geom g = dot2_geom(d, K, b, 0);
+        if (g.grid > 1024)
+            return K3_ERR_UNSUPPORTED;
+        if (g.cb == 16 && b == 1)
+            k_oproj_dot2<1, 16><<<g.grid, kBlock, g.lds, s>>>(a, lda, b, w_o, d, K, g.rpw,
+                                                             residual, gamma, eps, h32, ss_part,
+                                                             counter, y_norm);
+        else if (g.cb == 16)
+            k_oproj_dot2<kDot2MaxTokens, 16><<<g.grid, kBlock, g.lds, s>>>(
+                a, lda, b, w_o, d, K, g.rpw, residual, gamma, eps, h32, ss_part, counter, y_norm);
+        else if (g.cb == 4)
+            k_oproj_dot2<kDot2MaxTokens, 4><<<g.grid, kBlock, g.lds, s>>>(
+                a, lda, b, w_o, d, K, g.rpw, residual, gamma, eps, h32, ss_part, counter, y_norm);
+        else
+            k_oproj_dot2<kDot2MaxTokens, 1><<<g.grid, kBlock, g.lds, s>>>(
+                a, lda, b, w_o, d, K, g.rpw, residual, gamma, eps, h32, ss_part, counter, y_norm);
+        trace_end(K3_OP_OPROJ_RESIDUAL, s);
+    } else {
+        launch_dense(variant, a, lda, b, w_o, d, K, EpiResidualStore{EpiResidual{residual, h32, d}},
+                     s);
+        trace_end(K3_OP_OPROJ_RESIDUAL, s);
+        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
+    }
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_OPROJ_RESIDUAL, variant);

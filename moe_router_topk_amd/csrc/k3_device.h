@@ -77,3 +77,97 @@ __device__ __forceinline__ float silu(float g) {
 }
 
 }  // namespace k3
+
+namespace k3 {
+
+// ------------------------------------------------------------------ row streaming
+// The weight-streaming engine of the small-batch kernels. One wave walks
+// rows [r_begin, r_end) of a row set, RB rows at a time: row i is NV
+// 16-byte vectors long, lane l owns vectors l, l + 64, ... (CB of them, so
+// one load instruction reads 1 KB of a row contiguously). Two register
+// buffers alternate, so the next RB rows' loads are in flight while the
+// current ones are multiplied against the token vectors staged in LDS
+// (xs[t * xstride + v], t < nt <= TM). Activations come from LDS only: a
+// global activation load issued behind the weight loads would have to wait
+// for all of them (vector loads retire in order). After each row, every lane
+// holds the wave-reduced sum for each token and calls epi(row, t, sum).
+template <int TM, int RB, int CB, class RowPtr, class Epi>
+__device__ __forceinline__ void stream_rows(int r_begin, int r_end, int nv, const u32x4 *xs,
+                                            int xstride, int nt, RowPtr rowptr, Epi epi) {
+    const int lane = threadIdx.x & (kWave - 1);
+    u32x4 A[RB][CB], B[RB][CB];
+    auto load = [&](u32x4 (&buf)[RB][CB], int r) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const bool rv = r + i < r_end;
+            const uint16_t *p = rv ? rowptr(r + i) : nullptr;
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const int v = c * kWave + lane;
+                buf[i][c] = (rv && v < nv) ? ld_weight16(p + (int64_t)v * 8) : zero16();
+            }
+        }
+    };
+    auto finish = [&](u32x4 (&buf)[RB][CB], int r) {
+        float acc[RB][TM];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                acc[i][t] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const int v = c * kWave + lane;
+            if (v < nv) {
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    if (t < nt) {
+                        const u32x4 xv = xs[t * xstride + v];
+#pragma unroll
+                        for (int i = 0; i < RB; ++i)
+                            acc[i][t] = dot8(buf[i][c], xv, acc[i][t]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            if (r + i < r_end)
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+                    if (t < nt)
+                        epi(r + i, t, wave_sum(acc[i][t]));
+    };
+    if (r_begin >= r_end)
+        return;
+    load(A, r_begin);
+    for (int r = r_begin; r < r_end; r += 2 * RB) {
+        if (r + RB < r_end)
+            load(B, r + RB);
+        finish(A, r);
+        if (r + RB >= r_end)
+            break;
+        if (r + 2 * RB < r_end)
+            load(A, r + 2 * RB);
+        finish(B, r + RB);
+    }
+}
+
+// Copy nrows activation rows (nv 16-byte vectors each, row t starting at
+// src(t)) into LDS rows of xstride vectors; all threads of the block help.
+template <class Src>
+__device__ __forceinline__ void stage_rows(u32x4 *xs, int xstride, int nrows, int nv, Src src) {
+    for (int i = threadIdx.x; i < nrows * nv; i += blockDim.x) {
+        const int t = i / nv, v = i - t * nv;
+        xs[t * xstride + v] = ld_act16(src(t) + (int64_t)v * 8);
+    }
+}
+
+// Even split of [0, n) over `parts`: the part-th range.
+__device__ __forceinline__ void split_range(int n, int parts, int part, int &lo, int &hi) {
+    const int base = n / parts, rem = n % parts;
+    lo = part * base + min(part, rem);
+    hi = lo + base + (part < rem ? 1 : 0);
+}
+
+}  // namespace k3

@@ -33,8 +33,9 @@ inline int launch_status() {
 
 // Workspace layout of k3_moe_experts (offsets in bytes, 256-byte aligned).
 struct MoeWorkspace {
-    size_t n_active, active_expert, active_start, sorted_token, sorted_w, hbuf, total;
+    size_t n_light, n_heavy, light_expert, light_start, light_ntok, heavy_expert, heavy_start,
+        heavy_ntok, sorted_token, slot_pos, hbuf, part, total;
 };
-MoeWorkspace moe_workspace_layout(int b, int E, int k, int I);
+MoeWorkspace moe_workspace_layout(int b, int E, int k, int I, int d_out);
 
 }  // namespace k3

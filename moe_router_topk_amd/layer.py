@@ -48,9 +48,10 @@ class DecodeLayer:
         I_s = moe["w13_s"].shape[0] // 2
         self.E, self.d, self.d_lat, self.I, self.I_s, self.b_max = E, d, d_lat, I, I_s, b_max
         u8 = dict(dtype=torch.uint8, device=dev)
-        self.ws_router = torch.empty(max(workspace_size("router_topk", b=b_max, E=E), 256), **u8)
-        self.ws_moe = torch.empty(workspace_size("moe_experts", b=b_max, d_in=d_lat, E=E, k=k, I=I),
-                                  **u8)
+        # zero-filled: the router and o-proj workspaces hold completion counters
+        self.ws_router = torch.zeros(workspace_size("router_topk", b=b_max, E=E), **u8)
+        self.ws_moe = torch.empty(
+            workspace_size("moe_experts", b=b_max, d_in=d_lat, E=E, k=k, I=I, d_out=d), **u8)
         self.ws_shared = torch.empty(workspace_size("shared_expert", b=b_max, d=d, I=I_s), **u8)
         self.ids = torch.empty((b_max, k), dtype=torch.int32, device=dev)
         self.wts = torch.empty((b_max, k), dtype=torch.float32, device=dev)
@@ -62,7 +63,7 @@ class DecodeLayer:
             self.k_o = chain["w_o"].shape[1]
             self.q = torch.empty((b_max, n_in), dtype=torch.bfloat16, device=dev)
             self.x_moe = torch.empty((b_max, d), dtype=torch.bfloat16, device=dev)
-            self.ws_oproj = torch.empty(
+            self.ws_oproj = torch.zeros(
                 workspace_size("oproj_residual", b=b_max, K=self.k_o, d=d), **u8)
         self.side = torch.cuda.Stream(device=dev)
         self.pf_stream = torch.cuda.Stream(device=dev)
@@ -106,19 +107,23 @@ class DecodeLayer:
                           y_norm=x_moe, workspace=self.ws_oproj)
         return x_moe
 
+    PREFETCH_KEYS = ("w_router", "w_lat")
+
     def step(self, x: torch.Tensor, residual: torch.Tensor, prefetch: bool = False):
         """The whole hot path of a decode layer: chain, then the MoE block on
-        the normalised hidden state. With prefetch, the side stream warms the
-        cache with the router, latent and shared-expert weights while the
-        output projection runs."""
+        the normalised hidden state. With prefetch, a side stream reads the
+        router and latent weights (the MoE block's first reads) into the MALL
+        while the chain runs, on prefetch_cu compute units; the main stream
+        joins it only at the end of the step."""
+        main = torch.cuda.current_stream(self.device)
         if prefetch:
-            main = torch.cuda.current_stream(self.device)
             self.ev_in.record(main)
             self.pf_stream.wait_event(self.ev_in)
-            for key in ("w_router", "w_lat", "w13_s"):
+            for key in self.PREFETCH_KEYS:
                 k3_prefetch(self.moe[key], cu_budget=self.prefetch_cu, stream=self.pf_stream)
-        h = self.attn_chain(x, residual)
-        if prefetch:
             self.ev_side_done.record(self.pf_stream)
-            torch.cuda.current_stream(self.device).wait_event(self.ev_side_done)
-        return self.moe_block(h)
+        h = self.attn_chain(x, residual)
+        y = self.moe_block(h)
+        if prefetch:
+            main.wait_event(self.ev_side_done)
+        return y

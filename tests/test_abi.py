@@ -72,7 +72,8 @@ def test_workspace_sizes(L):
     import moe_router_topk_amd as k3
     assert k3.workspace_size("router_topk", b=64, E=384) >= 64 * 384 * 4
     assert k3.workspace_size("proj_skinny", b=64, K=7168, N=12288) == 0
-    assert k3.workspace_size("moe_experts", b=64, d_in=7168, E=384, k=8, I=2048) >= 512 * 2048 * 2
+    assert k3.workspace_size("moe_experts", b=64, d_in=7168, E=384, k=8, I=2048,
+                             d_out=7168) >= 512 * 2048 * 2 + 512 * 7168 * 4
     assert k3.workspace_size("shared_expert", b=64, d=7168, I=2048) >= 64 * 2048 * 2
     assert k3.workspace_size("oproj_residual", b=64, K=8192, d=7168) >= 64 * 7168 * 4
     assert k3.workspace_size("router_topk", b=0, E=384) == 0

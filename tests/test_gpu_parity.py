@@ -76,7 +76,7 @@ def test_router_topk_full(k3, full, b, zipf):
     keep = [t for t in range(b) if t not in differ]
     assert_rel_close(g[keep], ref_w[keep], "topk_w")
     assert (np.diff(g, axis=1) <= 1e-6).all(), "weights not in descending order"
-    want = "dot2" if b <= 8 else "mfma"
+    want = "dot2" if b <= 4 else "mfma"
     assert k3.k3_get_last_dispatch("router_topk") == want
 
 
@@ -112,15 +112,19 @@ def test_proj_skinny_latent(k3, full, b):
     rows = torch.arange(0, cfg.d_lat, 7)  # sampled output columns, every 7th
     ref = oracle.linear(x.cpu(), w["w_lat"][rows].cpu())
     assert_rel_close(y[:, rows].cpu(), ref, "z")
-    assert k3.k3_get_last_dispatch("proj_skinny") == ("dot2" if b <= 8 else "mfma")
+    assert k3.k3_get_last_dispatch("proj_skinny") == ("dot2" if b <= 4 else "mfma")
 
 
 @pytest.mark.parametrize("variant", ["dot2", "mfma"])
-@pytest.mark.parametrize("b,K,N", [(1, 256, 256), (2, 128, 40), (8, 1024, 1000), (7, 896, 33)])
+@pytest.mark.parametrize("b,K,N", [(1, 256, 256), (2, 128, 40), (4, 1024, 1000), (3, 896, 33),
+                                   (4, 8192, 77), (1, 2056, 5), (8, 1024, 1000), (7, 896, 33)])
 def test_proj_skinny_ragged(k3, variant, b, K, N):
-    """Both engines on small ragged shapes (N not a multiple of 16, few rows)."""
+    """Both engines on small ragged shapes (N not a multiple of 16, few rows,
+    K not a multiple of the 512-element row chunk)."""
     if variant == "mfma" and K % 128:
         pytest.skip("MFMA engine needs K % 128 == 0")
+    if variant == "dot2" and b > 4:
+        pytest.skip("dot2 engine takes at most 4 tokens")
     x = synth.randn_bf16((b, K), 1.0, 7, "rag_x", K * 100 + N, device=DEV)
     W = synth.randn_bf16((N, K), 1 / math.sqrt(K), 7, "rag_w", K * 100 + N, device=DEV)
     k3.k3_force_variant("proj_skinny", variant)
@@ -217,6 +221,74 @@ def test_moe_experts_deterministic(k3, full):
     a = _routed_case(k3, cfg, w, 16, 0.0, 600)[-1].clone()
     bb = _routed_case(k3, cfg, w, 16, 0.0, 600)[-1]
     assert torch.equal(a, bb)
+
+
+def test_moe_experts_b1_invalid_id_dropped(k3):
+    """Batch 1 (slots are experts, no permutation): an id outside [0, E)
+    contributes nothing."""
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    x = synth.make_tokens(cfg, device=DEV, b=1)
+    z = k3.k3_proj_skinny(x, w["w_lat"])
+    ids = torch.tensor([[6, 99]], dtype=torch.int32, device=DEV)
+    wts = torch.tensor([[0.625, 0.375]], dtype=torch.float32, device=DEV)
+    y = k3.k3_moe_experts(z, ids, wts, w["w13"], w["w2"])
+    torch.cuda.synchronize()
+    ref = oracle.moe_experts(z.cpu(), np.array([[6, 6]], np.int32), np.array([[0.625, 0.0]]),
+                             _experts_on_host(w), cfg.E)
+    assert_rel_close(y.cpu(), ref, "y")
+
+
+@pytest.mark.parametrize("b", [3, 4, 5, 8])
+def test_moe_experts_light_and_heavy_lists(k3, b):
+    """Tokens forced onto few experts so some have more than 4 tokens (MFMA
+    tiles) and some at most 4 (dot2 rows), at the tiny workload."""
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    x = synth.make_tokens(cfg, device=DEV, index=40 + b, b=b)
+    z = k3.k3_proj_skinny(x, w["w_lat"])
+    ids = torch.tensor([[3, t % cfg.E] if t % cfg.E != 3 else [3, 0] for t in range(b)],
+                       dtype=torch.int32, device=DEV)
+    wts = torch.full((b, 2), 0.5, dtype=torch.float32, device=DEV)
+    y_add = synth.randn_bf16((b, cfg.d), 0.1, 3, "ya_lh", b, device=DEV).float()
+    y = k3.k3_moe_experts(z, ids, wts, w["w13"], w["w2"], y_add=y_add)
+    torch.cuda.synchronize()
+    ref = oracle.moe_experts(z.cpu(), ids.cpu().numpy(), wts.cpu().numpy(), _experts_on_host(w),
+                             cfg.E, y_add=y_add.cpu())
+    assert_rel_close(y.cpu(), ref, "y")
+
+
+def test_counters_reset_between_calls(k3, full, chain_w):
+    """The router and o-proj kernels finish with a last-workgroup step and
+    leave their completion counter (offset 0 of the workspace) at zero, call
+    after call, also when one workspace serves several shapes."""
+    cfg, w = full
+    ws = torch.zeros(k3.workspace_size("router_topk", b=2, E=cfg.E), dtype=torch.uint8,
+                     device=DEV)
+    outs = []
+    xb = synth.make_tokens(cfg, device=DEV, index=901, b=1)
+    k3.k3_router_topk(xb, w["w_router"], None, cfg.k, workspace=ws)  # another shape first
+    for rep in range(3):
+        x = synth.make_tokens(cfg, device=DEV, index=900, b=2)
+        ids, wts = k3.k3_router_topk(x, w["w_router"], None, cfg.k, workspace=ws)
+        outs.append((ids.clone(), wts.clone()))
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32)[0]) == 0
+    for ids, wts in outs[1:]:
+        assert torch.equal(ids, outs[0][0]) and torch.equal(wts, outs[0][1])
+    cc = synth.CHAIN_CONFIG
+    wso = torch.zeros(k3.workspace_size("oproj_residual", b=1, K=cc.k_o, d=cc.d),
+                      dtype=torch.uint8, device=DEV)
+    a = synth.randn_bf16((1, cc.k_o), 1.0, 0, "cnt_a", device=DEV)
+    r0 = synth.randn_bf16((1, cc.d), 1.0, 0, "cnt_r", device=DEV)
+    ys = []
+    for rep in range(3):
+        r = r0.clone()
+        ys.append(k3.k3_oproj_residual(a, chain_w["w_o"], r, chain_w["gamma"], cc.eps,
+                                       workspace=wso).clone())
+    torch.cuda.synchronize()
+    assert int(wso[:4].view(torch.int32)[0]) == 0
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])
 
 
 def test_moe_experts_invalid_ids_dropped(k3):
