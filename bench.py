@@ -164,7 +164,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=2, help="weight copies rotated per step")
-    ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="run the side-stream prefetch inside the timed step")
     ap.add_argument("--cu-shared", type=int, default=0, help="CU budget of the shared expert")
     ap.add_argument("--prefetch-cu", type=int, default=32, help="CU budget of the prefetch")
     ap.add_argument("--no-sweep", action="store_true", help="skip the b = 1..64 sweep")
@@ -223,7 +224,7 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"weights + inputs ready in {time.perf_counter() - t_gen:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
-    prefetch = not args.no_prefetch
+    prefetch = args.prefetch
 
     def step(i, bb=b):
         lay = layers[i % len(layers)]
@@ -284,7 +285,31 @@ def main() -> int:
     log(f"MoE block b={b}: {moe_ms * 1e3:.1f} us, {moe_gbs:.0f} GB/s "
         f"({100 * moe_gbs / PEAK_GBS:.1f}% of peak)")
 
+    # the other configurations, for comparison (graph-timed like the step)
+    def step_alt(i):
+        lay = layers[i % len(layers)]
+        return lay.step(pool[i % NX]["x"][:b], pool[i % NX]["r"][:b], prefetch=not prefetch)
+
+    step_alt(0)
+    g = capture(torch, step_alt, K)
+    alt_ms, _ = replay_timed(torch, g, K)
+    del g
+
+    def block_streams(i, bb=b):
+        lay = layers[i % len(layers)]
+        return lay.moe_block_streams(pool[i % NX]["x"][:bb])
+
+    block_streams(0)
+    g = capture(torch, block_streams, K)
+    streams_ms, _ = replay_timed(torch, g, K)
+    del g
+    log(f"step with prefetch {'off' if prefetch else 'on'}: {alt_ms * 1e3:.1f} us; "
+        f"MoE block as two-stream composition: {streams_ms * 1e3:.1f} us")
+
     extra = {"moe_block_us": round(moe_ms * 1e3, 2), "moe_block_GBps": round(moe_gbs, 1),
+             ("step_us_prefetch_off" if prefetch else "step_us_prefetch_on"):
+                 round(alt_ms * 1e3, 2),
+             "moe_block_two_stream_us": round(streams_ms * 1e3, 2),
              "moe_block_frac_of_peak": round(moe_gbs / PEAK_GBS, 4),
              "eager_step_us": round(eager_ms * 1e3, 2),
              "eager_step_us_median": round(pct(per, 0.5) * 1e3, 2),
@@ -363,7 +388,7 @@ def main() -> int:
                          "o-proj 8192->7168 + residual + RMSNorm, router E=384 top-8 "
                          "renormalised softmax, latent 7168->7168, 8 routed + 1 shared "
                          "SwiGLU experts I=2048 (gate/up [4096x7168], down [7168x2048]), "
-                         "side-stream prefetch"),
+                         "side-stream prefetch " + ("on" if prefetch else "off")),
             "batch": b, "d": cfg.d, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
             "prefetch": prefetch, "hip_graph": not args.eager_only,
             "layers_rotated": args.layers,

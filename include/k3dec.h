@@ -73,6 +73,8 @@ int k3_version(void);
 #define K3_OP_SHARED_EXPERT 3
 #define K3_OP_OPROJ_RESIDUAL 4
 #define K3_OP_PREFETCH 5
+#define K3_OP_ROUTER_LATENT 6
+#define K3_OP_MOE_BLOCK 7
 
 #define K3_VARIANT_NONE 0
 #define K3_VARIANT_DOT2 1    /* VALU dot2 GEMV: whole weight rows per wave */
@@ -90,9 +92,10 @@ int k3_force_variant(int op, int variant);
 
 /* Tracing: while set, every call of `op` records `begin` (a hipEvent_t as
  * void*) on its stream right before the op's main kernel and `end` right
- * after it -- k3_moe_experts: the grouped gate/up kernel; k3_shared_expert:
- * its gate/up kernel; k3_router_topk: the logits kernel; the others: their
- * only or first kernel. NULL events clear the hook. The records are plain
+ * after it -- k3_moe_experts: the grouped gate/up kernel (also when
+ * k3_moe_block runs it); k3_shared_expert: its gate/up kernel;
+ * k3_router_topk(_latent): the projection kernel; k3_moe_block: its first
+ * kernel; the others: their only or first kernel. NULL events clear the hook. The records are plain
  * hipEventRecord calls, so they time eager calls; inside a stream capture
  * they only mark capture dependencies (ROCm rejects external event nodes).
  * Process-wide state, for measurement only; not safe against concurrent
@@ -101,19 +104,16 @@ int k3_trace_events(int op, void *begin, void *end);
 
 /* ------------------------------------------------------------ workspace sizes
  * Bytes of device workspace each entry point needs for the given shape
- * (16-byte aligned, caller-owned). k3_router_topk and k3_oproj_residual keep
- * a completion counter in the first 4 bytes of theirs: that workspace must
- * be zero-filled once before its first use, and every call leaves the
- * counter at zero again (whatever the shape, so one workspace can serve
- * calls of different shapes of the same entry point, one at a time).
- * The other workspaces need no initialisation. A workspace serves one call
- * at a time: calls that may overlap need workspaces of their own.
+ * (16-byte aligned, caller-owned). Workspaces need no initialisation and
+ * keep no state between calls. A workspace serves one call at a time: calls
+ * that may overlap need workspaces of their own.
  */
 size_t k3_router_topk_workspace_size(int b, int E);
 size_t k3_proj_skinny_workspace_size(int b, int K, int N);
 size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I, int d_out);
 size_t k3_shared_expert_workspace_size(int b, int d, int I);
 size_t k3_oproj_residual_workspace_size(int b, int K, int d);
+size_t k3_moe_block_workspace_size(int b, int d, int E, int k, int d_lat, int I, int I_s);
 
 /* ------------------------------------------------------------ entry points */
 
@@ -134,14 +134,34 @@ size_t k3_oproj_residual_workspace_size(int b, int K, int d);
  * bias     device, [E] fp32, or NULL for none
  * topk_ids device, [b x k] int32 (output)
  * topk_w   device, [b x k] fp32 (output)
- * workspace device, >= k3_router_topk_workspace_size(b, E) bytes,
- *          zero-filled before first use (see above)
+ * workspace device, >= k3_router_topk_workspace_size(b, E) bytes
  * Limits: 1 <= b <= 64, 1 <= k <= min(E, 32), E <= 1024.
  */
 int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
                    const uint16_t *w_router, const float *bias, int E, int k,
                    int32_t *topk_ids, float *topk_w,
                    void *workspace, size_t ws_bytes, void *stream);
+
+/* Router scores, top-k selection and the latent input projection in one
+ * pass over the same input. "Hyper Optimizing Kimi K3 in vLLM", Part 1
+ * section 3: the router scores and the latent input projection are combined
+ * into one matrix multiplication, removing a second read of the input and
+ * a kernel launch before the experts run.
+ *
+ * Computes exactly what k3_router_topk(x, ...) and
+ * k3_proj_skinny(x, w_lat -> z) compute, with one pass over the router and
+ * latent rows when b <= 4 (then a small top-k kernel) and as the separate
+ * computations otherwise.
+ *
+ * w_lat device, [d_lat x d] bf16;  z device, [b x d_lat] bf16 (output), row
+ * stride ldz; the other arguments, the workspace and the limits are those
+ * of k3_router_topk.
+ */
+int k3_router_topk_latent(const uint16_t *x, int64_t ldx, int b, int d,
+                          const uint16_t *w_router, const float *bias, int E, int k,
+                          const uint16_t *w_lat, int d_lat, int32_t *topk_ids, float *topk_w,
+                          uint16_t *z, int64_t ldz, void *workspace, size_t ws_bytes,
+                          void *stream);
 
 /* Skinny projection y = x . W^T, for the latent input projection
  * (Part 1 section 3) and the attention input projection (Part 1 section 1,
@@ -210,6 +230,37 @@ int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d,
                      float *y_s, int cu_budget,
                      void *workspace, size_t ws_bytes, void *stream);
 
+/* The whole MoE block on one stream: router top-k, latent projection, shared
+ * expert and routed experts, y = shared(x) + sum_j w_j routed_j(latent(x)).
+ * "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 3: router and latent
+ * projection share one matrix pass; the shared expert's work overlaps the
+ * routing. At b <= 4 the block runs as four kernels and nothing waits on
+ * another stream:
+ *   1. one pass over x for the router rows, the latent rows and the shared
+ *      expert's gate/up rows (logits, z, shared h);
+ *   2. the top-k in one workgroup while all the others stream the shared
+ *      expert's down projection (y_s);
+ *   3. routed gate/up + SwiGLU (after the permutation when b > 1);
+ *   4. routed down projection with the weighted combine, y_s added.
+ * Above b = 4 it runs the MFMA variants of the same steps in sequence.
+ * Results equal k3_router_topk_latent + k3_shared_expert + k3_moe_experts
+ * on the same inputs.
+ *
+ * x [b x d] bf16 (ldx); w_router [E x d], bias [E] fp32 or NULL, w_lat
+ * [d_lat x d], w13 [E x 2I x d_lat], w2 [E x d x I], w13_s [2I_s x d],
+ * w2_s [d x I_s] bf16. Outputs: topk_ids [b x k] int32, topk_w [b x k] fp32,
+ * z [b x d_lat] bf16 (ldz), y_s [b x d] fp32 (the shared expert's output),
+ * y [b x d] bf16. workspace >= k3_moe_block_workspace_size(...) bytes.
+ * Limits: those of k3_router_topk_latent, k3_shared_expert and
+ * k3_moe_experts.
+ */
+int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
+                 const float *bias, int E, int k, const uint16_t *w_lat, int d_lat,
+                 const uint16_t *w13, const uint16_t *w2, int I, const uint16_t *w13_s,
+                 const uint16_t *w2_s, int I_s, int32_t *topk_ids, float *topk_w, uint16_t *z,
+                 int64_t ldz, float *y_s, uint16_t *y, void *workspace, size_t ws_bytes,
+                 void *stream);
+
 /* Attention output projection with residual add and RMSNorm (Part 1
  * section 2, "Overlap computation and communication": the output
  * projection is fused with the attention residual that follows it).
@@ -225,8 +276,7 @@ int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d,
  * gamma    device, [d] bf16
  * y_norm   device, [b x d] bf16 (output); must not overlap residual or a
  * The norm is taken over fp32 h, before h is rounded for the store.
- * workspace: >= k3_oproj_residual_workspace_size(b, K, d) bytes,
- *          zero-filled before first use (see above).
+ * workspace: >= k3_oproj_residual_workspace_size(b, K, d) bytes.
  * Limits: 1 <= b <= 64, d % 8 == 0, eps >= 0.
  */
 int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,

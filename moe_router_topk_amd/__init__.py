@@ -16,8 +16,9 @@ import torch
 
 __all__ = [
     "K3Error", "lib", "library_path",
-    "k3_router_topk", "k3_proj_skinny", "k3_moe_experts", "k3_shared_expert",
-    "k3_oproj_residual", "k3_prefetch", "k3_get_last_dispatch", "k3_force_variant",
+    "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
+    "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_moe_block",
+    "k3_get_last_dispatch", "k3_force_variant",
     "k3_trace_events", "HipEvent",
     "k3_status_string", "k3_version", "workspace_size",
     "OP", "VARIANT", "EXPORTED_SYMBOLS",
@@ -28,7 +29,7 @@ _LIB_PATH = os.path.join(_HERE, "libk3dec.so")
 _lib = None
 
 OP = {"router_topk": 0, "proj_skinny": 1, "moe_experts": 2, "shared_expert": 3,
-      "oproj_residual": 4, "prefetch": 5}
+      "oproj_residual": 4, "prefetch": 5, "router_latent": 6, "moe_block": 7}
 VARIANT = {"none": 0, "dot2": 1, "mfma": 2, "grouped": 3, "stream": 4}
 VARIANT_NAME = {v: k for k, v in VARIANT.items()}
 
@@ -36,9 +37,9 @@ EXPORTED_SYMBOLS = [
     "k3_status_string", "k3_version", "k3_get_last_dispatch", "k3_force_variant",
     "k3_trace_events", "k3_router_topk_workspace_size", "k3_proj_skinny_workspace_size",
     "k3_moe_experts_workspace_size", "k3_shared_expert_workspace_size",
-    "k3_oproj_residual_workspace_size",
-    "k3_router_topk", "k3_proj_skinny", "k3_moe_experts", "k3_shared_expert",
-    "k3_oproj_residual", "k3_prefetch",
+    "k3_oproj_residual_workspace_size", "k3_moe_block_workspace_size",
+    "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
+    "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_moe_block",
 ]
 
 _vp = ctypes.c_void_p
@@ -83,12 +84,18 @@ def lib():
     L.k3_moe_experts_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
     L.k3_shared_expert_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_oproj_residual_workspace_size.argtypes = [_i32, _i32, _i32]
+    L.k3_moe_block_workspace_size.argtypes = [_i32] * 7
     for f in ("k3_router_topk_workspace_size", "k3_proj_skinny_workspace_size",
               "k3_moe_experts_workspace_size", "k3_shared_expert_workspace_size",
-              "k3_oproj_residual_workspace_size"):
+              "k3_oproj_residual_workspace_size", "k3_moe_block_workspace_size"):
         getattr(L, f).restype = _sz
+    L.k3_moe_block.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp,
+                               _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]
+    L.k3_moe_block.restype = _i32
     L.k3_router_topk.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                  _sz, _vp]
+    L.k3_router_topk_latent.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32,
+                                        _vp, _vp, _vp, _i64, _vp, _sz, _vp]
     L.k3_proj_skinny.argtypes = [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _i64, _vp, _sz, _vp]
     L.k3_moe_experts.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                  _i32, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
@@ -97,8 +104,8 @@ def lib():
     L.k3_oproj_residual.argtypes = [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, ctypes.c_float,
                                     _vp, _vp, _sz, _vp]
     L.k3_prefetch.argtypes = [_vp, _sz, _i32, _vp]
-    for f in ("k3_router_topk", "k3_proj_skinny", "k3_moe_experts", "k3_shared_expert",
-              "k3_oproj_residual", "k3_prefetch"):
+    for f in ("k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
+              "k3_shared_expert", "k3_oproj_residual", "k3_prefetch"):
         getattr(L, f).restype = _i32
     _lib = L
     return _lib
@@ -133,6 +140,7 @@ def _hiprt():
         _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         _hip.hipEventDestroy.argtypes = [_vp]
         _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        _hip.hipGetLastError.restype = ctypes.c_int
     return _hip
 
 
@@ -144,13 +152,15 @@ class HipEvent:
         self.handle = ctypes.c_void_p()
         rc = _hiprt().hipEventCreate(ctypes.byref(self.handle))
         if rc != 0:
+            _hiprt().hipGetLastError()
             raise RuntimeError(f"hipEventCreate failed ({rc})")
 
     def elapsed_ms(self, end: "HipEvent") -> float:
         ms = ctypes.c_float()
         rc = _hiprt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
         if rc != 0:
-            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            _hiprt().hipGetLastError()  # clear it, or the next runtime call reports it
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc}): event not recorded?")
         return ms.value
 
     def __del__(self):
@@ -209,8 +219,7 @@ def _workspace(device, nbytes: int, tag: str):
     key = (device.index if device.index is not None else torch.cuda.current_device(), tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        # zero-filled: the router and o-proj workspaces hold completion counters
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -228,6 +237,9 @@ def workspace_size(op: str, **kw) -> int:
         return L.k3_shared_expert_workspace_size(kw["b"], kw["d"], kw["I"])
     if op == "oproj_residual":
         return L.k3_oproj_residual_workspace_size(kw["b"], kw["K"], kw["d"])
+    if op == "moe_block":
+        return L.k3_moe_block_workspace_size(kw["b"], kw["d"], kw["E"], kw["k"], kw["d_lat"],
+                                             kw["I"], kw["I_s"])
     raise ValueError(op)
 
 
@@ -248,6 +260,29 @@ def k3_router_topk(x, w_router, bias, k, topk_ids=None, topk_w=None, workspace=N
         _ptr(x), _ld(x), b, d, _ptr(w_router), _ptr(bias), E, k, _ptr(topk_ids), _ptr(topk_w),
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
     return topk_ids, topk_w
+
+
+def k3_router_topk_latent(x, w_router, bias, k, w_lat, topk_ids=None, topk_w=None, z=None,
+                          workspace=None, stream=None):
+    """(topk_ids, topk_w, z): router top-k and the latent projection z = x . w_lat^T
+    from one pass over x."""
+    dev = _dev(x)
+    b, d = x.shape
+    E = w_router.shape[0]
+    d_lat = w_lat.shape[0]
+    if topk_ids is None:
+        topk_ids = torch.empty((b, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((b, k), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((b, d_lat), dtype=torch.bfloat16, device=dev)
+    nbytes = lib().k3_router_topk_workspace_size(b, E)
+    ws = workspace if workspace is not None else _workspace(dev, nbytes, "router_topk")
+    _check("k3_router_topk_latent", lib().k3_router_topk_latent(
+        _ptr(x), _ld(x), b, d, _ptr(w_router), _ptr(bias), E, k, _ptr(w_lat), d_lat,
+        _ptr(topk_ids), _ptr(topk_w), _ptr(z), _ld(z), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
+    return topk_ids, topk_w, z
 
 
 def k3_proj_skinny(x, w, y=None, workspace=None, stream=None):
@@ -318,6 +353,34 @@ def k3_oproj_residual(a, w_o, residual, gamma, eps, y_norm=None, workspace=None,
         _ptr(a), _ld(a), b, K, _ptr(w_o), d, _ptr(residual), _ptr(gamma), float(eps),
         _ptr(y_norm), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
     return y_norm
+
+
+def k3_moe_block(x, w_router, bias, k, w_lat, w13, w2, w13_s, w2_s, topk_ids=None,
+                 topk_w=None, z=None, y_s=None, y=None, workspace=None, stream=None):
+    """The whole MoE block on one stream: returns (y, topk_ids, topk_w, z, y_s)."""
+    dev = _dev(x)
+    b, d = x.shape
+    E = w_router.shape[0]
+    d_lat = w_lat.shape[0]
+    I = w13.shape[1] // 2
+    I_s = w13_s.shape[0] // 2
+    if topk_ids is None:
+        topk_ids = torch.empty((b, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((b, k), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((b, d_lat), dtype=torch.bfloat16, device=dev)
+    if y_s is None:
+        y_s = torch.empty((b, d), dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((b, d), dtype=torch.bfloat16, device=dev)
+    nbytes = lib().k3_moe_block_workspace_size(b, d, E, k, d_lat, I, I_s)
+    ws = workspace if workspace is not None else _workspace(dev, nbytes, "moe_block")
+    _check("k3_moe_block", lib().k3_moe_block(
+        _ptr(x), _ld(x), b, d, _ptr(w_router), _ptr(bias), E, k, _ptr(w_lat), d_lat, _ptr(w13),
+        _ptr(w2), I, _ptr(w13_s), _ptr(w2_s), I_s, _ptr(topk_ids), _ptr(topk_w), _ptr(z), _ld(z),
+        _ptr(y_s), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+    return y, topk_ids, topk_w, z, y_s
 
 
 def k3_prefetch(t, nbytes=None, cu_budget=0, stream=None):

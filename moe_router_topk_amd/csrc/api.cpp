@@ -46,12 +46,16 @@ void record_dispatch(int op, int variant) {
 }
 
 void trace_begin(int op, hipStream_t s) {
+    if (op < 0 || op >= 8)
+        return;
     void *ev = g_trace_begin[op].load();
     if (ev)
         (void)hipEventRecord((hipEvent_t)ev, s);
 }
 
 void trace_end(int op, hipStream_t s) {
+    if (op < 0 || op >= 8)
+        return;
     void *ev = g_trace_end[op].load();
     if (ev)
         (void)hipEventRecord((hipEvent_t)ev, s);
@@ -83,14 +87,15 @@ int k3_get_last_dispatch(int op) {
 }
 
 int k3_force_variant(int op, int variant) {
-    if (op < 0 || op > K3_OP_PREFETCH || variant < K3_VARIANT_NONE || variant > K3_VARIANT_STREAM)
+    if (op < 0 || op > K3_OP_MOE_BLOCK || variant < K3_VARIANT_NONE ||
+        variant > K3_VARIANT_STREAM)
         return K3_ERR_INVALID_ARG;
     k3::g_forced_variant[op].store(variant);
     return K3_OK;
 }
 
 int k3_trace_events(int op, void *begin, void *end) {
-    if (op < 0 || op > K3_OP_PREFETCH || (!begin) != (!end))
+    if (op < 0 || op > K3_OP_MOE_BLOCK || (!begin) != (!end))
         return K3_ERR_INVALID_ARG;
     k3::g_trace_begin[op].store(begin);
     k3::g_trace_end[op].store(end);

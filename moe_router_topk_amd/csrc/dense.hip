@@ -14,12 +14,11 @@
 //    work-splitting kernel the same section uses at larger batch, with the
 //    split kept inside one workgroup so no partial sums go through HBM.
 //
-// Router top-k and RMSNorm need every output of their projection. On the
-// dot2 path they run in the projection kernel itself: each workgroup
-// publishes its results, a device-scope fence orders them before a counter
-// increment, and the workgroup that brings the counter to the grid size
-// (after an acquire fence) finishes the job and resets the counter. All
-// cross-workgroup sums run in a fixed order, so results are deterministic.
+// Router top-k and RMSNorm need every output of their projection; each runs
+// as a small kernel after it. (Finishing them in the last workgroup of the
+// projection would need a device-scope release per workgroup, which on this
+// multi-XCD part writes back the L2 and drains every load in flight.) All
+// sums run in a fixed order, so results are deterministic.
 #include <math.h>
 
 #include "k3_device.h"
@@ -79,8 +78,6 @@ k_dense_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, const uint16_t 
              int N, int K, int rpw, Epi epi) {
     extern __shared__ u32x4 xs[];
     const int nv = K >> 3;
-    stage_rows(xs, nv, b, nv, [&](int t) { return x + (int64_t)t * ldx; });
-    __syncthreads();
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
     const int r0 = wave * rpw, r1 = min(N, r0 + rpw);
@@ -89,69 +86,14 @@ k_dense_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, const uint16_t 
         [&](int r, int t, float s) {
             if (lane == 0)
                 epi(t, r, s);
+        },
+        [&]() {
+            stage_rows(xs, nv, b, nv, [&](int t) { return x + (int64_t)t * ldx; });
+            __syncthreads();
         });
 }
 
 // ------------------------------------------------------------------ top-k
-// One wave picks token t's k experts: lane l holds logits l, l + 64, ...;
-// k rounds of a wave-wide argmax under the order (logit desc, index asc);
-// lane j keeps the j-th pick. The weights are the softmax over the k picked
-// logits (the full softmax renormalised over the selection).
-__device__ void topk_wave(const float *logits, int E, int k, int32_t *ids, float *wts) {
-    constexpr int PER = K3_MAX_EXPERTS / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    float v[PER];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = i * kWave + lane;
-        float l = -INFINITY;
-        if (e < E)
-            l = logits[e];
-        else
-            taken |= 1u << i;
-        v[i] = (l != l) ? -INFINITY : l;  // NaN never outranks a number
-    }
-    float sel_v = 0.0f, top = 0.0f;
-    int sel_e = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = i * kWave + lane;
-            if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-                bv = v[i];
-                be = e;
-            }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, kWave);
-            const int oe = __shfl_xor(be, m, kWave);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & (kWave - 1)) == lane)
-            taken |= 1u << (be / kWave);
-        if (lane == j) {
-            sel_v = bv;
-            sel_e = be;
-        }
-        if (j == 0)
-            top = bv;
-    }
-    const float dl = (sel_v == top) ? 0.0f : sel_v - top;
-    const float p = lane < k ? expf(dl) : 0.0f;
-    const float sum = wave_sum(p);
-    if (lane < k) {
-        ids[lane] = sel_e;
-        wts[lane] = p / sum;
-    }
-}
-
 __global__ void __launch_bounds__(kWave)
 k_topk_softmax(const float *__restrict__ logits, int E, int k, int32_t *__restrict__ ids,
                float *__restrict__ wts) {
@@ -159,108 +101,103 @@ k_topk_softmax(const float *__restrict__ logits, int E, int k, int32_t *__restri
     topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k);
 }
 
-// Publish this workgroup's results and count it; true in the one workgroup
-// that arrives last, after an acquire fence (all other workgroups' results
-// are then visible to its loads).
-__device__ bool arrive_last(int *counter) {
-    __shared__ int is_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0)
-        is_last = atomicAdd(counter, 1) == (int)gridDim.x - 1;
-    __syncthreads();
-    if (!is_last)
-        return false;
-    __threadfence();
-    return true;
-}
-
-// Router logits on the dot2 engine; the last workgroup runs the top-k for
-// every token (wave w takes tokens w, w + 4, ...) and resets the counter.
+// One pass over the staged input x for every row set that reads it: E router
+// rows (fp32 logits, + bias), NL latent rows (z, bf16) and, when Is > 0, the
+// shared expert's Is gate/up row pairs (h_s = silu(gate) * up, bf16). Wave w
+// takes an even share of each set, in that order, in one pipeline; the
+// router bias is staged in LDS beside x so the epilogues load nothing from
+// global memory behind the weight stream. No workgroup waits for another:
+// the top-k runs in the next kernel.
 template <int TM, int CB>
 __global__ void __launch_bounds__(kBlock)
-k_router_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, const uint16_t *__restrict__ W,
-              int E, int d, int rpw, const float *__restrict__ bias, float *logits, int *counter,
-              int k, int32_t *__restrict__ ids, float *__restrict__ wts) {
+k_rls_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, int d,
+           const uint16_t *__restrict__ Wr, const float *__restrict__ bias, int E,
+           float *__restrict__ logits, const uint16_t *__restrict__ Wl, int NL,
+           uint16_t *__restrict__ z, int64_t ldz, const uint16_t *__restrict__ W13s, int Is,
+           uint16_t *__restrict__ hs) {
     extern __shared__ u32x4 xs[];
     const int nv = d >> 3;
-    stage_rows(xs, nv, b, nv, [&](int t) { return x + (int64_t)t * ldx; });
-    __syncthreads();
+    float *bs = reinterpret_cast<float *>(xs + b * nv);
     const int lane = threadIdx.x & (kWave - 1);
-    const int wq = threadIdx.x / kWave;
-    const int wave = blockIdx.x * (kBlock / kWave) + wq;
-    const int r0 = wave * rpw, r1 = min(E, r0 + rpw);
-    stream_rows<TM, 16 / CB, CB>(
-        r0, r1, nv, xs, nv, b, [&](int r) { return W + (int64_t)r * d; },
-        [&](int r, int t, float s) {
-            if (lane == 0)
-                logits[(int64_t)t * E + r] = bias ? s + bias[r] : s;
+    const int waves = gridDim.x * (kBlock / kWave);
+    const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    int ra, rb, la, lb, sa, sb;
+    split_range(E, waves, wave, ra, rb);
+    split_range(NL, waves, waves - 1 - wave, la, lb);  // spare latent rows to router-free waves
+    split_range(Is, waves, wave, sa, sb);
+    const int nr = rb - ra, nrl = nr + (lb - la);
+    float gsave[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+        gsave[t] = 0.0f;
+    stream_rows<TM, (CB == 1 && TM > 1) ? 4 : 16 / CB, CB>(
+        0, nrl + 2 * (sb - sa), nv, xs, nv, b,
+        [&](int i) {
+            if (i < nr)
+                return Wr + (int64_t)(ra + i) * d;
+            if (i < nrl)
+                return Wl + (int64_t)(la + i - nr) * d;
+            const int q = i - nrl, j = sa + (q >> 1);
+            return W13s + (int64_t)((q & 1) ? Is + j : j) * d;
+        },
+        [&](int i, int t, float s) {
+            if (i < nr) {
+                if (lane == 0)
+                    logits[(int64_t)t * E + ra + i] = s + bs[ra + i];
+            } else if (i < nrl) {
+                if (lane == 0)
+                    z[(int64_t)t * ldz + la + i - nr] = f32_to_bf16(s);
+            } else {
+                const int q = i - nrl;
+                if ((q & 1) == 0)
+                    gsave[t] = s;
+                else if (lane == 0)
+                    hs[(int64_t)t * Is + sa + (q >> 1)] = f32_to_bf16(silu(gsave[t]) * s);
+            }
+        },
+        [&]() {
+            stage_rows(xs, nv, b, nv, [&](int t) { return x + (int64_t)t * ldx; });
+            for (int e = threadIdx.x; e < E; e += kBlock)
+                bs[e] = bias ? bias[e] : 0.0f;
+            __syncthreads();
         });
-    if (!arrive_last(counter))
-        return;
-    for (int t = wq; t < b; t += kBlock / kWave)
-        topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k);
-    if (threadIdx.x == 0)
-        atomicExch(counter, 0);
 }
 
-// Output projection + residual on the dot2 engine. Lane 0 of each wave keeps
-// the running sum of h^2 per token over its rows; the workgroup's four wave
-// sums are added in order into ss_part[block][t]; the last workgroup adds the
-// ss_part of all workgroups in block order and writes y = h * inv * gamma.
+// Output projection + residual on the dot2 engine: h = r + a . Wo^T, written
+// as fp32 (for the norm) and bf16 (back into r). The residuals of the
+// block's rows are staged in LDS with the activations, so the epilogue loads
+// nothing from global memory behind the weight stream. RMSNorm follows in
+// its own kernel.
 template <int TM, int CB>
 __global__ void __launch_bounds__(kBlock)
 k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t *__restrict__ Wo,
-             int d, int K, int rpw, uint16_t *res, const uint16_t *__restrict__ gamma, float eps,
-             float *h32, float *ss_part, int *counter, uint16_t *__restrict__ y) {
+             int d, int K, int rpw, uint16_t *res, float *__restrict__ h32) {
     extern __shared__ u32x4 xs[];
-    __shared__ float wss[kBlock / kWave][TM];
-    __shared__ float inv[TM];
     const int nv = K >> 3;
-    stage_rows(xs, nv, b, nv, [&](int t) { return a + (int64_t)t * lda; });
-    __syncthreads();
+    const int rows_blk = rpw * (kBlock / kWave);
+    const int rblk = blockIdx.x * rows_blk;
+    float *rs = reinterpret_cast<float *>(xs + b * nv);  // [b][rows_blk]
     const int lane = threadIdx.x & (kWave - 1);
-    const int wq = threadIdx.x / kWave;
-    const int wave = blockIdx.x * (kBlock / kWave) + wq;
+    const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
     const int r0 = wave * rpw, r1 = min(d, r0 + rpw);
-    const EpiResidual er{res, h32, d};
-    float ss[TM];
-#pragma unroll
-    for (int t = 0; t < TM; ++t)
-        ss[t] = 0.0f;
     stream_rows<TM, 16 / CB, CB>(
         r0, r1, nv, xs, nv, b, [&](int r) { return Wo + (int64_t)r * K; },
         [&](int r, int t, float s) {
             if (lane == 0) {
-                const float h = er(t, r, s);
-                ss[t] += h * h;
+                const int64_t i = (int64_t)t * d + r;
+                const float h = rs[t * rows_blk + (r - rblk)] + s;
+                h32[i] = h;
+                res[i] = f32_to_bf16(h);
             }
+        },
+        [&]() {
+            stage_rows(xs, nv, b, nv, [&](int t) { return a + (int64_t)t * lda; });
+            for (int i = threadIdx.x; i < b * rows_blk; i += kBlock) {
+                const int t = i / rows_blk, r = rblk + (i - t * rows_blk);
+                rs[i] = r < d ? bf16_to_f32(res[(int64_t)t * d + r]) : 0.0f;
+            }
+            __syncthreads();
         });
-    if (lane == 0)
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-            wss[wq][t] = ss[t];
-    __syncthreads();
-    if (threadIdx.x < b)
-        ss_part[(int64_t)blockIdx.x * TM + threadIdx.x] =
-            (wss[0][threadIdx.x] + wss[1][threadIdx.x]) + (wss[2][threadIdx.x] + wss[3][threadIdx.x]);
-    if (!arrive_last(counter))
-        return;
-    if (wq < b) {  // wave t sums token t's partials: lanes take blocks l, l+64, ...
-        float s = 0.0f;
-        for (int g = lane; g < (int)gridDim.x; g += kWave)
-            s += ss_part[(int64_t)g * TM + wq];
-        s = wave_sum(s);
-        if (lane == 0)
-            inv[wq] = 1.0f / sqrtf(s / (float)d + eps);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < b * d; i += kBlock) {
-        const int t = i / d, n = i - t * d;
-        y[i] = f32_to_bf16(h32[i] * inv[t] * bf16_to_f32(gamma[n]));
-    }
-    if (threadIdx.x == 0)
-        atomicExch(counter, 0);
 }
 
 // ------------------------------------------------------------------ mfma engine
@@ -440,29 +377,24 @@ static int pick_dense_variant(int op, int b, int K) {
 using namespace k3;
 
 // ------------------------------------------------------------------ workspace layouts
-// The completion counter sits at offset 0, where it stays whatever the shape
-// of the call, so a workspace reused for other shapes of the same entry
-// point still finds it at zero.
+// Each workspace starts with a 256-byte head that no kernel touches.
 namespace {
-constexpr size_t kCounterBytes = 256;
-size_t oproj_h32_offset() { return kCounterBytes; }
-size_t oproj_ss_offset(int b, int d) {
-    return kCounterBytes + align_up((size_t)b * d * sizeof(float), 256);
-}
-size_t router_logits_offset() { return kCounterBytes; }
+constexpr size_t kHeadBytes = 256;
+size_t router_logits_offset() { return kHeadBytes; }
+size_t oproj_h32_offset() { return kHeadBytes; }
 }  // namespace
 
 extern "C" size_t k3_router_topk_workspace_size(int b, int E) {
     if (b <= 0 || E <= 0)
         return 0;
-    return router_logits_offset() + align_up((size_t)b * E * sizeof(float), 256);
+    return kHeadBytes + align_up((size_t)b * E * sizeof(float), 256);
 }
 
 extern "C" size_t k3_oproj_residual_workspace_size(int b, int K, int d) {
     (void)K;
     if (b <= 0 || d <= 0)
         return 0;
-    return oproj_ss_offset(b, d) + align_up((size_t)1024 * kDot2MaxTokens * sizeof(float), 256);
+    return kHeadBytes + align_up((size_t)b * d * sizeof(float), 256);
 }
 
 extern "C" size_t k3_proj_skinny_workspace_size(int b, int K, int N) {
@@ -471,6 +403,89 @@ extern "C" size_t k3_proj_skinny_workspace_size(int b, int K, int N) {
     (void)N;
     return 0;
 }
+
+// ------------------------------------------------------------------ launchers
+namespace k3 {
+
+bool rls_fits(int b, int d, int E) {
+    return dot2_fits(b, d) && (size_t)b * d * 2 + (size_t)E * 4 <= 65536;
+}
+
+void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
+                const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
+                uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
+                hipStream_t s) {
+    const int cus = budget_grid(1 << 30, 0, 1);
+    const int grid = (NL > 0 || Is > 0) ? cus : (E + kBlock / kWave - 1) / (kBlock / kWave);
+    const size_t lds = (size_t)b * d * sizeof(uint16_t) + (size_t)E * sizeof(float);
+    const int cb = d > 2048 ? 16 : (d > 512 ? 4 : 1);
+#define K3_RLS(TM_, CB_)                                                                       \
+    k_rls_dot2<TM_, CB_><<<grid, kBlock, lds, s>>>(x, ldx, b, d, w_router, bias, E, logits,   \
+                                                   w_lat, NL, z, ldz, w13s, Is, hs)
+    if (b == 1) {
+        if (cb == 16)
+            K3_RLS(1, 16);
+        else if (cb == 4)
+            K3_RLS(1, 4);
+        else
+            K3_RLS(1, 1);
+    } else {
+        if (cb == 16)
+            K3_RLS(kDot2MaxTokens, 16);
+        else if (cb == 4)
+            K3_RLS(kDot2MaxTokens, 4);
+        else
+            K3_RLS(kDot2MaxTokens, 1);
+    }
+#undef K3_RLS
+}
+
+void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *wts,
+                 hipStream_t s) {
+    k_topk_softmax<<<b, kWave, 0, s>>>(logits, E, k, ids, wts);
+}
+
+void launch_dense_bf16(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
+                       uint16_t *y, int64_t ldy, hipStream_t s) {
+    launch_dense(pick_dense_variant(-1, b, K), x, ldx, b, W, N, K, EpiBf16{y, ldy}, s);
+}
+
+void launch_dense_logits(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int E, int K,
+                         const float *bias, float *logits, hipStream_t s) {
+    launch_dense(pick_dense_variant(-1, b, K), x, ldx, b, W, E, K, EpiLogits{logits, E, bias}, s);
+}
+
+}  // namespace k3
+
+namespace {
+
+int check_router_args(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
+                      int E, int k, const int32_t *ids, const float *wts, void *workspace,
+                      size_t ws_bytes) {
+    if (!x || !w_router || !ids || !wts)
+        return K3_ERR_INVALID_ARG;
+    if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || ldx < d)
+        return K3_ERR_INVALID_ARG;
+    if (b > K3_MAX_BATCH || E > K3_MAX_EXPERTS || k > K3_MAX_TOPK || k > E || d % 8 || ldx % 8 ||
+        !aligned16(x) || !aligned16(w_router))
+        return K3_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < k3_router_topk_workspace_size(b, E) || !aligned16(workspace))
+        return K3_ERR_WORKSPACE;
+    return K3_OK;
+}
+
+// dot2 for the router (+ latent) only when the bias fits beside the tokens
+int pick_router_variant(int op, int b, int d, int E) {
+    int v = pick_dense_variant(op, b, d);
+    if (v == K3_VARIANT_DOT2 && !rls_fits(b, d, E)) {
+        if (forced_variant(op) == K3_VARIANT_DOT2)
+            return -1;
+        v = d % 128 == 0 ? K3_VARIANT_MFMA : -1;
+    }
+    return v;
+}
+
+}  // namespace
 
 // ------------------------------------------------------------------ entry points
 extern "C" int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K, const uint16_t *w,
@@ -501,46 +516,62 @@ extern "C" int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
                               const uint16_t *w_router, const float *bias, int E, int k,
                               int32_t *topk_ids, float *topk_w, void *workspace, size_t ws_bytes,
                               void *stream) {
-    if (!x || !w_router || !topk_ids || !topk_w)
-        return K3_ERR_INVALID_ARG;
-    if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || ldx < d)
-        return K3_ERR_INVALID_ARG;
-    if (b > K3_MAX_BATCH || E > K3_MAX_EXPERTS || k > K3_MAX_TOPK || k > E || d % 8 || ldx % 8 ||
-        !aligned16(x) || !aligned16(w_router))
-        return K3_ERR_UNSUPPORTED;
-    if (!workspace || ws_bytes < k3_router_topk_workspace_size(b, E) || !aligned16(workspace))
-        return K3_ERR_WORKSPACE;
-    const int variant = pick_dense_variant(K3_OP_ROUTER_TOPK, b, d);
+    const int chk = check_router_args(x, ldx, b, d, w_router, E, k, topk_ids, topk_w, workspace,
+                                      ws_bytes);
+    if (chk != K3_OK)
+        return chk;
+    const int variant = pick_router_variant(K3_OP_ROUTER_TOPK, b, d, E);
     if (variant < 0)
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    int *counter = (int *)workspace;
     float *logits = (float *)((char *)workspace + router_logits_offset());
     trace_begin(K3_OP_ROUTER_TOPK, s);
-    if (variant == K3_VARIANT_DOT2) {
-        const Dot2Geom g = dot2_geom(E, d, b, 0);
-        if (g.cb == 16 && b == 1)
-            k_router_dot2<1, 16><<<g.grid, kBlock, g.lds, s>>>(x, ldx, b, w_router, E, d, g.rpw,
-                                                              bias, logits, counter, k, topk_ids,
-                                                              topk_w);
-        else if (g.cb == 16)
-            k_router_dot2<kDot2MaxTokens, 16><<<g.grid, kBlock, g.lds, s>>>(
-                x, ldx, b, w_router, E, d, g.rpw, bias, logits, counter, k, topk_ids, topk_w);
-        else if (g.cb == 4)
-            k_router_dot2<kDot2MaxTokens, 4><<<g.grid, kBlock, g.lds, s>>>(
-                x, ldx, b, w_router, E, d, g.rpw, bias, logits, counter, k, topk_ids, topk_w);
-        else
-            k_router_dot2<kDot2MaxTokens, 1><<<g.grid, kBlock, g.lds, s>>>(
-                x, ldx, b, w_router, E, d, g.rpw, bias, logits, counter, k, topk_ids, topk_w);
-        trace_end(K3_OP_ROUTER_TOPK, s);
-    } else {
+    if (variant == K3_VARIANT_DOT2)
+        launch_rls(x, ldx, b, d, w_router, bias, E, logits, nullptr, 0, nullptr, 0, nullptr, 0,
+                   nullptr, s);
+    else
         launch_dense(variant, x, ldx, b, w_router, E, d, EpiLogits{logits, E, bias}, s);
-        trace_end(K3_OP_ROUTER_TOPK, s);
-        k_topk_softmax<<<b, kWave, 0, s>>>(logits, E, k, topk_ids, topk_w);
-    }
+    trace_end(K3_OP_ROUTER_TOPK, s);
+    launch_topk(logits, b, E, k, topk_ids, topk_w, s);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_ROUTER_TOPK, variant);
+    return st;
+}
+
+extern "C" int k3_router_topk_latent(const uint16_t *x, int64_t ldx, int b, int d,
+                                     const uint16_t *w_router, const float *bias, int E, int k,
+                                     const uint16_t *w_lat, int d_lat, int32_t *topk_ids,
+                                     float *topk_w, uint16_t *z, int64_t ldz, void *workspace,
+                                     size_t ws_bytes, void *stream) {
+    const int chk = check_router_args(x, ldx, b, d, w_router, E, k, topk_ids, topk_w, workspace,
+                                      ws_bytes);
+    if (chk != K3_OK)
+        return chk;
+    if (!w_lat || !z)
+        return K3_ERR_INVALID_ARG;
+    if (d_lat <= 0 || ldz < d_lat)
+        return K3_ERR_INVALID_ARG;
+    if (!aligned16(w_lat))
+        return K3_ERR_UNSUPPORTED;
+    const int variant = pick_router_variant(K3_OP_ROUTER_LATENT, b, d, E);
+    if (variant < 0)
+        return K3_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    float *logits = (float *)((char *)workspace + router_logits_offset());
+    trace_begin(K3_OP_ROUTER_LATENT, s);
+    if (variant == K3_VARIANT_DOT2) {
+        launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, nullptr, 0,
+                   nullptr, s);
+    } else {
+        launch_dense(variant, x, ldx, b, w_router, E, d, EpiLogits{logits, E, bias}, s);
+        launch_dense(variant, x, ldx, b, w_lat, d_lat, d, EpiBf16{z, ldz}, s);
+    }
+    trace_end(K3_OP_ROUTER_LATENT, s);
+    launch_topk(logits, b, E, k, topk_ids, topk_w, s);
+    const int st = launch_status();
+    if (st == K3_OK)
+        record_dispatch(K3_OP_ROUTER_LATENT, variant);
     return st;
 }
 
@@ -552,45 +583,50 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         return K3_ERR_INVALID_ARG;
     if (b <= 0 || K <= 0 || d <= 0 || lda < K || !(eps >= 0.0f))
         return K3_ERR_INVALID_ARG;
-    if (b > K3_MAX_BATCH || K % 8 || lda % 8 || d % 8 || !aligned16(a) || !aligned16(w_o) ||
-        !aligned16(residual))
+    if (b > K3_MAX_BATCH || K % 8 || lda % 8 || d % 8 || !aligned16(a) || !aligned16(w_o))
         return K3_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < k3_oproj_residual_workspace_size(b, K, d) ||
         !aligned16(workspace))
         return K3_ERR_WORKSPACE;
-    const int variant = pick_dense_variant(K3_OP_OPROJ_RESIDUAL, b, K);
+    int variant = pick_dense_variant(K3_OP_OPROJ_RESIDUAL, b, K);
+    Dot2Geom g{};
+    if (variant == K3_VARIANT_DOT2) {
+        g = dot2_geom(d, K, b, 0);
+        g.lds += (size_t)b * g.rpw * (kBlock / kWave) * sizeof(float);  // staged residuals
+        if (g.lds > 65536) {
+            if (forced_variant(K3_OP_OPROJ_RESIDUAL) == K3_VARIANT_DOT2)
+                return K3_ERR_UNSUPPORTED;
+            variant = K % 128 == 0 ? K3_VARIANT_MFMA : -1;
+        }
+    }
     if (variant < 0)
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    char *ws = (char *)workspace;
-    int *counter = (int *)ws;
-    float *h32 = (float *)(ws + oproj_h32_offset());
-    float *ss_part = (float *)(ws + oproj_ss_offset(b, d));
+    float *h32 = (float *)((char *)workspace + oproj_h32_offset());
     trace_begin(K3_OP_OPROJ_RESIDUAL, s);
     if (variant == K3_VARIANT_DOT2) {
-        const Dot2Geom g = dot2_geom(d, K, b, 0);
-        if (g.grid > 1024)
-            return K3_ERR_UNSUPPORTED;
-        if (g.cb == 16 && b == 1)
-            k_oproj_dot2<1, 16><<<g.grid, kBlock, g.lds, s>>>(a, lda, b, w_o, d, K, g.rpw,
-                                                             residual, gamma, eps, h32, ss_part,
-                                                             counter, y_norm);
+#define K3_OPROJ(TM_, CB_)                                                                     \
+    k_oproj_dot2<TM_, CB_><<<g.grid, kBlock, g.lds, s>>>(a, lda, b, w_o, d, K, g.rpw, residual, \
+                                                         h32)
+        if (b == 1 && g.cb == 16)
+            K3_OPROJ(1, 16);
+        else if (b == 1 && g.cb == 4)
+            K3_OPROJ(1, 4);
+        else if (b == 1)
+            K3_OPROJ(1, 1);
         else if (g.cb == 16)
-            k_oproj_dot2<kDot2MaxTokens, 16><<<g.grid, kBlock, g.lds, s>>>(
-                a, lda, b, w_o, d, K, g.rpw, residual, gamma, eps, h32, ss_part, counter, y_norm);
+            K3_OPROJ(kDot2MaxTokens, 16);
         else if (g.cb == 4)
-            k_oproj_dot2<kDot2MaxTokens, 4><<<g.grid, kBlock, g.lds, s>>>(
-                a, lda, b, w_o, d, K, g.rpw, residual, gamma, eps, h32, ss_part, counter, y_norm);
+            K3_OPROJ(kDot2MaxTokens, 4);
         else
-            k_oproj_dot2<kDot2MaxTokens, 1><<<g.grid, kBlock, g.lds, s>>>(
-                a, lda, b, w_o, d, K, g.rpw, residual, gamma, eps, h32, ss_part, counter, y_norm);
-        trace_end(K3_OP_OPROJ_RESIDUAL, s);
+            K3_OPROJ(kDot2MaxTokens, 1);
+#undef K3_OPROJ
     } else {
         launch_dense(variant, a, lda, b, w_o, d, K, EpiResidualStore{EpiResidual{residual, h32, d}},
                      s);
-        trace_end(K3_OP_OPROJ_RESIDUAL, s);
-        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     }
+    trace_end(K3_OP_OPROJ_RESIDUAL, s);
+    k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_OPROJ_RESIDUAL, variant);

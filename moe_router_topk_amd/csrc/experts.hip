@@ -183,10 +183,8 @@ k_gateup_dot2(const uint16_t *__restrict__ z, int64_t ldz, int d,
         const int s1 = min(g1, (a + 1) * I);
         int e, p0, na;
         L.get(a, e, p0, na);
-        __syncthreads();
-        stage_rows(xs, nv, na, nv, [&](int t) { return z + (int64_t)L.token(p0 + t) * ldz; });
-        __syncthreads();
         if (na > 0) {
+            __syncthreads();  // the previous segment's readers of xs are done
             int j0, j1;
             split_range(s1 - s0, kBlock / kWave, wq, j0, j1);
             j0 += s0 - a * I;
@@ -207,6 +205,11 @@ k_gateup_dot2(const uint16_t *__restrict__ z, int64_t ldz, int d,
                         gsave[t] = s;
                     else if (lane == 0)
                         hbuf[(int64_t)(p0 + t) * I + (i >> 1)] = f32_to_bf16(silu(gsave[t]) * s);
+                },
+                [&]() {
+                    stage_rows(xs, nv, na, nv,
+                               [&](int t) { return z + (int64_t)L.token(p0 + t) * ldz; });
+                    __syncthreads();
                 });
         }
         s0 = s1;
@@ -239,10 +242,8 @@ k_down_dot2(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict
         const int s1 = min(g1, (a + 1) * d_out);
         int e, p0, na;
         L.get(a, e, p0, na);
-        __syncthreads();
-        stage_rows(xs, nv, na, nv, [&](int t) { return hbuf + (int64_t)(p0 + t) * I; });
-        __syncthreads();
         if (na > 0) {
+            __syncthreads();  // the previous segment's readers of xs are done
             int r0, r1;
             split_range(s1 - s0, kBlock / kWave, wq, r0, r1);
             r0 += s0 - a * d_out;
@@ -253,6 +254,10 @@ k_down_dot2(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict
                 [&](int r, int t, float s) {
                     if (lane == 0)
                         out(p0 + t, r, s);
+                },
+                [&]() {
+                    stage_rows(xs, nv, na, nv, [&](int t) { return hbuf + (int64_t)(p0 + t) * I; });
+                    __syncthreads();
                 });
         }
         s0 = s1;
@@ -419,29 +424,161 @@ k_down_mfma(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict
 }
 
 // ------------------------------------------------------------------ combine
-// y[t][r] = bf16(y_add[t][r] + sum_j w[t][j] * part[pos(t, j)][r]), slots in
-// order; pos = slot_pos[t k + j] (or j at batch 1 when ids[j] is valid).
+// y[t][r] = bf16(y_add[t][r] + sum_j w[t][j] * part[slot_pos[t][j]][r]),
+// slots added in order j = 0..k-1; eight slots' loads go out together.
 __global__ void __launch_bounds__(kBlock)
 k_combine(const float *__restrict__ part, int d_out, const int *__restrict__ slot_pos,
-          const int32_t *__restrict__ ids, int E, const float *__restrict__ topk_w, int b, int k,
-          const float *__restrict__ y_add, uint16_t *__restrict__ y) {
+          const float *__restrict__ topk_w, int b, int k, const float *__restrict__ y_add,
+          uint16_t *__restrict__ y) {
     const int i = blockIdx.x * kBlock + threadIdx.x;
     if (i >= b * d_out)
         return;
     const int t = i / d_out, r = i - t * d_out;
     float s = y_add ? y_add[i] : 0.0f;
-    for (int j = 0; j < k; ++j) {
-        int pos;
-        if (slot_pos) {
-            pos = slot_pos[t * k + j];
-        } else {
-            const int e = ids[j];
-            pos = (e >= 0 && e < E) ? j : -1;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float pv[8], wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            const int pos = j < k ? slot_pos[t * k + j] : -1;
+            wv[u] = pos >= 0 ? topk_w[t * k + j] : 0.0f;
+            pv[u] = pos >= 0 ? part[(int64_t)pos * d_out + r] : 0.0f;
         }
-        if (pos >= 0)
-            s += topk_w[t * k + j] * part[(int64_t)pos * d_out + r];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < k && slot_pos[t * k + j0 + u] >= 0)
+                s += wv[u] * pv[u];
     }
     y[i] = f32_to_bf16(s);
+}
+
+// slot_pos for batch 1 without a permutation: slot j sits at position j when
+// its id is valid.
+__global__ void k_slot_identity(const int32_t *__restrict__ ids, int k, int E, int *slot_pos) {
+    const int j = threadIdx.x;
+    if (j < k)
+        slot_pos[j] = (ids[j] >= 0 && ids[j] < E) ? j : -1;
+}
+
+// ------------------------------------------------------------------ batch-1 down
+// Batch 1 (the slots are the experts): the down projection with the weighted
+// combine folded in. Wave w owns an even share of the output rows; a unit is
+// one output row r and a group of four slots, i.e. four w2 rows (one per
+// slot's expert) of CPS 16-byte vectors per lane. Each lane accumulates
+// w_j * (its partial dot of slot j) over the row's units, so the row needs a
+// single wave reduction; then y[r] = bf16(y_add[r] + sum). The h rows of all
+// k slots sit in LDS. Slots with an id outside [0, E) are skipped.
+template <int CPS>
+__global__ void __launch_bounds__(kBlock)
+k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__ w2, int d_out,
+          const int32_t *__restrict__ ids, const float *__restrict__ topk_w, int k, int E,
+          const float *__restrict__ y_add, uint16_t *__restrict__ y) {
+    extern __shared__ u32x4 hs[];
+    __shared__ int sid[K3_MAX_TOPK];
+    __shared__ float sw[K3_MAX_TOPK];
+    const int nv = I >> 3;
+    if (threadIdx.x < k) {
+        const int e = ids[threadIdx.x];
+        const bool ok = e >= 0 && e < E;
+        sid[threadIdx.x] = ok ? e : -1;
+        sw[threadIdx.x] = ok ? topk_w[threadIdx.x] : 0.0f;
+    }
+    __syncthreads();  // the first unit's loads read sid
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = gridDim.x * (kBlock / kWave);
+    const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    int r0, r1;
+    split_range(d_out, waves, wave, r0, r1);
+    // y_add of the block's rows, staged with h so the epilogue loads nothing
+    int rblk, rblk_end, unused;
+    split_range(d_out, waves, blockIdx.x * (kBlock / kWave), rblk, unused);
+    split_range(d_out, waves, blockIdx.x * (kBlock / kWave) + kBlock / kWave - 1, unused, rblk_end);
+    const int rows_blk = rblk_end - rblk;
+    float *ya = reinterpret_cast<float *>(hs + k * nv);
+    const int groups = (k + 3) >> 2;
+    float acc = 0.0f;
+    stream_units<4 * CPS>(
+        0, (r1 - r0) * groups,
+        [&](u32x4 (&buf)[4 * CPS], int u) {
+            const int r = r0 + u / groups, g = u % groups;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = 4 * g + q;
+                const int e = j < k ? sid[j] : -1;
+                const uint16_t *row = w2 + ((int64_t)(e < 0 ? 0 : e) * d_out + r) * I;
+#pragma unroll
+                for (int c = 0; c < CPS; ++c) {
+                    const int v = c * kWave + lane;
+                    buf[q * CPS + c] = (e >= 0 && v < nv) ? ld_weight16(row + (int64_t)v * 8)
+                                                          : zero16();
+                }
+            }
+        },
+        [&](u32x4 (&buf)[4 * CPS], int u) {
+            const int r = r0 + u / groups, g = u % groups;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = 4 * g + q;
+                if (j < k && sid[j] >= 0) {
+                    float p = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < CPS; ++c) {
+                        const int v = c * kWave + lane;
+                        if (v < nv)
+                            p = dot8(buf[q * CPS + c], hs[j * nv + v], p);
+                    }
+                    acc += sw[j] * p;
+                }
+            }
+            if (g == groups - 1) {
+                const float sum = wave_sum(acc);
+                acc = 0.0f;
+                if (lane == 0)
+                    y[r] = f32_to_bf16(ya[r - rblk] + sum);
+            }
+        },
+        [&]() {
+            stage_rows(hs, nv, k, nv, [&](int j) { return hbuf + (int64_t)j * I; });
+            for (int i = threadIdx.x; i < rows_blk; i += kBlock)
+                ya[i] = (y_add && rblk + i < d_out) ? y_add[rblk + i] : 0.0f;
+            __syncthreads();
+        });
+}
+
+// ------------------------------------------------------------------ top-k + shared down
+// Second kernel of the fused MoE block: workgroup 0 picks every token's
+// experts from the logits the first kernel wrote (one wave per token); the
+// other workgroups stream the shared expert's down projection meanwhile, so
+// the selection's latency hides under useful weight reads.
+template <int TM, int CB>
+__global__ void __launch_bounds__(kBlock)
+k_topk_shared_down(const float *__restrict__ logits, int E, int k, int b,
+                   int32_t *__restrict__ ids, float *__restrict__ wts,
+                   const uint16_t *__restrict__ hs, int Is, const uint16_t *__restrict__ W2s,
+                   int d, float *__restrict__ y_s) {
+    const int wq = threadIdx.x / kWave;
+    if (blockIdx.x == 0) {
+        for (int t = wq; t < b; t += kBlock / kWave)
+            topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k);
+        return;
+    }
+    extern __shared__ u32x4 xs[];
+    const int nv = Is >> 3;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves = (gridDim.x - 1) * (kBlock / kWave);
+    const int wave = (blockIdx.x - 1) * (kBlock / kWave) + wq;
+    int r0, r1;
+    split_range(d, waves, wave, r0, r1);
+    stream_rows<TM, 16 / CB, CB>(
+        r0, r1, nv, xs, nv, b, [&](int r) { return W2s + (int64_t)r * Is; },
+        [&](int r, int t, float s) {
+            if (lane == 0)
+                y_s[(int64_t)t * d + r] = s;
+        },
+        [&]() {
+            stage_rows(xs, nv, b, nv, [&](int t) { return hs + (int64_t)t * Is; });
+            __syncthreads();
+        });
 }
 
 }  // namespace k3
@@ -478,6 +615,22 @@ MoeWorkspace moe_workspace_layout(int b, int E, int k, int I, int d_out) {
 }
 }  // namespace k3
 
+namespace {
+// Fused-block workspace: router logits, shared-expert h, then the routed
+// experts' workspace.
+struct BlockWorkspace {
+    size_t logits, hs, moe, total;
+};
+BlockWorkspace block_workspace_layout(int b, int E, int k, int I, int d, int I_s) {
+    BlockWorkspace w;
+    w.logits = 256;
+    w.hs = w.logits + align_up((size_t)b * E * sizeof(float), 256);
+    w.moe = w.hs + align_up((size_t)b * I_s * sizeof(uint16_t), 256);
+    w.total = w.moe + moe_workspace_layout(b, E, k, I, d).total;
+    return w;
+}
+}  // namespace
+
 extern "C" size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I, int d_out) {
     (void)d_in;
     if (b <= 0 || E <= 0 || k <= 0 || I <= 0 || d_out <= 0)
@@ -490,6 +643,14 @@ extern "C" size_t k3_shared_expert_workspace_size(int b, int d, int I) {
     if (b <= 0 || I <= 0)
         return 0;
     return align_up((size_t)b * I * sizeof(uint16_t), 256);
+}
+
+extern "C" size_t k3_moe_block_workspace_size(int b, int d, int E, int k, int d_lat, int I,
+                                              int I_s) {
+    (void)d_lat;
+    if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || I <= 0 || I_s <= 0)
+        return 0;
+    return block_workspace_layout(b, E, k, I, d, I_s).total;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -534,6 +695,120 @@ void launch_down_dot2(int tm, const uint16_t *hbuf, int I, const uint16_t *w2, i
 #undef K3_DOWN
 }
 
+void launch_down_b1(const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
+                    const int32_t *ids, const float *wts, int k, int E, const float *y_add,
+                    uint16_t *y, int cu_budget, hipStream_t s) {
+    const int grid = dot2_grid(cu_budget);
+    const int waves = grid * (kBlock / kWave);
+    const int rows_blk = (d_out + waves - 1) / waves * (kBlock / kWave);
+    const size_t lds = (size_t)k * I * sizeof(uint16_t) + (size_t)rows_blk * sizeof(float);
+    if (I > 1024)
+        k_down_b1<4><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y);
+    else if (I > 512)
+        k_down_b1<2><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y);
+    else
+        k_down_b1<1><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y);
+}
+
+bool down_b1_fits(int k, int I, int d_out) {
+    const int rows_blk = (d_out + 1023) / 1024 * 4;  // at the smallest grid of 256 workgroups
+    return I <= 2048 && (size_t)k * I * 2 + (size_t)rows_blk * 4 * 4 <= 65536;
+}
+
+struct OutDense {  // y_s[t][r] = s (positions are tokens for the dense list)
+    float *y;
+    int d;
+    __device__ void operator()(int p, int r, float s) const { y[(int64_t)p * d + r] = s; }
+};
+
+// The routed experts after validation: batch 1 reads the ids directly; larger
+// batches permute, then run light experts on dot2 rows and heavy ones on MFMA
+// tiles; y = y_add + the weighted expert outputs.
+void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int32_t *topk_ids,
+                     const float *topk_w, int k, const uint16_t *w13, const uint16_t *w2, int E,
+                     int I, int d_out, const float *y_add, hipEvent_t y_add_ready, uint16_t *y,
+                     int cu_budget, char *ws, int trace_op, hipStream_t s) {
+    const MoeWorkspace L = moe_workspace_layout(b, E, k, I, d_out);
+    uint16_t *hbuf = (uint16_t *)(ws + L.hbuf);
+    float *part = (float *)(ws + L.part);
+    const OutPart out{part, d_out};
+    int *slot_pos = (int *)(ws + L.slot_pos);
+    trace_begin(trace_op, s);
+    if (b == 1) {
+        const SlotList sl{topk_ids, k, E};
+        launch_gateup_dot2(1, z, ldz, d_in, w13, I, sl, hbuf, cu_budget, s);
+        trace_end(trace_op, s);
+        if (y_add_ready)
+            (void)hipStreamWaitEvent(s, y_add_ready, 0);
+        if (down_b1_fits(k, I, d_out)) {
+            launch_down_b1(hbuf, I, w2, d_out, topk_ids, topk_w, k, E, y_add, y, cu_budget, s);
+            return;
+        }
+        launch_down_dot2(1, hbuf, I, w2, d_out, sl, out, cu_budget, s);
+        k_slot_identity<<<1, kBlock, 0, s>>>(topk_ids, k, E, slot_pos);
+    } else {
+        int *n_light = (int *)(ws + L.n_light), *n_heavy = (int *)(ws + L.n_heavy);
+        const ExpertList light{n_light, (int *)(ws + L.light_expert), (int *)(ws + L.light_start),
+                               (int *)(ws + L.light_ntok), (int *)(ws + L.sorted_token)};
+        const ExpertList heavy{n_heavy, (int *)(ws + L.heavy_expert), (int *)(ws + L.heavy_start),
+                               (int *)(ws + L.heavy_ntok), (int *)(ws + L.sorted_token)};
+        k_moe_permute<<<1, kBlock, 0, s>>>(
+            topk_ids, b, k, E, n_light, (int *)(ws + L.light_expert), (int *)(ws + L.light_start),
+            (int *)(ws + L.light_ntok), n_heavy, (int *)(ws + L.heavy_expert),
+            (int *)(ws + L.heavy_start), (int *)(ws + L.heavy_ntok), (int *)(ws + L.sorted_token),
+            slot_pos);
+        launch_gateup_dot2(kDot2MaxTokens, z, ldz, d_in, w13, I, light, hbuf, cu_budget, s);
+        const bool any_heavy = b > kDot2MaxTokens;
+        const int max_heavy = (b * k) / (kDot2MaxTokens + 1) < E ? (b * k) / (kDot2MaxTokens + 1)
+                                                                 : E;
+        if (any_heavy) {
+            const int g = budget_grid(max_heavy * (I / 16), cu_budget, 4);
+            k_gateup_mfma<8, ExpertList><<<g, kBlock, 0, s>>>(z, ldz, d_in, w13, I, heavy, hbuf);
+        }
+        trace_end(trace_op, s);
+        launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
+        if (any_heavy) {
+            const int g = budget_grid(max_heavy * (d_out / 16), cu_budget, 4);
+            k_down_mfma<16, ExpertList, OutPart><<<g, kBlock, 0, s>>>(hbuf, I, w2, d_out, heavy,
+                                                                     out);
+        }
+        if (y_add_ready)
+            (void)hipStreamWaitEvent(s, y_add_ready, 0);
+    }
+    const int n = b * d_out;
+    k_combine<<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(part, d_out, slot_pos, topk_w, b, k,
+                                                            y_add, y);
+}
+
+void run_shared_expert(int variant, const uint16_t *x, int64_t ldx, int b, int d,
+                       const uint16_t *w13, const uint16_t *w2, int I, float *y_s, int cu_budget,
+                       uint16_t *hbuf, int trace_op, hipStream_t s) {
+    const DenseList dl{b};
+    const OutDense out{y_s, d};
+    trace_begin(trace_op, s);
+    if (variant == K3_VARIANT_DOT2) {
+        const int tm = b == 1 ? 1 : kDot2MaxTokens;
+        launch_gateup_dot2(tm, x, ldx, d, w13, I, dl, hbuf, cu_budget, s);
+        trace_end(trace_op, s);
+        launch_down_dot2(tm, hbuf, I, w2, d, dl, out, cu_budget, s);
+    } else {
+        const int g1 = budget_grid(I / 16, cu_budget, 4);
+        k_gateup_mfma<8, DenseList><<<g1, kBlock, 0, s>>>(x, ldx, d, w13, I, dl, hbuf);
+        trace_end(trace_op, s);
+        const int g2 = budget_grid(d / 16, cu_budget, 4);
+        k_down_mfma<16, DenseList, OutDense><<<g2, kBlock, 0, s>>>(hbuf, I, w2, d, dl, out);
+    }
+}
+
+int check_moe_shapes(int b, int d_in, int k, int E, int I, int d_out, int64_t ldz) {
+    if (b <= 0 || d_in <= 0 || k <= 0 || E <= 0 || I <= 0 || d_out <= 0 || ldz < d_in)
+        return K3_ERR_INVALID_ARG;
+    if (b > K3_MAX_BATCH || k > K3_MAX_TOPK || k > E || E > K3_MAX_EXPERTS || I % 128 ||
+        d_in % 128 || d_in > 8192 || I > 8192 || d_out % 16 || ldz % 8)
+        return K3_ERR_UNSUPPORTED;
+    return K3_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ entry points
@@ -542,81 +817,28 @@ extern "C" int k3_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in,
                               const uint16_t *w13, const uint16_t *w2, int E, int I, int d_out,
                               const float *y_add, void *y_add_ready, uint16_t *y, int cu_budget,
                               void *workspace, size_t ws_bytes, void *stream) {
-    if (!z || !topk_ids || !topk_w || !w13 || !w2 || !y)
+    if (!z || !topk_ids || !topk_w || !w13 || !w2 || !y || cu_budget < 0)
         return K3_ERR_INVALID_ARG;
-    if (b <= 0 || d_in <= 0 || k <= 0 || E <= 0 || I <= 0 || d_out <= 0 || ldz < d_in ||
-        cu_budget < 0)
-        return K3_ERR_INVALID_ARG;
-    if (b > K3_MAX_BATCH || k > K3_MAX_TOPK || E > K3_MAX_EXPERTS || I % 128 || d_in % 128 ||
-        d_in > 8192 || I > 8192 || d_out % 16 || ldz % 8 || !aligned16(z) || !aligned16(w13) ||
-        !aligned16(w2))
+    const int chk = check_moe_shapes(b, d_in, k, E, I, d_out, ldz);
+    if (chk != K3_OK)
+        return chk;
+    if (!aligned16(z) || !aligned16(w13) || !aligned16(w2))
         return K3_ERR_UNSUPPORTED;
     const int fv = forced_variant(K3_OP_MOE_EXPERTS);
     if (fv != K3_VARIANT_NONE && fv != K3_VARIANT_GROUPED)
         return K3_ERR_UNSUPPORTED;
-    const MoeWorkspace L = moe_workspace_layout(b, E, k, I, d_out);
-    if (!workspace || ws_bytes < L.total || !aligned16(workspace))
+    if (!workspace || ws_bytes < moe_workspace_layout(b, E, k, I, d_out).total ||
+        !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    char *ws = (char *)workspace;
-    uint16_t *hbuf = (uint16_t *)(ws + L.hbuf);
-    float *part = (float *)(ws + L.part);
-    const OutPart out{part, d_out};
-    const int *slot_pos = nullptr;
-    trace_begin(K3_OP_MOE_EXPERTS, s);
-    if (b == 1) {
-        const SlotList sl{topk_ids, k, E};
-        launch_gateup_dot2(1, z, ldz, d_in, w13, I, sl, hbuf, cu_budget, s);
-        trace_end(K3_OP_MOE_EXPERTS, s);
-        if (y_add_ready && hipStreamWaitEvent(s, (hipEvent_t)y_add_ready, 0) != hipSuccess)
-            return K3_ERR_HIP;
-        launch_down_dot2(1, hbuf, I, w2, d_out, sl, out, cu_budget, s);
-    } else {
-        int *n_light = (int *)(ws + L.n_light), *n_heavy = (int *)(ws + L.n_heavy);
-        const ExpertList light{n_light, (int *)(ws + L.light_expert), (int *)(ws + L.light_start),
-                               (int *)(ws + L.light_ntok), (int *)(ws + L.sorted_token)};
-        const ExpertList heavy{n_heavy, (int *)(ws + L.heavy_expert), (int *)(ws + L.heavy_start),
-                               (int *)(ws + L.heavy_ntok), (int *)(ws + L.sorted_token)};
-        slot_pos = (const int *)(ws + L.slot_pos);
-        k_moe_permute<<<1, kBlock, 0, s>>>(
-            topk_ids, b, k, E, n_light, (int *)(ws + L.light_expert), (int *)(ws + L.light_start),
-            (int *)(ws + L.light_ntok), n_heavy, (int *)(ws + L.heavy_expert),
-            (int *)(ws + L.heavy_start), (int *)(ws + L.heavy_ntok), (int *)(ws + L.sorted_token),
-            (int *)(ws + L.slot_pos));
-        launch_gateup_dot2(kDot2MaxTokens, z, ldz, d_in, w13, I, light, hbuf, cu_budget, s);
-        const bool any_heavy = b > kDot2MaxTokens;
-        if (any_heavy) {
-            const int max_heavy = (b * k) / (kDot2MaxTokens + 1);
-            const int g = budget_grid((max_heavy < E ? max_heavy : E) * (I / 16), cu_budget, 4);
-            k_gateup_mfma<8, ExpertList><<<g, kBlock, 0, s>>>(z, ldz, d_in, w13, I, heavy, hbuf);
-        }
-        trace_end(K3_OP_MOE_EXPERTS, s);
-        launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
-        if (any_heavy) {
-            const int max_heavy = (b * k) / (kDot2MaxTokens + 1);
-            const int g = budget_grid((max_heavy < E ? max_heavy : E) * (d_out / 16), cu_budget, 4);
-            k_down_mfma<16, ExpertList, OutPart><<<g, kBlock, 0, s>>>(hbuf, I, w2, d_out, heavy,
-                                                                     out);
-        }
-        if (y_add_ready && hipStreamWaitEvent(s, (hipEvent_t)y_add_ready, 0) != hipSuccess)
-            return K3_ERR_HIP;
-    }
-    const int n = b * d_out;
-    k_combine<<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(part, d_out, slot_pos, topk_ids, E,
-                                                            topk_w, b, k, y_add, y);
+    run_moe_experts(z, ldz, b, d_in, topk_ids, topk_w, k, w13, w2, E, I, d_out, y_add,
+                    (hipEvent_t)y_add_ready, y, cu_budget, (char *)workspace, K3_OP_MOE_EXPERTS,
+                    s);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_MOE_EXPERTS, K3_VARIANT_GROUPED);
     return st;
 }
-
-namespace {
-struct OutDense {  // y_s[t][r] = s (positions are tokens for the dense list)
-    float *y;
-    int d;
-    __device__ void operator()(int p, int r, float s) const { y[(int64_t)p * d + r] = s; }
-};
-}  // namespace
 
 extern "C" int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w13,
                                 const uint16_t *w2, int I, float *y_s, int cu_budget,
@@ -636,25 +858,87 @@ extern "C" int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d, co
         return K3_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < k3_shared_expert_workspace_size(b, d, I) || !aligned16(workspace))
         return K3_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    uint16_t *hbuf = (uint16_t *)workspace;
-    const DenseList dl{b};
-    const OutDense out{y_s, d};
-    trace_begin(K3_OP_SHARED_EXPERT, s);
-    if (variant == K3_VARIANT_DOT2) {
-        const int tm = b == 1 ? 1 : kDot2MaxTokens;
-        launch_gateup_dot2(tm, x, ldx, d, w13, I, dl, hbuf, cu_budget, s);
-        trace_end(K3_OP_SHARED_EXPERT, s);
-        launch_down_dot2(tm, hbuf, I, w2, d, dl, out, cu_budget, s);
-    } else {
-        const int g1 = budget_grid(I / 16, cu_budget, 4);
-        k_gateup_mfma<8, DenseList><<<g1, kBlock, 0, s>>>(x, ldx, d, w13, I, dl, hbuf);
-        trace_end(K3_OP_SHARED_EXPERT, s);
-        const int g2 = budget_grid(d / 16, cu_budget, 4);
-        k_down_mfma<16, DenseList, OutDense><<<g2, kBlock, 0, s>>>(hbuf, I, w2, d, dl, out);
-    }
+    run_shared_expert(variant, x, ldx, b, d, w13, w2, I, y_s, cu_budget, (uint16_t *)workspace,
+                      K3_OP_SHARED_EXPERT, (hipStream_t)stream);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_SHARED_EXPERT, variant);
+    return st;
+}
+
+extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
+                            const uint16_t *w_router, const float *bias, int E, int k,
+                            const uint16_t *w_lat, int d_lat, const uint16_t *w13,
+                            const uint16_t *w2, int I, const uint16_t *w13_s,
+                            const uint16_t *w2_s, int I_s, int32_t *topk_ids, float *topk_w,
+                            uint16_t *z, int64_t ldz, float *y_s, uint16_t *y, void *workspace,
+                            size_t ws_bytes, void *stream) {
+    if (!x || !w_router || !w_lat || !w13 || !w2 || !w13_s || !w2_s || !topk_ids || !topk_w ||
+        !z || !y_s || !y)
+        return K3_ERR_INVALID_ARG;
+    if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || d_lat <= 0 || I <= 0 || I_s <= 0 || ldx < d ||
+        ldz < d_lat)
+        return K3_ERR_INVALID_ARG;
+    const int chk = check_moe_shapes(b, d_lat, k, E, I, d, ldz);
+    if (chk != K3_OK)
+        return chk;
+    if (d % 128 || d > 8192 || I_s % 128 || I_s > 8192 || ldx % 8 || !aligned16(x) ||
+        !aligned16(w_router) || !aligned16(w_lat) || !aligned16(w13) || !aligned16(w2) ||
+        !aligned16(w13_s) || !aligned16(w2_s) || !aligned16(z))
+        return K3_ERR_UNSUPPORTED;
+    const BlockWorkspace L = block_workspace_layout(b, E, k, I, d, I_s);
+    if (!workspace || ws_bytes < L.total || !aligned16(workspace))
+        return K3_ERR_WORKSPACE;
+    int variant = forced_variant(K3_OP_MOE_BLOCK);
+    const bool fits = b <= kDot2MaxTokens && rls_fits(b, d, E) &&
+                      (size_t)b * I_s * 2 <= 65536;
+    if (variant == K3_VARIANT_NONE)
+        variant = fits ? K3_VARIANT_DOT2 : K3_VARIANT_MFMA;
+    if ((variant != K3_VARIANT_DOT2 && variant != K3_VARIANT_MFMA) ||
+        (variant == K3_VARIANT_DOT2 && !fits))
+        return K3_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *logits = (float *)(ws + L.logits);
+    uint16_t *hs = (uint16_t *)(ws + L.hs);
+    trace_begin(K3_OP_MOE_BLOCK, s);
+    if (variant == K3_VARIANT_DOT2) {
+        // 1. router, latent and shared gate/up rows in one pass over x
+        launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, w13_s, I_s, hs,
+                   s);
+        trace_end(K3_OP_MOE_BLOCK, s);
+        // 2. top-k in workgroup 0, the shared down projection in the others
+        const int grid = dot2_grid(0);
+        const size_t lds = (size_t)b * I_s * sizeof(uint16_t);
+        const int cb = I_s > 2048 ? 16 : (I_s > 512 ? 4 : 1);
+#define K3_TSD(TM_, CB_)                                                                       \
+    k_topk_shared_down<TM_, CB_><<<grid, kBlock, lds, s>>>(logits, E, k, b, topk_ids, topk_w, \
+                                                           hs, I_s, w2_s, d, y_s)
+        if (b == 1 && cb == 16)
+            K3_TSD(1, 16);
+        else if (b == 1 && cb == 4)
+            K3_TSD(1, 4);
+        else if (b == 1)
+            K3_TSD(1, 1);
+        else if (cb == 16)
+            K3_TSD(kDot2MaxTokens, 16);
+        else if (cb == 4)
+            K3_TSD(kDot2MaxTokens, 4);
+        else
+            K3_TSD(kDot2MaxTokens, 1);
+#undef K3_TSD
+    } else {
+        launch_dense_logits(x, ldx, b, w_router, E, d, bias, logits, s);
+        launch_dense_bf16(x, ldx, b, w_lat, d_lat, d, z, ldz, s);
+        trace_end(K3_OP_MOE_BLOCK, s);
+        launch_topk(logits, b, E, k, topk_ids, topk_w, s);
+        run_shared_expert(K3_VARIANT_MFMA, x, ldx, b, d, w13_s, w2_s, I_s, y_s, 0, hs, -1, s);
+    }
+    // 3-4. routed gate/up, down and combine with the shared output added
+    run_moe_experts(z, ldz, b, d_lat, topk_ids, topk_w, k, w13, w2, E, I, d, y_s, nullptr, y, 0,
+                    ws + L.moe, K3_OP_MOE_EXPERTS, s);
+    const int st = launch_status();
+    if (st == K3_OK)
+        record_dispatch(K3_OP_MOE_BLOCK, variant);
     return st;
 }

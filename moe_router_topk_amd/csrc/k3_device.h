@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/k3dec.h"
+
 namespace k3 {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -81,85 +83,128 @@ __device__ __forceinline__ float silu(float g) {
 namespace k3 {
 
 // ------------------------------------------------------------------ row streaming
-// The weight-streaming engine of the small-batch kernels. One wave walks
-// rows [r_begin, r_end) of a row set, RB rows at a time: row i is NV
-// 16-byte vectors long, lane l owns vectors l, l + 64, ... (CB of them, so
-// one load instruction reads 1 KB of a row contiguously). Two register
-// buffers alternate, so the next RB rows' loads are in flight while the
-// current ones are multiplied against the token vectors staged in LDS
-// (xs[t * xstride + v], t < nt <= TM). Activations come from LDS only: a
-// global activation load issued behind the weight loads would have to wait
-// for all of them (vector loads retire in order). After each row, every lane
-// holds the wave-reduced sum for each token and calls epi(row, t, sum).
-template <int TM, int RB, int CB, class RowPtr, class Epi>
+// The weight-streaming engine of the small-batch kernels. A wave walks a
+// sequence of units; load(buf, u) issues unit u's 16-byte weight loads into a
+// register buffer of NB vectors and finish(buf, u) consumes them. Two buffers
+// alternate, so unit u+1's loads are in flight while unit u is multiplied.
+// Weight rows are read with lane l taking vectors l, l + 64, ..., so one
+// load instruction covers 1 KB of a row contiguously. Activations come from
+// LDS only: a global activation load issued behind the weight loads would
+// have to wait for all of them (vector loads retire in order).
+//
+// stream_rows: units of RB rows, each multiplied against the token vectors
+// staged in LDS (xs[t * xstride + v], t < nt <= TM); after each row, every
+// lane holds the wave-reduced sum per token and calls epi(row, t, sum).
+struct NoPrologue {
+    __device__ void operator()() const {}
+};
+
+// pre() runs once, after the first unit's loads are issued and before any
+// unit is consumed, in every wave (also waves without units), so it may stage
+// activations and hold a block barrier: its latency overlaps the first loads.
+template <int NB, class Load, class Finish, class Pre = NoPrologue>
+__device__ __forceinline__ void stream_units(int u_begin, int u_end, Load load, Finish finish,
+                                             Pre pre = Pre()) {
+    u32x4 A[NB], B[NB];
+    if (u_begin < u_end)
+        load(A, u_begin);
+    pre();
+    if (u_begin >= u_end)
+        return;
+    for (int u = u_begin; u < u_end; u += 2) {
+        if (u + 1 < u_end)
+            load(B, u + 1);
+        finish(A, u);
+        if (u + 1 >= u_end)
+            break;
+        if (u + 2 < u_end)
+            load(A, u + 2);
+        finish(B, u + 1);
+    }
+}
+
+// Rows of a row set, RB rows per unit: row i is nv 16-byte vectors long,
+// starting at rowptr(i); lane l owns vectors l, l + 64, ... (CB of them).
+template <int TM, int RB, int CB, class RowPtr, class Epi, class Pre = NoPrologue>
 __device__ __forceinline__ void stream_rows(int r_begin, int r_end, int nv, const u32x4 *xs,
-                                            int xstride, int nt, RowPtr rowptr, Epi epi) {
+                                            int xstride, int nt, RowPtr rowptr, Epi epi,
+                                            Pre pre = Pre()) {
     const int lane = threadIdx.x & (kWave - 1);
-    u32x4 A[RB][CB], B[RB][CB];
-    auto load = [&](u32x4 (&buf)[RB][CB], int r) {
+    const int units = (r_end - r_begin + RB - 1) / RB;
+    stream_units<RB * CB>(
+        0, units,
+        [&](u32x4 (&buf)[RB * CB], int u) {
+            const int r = r_begin + u * RB;
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const bool rv = r + i < r_end;
-            const uint16_t *p = rv ? rowptr(r + i) : nullptr;
+            for (int i = 0; i < RB; ++i) {
+                const bool rv = r + i < r_end;
+                const uint16_t *p = rv ? rowptr(r + i) : nullptr;
+#pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    const int v = c * kWave + lane;
+                    buf[i * CB + c] = (rv && v < nv) ? ld_weight16(p + (int64_t)v * 8) : zero16();
+                }
+            }
+        },
+        [&](u32x4 (&buf)[RB * CB], int u) {
+            const int r = r_begin + u * RB;
+            float acc[RB][TM];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+                    acc[i][t] = 0.0f;
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
                 const int v = c * kWave + lane;
-                buf[i][c] = (rv && v < nv) ? ld_weight16(p + (int64_t)v * 8) : zero16();
-            }
-        }
-    };
-    auto finish = [&](u32x4 (&buf)[RB][CB], int r) {
-        float acc[RB][TM];
+                if (v < nv) {
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
+                    for (int t = 0; t < TM; ++t) {
+                        if (t < nt) {
+                            const u32x4 xv = xs[t * xstride + v];
 #pragma unroll
-            for (int t = 0; t < TM; ++t)
-                acc[i][t] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            const int v = c * kWave + lane;
-            if (v < nv) {
-#pragma unroll
-                for (int t = 0; t < TM; ++t) {
-                    if (t < nt) {
-                        const u32x4 xv = xs[t * xstride + v];
-#pragma unroll
-                        for (int i = 0; i < RB; ++i)
-                            acc[i][t] = dot8(buf[i][c], xv, acc[i][t]);
+                            for (int i = 0; i < RB; ++i)
+                                acc[i][t] = dot8(buf[i * CB + c], xv, acc[i][t]);
+                        }
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
-            if (r + i < r_end)
+            for (int i = 0; i < RB; ++i)
+                if (r + i < r_end)
 #pragma unroll
-                for (int t = 0; t < TM; ++t)
-                    if (t < nt)
-                        epi(r + i, t, wave_sum(acc[i][t]));
-    };
-    if (r_begin >= r_end)
-        return;
-    load(A, r_begin);
-    for (int r = r_begin; r < r_end; r += 2 * RB) {
-        if (r + RB < r_end)
-            load(B, r + RB);
-        finish(A, r);
-        if (r + RB >= r_end)
-            break;
-        if (r + 2 * RB < r_end)
-            load(A, r + 2 * RB);
-        finish(B, r + RB);
-    }
+                    for (int t = 0; t < TM; ++t)
+                        if (t < nt)
+                            epi(r + i, t, wave_sum(acc[i][t]));
+        },
+        pre);
 }
 
 // Copy nrows activation rows (nv 16-byte vectors each, row t starting at
 // src(t)) into LDS rows of xstride vectors; all threads of the block help.
+// Loads go out eight at a time before their LDS stores, so staging costs
+// about one memory latency per 8 vectors a thread moves, not one per vector.
 template <class Src>
 __device__ __forceinline__ void stage_rows(u32x4 *xs, int xstride, int nrows, int nv, Src src) {
-    for (int i = threadIdx.x; i < nrows * nv; i += blockDim.x) {
-        const int t = i / nv, v = i - t * nv;
-        xs[t * xstride + v] = ld_act16(src(t) + (int64_t)v * 8);
+    const int n = nrows * nv;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * kBlock) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kBlock;
+            if (i < n) {
+                const int t = i / nv;
+                v[u] = ld_act16(src(t) + (int64_t)(i - t * nv) * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kBlock;
+            if (i < n) {
+                const int t = i / nv;
+                xs[t * xstride + (i - t * nv)] = v[u];
+            }
+        }
     }
 }
 
@@ -168,6 +213,67 @@ __device__ __forceinline__ void split_range(int n, int parts, int part, int &lo,
     const int base = n / parts, rem = n % parts;
     lo = part * base + min(part, rem);
     hi = lo + base + (part < rem ? 1 : 0);
+}
+
+// ------------------------------------------------------------------ top-k
+// One wave picks token t's k experts: lane l holds logits l, l + 64, ...;
+// k rounds of a wave-wide argmax under the order (logit desc, index asc);
+// lane j keeps the j-th pick. The weights are the softmax over the k picked
+// logits (the full softmax renormalised over the selection).
+__device__ __forceinline__ void topk_wave(const float *logits, int E, int k, int32_t *ids,
+                                          float *wts) {
+    constexpr int PER = K3_MAX_EXPERTS / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    float v[PER];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = i * kWave + lane;
+        float l = -INFINITY;
+        if (e < E)
+            l = logits[e];
+        else
+            taken |= 1u << i;
+        v[i] = (l != l) ? -INFINITY : l;  // NaN never outranks a number
+    }
+    float sel_v = 0.0f, top = 0.0f;
+    int sel_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = i * kWave + lane;
+            if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
+                bv = v[i];
+                be = e;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, kWave);
+            const int oe = __shfl_xor(be, m, kWave);
+            if (ov > bv || (ov == bv && oe < be)) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & (kWave - 1)) == lane)
+            taken |= 1u << (be / kWave);
+        if (lane == j) {
+            sel_v = bv;
+            sel_e = be;
+        }
+        if (j == 0)
+            top = bv;
+    }
+    const float dl = (sel_v == top) ? 0.0f : sel_v - top;
+    const float p = lane < k ? expf(dl) : 0.0f;
+    const float sum = wave_sum(p);
+    if (lane < k) {
+        ids[lane] = sel_e;
+        wts[lane] = p / sum;
+    }
 }
 
 }  // namespace k3

@@ -38,4 +38,17 @@ struct MoeWorkspace {
 };
 MoeWorkspace moe_workspace_layout(int b, int E, int k, int I, int d_out);
 
+// Dense launchers defined in dense.hip, shared with the fused MoE block.
+bool rls_fits(int b, int d, int E);
+void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
+                const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
+                uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
+                hipStream_t s);
+void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *wts,
+                 hipStream_t s);
+void launch_dense_bf16(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
+                       uint16_t *y, int64_t ldy, hipStream_t s);
+void launch_dense_logits(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int E, int K,
+                         const float *bias, float *logits, hipStream_t s);
+
 }  // namespace k3

@@ -20,8 +20,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (k3_moe_experts, k3_oproj_residual, k3_prefetch, k3_proj_skinny, k3_router_topk,
-               k3_shared_expert, workspace_size)
+from . import (k3_moe_block, k3_moe_experts, k3_oproj_residual, k3_prefetch, k3_proj_skinny,
+               k3_router_topk_latent, k3_shared_expert, workspace_size)
 
 
 class DecodeLayer:
@@ -48,11 +48,12 @@ class DecodeLayer:
         I_s = moe["w13_s"].shape[0] // 2
         self.E, self.d, self.d_lat, self.I, self.I_s, self.b_max = E, d, d_lat, I, I_s, b_max
         u8 = dict(dtype=torch.uint8, device=dev)
-        # zero-filled: the router and o-proj workspaces hold completion counters
-        self.ws_router = torch.zeros(workspace_size("router_topk", b=b_max, E=E), **u8)
+        self.ws_router = torch.empty(workspace_size("router_topk", b=b_max, E=E), **u8)
         self.ws_moe = torch.empty(
             workspace_size("moe_experts", b=b_max, d_in=d_lat, E=E, k=k, I=I, d_out=d), **u8)
         self.ws_shared = torch.empty(workspace_size("shared_expert", b=b_max, d=d, I=I_s), **u8)
+        self.ws_block = torch.empty(workspace_size("moe_block", b=b_max, d=d, E=E, k=k,
+                                                   d_lat=d_lat, I=I, I_s=I_s), **u8)
         self.ids = torch.empty((b_max, k), dtype=torch.int32, device=dev)
         self.wts = torch.empty((b_max, k), dtype=torch.float32, device=dev)
         self.z = torch.empty((b_max, d_lat), dtype=torch.bfloat16, device=dev)
@@ -63,7 +64,7 @@ class DecodeLayer:
             self.k_o = chain["w_o"].shape[1]
             self.q = torch.empty((b_max, n_in), dtype=torch.bfloat16, device=dev)
             self.x_moe = torch.empty((b_max, d), dtype=torch.bfloat16, device=dev)
-            self.ws_oproj = torch.zeros(
+            self.ws_oproj = torch.empty(
                 workspace_size("oproj_residual", b=b_max, K=self.k_o, d=d), **u8)
         self.side = torch.cuda.Stream(device=dev)
         self.pf_stream = torch.cuda.Stream(device=dev)
@@ -73,7 +74,20 @@ class DecodeLayer:
 
     # -------------------------------------------------------------- MoE block
     def moe_block(self, x: torch.Tensor) -> torch.Tensor:
-        """y [b x d] bf16 = shared(x) + sum_j w_j routed_j(latent(x))."""
+        """y [b x d] bf16 = shared(x) + sum_j w_j routed_j(latent(x)), one
+        stream (k3_moe_block)."""
+        b = x.shape[0]
+        assert b <= self.b_max
+        m = self.moe
+        y, _, _, _, _ = k3_moe_block(
+            x, m["w_router"], m["bias"], self.k, m["w_lat"], m["w13"], m["w2"], m["w13_s"],
+            m["w2_s"], topk_ids=self.ids[:b], topk_w=self.wts[:b], z=self.z[:b],
+            y_s=self.y_s[:b], y=self.y[:b], workspace=self.ws_block)
+        return y
+
+    def moe_block_streams(self, x: torch.Tensor) -> torch.Tensor:
+        """The same block composed from the separate entry points, with the
+        shared expert on a second stream (joined before the combine)."""
         b = x.shape[0]
         assert b <= self.b_max
         m = self.moe
@@ -84,11 +98,9 @@ class DecodeLayer:
         k3_shared_expert(x, m["w13_s"], m["w2_s"], y_s=y_s, cu_budget=self.cu_shared,
                          workspace=self.ws_shared, stream=self.side)
         self.ev_shared.record(self.side)
-        ids, wts = self.ids[:b], self.wts[:b]
-        k3_router_topk(x, m["w_router"], m["bias"], self.k, topk_ids=ids, topk_w=wts,
-                       workspace=self.ws_router, stream=main)
-        z = self.z[:b]
-        k3_proj_skinny(x, m["w_lat"], y=z, stream=main)
+        ids, wts, z = self.ids[:b], self.wts[:b], self.z[:b]
+        k3_router_topk_latent(x, m["w_router"], m["bias"], self.k, m["w_lat"], topk_ids=ids,
+                              topk_w=wts, z=z, workspace=self.ws_router, stream=main)
         y = self.y[:b]
         k3_moe_experts(z, ids, wts, m["w13"], m["w2"], y_add=y_s, y_add_ready=self.ev_shared,
                        y=y, workspace=self.ws_moe, stream=main)

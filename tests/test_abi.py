@@ -64,6 +64,10 @@ def test_status_strings(L):
 def test_force_variant_validation(L):
     assert L.k3_force_variant(1, 2) == K3_OK
     assert L.k3_force_variant(1, 0) == K3_OK
+    assert L.k3_force_variant(7, 2) == K3_OK
+    assert L.k3_force_variant(7, 0) == K3_OK
+    assert L.k3_force_variant(6, 1) == K3_OK
+    assert L.k3_force_variant(6, 0) == K3_OK
     assert L.k3_force_variant(9, 0) == INVALID
     assert L.k3_force_variant(1, 17) == INVALID
 
@@ -99,6 +103,53 @@ def test_router_topk_validation(L):
     assert _router(L, x=MIS) == UNSUP
     assert _router(L, ws=None) == WORKSPACE
     assert _router(L, wsb=16) == WORKSPACE
+
+
+def _router_latent(L, **kw):
+    a = dict(x=P, ldx=256, b=1, d=256, w=P, bias=None, E=8, k=2, wl=P, dl=256, ids=P, wts=P,
+             z=P, ldz=256, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return L.k3_router_topk_latent(a["x"], a["ldx"], a["b"], a["d"], a["w"], a["bias"], a["E"],
+                                   a["k"], a["wl"], a["dl"], a["ids"], a["wts"], a["z"], a["ldz"],
+                                   a["ws"], a["wsb"], None)
+
+
+def test_router_topk_latent_validation(L):
+    assert _router_latent(L, wl=None) == INVALID
+    assert _router_latent(L, z=None) == INVALID
+    assert _router_latent(L, ldz=128) == INVALID
+    assert _router_latent(L, dl=0) == INVALID
+    assert _router_latent(L, x=None) == INVALID
+    assert _router_latent(L, b=65) == UNSUP
+    assert _router_latent(L, wl=MIS) == UNSUP
+    assert _router_latent(L, k=9) == UNSUP
+    assert _router_latent(L, ws=None) == WORKSPACE
+
+
+def _block(L, **kw):
+    a = dict(x=P, ldx=256, b=1, d=256, wr=P, bias=None, E=8, k=2, wl=P, dl=256, w13=P, w2=P,
+             I=128, w13s=P, w2s=P, Is=128, ids=P, wts=P, z=P, ldz=256, ys=P, y=P, ws=P,
+             wsb=1 << 24)
+    a.update(kw)
+    return L.k3_moe_block(a["x"], a["ldx"], a["b"], a["d"], a["wr"], a["bias"], a["E"], a["k"],
+                          a["wl"], a["dl"], a["w13"], a["w2"], a["I"], a["w13s"], a["w2s"],
+                          a["Is"], a["ids"], a["wts"], a["z"], a["ldz"], a["ys"], a["y"],
+                          a["ws"], a["wsb"], None)
+
+
+def test_moe_block_validation(L):
+    assert _block(L, y=None) == INVALID
+    assert _block(L, ys=None) == INVALID
+    assert _block(L, Is=0) == INVALID
+    assert _block(L, ldz=128) == INVALID
+    assert _block(L, b=65) == UNSUP
+    assert _block(L, I=100) == UNSUP
+    assert _block(L, Is=200) == UNSUP
+    assert _block(L, d=200, ldx=256) == UNSUP
+    assert _block(L, w2s=MIS) == UNSUP
+    assert _block(L, k=9) == UNSUP
+    assert _block(L, ws=None) == WORKSPACE
+    assert _block(L, wsb=4096) == WORKSPACE
 
 
 def _proj(L, **kw):

@@ -102,6 +102,47 @@ def test_router_topk_k_equals_E(k3):
     assert_rel_close(wts.cpu(), ref_w, "topk_w")
 
 
+@pytest.mark.parametrize("b,zipf", [(1, 0.0), (2, 0.0), (4, 1.1), (16, 0.0), (64, 1.1)])
+def test_router_topk_latent_full(k3, full, b, zipf):
+    """The fused router + latent pass: ids and weights as k3_router_topk, z as
+    k3_proj_skinny, at full size (dot2 up to 4 tokens, MFMA above)."""
+    cfg, w = full
+    bias = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
+    x = synth.make_tokens(cfg, device=DEV, index=150 + b, b=b)
+    ids, wts, z = k3.k3_router_topk_latent(x, w["w_router"], bias, cfg.k, w["w_lat"])
+    torch.cuda.synchronize()
+    assert k3.k3_get_last_dispatch("router_latent") == ("dot2" if b <= 4 else "mfma")
+    logits = oracle.router_logits(x.cpu(), w["w_router"].cpu(),
+                                  bias.cpu() if bias is not None else None)
+    ref_ids, ref_w = oracle.topk_softmax(logits, cfg.k)
+    differ = check_ids(ids, ref_ids, logits, cfg.k)
+    keep = [t for t in range(b) if t not in differ]
+    assert_rel_close(wts.cpu().numpy()[keep], ref_w[keep], "topk_w")
+    rows = torch.arange(3, cfg.d_lat, 13)
+    assert_rel_close(z[:, rows].cpu(), oracle.linear(x.cpu(), w["w_lat"][rows].cpu()), "z")
+    # the same bits as the two separate calls
+    ids2, wts2 = k3.k3_router_topk(x, w["w_router"], bias, cfg.k)
+    z2 = k3.k3_proj_skinny(x, w["w_lat"])
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(wts, wts2) and torch.equal(z, z2)
+
+
+def test_router_topk_latent_tiny_repeated(k3):
+    """Tiny workload, several calls in a row on one workspace (the counter
+    resets) and E not a multiple of the wave count."""
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    for b in (1, 3, 4, 1):
+        x = synth.make_tokens(cfg, device=DEV, index=60 + b, b=b)
+        ids, wts, z = k3.k3_router_topk_latent(x, w["w_router"], None, cfg.k, w["w_lat"])
+        torch.cuda.synchronize()
+        logits = oracle.router_logits(x.cpu(), w["w_router"].cpu())
+        ref_ids, ref_w = oracle.topk_softmax(logits, cfg.k)
+        check_ids(ids, ref_ids, logits, cfg.k)
+        assert_rel_close(wts.cpu(), ref_w, "topk_w")
+        assert_rel_close(z.cpu(), oracle.linear(x.cpu(), w["w_lat"].cpu()), "z")
+
+
 # ---------------------------------------------------------------- skinny projection
 @pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 8, 9, 16, 33, 64])
 def test_proj_skinny_latent(k3, full, b):
@@ -236,6 +277,24 @@ def test_moe_experts_b1_invalid_id_dropped(k3):
     torch.cuda.synchronize()
     ref = oracle.moe_experts(z.cpu(), np.array([[6, 6]], np.int32), np.array([[0.625, 0.0]]),
                              _experts_on_host(w), cfg.E)
+    assert_rel_close(y.cpu(), ref, "y")
+
+
+def test_moe_experts_b1_generic_down(k3):
+    """Batch 1 with I > 2048: the generic down kernel and the ordered combine
+    (slot positions from the ids) instead of the row-owning kernel."""
+    E, d, I, k = 6, 256, 2176, 3
+    w13 = synth.randn_bf16((E, 2 * I, d), 1 / 16, 2, "g_w13", device=DEV)
+    w2 = synth.randn_bf16((E, d, I), 1 / math.sqrt(I), 2, "g_w2", device=DEV)
+    z = synth.randn_bf16((1, d), 1.0, 2, "g_z", device=DEV)
+    ids = torch.tensor([[4, 1, 5]], dtype=torch.int32, device=DEV)
+    wts = torch.tensor([[0.5, 0.3, 0.2]], dtype=torch.float32, device=DEV)
+    y_add = synth.randn_bf16((1, d), 0.1, 2, "g_ya", device=DEV).float()
+    y = k3.k3_moe_experts(z, ids, wts, w13, w2, y_add=y_add)
+    torch.cuda.synchronize()
+    fn = lambda e: (w13[e].cpu(), w2[e].cpu())  # noqa: E731
+    ref = oracle.moe_experts(z.cpu(), ids.cpu().numpy(), wts.cpu().numpy(), fn, E,
+                             y_add=y_add.cpu())
     assert_rel_close(y.cpu(), ref, "y")
 
 
@@ -396,6 +455,45 @@ def test_moe_block_end_to_end_full(k3, full, b, zipf):
     y_s = oracle.shared_expert(xs, w["w13_s"].cpu(), w["w2_s"].cpu())
     ref = oracle.moe_experts(z, ref_ids, ref_w, _experts_on_host(w), cfg.E, y_add=y_s)
     assert_rel_close(y[ts].cpu(), ref, "y")
+
+
+@pytest.mark.parametrize("b", [1, 2, 4, 5, 8])
+def test_moe_block_tiny(k3, b):
+    """The fused block entry at the tiny workload against the oracle; dot2
+    kernels up to 4 tokens, MFMA above."""
+    from moe_router_topk_amd.layer import DecodeLayer
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    layer = DecodeLayer(w, cfg.k, b_max=8)
+    x = synth.make_tokens(cfg, device=DEV, index=80 + b, b=b)
+    y = layer.moe_block(x)
+    torch.cuda.synchronize()
+    assert k3.k3_get_last_dispatch("moe_block") == ("dot2" if b <= 4 else "mfma")
+    wc = {key: (v.cpu() if v is not None else None) for key, v in w.items()}
+    ref = oracle.moe_block(x.cpu(), wc, cfg.k)
+    check_ids(layer.ids[:b], ref["ids"], ref["logits"], cfg.k)
+    assert_rel_close(layer.z[:b].cpu(), ref["z"], "z")
+    assert_rel_close(layer.y_s[:b].cpu(), ref["y_s"], "y_s")
+    assert_rel_close(y.cpu(), ref["y"], "y")
+
+
+@pytest.mark.parametrize("b,zipf", [(1, 0.0), (4, 0.0), (16, 0.0), (64, 1.1)])
+def test_moe_block_matches_stream_composition(k3, full, b, zipf):
+    """k3_moe_block gives the same bits as the separate entry points composed
+    on two streams (router+latent, shared expert, routed experts)."""
+    from moe_router_topk_amd.layer import DecodeLayer
+    cfg, w = full
+    w = dict(w)
+    w["bias"] = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
+    layer = DecodeLayer(w, cfg.k, b_max=b)
+    x = synth.make_tokens(cfg, device=DEV, index=720 + b, b=b)
+    y1 = layer.moe_block(x).clone()
+    ids1, ys1 = layer.ids[:b].clone(), layer.y_s[:b].clone()
+    y2 = layer.moe_block_streams(x)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.ids[:b], ids1)
+    assert torch.equal(layer.y_s[:b], ys1)
+    assert torch.equal(y2, y1)
 
 
 def test_layer_step_chain_then_moe(k3, full, chain_w):
