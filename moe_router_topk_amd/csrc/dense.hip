@@ -79,7 +79,7 @@ k_dense_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, const uint16_t 
     extern __shared__ u32x4 xs[];
     const int nv = K >> 3;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    const int wave = blockIdx.x * (kBlock / kWave) + wave_in_block();
     const int r0 = wave * rpw, r1 = min(N, r0 + rpw);
     stream_rows<TM, 16 / CB, CB>(
         r0, r1, nv, xs, nv, b, [&](int r) { return W + (int64_t)r * K; },
@@ -120,7 +120,7 @@ k_rls_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, int d,
     float *bs = reinterpret_cast<float *>(xs + b * nv);
     const int lane = threadIdx.x & (kWave - 1);
     const int waves = gridDim.x * (kBlock / kWave);
-    const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    const int wave = blockIdx.x * (kBlock / kWave) + wave_in_block();
     int ra, rb, la, lb, sa, sb;
     split_range(E, waves, wave, ra, rb);
     split_range(NL, waves, waves - 1 - wave, la, lb);  // spare latent rows to router-free waves
@@ -178,7 +178,7 @@ k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t 
     const int rblk = blockIdx.x * rows_blk;
     float *rs = reinterpret_cast<float *>(xs + b * nv);  // [b][rows_blk]
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+    const int wave = blockIdx.x * (kBlock / kWave) + wave_in_block();
     const int r0 = wave * rpw, r1 = min(d, r0 + rpw);
     stream_rows<TM, 16 / CB, CB>(
         r0, r1, nv, xs, nv, b, [&](int r) { return Wo + (int64_t)r * K; },
@@ -210,7 +210,7 @@ k_gemm_mfma(const uint16_t *__restrict__ x, int64_t ldx, int b,
             const uint16_t *__restrict__ W, int N, int K, Epi epi) {
     __shared__ float red[4][4][4][kWave];  // [wave][m tile][element][lane]
     const int lane = threadIdx.x & (kWave - 1);
-    const int wq = threadIdx.x / kWave;
+    const int wq = wave_in_block();
     const int MT = (b + 15) >> 4;
     const int kq = K >> 2;
     const int k_begin = wq * kq;
@@ -316,7 +316,7 @@ static Dot2Geom dot2_geom(int N, int K, int b, int cu_budget) {
     Dot2Geom g;
     g.cb = K > 2048 ? 16 : (K > 512 ? 4 : 1);
     const int rb = 16 / g.cb;
-    const int cus = budget_grid(1 << 30, cu_budget, 1);
+    const int cus = budget_grid(1 << 30, cu_budget, 2);
     g.rpw = rows_per_wave(N, cus * (kBlock / kWave), rb);
     const int waves = (N + g.rpw - 1) / g.rpw;
     g.grid = (waves + 3) / 4;
@@ -415,7 +415,7 @@ void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
                 hipStream_t s) {
-    const int cus = budget_grid(1 << 30, 0, 1);
+    const int cus = budget_grid(1 << 30, 0, 2);
     const int grid = (NL > 0 || Is > 0) ? cus : (E + kBlock / kWave - 1) / (kBlock / kWave);
     const size_t lds = (size_t)b * d * sizeof(uint16_t) + (size_t)E * sizeof(float);
     const int cb = d > 2048 ? 16 : (d > 512 ? 4 : 1);

@@ -21,6 +21,41 @@ __device__ __forceinline__ u32x4 ld_weight16(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// Weight loads through a buffer resource: the hardware checks each lane's
+// byte offset against the range and returns zeros past its end, with no
+// memory access, so masked-off lanes (row tails, invalid rows) need no branch
+// -- a branch around a load makes the compiler wait for it at the join. The
+// range base must be wave-uniform (it lives in scalar registers).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t weight_range(const uint16_t *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes at byte offset off of the range (non-temporal).
+__device__ __forceinline__ u32x4 ld_weight16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+
+// An offset past every range: the load returns zeros.
+constexpr uint32_t kOffNone = 0x80000000u;
+
+// Index of the calling wave in its workgroup, known uniform to the compiler.
+__device__ __forceinline__ int wave_in_block() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+// A pointer every lane of the wave holds (e.g. read from LDS), made known
+// uniform to the compiler so that a range built from it stays scalar.
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (T *)(((uint64_t)hi << 32) | lo);
+}
+
 // Activations are produced by earlier kernels: ordinary cached loads.
 __device__ __forceinline__ u32x4 ld_act16(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
@@ -65,13 +100,41 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Sum over the 64 lanes of a wave; every lane receives the same bits
-// (each butterfly step adds the same two operands on both partners).
+// ------------------------------------------------------------------ wave reductions
+// Cross-lane steps use DPP (GFX9 data-parallel primitives): row_shr 1, 2, 4, 8
+// leave each 16-lane row's total in its lane 15, row_bcast 15 and 31 carry
+// those totals into lane 63, and v_readlane broadcasts it, so every lane
+// receives the same bits. Lanes a step reads from outside the row, and rows
+// the step's row mask leaves out, contribute the operation's identity (`id`).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t id) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t id, Op op) {
+    v = op(v, dpp_u32<0x111, 0xf>(v, id));  // row_shr:1
+    v = op(v, dpp_u32<0x112, 0xf>(v, id));  // row_shr:2
+    v = op(v, dpp_u32<0x114, 0xf>(v, id));  // row_shr:4
+    v = op(v, dpp_u32<0x118, 0xf>(v, id));  // row_shr:8
+    v = op(v, dpp_u32<0x142, 0xa>(v, id));  // row_bcast:15 into rows 1 and 3
+    v = op(v, dpp_u32<0x143, 0xc>(v, id));  // row_bcast:31 into rows 2 and 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Sum over the 64 lanes of a wave, in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, kWave);
-    return v;
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    return wave_reduce_u32(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 __device__ __forceinline__ float silu(float g) {
@@ -102,15 +165,19 @@ struct NoPrologue {
 // pre() runs once, after the first unit's loads are issued and before any
 // unit is consumed, in every wave (also waves without units), so it may stage
 // activations and hold a block barrier: its latency overlaps the first loads.
+// With early == false the first unit is loaded only after pre() (its address
+// depends on what pre() produces).
 template <int NB, class Load, class Finish, class Pre = NoPrologue>
 __device__ __forceinline__ void stream_units(int u_begin, int u_end, Load load, Finish finish,
-                                             Pre pre = Pre()) {
+                                             Pre pre = Pre(), bool early = true) {
     u32x4 A[NB], B[NB];
-    if (u_begin < u_end)
+    if (early && u_begin < u_end)
         load(A, u_begin);
     pre();
     if (u_begin >= u_end)
         return;
+    if (!early)
+        load(A, u_begin);
     for (int u = u_begin; u < u_end; u += 2) {
         if (u + 1 < u_end)
             load(B, u + 1);
@@ -138,12 +205,11 @@ __device__ __forceinline__ void stream_rows(int r_begin, int r_end, int nv, cons
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const bool rv = r + i < r_end;
-                const uint16_t *p = rv ? rowptr(r + i) : nullptr;
+                const rsrc_t rr = weight_range(uniform_ptr(rowptr(rv ? r + i : r_begin)),
+                                               rv ? (uint32_t)nv * 16 : 0u);
 #pragma unroll
-                for (int c = 0; c < CB; ++c) {
-                    const int v = c * kWave + lane;
-                    buf[i * CB + c] = (rv && v < nv) ? ld_weight16(p + (int64_t)v * 8) : zero16();
-                }
+                for (int c = 0; c < CB; ++c)
+                    buf[i * CB + c] = ld_weight16(rr, (uint32_t)(c * kWave + lane) * 16);
             }
         },
         [&](u32x4 (&buf)[RB * CB], int u) {
@@ -216,57 +282,79 @@ __device__ __forceinline__ void split_range(int n, int parts, int part, int &lo,
 }
 
 // ------------------------------------------------------------------ top-k
-// One wave picks token t's k experts: lane l holds logits l, l + 64, ...;
-// k rounds of a wave-wide argmax under the order (logit desc, index asc);
-// lane j keeps the j-th pick. The weights are the softmax over the k picked
-// logits (the full softmax renormalised over the selection).
-__device__ __forceinline__ void topk_wave(const float *logits, int E, int k, int32_t *ids,
-                                          float *wts) {
-    constexpr int PER = K3_MAX_EXPERTS / kWave;
+// Selection order: logit descending, expert index ascending on equal logits;
+// a NaN logit ranks with -inf and -0 with +0. order_key maps a logit to a
+// 32-bit key whose unsigned order is that order of values (key 0 is never
+// produced and marks an empty or taken entry).
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        u = 0xff800000u;
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+}
+
+constexpr int kTopkPer = K3_MAX_EXPERTS / kWave;  // logits per lane
+
+// Lane l loads logits l, l + 64, ... (entries past E are empty). The loads
+// are unconditional (clamped index) so that all of them are in flight at
+// once; the keys are formed later, by topk_keys.
+__device__ __forceinline__ void topk_load(const float *logits, int E, float (&lv)[kTopkPer]) {
     const int lane = threadIdx.x & (kWave - 1);
-    float v[PER];
-    uint32_t taken = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
+    for (int i = 0; i < kTopkPer; ++i) {
         const int e = i * kWave + lane;
-        float l = -INFINITY;
-        if (e < E)
-            l = logits[e];
-        else
-            taken |= 1u << i;
-        v[i] = (l != l) ? -INFINITY : l;  // NaN never outranks a number
+        lv[i] = logits[e < E ? e : E - 1];
     }
-    float sel_v = 0.0f, top = 0.0f;
+}
+
+__device__ __forceinline__ void topk_keys(const float (&lv)[kTopkPer], int E,
+                                          uint32_t (&key)[kTopkPer]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < kTopkPer; ++i)
+        key[i] = i * kWave + lane < E ? order_key(lv[i]) : 0u;
+}
+
+// One wave picks k experts from the keys topk_load gave it: k rounds of a
+// wave-wide maximum of the keys, then the smallest expert index holding it;
+// lane j keeps the j-th pick. The weights are the softmax over the k picked
+// logits (the full softmax renormalised over the selection), written by
+// lanes j < k to ids[j], wts[j].
+__device__ __forceinline__ void topk_select(uint32_t (&key)[kTopkPer], int k, int32_t *ids,
+                                            float *wts) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t sel_key = 0u, top_key = 0u;
     int sel_e = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
+        uint32_t bk = 0u;
+        int bi = 0;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = i * kWave + lane;
-            if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-                bv = v[i];
-                be = e;
+        for (int i = 0; i < kTopkPer; ++i) {
+            if (key[i] > bk) {
+                bk = key[i];
+                bi = i;
             }
         }
+        const uint32_t m = wave_max_u32(bk);
+        const uint32_t w = wave_min_u32(bk == m ? (uint32_t)(bi * kWave + lane) : 0xffffffffu);
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, kWave);
-            const int oe = __shfl_xor(be, m, kWave);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & (kWave - 1)) == lane)
-            taken |= 1u << (be / kWave);
+        for (int i = 0; i < kTopkPer; ++i)
+            if ((int)(w >> 6) == i && (int)(w & (kWave - 1)) == lane)
+                key[i] = 0u;
         if (lane == j) {
-            sel_v = bv;
-            sel_e = be;
+            sel_key = m;
+            sel_e = (int)w;
         }
         if (j == 0)
-            top = bv;
+            top_key = m;
     }
+    const float sel_v = key_value(sel_key), top = key_value(top_key);
     const float dl = (sel_v == top) ? 0.0f : sel_v - top;
     const float p = lane < k ? expf(dl) : 0.0f;
     const float sum = wave_sum(p);
@@ -274,6 +362,15 @@ __device__ __forceinline__ void topk_wave(const float *logits, int E, int k, int
         ids[lane] = sel_e;
         wts[lane] = p / sum;
     }
+}
+
+__device__ __forceinline__ void topk_wave(const float *logits, int E, int k, int32_t *ids,
+                                          float *wts) {
+    float lv[kTopkPer];
+    uint32_t key[kTopkPer];
+    topk_load(logits, E, lv);
+    topk_keys(lv, E, key);
+    topk_select(key, k, ids, wts);
 }
 
 }  // namespace k3
