@@ -40,7 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_expert_gateup_b1_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_moe_up_b1_traffic.json")
 DOMINANT_SOURCES = ["moe_router_topk_amd/csrc/experts.hip", "moe_router_topk_amd/csrc/k3_device.h"]
 
 
@@ -78,9 +78,23 @@ def chain_bytes(cc, b: int) -> int:
 
 
 def gateup_bytes(cfg, b: int, n_active: int) -> int:
-    """Per launch of the routed gate/up kernel: n_active experts' [2I x d]
-    weights, the z rows it reads and the h rows it writes."""
-    return 2 * n_active * 2 * cfg.I * cfg.d_lat + 2 * b * cfg.d_lat + 2 * b * cfg.k * cfg.I
+    """Per launch of the kernel traced as the routed experts' gate/up pass.
+    Always: n_active experts' [2I x d_lat] weights, the z rows it reads and the
+    h rows it writes. At batch 1 that kernel (k_moe_up_b1) also selects the
+    experts and streams the shared expert's down projection: + the [d x I_s]
+    weights, the logits and shared h it reads, y_s, ids and weights it writes."""
+    d, dl, I, Is, E, k = cfg.d, cfg.d_lat, cfg.I, cfg.I_s, cfg.E, cfg.k
+    n = 2 * n_active * 2 * I * dl + 2 * b * dl + 2 * b * k * I
+    if b == 1:
+        n += 2 * d * Is + 4 * E + 2 * Is + 4 * d + 8 * k
+    return n
+
+
+def gateup_kernel_name(b: int) -> str:
+    if b == 1:
+        return ("k_moe_up_b1<true> (expert selection + shared down projection + "
+                "routed gate/up + SwiGLU)")
+    return "routed gate/up + SwiGLU (dot2 rows for light experts, MFMA tiles for heavy)"
 
 
 def sources_digest(paths) -> str:
@@ -395,12 +409,12 @@ def main() -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_expert_gateup (routed gate/up + SwiGLU)",
+            "kernel": gateup_kernel_name(b),
             "achieved": round(gu_gbs, 1),
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gu_gbs / PEAK_GBS, 4),
-            "traffic": traffic_per_launch(),
+            "traffic": traffic_per_launch() if b == 1 else None,
             "bytes_per_launch": int(gu_bytes),
             "avg_launch_us": round(kern_avg * 1e3, 2),
         },
