@@ -109,6 +109,7 @@ int k3_trace_events(int op, void *begin, void *end);
  * that may overlap need workspaces of their own.
  */
 size_t k3_router_topk_workspace_size(int b, int E);
+size_t k3_router_topk_latent_workspace_size(int b, int E, int d_lat);
 size_t k3_proj_skinny_workspace_size(int b, int K, int N);
 size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I, int d_out);
 size_t k3_shared_expert_workspace_size(int b, int d, int I);
@@ -148,14 +149,13 @@ int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
  * into one matrix multiplication, removing a second read of the input and
  * a kernel launch before the experts run.
  *
- * Computes exactly what k3_router_topk(x, ...) and
- * k3_proj_skinny(x, w_lat -> z) compute, with one pass over the router and
- * latent rows when b <= 4 (then a small top-k kernel) and as the separate
- * computations otherwise.
+ * Computes what k3_router_topk(x, ...) and k3_proj_skinny(x, w_lat -> z)
+ * compute, with one pass over the router and latent rows (then a small
+ * top-k kernel).
  *
  * w_lat device, [d_lat x d] bf16;  z device, [b x d_lat] bf16 (output), row
- * stride ldz; the other arguments, the workspace and the limits are those
- * of k3_router_topk.
+ * stride ldz; workspace >= k3_router_topk_latent_workspace_size(b, E, d_lat)
+ * bytes; the other arguments and the limits are those of k3_router_topk.
  */
 int k3_router_topk_latent(const uint16_t *x, int64_t ldx, int b, int d,
                           const uint16_t *w_router, const float *bias, int E, int k,
@@ -173,8 +173,10 @@ int k3_router_topk_latent(const uint16_t *x, int64_t ldx, int b, int d,
  * x device, [b x K] bf16, row stride ldx;  w device, [N x K] bf16;
  * y device, [b x N] bf16 (output), row stride ldy; y must not overlap x.
  * Variant: K3_VARIANT_DOT2 for b <= 4 and K <= 8192, K3_VARIANT_MFMA
- * otherwise (which needs K % 128 == 0).
- * Limits: 1 <= b <= 64.
+ * otherwise: K is split into ranges whose fp32 partial sums go through the
+ * workspace (>= k3_proj_skinny_workspace_size(b, K, N) bytes; the dot2
+ * variant needs none and accepts NULL) and are summed in range order.
+ * Limits: 1 <= b <= 64, K % 8 == 0.
  */
 int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K,
                    const uint16_t *w, int N, uint16_t *y, int64_t ldy,
@@ -234,17 +236,19 @@ int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d,
  * expert and routed experts, y = shared(x) + sum_j w_j routed_j(latent(x)).
  * "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 3: router and latent
  * projection share one matrix pass; the shared expert's work overlaps the
- * routing. At b <= 4 the block runs as four kernels and nothing waits on
- * another stream:
+ * routing. Nothing waits on another stream. At b = 1:
  *   1. one pass over x for the router rows, the latent rows and the shared
  *      expert's gate/up rows (logits, z, shared h);
- *   2. the top-k in one workgroup while all the others stream the shared
- *      expert's down projection (y_s);
- *   3. routed gate/up + SwiGLU (after the permutation when b > 1);
- *   4. routed down projection with the weighted combine, y_s added.
- * Above b = 4 it runs the MFMA variants of the same steps in sequence.
- * Results equal k3_router_topk_latent + k3_shared_expert + k3_moe_experts
- * on the same inputs.
+ *   2. every workgroup selects the experts while its first units -- the
+ *      shared expert's down rows (y_s) -- stream, then the routed gate/up
+ *      rows + SwiGLU follow;
+ *   3. routed down projection with the weighted combine, y_s added.
+ * At 2 <= b <= 4 the selection runs in one workgroup beside the shared
+ * down rows and the routed experts follow the permutation. Above b = 4 the
+ * same steps run on the split-K MFMA engine (router, latent and shared
+ * gate/up rows in one pass), the shared down projection after the
+ * selection. Results equal k3_router_topk_latent + k3_shared_expert +
+ * k3_moe_experts on the same inputs, bit for bit.
  *
  * x [b x d] bf16 (ldx); w_router [E x d], bias [E] fp32 or NULL, w_lat
  * [d_lat x d], w13 [E x 2I x d_lat], w2 [E x d x I], w13_s [2I_s x d],

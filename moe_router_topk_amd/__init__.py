@@ -35,7 +35,8 @@ VARIANT_NAME = {v: k for k, v in VARIANT.items()}
 
 EXPORTED_SYMBOLS = [
     "k3_status_string", "k3_version", "k3_get_last_dispatch", "k3_force_variant",
-    "k3_trace_events", "k3_router_topk_workspace_size", "k3_proj_skinny_workspace_size",
+    "k3_trace_events", "k3_router_topk_workspace_size",
+    "k3_router_topk_latent_workspace_size", "k3_proj_skinny_workspace_size",
     "k3_moe_experts_workspace_size", "k3_shared_expert_workspace_size",
     "k3_oproj_residual_workspace_size", "k3_moe_block_workspace_size",
     "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
@@ -80,12 +81,14 @@ def lib():
     L.k3_trace_events.argtypes = [_i32, _vp, _vp]
     L.k3_trace_events.restype = _i32
     L.k3_router_topk_workspace_size.argtypes = [_i32, _i32]
+    L.k3_router_topk_latent_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_proj_skinny_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_moe_experts_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
     L.k3_shared_expert_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_oproj_residual_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_moe_block_workspace_size.argtypes = [_i32] * 7
-    for f in ("k3_router_topk_workspace_size", "k3_proj_skinny_workspace_size",
+    for f in ("k3_router_topk_workspace_size", "k3_router_topk_latent_workspace_size",
+              "k3_proj_skinny_workspace_size",
               "k3_moe_experts_workspace_size", "k3_shared_expert_workspace_size",
               "k3_oproj_residual_workspace_size", "k3_moe_block_workspace_size"):
         getattr(L, f).restype = _sz
@@ -228,6 +231,8 @@ def workspace_size(op: str, **kw) -> int:
     L = lib()
     if op == "router_topk":
         return L.k3_router_topk_workspace_size(kw["b"], kw["E"])
+    if op == "router_topk_latent":
+        return L.k3_router_topk_latent_workspace_size(kw["b"], kw["E"], kw["d_lat"])
     if op == "proj_skinny":
         return L.k3_proj_skinny_workspace_size(kw["b"], kw["K"], kw["N"])
     if op == "moe_experts":
@@ -276,8 +281,8 @@ def k3_router_topk_latent(x, w_router, bias, k, w_lat, topk_ids=None, topk_w=Non
         topk_w = torch.empty((b, k), dtype=torch.float32, device=dev)
     if z is None:
         z = torch.empty((b, d_lat), dtype=torch.bfloat16, device=dev)
-    nbytes = lib().k3_router_topk_workspace_size(b, E)
-    ws = workspace if workspace is not None else _workspace(dev, nbytes, "router_topk")
+    nbytes = lib().k3_router_topk_latent_workspace_size(b, E, d_lat)
+    ws = workspace if workspace is not None else _workspace(dev, nbytes, "router_topk_latent")
     _check("k3_router_topk_latent", lib().k3_router_topk_latent(
         _ptr(x), _ld(x), b, d, _ptr(w_router), _ptr(bias), E, k, _ptr(w_lat), d_lat,
         _ptr(topk_ids), _ptr(topk_w), _ptr(z), _ld(z), _ptr(ws),

@@ -7,12 +7,10 @@
 //    row buffers in flight, and multiplies against the tokens staged in LDS
 //    with v_dot2c_f32_bf16. The small-batch kernels of "Hyper Optimizing
 //    Kimi K3 in vLLM", Part 1 section 1 ("Tune shapes for the workload").
-//  * mfma (batch > 4): one workgroup per 16-row tile of W; its four waves
-//    split K into quarters and run v_mfma_f32_16x16x32_bf16 with the tokens
-//    as the A operand (up to four 16-token tiles) and the weight rows as B,
-//    then sum the four partial tiles in LDS in a fixed order: the
-//    work-splitting kernel the same section uses at larger batch, with the
-//    split kept inside one workgroup so no partial sums go through HBM.
+//  * mfma (batch > 4): the split-K MFMA engine of k3_skinny.h (skinny.hip),
+//    whose partial sums a small kernel finishes (bf16 projection, fp32
+//    logits, or residual + RMSNorm): the work-splitting kernels the same
+//    section uses at larger batch.
 //
 // Router top-k and RMSNorm need every output of their projection; each runs
 // as a small kernel after it. (Finishing them in the last workgroup of the
@@ -44,24 +42,6 @@ struct EpiLogits {  // logits[t][e] = s (+ bias[e]), fp32
     __device__ void operator()(int t, int n, float s) const {
         logits[(int64_t)t * E + n] = bias ? s + bias[n] : s;
     }
-};
-
-struct EpiResidual {  // h = r + s: fp32 copy for the norm, bf16 back into r
-    uint16_t *res;
-    float *h32;
-    int d;
-    __device__ float operator()(int t, int n, float s) const {
-        const int64_t i = (int64_t)t * d + n;
-        const float h = bf16_to_f32(res[i]) + s;
-        h32[i] = h;
-        res[i] = f32_to_bf16(h);
-        return h;
-    }
-};
-
-struct EpiResidualStore {  // EpiResidual without the return value
-    EpiResidual r;
-    __device__ void operator()(int t, int n, float s) const { (void)r(t, n, s); }
 };
 
 // Rows per wave so that N rows spread evenly over `waves` waves, rounded up
@@ -200,82 +180,11 @@ k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t 
         });
 }
 
-// ------------------------------------------------------------------ mfma engine
-// Workgroup per 16-row tile of W (grid-stride over tiles). Wave q handles
-// K range [q K/4, (q+1) K/4) in steps of 32; lane l loads B = W[n0 + l%16]
-// at k + 8(l/16) (16 bytes) and A = x[m][same k] for m = 16 mt + l%16.
-template <int U, class Epi>
-__global__ void __launch_bounds__(kBlock)
-k_gemm_mfma(const uint16_t *__restrict__ x, int64_t ldx, int b,
-            const uint16_t *__restrict__ W, int N, int K, Epi epi) {
-    __shared__ float red[4][4][4][kWave];  // [wave][m tile][element][lane]
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wq = wave_in_block();
-    const int MT = (b + 15) >> 4;
-    const int kq = K >> 2;
-    const int k_begin = wq * kq;
-    const int k_end = k_begin + kq;
-    const int kgrp = (lane >> 4) * 8;
-    int64_t aoff[4];
-    bool aval[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        aval[mt] = m < b;
-        aoff[mt] = (int64_t)(aval[mt] ? m : 0) * ldx;
-    }
-    const int tiles = (N + 15) >> 4;
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int n = tile * 16 + (lane & 15);
-        const bool nval = n < N;
-        const uint16_t *wrow = W + (int64_t)(nval ? n : 0) * K;
-        f32x4 acc[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = k_begin; ks < k_end; ks += 32 * U) {
-            u32x4 bfr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k = ks + 32 * u + kgrp;
-                bfr[u] = (ks + 32 * u < k_end && nval) ? ld_weight16(wrow + k) : zero16();
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (ks + 32 * u < k_end) {
-                    const int k = ks + 32 * u + kgrp;
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        if (mt < MT) {
-                            const u32x4 av = aval[mt] ? ld_act16(x + aoff[mt] + k) : zero16();
-                            acc[mt] = mfma16x16x32(av, bfr[u], acc[mt]);
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            if (mt < MT)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[wq][mt][i][lane] = acc[mt][i];
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < MT * 256; idx += kBlock) {
-            const int mt = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
-            const float s = red[0][mt][i][l] + red[1][mt][i][l] + red[2][mt][i][l] + red[3][mt][i][l];
-            const int m = mt * 16 + 4 * (l >> 4) + i;
-            const int nn = tile * 16 + (l & 15);
-            if (m < b && nn < N)
-                epi(m, nn, s);
-        }
-        __syncthreads();
-    }
-}
-
 // One workgroup per token: y = h / sqrt(mean(h^2) + eps) * gamma, the mean in
-// fp32 with a fixed reduction order; loads are issued in 16-byte vectors so
-// the loop is not latency-bound (d % 4 == 0).
+// fp32 with a fixed reduction order (d % 4 == 0, d <= 8192). Every load of
+// h and gamma is issued before the first is used (indexes clamped, no
+// branches), so the kernel costs about one memory latency, not several.
+constexpr int kNormVec = 8;
 __global__ void __launch_bounds__(kBlock)
 k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gamma, float eps,
           uint16_t *__restrict__ y) {
@@ -283,24 +192,36 @@ k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gam
     const int t = blockIdx.x;
     const f32x4 *h = reinterpret_cast<const f32x4 *>(h32 + (int64_t)t * d);
     const int n4 = d >> 2;
-    float ss = 0.0f;
-#pragma unroll 8
-    for (int i = threadIdx.x; i < n4; i += kBlock) {
-        const f32x4 v = h[i];
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    f32x4 v[kNormVec];
+    uint16_t gm[kNormVec][4];
+#pragma unroll
+    for (int j = 0; j < kNormVec; ++j) {
+        const int i = threadIdx.x + j * kBlock;
+        const int ic = i < n4 ? i : 0;
+        v[j] = h[ic];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            gm[j][q] = gamma[4 * ic + q];
     }
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kNormVec; ++j)
+        if (threadIdx.x + j * kBlock < n4)
+            ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
     ss = wave_sum(ss);
     if ((threadIdx.x & (kWave - 1)) == 0)
         part[threadIdx.x / kWave] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)d + eps);
-#pragma unroll 8
-    for (int i = threadIdx.x; i < n4; i += kBlock) {
-        const f32x4 v = h[i];
-        uint16_t *o = y + (int64_t)t * d + 4 * i;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            o[j] = f32_to_bf16(v[j] * inv * bf16_to_f32(gamma[4 * i + j]));
+    for (int j = 0; j < kNormVec; ++j) {
+        const int i = threadIdx.x + j * kBlock;
+        if (i < n4) {
+            uint16_t *o = y + (int64_t)t * d + 4 * i;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = f32_to_bf16(v[j][q] * inv * bf16_to_f32(gm[j][q]));
+        }
     }
 }
 
@@ -343,29 +264,21 @@ static void launch_dense_dot2_t(const uint16_t *x, int64_t ldx, int b, const uin
 }
 
 template <class Epi>
-static void launch_dense(int variant, const uint16_t *x, int64_t ldx, int b, const uint16_t *W,
-                         int N, int K, Epi epi, hipStream_t s) {
-    if (variant == K3_VARIANT_DOT2) {
-        if (b == 1)
-            launch_dense_dot2_t<1>(x, ldx, b, W, N, K, epi, s);
-        else
-            launch_dense_dot2_t<kDot2MaxTokens>(x, ldx, b, W, N, K, epi, s);
-    } else {
-        const int grid = budget_grid((N + 15) / 16, 0, 4);
-        k_gemm_mfma<8, Epi><<<grid, kBlock, 0, s>>>(x, ldx, b, W, N, K, epi);
-    }
+static void launch_dense_dot2(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N,
+                              int K, Epi epi, hipStream_t s) {
+    if (b == 1)
+        launch_dense_dot2_t<1>(x, ldx, b, W, N, K, epi, s);
+    else
+        launch_dense_dot2_t<kDot2MaxTokens>(x, ldx, b, W, N, K, epi, s);
 }
 
 // Variant for a dense [N x K] read at batch b: dot2 while the tokens fit the
-// engine, MFMA above (MFMA needs K % 128 == 0 so each K quarter is whole
-// 32-wide steps).
+// engine, the split-K MFMA engine above.
 static int pick_dense_variant(int op, int b, int K) {
     int v = forced_variant(op);
     if (v == K3_VARIANT_NONE)
         v = dot2_fits(b, K) ? K3_VARIANT_DOT2 : K3_VARIANT_MFMA;
     if (v == K3_VARIANT_DOT2 && !dot2_fits(b, K))
-        return -1;
-    if (v == K3_VARIANT_MFMA && K % 128 != 0)
         return -1;
     if (v != K3_VARIANT_DOT2 && v != K3_VARIANT_MFMA)
         return -1;
@@ -377,31 +290,45 @@ static int pick_dense_variant(int op, int b, int K) {
 using namespace k3;
 
 // ------------------------------------------------------------------ workspace layouts
-// Each workspace starts with a 256-byte head that no kernel touches.
+// Each workspace starts with a 256-byte head that no kernel touches; the
+// MFMA variants keep the fp32 partial sums of their K ranges after it.
 namespace {
 constexpr size_t kHeadBytes = 256;
 size_t router_logits_offset() { return kHeadBytes; }
+size_t router_partial_offset(int b, int E) {
+    return kHeadBytes + align_up((size_t)b * E * sizeof(float), 256);
+}
 size_t oproj_h32_offset() { return kHeadBytes; }
 }  // namespace
 
 extern "C" size_t k3_router_topk_workspace_size(int b, int E) {
     if (b <= 0 || E <= 0)
         return 0;
-    return kHeadBytes + align_up((size_t)b * E * sizeof(float), 256);
+    return router_partial_offset(b, E) + sk_partial_bytes(b, E);
+}
+
+extern "C" size_t k3_router_topk_latent_workspace_size(int b, int E, int d_lat) {
+    if (b <= 0 || E <= 0 || d_lat <= 0)
+        return 0;
+    return router_partial_offset(b, E) + sk_partial_bytes(b, E + d_lat);
+}
+
+static size_t oproj_part_offset(int b, int d) {
+    return kHeadBytes + align_up((size_t)b * d * sizeof(float), 256);
 }
 
 extern "C" size_t k3_oproj_residual_workspace_size(int b, int K, int d) {
     (void)K;
     if (b <= 0 || d <= 0)
         return 0;
-    return kHeadBytes + align_up((size_t)b * d * sizeof(float), 256);
+    return oproj_part_offset(b, d) + sk_partial_bytes(b, d);
 }
 
 extern "C" size_t k3_proj_skinny_workspace_size(int b, int K, int N) {
-    (void)b;
     (void)K;
-    (void)N;
-    return 0;
+    if (b <= 0 || N <= 0)
+        return 0;
+    return kHeadBytes + sk_partial_bytes(b, N);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -445,23 +372,13 @@ void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *
     k_topk_softmax<<<b, kWave, 0, s>>>(logits, E, k, ids, wts);
 }
 
-void launch_dense_bf16(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
-                       uint16_t *y, int64_t ldy, hipStream_t s) {
-    launch_dense(pick_dense_variant(-1, b, K), x, ldx, b, W, N, K, EpiBf16{y, ldy}, s);
-}
-
-void launch_dense_logits(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int E, int K,
-                         const float *bias, float *logits, hipStream_t s) {
-    launch_dense(pick_dense_variant(-1, b, K), x, ldx, b, W, E, K, EpiLogits{logits, E, bias}, s);
-}
-
 }  // namespace k3
 
 namespace {
 
 int check_router_args(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
                       int E, int k, const int32_t *ids, const float *wts, void *workspace,
-                      size_t ws_bytes) {
+                      size_t ws_bytes, size_t need) {
     if (!x || !w_router || !ids || !wts)
         return K3_ERR_INVALID_ARG;
     if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || ldx < d)
@@ -469,7 +386,7 @@ int check_router_args(const uint16_t *x, int64_t ldx, int b, int d, const uint16
     if (b > K3_MAX_BATCH || E > K3_MAX_EXPERTS || k > K3_MAX_TOPK || k > E || d % 8 || ldx % 8 ||
         !aligned16(x) || !aligned16(w_router))
         return K3_ERR_UNSUPPORTED;
-    if (!workspace || ws_bytes < k3_router_topk_workspace_size(b, E) || !aligned16(workspace))
+    if (!workspace || ws_bytes < need || !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     return K3_OK;
 }
@@ -480,7 +397,7 @@ int pick_router_variant(int op, int b, int d, int E) {
     if (v == K3_VARIANT_DOT2 && !rls_fits(b, d, E)) {
         if (forced_variant(op) == K3_VARIANT_DOT2)
             return -1;
-        v = d % 128 == 0 ? K3_VARIANT_MFMA : -1;
+        v = K3_VARIANT_MFMA;
     }
     return v;
 }
@@ -491,8 +408,6 @@ int pick_router_variant(int op, int b, int d, int E) {
 extern "C" int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K, const uint16_t *w,
                               int N, uint16_t *y, int64_t ldy, void *workspace, size_t ws_bytes,
                               void *stream) {
-    (void)workspace;
-    (void)ws_bytes;
     if (!x || !w || !y)
         return K3_ERR_INVALID_ARG;
     if (b <= 0 || K <= 0 || N <= 0 || ldx < K || ldy < N)
@@ -502,9 +417,15 @@ extern "C" int k3_proj_skinny(const uint16_t *x, int64_t ldx, int b, int K, cons
     const int variant = pick_dense_variant(K3_OP_PROJ_SKINNY, b, K);
     if (variant < 0)
         return K3_ERR_UNSUPPORTED;
+    if (variant == K3_VARIANT_MFMA &&
+        (!workspace || ws_bytes < k3_proj_skinny_workspace_size(b, K, N) || !aligned16(workspace)))
+        return K3_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     trace_begin(K3_OP_PROJ_SKINNY, s);
-    launch_dense(variant, x, ldx, b, w, N, K, EpiBf16{y, ldy}, s);
+    if (variant == K3_VARIANT_DOT2)
+        launch_dense_dot2(x, ldx, b, w, N, K, EpiBf16{y, ldy}, s);
+    else
+        sk_proj_bf16(x, ldx, b, w, N, K, y, ldy, (float *)((char *)workspace + kHeadBytes), s);
     trace_end(K3_OP_PROJ_SKINNY, s);
     const int st = launch_status();
     if (st == K3_OK)
@@ -517,7 +438,7 @@ extern "C" int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
                               int32_t *topk_ids, float *topk_w, void *workspace, size_t ws_bytes,
                               void *stream) {
     const int chk = check_router_args(x, ldx, b, d, w_router, E, k, topk_ids, topk_w, workspace,
-                                      ws_bytes);
+                                      ws_bytes, k3_router_topk_workspace_size(b, E));
     if (chk != K3_OK)
         return chk;
     const int variant = pick_router_variant(K3_OP_ROUTER_TOPK, b, d, E);
@@ -525,12 +446,13 @@ extern "C" int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     float *logits = (float *)((char *)workspace + router_logits_offset());
+    float *part = (float *)((char *)workspace + router_partial_offset(b, E));
     trace_begin(K3_OP_ROUTER_TOPK, s);
     if (variant == K3_VARIANT_DOT2)
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, nullptr, 0, nullptr, 0, nullptr, 0,
                    nullptr, s);
     else
-        launch_dense(variant, x, ldx, b, w_router, E, d, EpiLogits{logits, E, bias}, s);
+        sk_logits(x, ldx, b, w_router, E, d, bias, logits, part, s);
     trace_end(K3_OP_ROUTER_TOPK, s);
     launch_topk(logits, b, E, k, topk_ids, topk_w, s);
     const int st = launch_status();
@@ -544,14 +466,14 @@ extern "C" int k3_router_topk_latent(const uint16_t *x, int64_t ldx, int b, int 
                                      const uint16_t *w_lat, int d_lat, int32_t *topk_ids,
                                      float *topk_w, uint16_t *z, int64_t ldz, void *workspace,
                                      size_t ws_bytes, void *stream) {
-    const int chk = check_router_args(x, ldx, b, d, w_router, E, k, topk_ids, topk_w, workspace,
-                                      ws_bytes);
-    if (chk != K3_OK)
-        return chk;
     if (!w_lat || !z)
         return K3_ERR_INVALID_ARG;
     if (d_lat <= 0 || ldz < d_lat)
         return K3_ERR_INVALID_ARG;
+    const int chk = check_router_args(x, ldx, b, d, w_router, E, k, topk_ids, topk_w, workspace,
+                                      ws_bytes, k3_router_topk_latent_workspace_size(b, E, d_lat));
+    if (chk != K3_OK)
+        return chk;
     if (!aligned16(w_lat))
         return K3_ERR_UNSUPPORTED;
     const int variant = pick_router_variant(K3_OP_ROUTER_LATENT, b, d, E);
@@ -559,14 +481,13 @@ extern "C" int k3_router_topk_latent(const uint16_t *x, int64_t ldx, int b, int 
         return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     float *logits = (float *)((char *)workspace + router_logits_offset());
+    float *part = (float *)((char *)workspace + router_partial_offset(b, E));
     trace_begin(K3_OP_ROUTER_LATENT, s);
-    if (variant == K3_VARIANT_DOT2) {
+    if (variant == K3_VARIANT_DOT2)
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, nullptr, 0,
                    nullptr, s);
-    } else {
-        launch_dense(variant, x, ldx, b, w_router, E, d, EpiLogits{logits, E, bias}, s);
-        launch_dense(variant, x, ldx, b, w_lat, d_lat, d, EpiBf16{z, ldz}, s);
-    }
+    else
+        sk_logits_latent(x, ldx, b, d, w_router, E, bias, logits, w_lat, d_lat, z, ldz, part, s);
     trace_end(K3_OP_ROUTER_LATENT, s);
     launch_topk(logits, b, E, k, topk_ids, topk_w, s);
     const int st = launch_status();
@@ -583,7 +504,8 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         return K3_ERR_INVALID_ARG;
     if (b <= 0 || K <= 0 || d <= 0 || lda < K || !(eps >= 0.0f))
         return K3_ERR_INVALID_ARG;
-    if (b > K3_MAX_BATCH || K % 8 || lda % 8 || d % 8 || !aligned16(a) || !aligned16(w_o))
+    if (b > K3_MAX_BATCH || K % 8 || lda % 8 || d % 8 || d > 8192 || !aligned16(a) ||
+        !aligned16(w_o))
         return K3_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < k3_oproj_residual_workspace_size(b, K, d) ||
         !aligned16(workspace))
@@ -596,7 +518,7 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         if (g.lds > 65536) {
             if (forced_variant(K3_OP_OPROJ_RESIDUAL) == K3_VARIANT_DOT2)
                 return K3_ERR_UNSUPPORTED;
-            variant = K % 128 == 0 ? K3_VARIANT_MFMA : -1;
+            variant = K3_VARIANT_MFMA;
         }
     }
     if (variant < 0)
@@ -621,12 +543,14 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         else
             K3_OPROJ(kDot2MaxTokens, 1);
 #undef K3_OPROJ
+        trace_end(K3_OP_OPROJ_RESIDUAL, s);
+        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     } else {
-        launch_dense(variant, a, lda, b, w_o, d, K, EpiResidualStore{EpiResidual{residual, h32, d}},
-                     s);
+        sk_oproj_residual(a, lda, b, K, w_o, d, residual, h32,
+                          (float *)((char *)workspace + oproj_part_offset(b, d)), s);
+        trace_end(K3_OP_OPROJ_RESIDUAL, s);
+        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     }
-    trace_end(K3_OP_OPROJ_RESIDUAL, s);
-    k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_OPROJ_RESIDUAL, variant);

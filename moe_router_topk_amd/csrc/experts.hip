@@ -20,6 +20,7 @@
 
 #include "k3_device.h"
 #include "k3_internal.h"
+#include "k3_skinny.h"
 
 namespace k3 {
 
@@ -264,164 +265,121 @@ k_down_dot2(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict
     }
 }
 
-// ------------------------------------------------------------------ mfma gate/up
-// Item = (list entry a, tile of 16 intermediate columns j). Lane l streams
-// gate row j0 + l%16 and up row I + j0 + l%16 of w13[e]; wave q covers input
-// range [q d/4, (q+1) d/4); the four partial tiles are summed in LDS.
-template <int U, class List>
-__global__ void __launch_bounds__(kBlock)
-k_gateup_mfma(const uint16_t *__restrict__ z, int64_t ldz, int d, const uint16_t *__restrict__ w13,
-              int I, List L, uint16_t *__restrict__ hbuf) {
-    __shared__ float red[4][2][4][4][kWave];  // [wave][gate/up][m tile][element][lane]
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wq = wave_in_block();
-    const int kq = d >> 2;
-    const int k_begin = wq * kq, k_end = k_begin + kq;
-    const int kgrp = (lane >> 4) * 8;
-    const int tiles = I >> 4;
-    const int total = L.count() * tiles;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int a = item / tiles;
-        const int tile = item - a * tiles;
-        int e, p0, na;
-        L.get(a, e, p0, na);
-        const int MT = min((na + 15) >> 4, 4);
-        const int j = tile * 16 + (lane & 15);
-        const uint16_t *grow = w13 + ((int64_t)e * 2 * I + j) * d;
-        const uint16_t *urow = grow + (int64_t)I * d;
-        int64_t aoff[4];
-        bool aval[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int m = mt * 16 + (lane & 15);
-            aval[mt] = m < na;
-            aoff[mt] = aval[mt] ? (int64_t)L.token(p0 + m) * ldz : 0;
-        }
-        f32x4 ag[4], au[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            ag[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            au[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        for (int ks = k_begin; ks < k_end; ks += 32 * U) {
-            u32x4 bg[U], bu[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool in = ks + 32 * u < k_end;
-                const int k = ks + 32 * u + kgrp;
-                bg[u] = in ? ld_weight16(grow + k) : zero16();
-                bu[u] = in ? ld_weight16(urow + k) : zero16();
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (ks + 32 * u < k_end) {
-                    const int k = ks + 32 * u + kgrp;
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        if (mt < MT) {
-                            const u32x4 av = aval[mt] ? ld_act16(z + aoff[mt] + k) : zero16();
-                            ag[mt] = mfma16x16x32(av, bg[u], ag[mt]);
-                            au[mt] = mfma16x16x32(av, bu[u], au[mt]);
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            if (mt < MT)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    red[wq][0][mt][i][lane] = ag[mt][i];
-                    red[wq][1][mt][i][lane] = au[mt][i];
-                }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < MT * 256; idx += kBlock) {
-            const int mt = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
-            const float g = red[0][0][mt][i][l] + red[1][0][mt][i][l] + red[2][0][mt][i][l] +
-                            red[3][0][mt][i][l];
-            const float u = red[0][1][mt][i][l] + red[1][1][mt][i][l] + red[2][1][mt][i][l] +
-                            red[3][1][mt][i][l];
-            const int m = mt * 16 + 4 * (l >> 4) + i;
-            if (m < na)
-                hbuf[(int64_t)(p0 + m) * I + tile * 16 + (l & 15)] = f32_to_bf16(silu(g) * u);
-        }
-        __syncthreads();
-    }
-}
+// ------------------------------------------------------------------ heavy experts (MFMA)
+// Experts with more than kDot2MaxTokens tokens run on the split-K MFMA
+// engine of k3_skinny.h with one K range per tile, so the epilogue finishes
+// the outputs itself. Gate/up (pair == true): a tile is 32 columns j of h;
+// waves 0-1 stream gate rows j, waves 2-3 the matching up rows I + j, the up
+// sums cross to the gate waves through LDS and h = silu(g) * u is written
+// for the expert's positions. Down (pair == false): a tile is 64 output
+// rows; the sums go to part[p][n]. A down launch may carry one extra dense
+// job after the list: the shared expert's down projection into y_s.
+struct SkExperts {
+    ExpertList L;
+    const uint16_t *w;  // expert e: w + e * w_stride, [rows][K] (gate/up: [2I][K])
+    int64_t w_stride;
+    int K;
+    bool pair;
+    int I;     // gate/up: columns of h
+    int rows;  // down: output rows
+    const uint16_t *x;  // gate/up: z rows by token; down: h rows by position
+    int64_t ldx;
+    bool gather;
+    uint16_t *h;  // gate/up output [P][I]
+    float *out;   // down output [P][rows]
+    const uint16_t *w_x;  // extra job: weights [rows][K], or null
+    const uint16_t *x_x;
+    int64_t ldx_x;
+    int xT;
+    float *out_x;  // [xT][rows]
 
-// ------------------------------------------------------------------ mfma down
-// Item = (list entry a, tile of 16 output rows); wave q covers the
-// intermediate range [q I/4, (q+1) I/4); output for position p0 + m.
-template <int U, class List, class Out>
-__global__ void __launch_bounds__(kBlock)
-k_down_mfma(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__ w2, int d_out,
-            List L, Out out) {
-    __shared__ float red[4][4][4][kWave];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wq = wave_in_block();
-    const int kq = I >> 2;
-    const int k_begin = wq * kq, k_end = k_begin + kq;
-    const int kgrp = (lane >> 4) * 8;
-    const int tiles = d_out >> 4;
-    const int total = L.count() * tiles;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int a = item / tiles;
-        const int tile = item - a * tiles;
+    struct Job {
+        int T;
+        int e;       // expert id (list jobs)
+        int p0;      // first position (list jobs)
+        bool extra;  // the extra dense job
+    };
+    __device__ int nlist() const { return *L.n; }
+    __device__ int count() const { return nlist() + (w_x ? 1 : 0); }
+    __device__ int tiles() const { return pair ? I / 32 : (rows + kSkRows - 1) / kSkRows; }
+    __device__ Job job(int a) const {
+        if (w_x && a == nlist())
+            return Job{xT, 0, 0, true};
         int e, p0, na;
         L.get(a, e, p0, na);
-        const int MT = min((na + 15) >> 4, 4);
-        const uint16_t *wrow = w2 + ((int64_t)e * d_out + tile * 16 + (lane & 15)) * I;
-        int64_t aoff[4];
-        bool aval[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int m = mt * 16 + (lane & 15);
-            aval[mt] = m < na;
-            aoff[mt] = (int64_t)(aval[mt] ? p0 + m : 0) * I;
-        }
-        f32x4 acc[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = k_begin; ks < k_end; ks += 32 * U) {
-            u32x4 bfr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k = ks + 32 * u + kgrp;
-                bfr[u] = (ks + 32 * u < k_end) ? ld_weight16(wrow + k) : zero16();
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (ks + 32 * u < k_end) {
-                    const int k = ks + 32 * u + kgrp;
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        if (mt < MT) {
-                            const u32x4 av = aval[mt] ? ld_act16(hbuf + aoff[mt] + k) : zero16();
-                            acc[mt] = mfma16x16x32(av, bfr[u], acc[mt]);
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            if (mt < MT)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[wq][mt][i][lane] = acc[mt][i];
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < MT * 256; idx += kBlock) {
-            const int mt = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
-            const float s = (red[0][mt][i][l] + red[1][mt][i][l]) + (red[2][mt][i][l] + red[3][mt][i][l]);
-            const int m = mt * 16 + 4 * (l >> 4) + i;
-            if (m < na)
-                out(p0 + m, tile * 16 + (l & 15), s);
-        }
-        __syncthreads();
+        return Job{na, e, p0, false};
     }
-}
+    __device__ void wave_rows(const Job &jb, int tile, int wq, const uint16_t *&wr,
+                              int &n) const {
+        if (jb.extra) {
+            const int r0 = tile * kSkRows + wq * 16;
+            n = max(0, min(16, rows - r0));
+            wr = w_x + (int64_t)(n > 0 ? r0 : 0) * K;
+            return;
+        }
+        const uint16_t *base = w + (int64_t)jb.e * w_stride;
+        if (pair) {
+            const int r = wq < 2 ? 32 * tile + 16 * wq : I + 32 * tile + 16 * (wq - 2);
+            n = 16;
+            wr = base + (int64_t)r * K;
+        } else {
+            const int r0 = tile * kSkRows + wq * 16;
+            n = max(0, min(16, rows - r0));
+            wr = base + (int64_t)(n > 0 ? r0 : 0) * K;
+        }
+    }
+    // Branch-free, so the token-row loads of an item all go out together:
+    // sorted_token[p] is read unconditionally (p < b k for every job).
+    __device__ const uint16_t *xrow(const Job &jb, int t) const {
+        const int p = jb.p0 + t;
+        const int tok = L.token(p);
+        const int row = jb.extra ? t : (gather ? tok : p);
+        const uint16_t *base = jb.extra ? x_x : x;
+        const int64_t ld = jb.extra ? ldx_x : ldx;
+        return base + (int64_t)row * ld;
+    }
+    template <int MT>
+    __device__ void store(const Job &jb, int tile, int, int wq, const f32x4 (&acc)[MT],
+                          float (*xch)[MT][4][kWave]) const {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int g = lane >> 4, rl = lane & 15;
+        const int T = jb.T;
+        if (pair) {
+            if (wq >= 2)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xch[wq - 2][mt][i][lane] = acc[mt][i];
+            __syncthreads();
+            if (wq < 2) {
+                const int j = 32 * tile + 16 * wq + rl;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = mt * 16 + 4 * g + i;
+                        if (t < T)
+                            h[(int64_t)(jb.p0 + t) * I + j] =
+                                f32_to_bf16(silu(acc[mt][i]) * xch[wq][mt][i][lane]);
+                    }
+            }
+            return;
+        }
+        const int n = tile * kSkRows + wq * 16 + rl;
+        if (n >= rows)
+            return;
+        float *o = jb.extra ? out_x : out + (int64_t)jb.p0 * rows;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = mt * 16 + 4 * g + i;
+                if (t < T)
+                    o[(int64_t)t * rows + n] = acc[mt][i];
+            }
+    }
+};
 
 // ------------------------------------------------------------------ combine
 // y[t][r] = bf16(y_add[t][r] + sum_j w[t][j] * part[slot_pos[t][j]][r]),
@@ -782,14 +740,16 @@ namespace {
 // Fused-block workspace: router logits, shared-expert h, then the routed
 // experts' workspace.
 struct BlockWorkspace {
-    size_t logits, hs, moe, total;
+    size_t logits, hs, moe, part, total;
 };
-BlockWorkspace block_workspace_layout(int b, int E, int k, int I, int d, int I_s) {
+BlockWorkspace block_workspace_layout(int b, int E, int k, int I, int d, int d_lat, int I_s) {
     BlockWorkspace w;
     w.logits = 256;
     w.hs = w.logits + align_up((size_t)b * E * sizeof(float), 256);
     w.moe = w.hs + align_up((size_t)b * I_s * sizeof(uint16_t), 256);
-    w.total = w.moe + moe_workspace_layout(b, E, k, I, d).total;
+    w.part = w.moe + moe_workspace_layout(b, E, k, I, d).total;
+    const int rows1 = E + d_lat + 2 * I_s;
+    w.total = w.part + sk_partial_bytes(b, rows1 > d ? rows1 : d);
     return w;
 }
 }  // namespace
@@ -801,19 +761,21 @@ extern "C" size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, i
     return moe_workspace_layout(b, E, k, I, d_out).total;
 }
 
+namespace {
+size_t shared_part_offset(int b, int I) { return align_up((size_t)b * I * sizeof(uint16_t), 256); }
+}  // namespace
+
 extern "C" size_t k3_shared_expert_workspace_size(int b, int d, int I) {
-    (void)d;
-    if (b <= 0 || I <= 0)
+    if (b <= 0 || I <= 0 || d <= 0)
         return 0;
-    return align_up((size_t)b * I * sizeof(uint16_t), 256);
+    return shared_part_offset(b, I) + sk_partial_bytes(b, 2 * I > d ? 2 * I : d);
 }
 
 extern "C" size_t k3_moe_block_workspace_size(int b, int d, int E, int k, int d_lat, int I,
                                               int I_s) {
-    (void)d_lat;
-    if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || I <= 0 || I_s <= 0)
+    if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || I <= 0 || I_s <= 0 || d_lat <= 0)
         return 0;
-    return block_workspace_layout(b, E, k, I, d, I_s).total;
+    return block_workspace_layout(b, E, k, I, d, d_lat, I_s).total;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -908,6 +870,23 @@ struct OutDense {  // y_s[t][r] = s (positions are tokens for the dense list)
     __device__ void operator()(int p, int r, float s) const { y[(int64_t)p * d + r] = s; }
 };
 
+// Heavy-expert launch: up to `items` (job, tile) items; surplus workgroups
+// exit at once when fewer experts are heavy.
+void launch_sk_experts(const SkExperts &J, int b, int items, int cu_budget, hipStream_t s) {
+    const int grid = budget_grid(items < 1 ? 1 : items, cu_budget, 64);
+    switch (sk_mt(b)) {
+    case 1:
+        k_sk_gemm<1, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        break;
+    case 2:
+        k_sk_gemm<2, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        break;
+    default:
+        k_sk_gemm<4, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        break;
+    }
+}
+
 // The routed experts after validation: batch 1 reads the ids directly; larger
 // batches permute, then run light experts on dot2 rows and heavy ones on MFMA
 // tiles; y = y_add + the weighted expert outputs.
@@ -953,15 +932,32 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
         const int max_heavy = (b * k) / (kDot2MaxTokens + 1) < E ? (b * k) / (kDot2MaxTokens + 1)
                                                                  : E;
         if (any_heavy) {
-            const int g = budget_grid(max_heavy * (I / 16), cu_budget, 4);
-            k_gateup_mfma<8, ExpertList><<<g, kBlock, 0, s>>>(z, ldz, d_in, w13, I, heavy, hbuf);
+            SkExperts J{};
+            J.L = heavy;
+            J.w = w13;
+            J.w_stride = (int64_t)2 * I * d_in;
+            J.K = d_in;
+            J.pair = true;
+            J.I = I;
+            J.x = z;
+            J.ldx = ldz;
+            J.gather = true;
+            J.h = hbuf;
+            launch_sk_experts(J, b, max_heavy * (I / 32), cu_budget, s);
         }
         trace_end(trace_op, s);
         launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
         if (any_heavy) {
-            const int g = budget_grid(max_heavy * (d_out / 16), cu_budget, 4);
-            k_down_mfma<16, ExpertList, OutPart><<<g, kBlock, 0, s>>>(hbuf, I, w2, d_out, heavy,
-                                                                     out);
+            SkExperts J{};
+            J.L = heavy;
+            J.w = w2;
+            J.w_stride = (int64_t)d_out * I;
+            J.K = I;
+            J.rows = d_out;
+            J.x = hbuf;
+            J.ldx = I;
+            J.out = part;
+            launch_sk_experts(J, b, max_heavy * ((d_out + kSkRows - 1) / kSkRows), cu_budget, s);
         }
         if (y_add_ready)
             (void)hipStreamWaitEvent(s, y_add_ready, 0);
@@ -971,9 +967,11 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
                                                             y_add, y);
 }
 
+// The shared expert; the MFMA variant keeps the partial sums of its K
+// ranges in `part` (sk_partial_bytes(b, max(2I, d)) bytes).
 void run_shared_expert(int variant, const uint16_t *x, int64_t ldx, int b, int d,
                        const uint16_t *w13, const uint16_t *w2, int I, float *y_s, int cu_budget,
-                       uint16_t *hbuf, int trace_op, hipStream_t s) {
+                       uint16_t *hbuf, float *part, int trace_op, hipStream_t s) {
     const DenseList dl{b};
     const OutDense out{y_s, d};
     trace_begin(trace_op, s);
@@ -983,11 +981,9 @@ void run_shared_expert(int variant, const uint16_t *x, int64_t ldx, int b, int d
         trace_end(trace_op, s);
         launch_down_dot2(tm, hbuf, I, w2, d, dl, out, cu_budget, s);
     } else {
-        const int g1 = budget_grid(I / 16, cu_budget, 4);
-        k_gateup_mfma<8, DenseList><<<g1, kBlock, 0, s>>>(x, ldx, d, w13, I, dl, hbuf);
+        sk_swiglu(x, ldx, b, d, w13, I, hbuf, part, cu_budget, s);
         trace_end(trace_op, s);
-        const int g2 = budget_grid(d / 16, cu_budget, 4);
-        k_down_mfma<16, DenseList, OutDense><<<g2, kBlock, 0, s>>>(hbuf, I, w2, d, dl, out);
+        sk_proj_f32(hbuf, I, b, w2, d, I, y_s, d, part, cu_budget, s);
     }
 }
 
@@ -1050,6 +1046,7 @@ extern "C" int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d, co
     if (!workspace || ws_bytes < k3_shared_expert_workspace_size(b, d, I) || !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     run_shared_expert(variant, x, ldx, b, d, w13, w2, I, y_s, cu_budget, (uint16_t *)workspace,
+                      (float *)((char *)workspace + shared_part_offset(b, I)),
                       K3_OP_SHARED_EXPERT, (hipStream_t)stream);
     const int st = launch_status();
     if (st == K3_OK)
@@ -1077,7 +1074,7 @@ extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
         !aligned16(w_router) || !aligned16(w_lat) || !aligned16(w13) || !aligned16(w2) ||
         !aligned16(w13_s) || !aligned16(w2_s) || !aligned16(z))
         return K3_ERR_UNSUPPORTED;
-    const BlockWorkspace L = block_workspace_layout(b, E, k, I, d, I_s);
+    const BlockWorkspace L = block_workspace_layout(b, E, k, I, d, d_lat, I_s);
     if (!workspace || ws_bytes < L.total || !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     int variant = forced_variant(K3_OP_MOE_BLOCK);
@@ -1138,11 +1135,14 @@ extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
             K3_TSD(kDot2MaxTokens, 1);
 #undef K3_TSD
     } else {
-        launch_dense_logits(x, ldx, b, w_router, E, d, bias, logits, s);
-        launch_dense_bf16(x, ldx, b, w_lat, d_lat, d, z, ldz, s);
+        // router, latent and shared gate/up rows in one split-K pass over x;
+        // the shared down projection follows the selection
+        float *part = (float *)(ws + L.part);
+        sk_router_latent_shared(x, ldx, b, d, w_router, E, bias, logits, w_lat, d_lat, z, ldz,
+                                w13_s, I_s, hs, part, s);
         trace_end(K3_OP_MOE_BLOCK, s);
         launch_topk(logits, b, E, k, topk_ids, topk_w, s);
-        run_shared_expert(K3_VARIANT_MFMA, x, ldx, b, d, w13_s, w2_s, I_s, y_s, 0, hs, -1, s);
+        sk_proj_f32(hs, I_s, b, w2_s, d, I_s, y_s, d, part, 0, s);
     }
     // 3-4. routed gate/up, down and combine with the shared output added
     run_moe_experts(z, ldz, b, d_lat, topk_ids, topk_w, k, w13, w2, E, I, d, y_s, nullptr, y, 0,

@@ -46,9 +46,29 @@ void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_
                 hipStream_t s);
 void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *wts,
                  hipStream_t s);
-void launch_dense_bf16(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
-                       uint16_t *y, int64_t ldy, hipStream_t s);
-void launch_dense_logits(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int E, int K,
-                         const float *bias, float *logits, hipStream_t s);
+
+// The split-K MFMA engine (skinny.hip). Each projection writes fp32 partial
+// sums of its K ranges into `part` (sk_partial_bytes(T, rows) bytes, rows
+// = all output rows of the call) and a small kernel finishes them.
+size_t sk_partial_bytes(int T, int rows);
+int sk_ksplit(int K);
+int sk_mt(int T);
+void sk_proj_bf16(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
+                  uint16_t *y, int64_t ldy, float *part, hipStream_t s);
+void sk_proj_f32(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
+                 float *y, int64_t ldy, float *part, int cu_budget, hipStream_t s);
+void sk_logits(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int E, int K,
+               const float *bias, float *logits, float *part, hipStream_t s);
+void sk_logits_latent(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r, int E,
+                      const float *bias, float *logits, const uint16_t *W_lat, int d_lat,
+                      uint16_t *z, int64_t ldz, float *part, hipStream_t s);
+void sk_router_latent_shared(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r,
+                             int E, const float *bias, float *logits, const uint16_t *W_lat,
+                             int d_lat, uint16_t *z, int64_t ldz, const uint16_t *W13_s, int I_s,
+                             uint16_t *hs, float *part, hipStream_t s);
+void sk_swiglu(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W13, int I,
+               uint16_t *hs, float *part, int cu_budget, hipStream_t s);
+void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
+                       uint16_t *residual, float *h32, float *part, hipStream_t s);
 
 }  // namespace k3

@@ -1,0 +1,200 @@
+// k3_skinny.h -- the MFMA engine for 5..64 tokens: out[t][n] = sum_k W[n][k] x[t][k].
+//
+// "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 1 ("Tune shapes for
+// the workload"): above batch 2 the projections switch to split-K kernels.
+// Here a workgroup owns a tile of 64 weight rows (16 per wave) and one of
+// `ksplit` K ranges; its four waves share each 256-wide K chunk of the
+// token rows, staged in LDS, while each wave streams its own 16 rows with
+// two register buffers in flight. The product runs on
+// v_mfma_f32_16x16x32_bf16 with the tokens as the A operand (up to four
+// 16-token tiles) and the weight rows as B. A job's epilogue either writes
+// fp32 partial sums per K range (summed in a fixed order by a small reduce
+// kernel), or, with one K range, finishes the outputs directly.
+#pragma once
+#include "k3_device.h"
+
+namespace k3 {
+
+constexpr int kSkRows = 64;           // weight rows per workgroup tile (16 per wave)
+constexpr int kSkKc = 256;            // K per chunk
+constexpr int kSkKq = kSkKc / 8;      // 16-byte vectors per token row of a chunk
+constexpr int kSkKb = kSkKc / 32;     // MFMA k-steps per chunk
+constexpr int kSkMaxSplit = 4;        // most K ranges a projection is split into
+constexpr int kSkMaxTokens = 64;
+
+// Jobs policy (see SkDense and the expert jobs in experts.hip):
+//   int  count()                          jobs in this launch (may read device memory)
+//   int  tiles()                          tile slots per job
+//   Job  job(a)                           what the item needs of job a, read once:
+//                                         it has a member T (tokens; 0 skips the job)
+//   void wave_rows(jb, tile, wq, w, n)    first weight row of wave wq's 16 and how many are valid
+//   const uint16_t *xrow(jb, t)           token row t of the job (t < T)
+//   void store(jb, tile, ks, wq, acc, xch)   epilogue (may hold a block barrier)
+template <int MT, class Jobs>
+__global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
+    __shared__ u32x4 xs[MT * 16][kSkKq + 1];  // +1 vector per row keeps the MFMA reads conflict-free
+    __shared__ float xch[2][MT][4][kWave];     // epilogue exchange between waves
+    constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
+    const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
+    const int g = lane >> 4, rl = lane & 15;
+    const int nchunks = (K + kSkKc - 1) / kSkKc;
+    const int per_job = J.tiles() * ksplit;
+    const int items = J.count() * per_job;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int a = item / per_job, rem = item - a * per_job;
+        const int tile = rem / ksplit, ks = rem - tile * ksplit;
+        const auto jb = J.job(a);
+        const int T = jb.T;
+        if (T <= 0)
+            continue;  // the whole workgroup skips together
+        const int mt_n = min((T + 15) >> 4, MT);
+        const uint16_t *wr;
+        int nvalid;
+        J.wave_rows(jb, tile, wq, wr, nvalid);
+        // wave-uniform (scalar) range parts; the range itself is built where
+        // it is used, so it never has to live in vector registers
+        const uint16_t *wbase = uniform_ptr(wr);
+        const uint32_t wbytes =
+            (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u;
+        // This thread stages vectors q = tid + j * 256 of each chunk: token
+        // q / kSkKq, vector q % kSkKq. Rows past T load token 0 and are
+        // zeroed, so the loads carry no branch.
+        const uint16_t *xr[SQ];
+        bool xv[SQ];
+#pragma unroll
+        for (int j = 0; j < SQ; ++j) {
+            const int t = (threadIdx.x + j * kBlock) / kSkKq;
+            xv[j] = t < T;
+            xr[j] = J.xrow(jb, xv[j] ? t : 0);
+        }
+        const int vq = threadIdx.x % kSkKq;
+        int c0, c1;
+        split_range(nchunks, ksplit, ks, c0, c1);
+        auto wload = [&](u32x4 (&buf)[kSkKb], int c) {
+            const rsrc_t rw = weight_range(wbase, wbytes);
+#pragma unroll
+            for (int u = 0; u < kSkKb; ++u) {
+                const int k = c * kSkKc + 32 * u + 8 * g;
+                buf[u] = ld_weight16(rw, k < K ? (uint32_t)(rl * K + k) * 2u : kOffNone);
+            }
+        };
+        auto aload = [&](u32x4 (&st)[SQ], int c) {
+            const int k = c * kSkKc + 8 * vq;
+            const bool kv = k < K;
+#pragma unroll
+            for (int j = 0; j < SQ; ++j) {
+                const u32x4 v = ld_act16(xr[j] + (kv ? k : 0));
+                st[j] = (xv[j] && kv) ? v : zero16();
+            }
+        };
+        auto astore = [&](u32x4 (&st)[SQ]) {
+#pragma unroll
+            for (int j = 0; j < SQ; ++j) {
+                const int q = threadIdx.x + j * kBlock;
+                xs[q / kSkKq][q % kSkKq] = st[j];
+            }
+        };
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](u32x4 (&buf)[kSkKb]) {
+#pragma unroll
+            for (int u = 0; u < kSkKb; ++u)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (mt < mt_n)
+                        acc[mt] = mfma16x16x32(xs[mt * 16 + rl][4 * u + g], buf[u], acc[mt]);
+        };
+        // Weights of chunk c + 1 and the tokens of chunk c + 1 are in flight
+        // while chunk c is multiplied; the token loads go out first, so
+        // waiting for them never waits for the weights issued after them.
+        u32x4 A[kSkKb], B[kSkKb], st[SQ];
+        if (c0 < c1) {
+            wload(A, c0);
+            aload(st, c0);
+            astore(st);
+            __syncthreads();
+            for (int c = c0; c < c1; c += 2) {
+                if (c + 1 < c1) {
+                    aload(st, c + 1);
+                    wload(B, c + 1);
+                }
+                compute(A);
+                __syncthreads();
+                if (c + 1 >= c1)
+                    break;
+                astore(st);
+                __syncthreads();
+                if (c + 2 < c1) {
+                    aload(st, c + 2);
+                    wload(A, c + 2);
+                }
+                compute(B);
+                __syncthreads();
+                if (c + 2 >= c1)
+                    break;
+                astore(st);
+                __syncthreads();
+            }
+        }
+        // acc[mt][i] = out[token 16 mt + 4 g + i][row rl of this wave's 16]
+        J.store(jb, tile, ks, wq, acc, xch);
+        __syncthreads();  // xs and xch are reused by the next item
+    }
+}
+
+// One dense projection made of up to three row segments (e.g. router,
+// latent and shared gate/up rows, all against the same tokens). Segment s
+// has N[s] rows (a multiple of 16) of W[s]; its rows are numbered after the
+// previous segments' rows in the output. The epilogue writes fp32 partials
+// part[(ks * T + t) * ldp + n], n the row in that numbering.
+struct SkDense {
+    const uint16_t *W[3];
+    int N[3];
+    int tiles_before[4];  // tiles of the segments before s; [3] = all tiles
+    int rows_before[3];
+    int K;
+    const uint16_t *x;
+    int64_t ldx;
+    int T;
+    float *part;
+    int64_t ldp;
+
+    struct Job {
+        int T;
+    };
+    __device__ int count() const { return 1; }
+    __device__ int tiles() const { return tiles_before[3]; }
+    __device__ Job job(int) const { return Job{T}; }
+    __device__ int seg(int tile) const {
+        return tile >= tiles_before[2] ? 2 : (tile >= tiles_before[1] ? 1 : 0);
+    }
+    __device__ void wave_rows(const Job &, int tile, int wq, const uint16_t *&w, int &n) const {
+        const int s = seg(tile);
+        const int r0 = (tile - tiles_before[s]) * kSkRows + wq * 16;
+        n = max(0, min(16, N[s] - r0));
+        w = W[s] + (int64_t)(n > 0 ? r0 : 0) * K;
+    }
+    __device__ const uint16_t *xrow(const Job &, int t) const { return x + (int64_t)t * ldx; }
+    template <int MT>
+    __device__ void store(const Job &, int tile, int ks, int wq, const f32x4 (&acc)[MT],
+                          float (*)[MT][4][kWave]) const {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int s = seg(tile);
+        const int r = (tile - tiles_before[s]) * kSkRows + wq * 16 + (lane & 15);
+        if (r >= N[s])
+            return;
+        const int n = rows_before[s] + r;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = mt * 16 + 4 * (lane >> 4) + i;
+                if (t < T)
+                    part[((int64_t)ks * T + t) * ldp + n] = acc[mt][i];
+            }
+    }
+};
+
+}  // namespace k3

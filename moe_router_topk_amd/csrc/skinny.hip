@@ -1,0 +1,230 @@
+// skinny.hip -- launchers of the MFMA engine (k3_skinny.h) for dense
+// projections above batch 4, and the kernels that finish their outputs from
+// the fp32 partial sums of the K ranges (always summed in range order).
+#include <math.h>
+
+#include "k3_device.h"
+#include "k3_internal.h"
+#include "k3_skinny.h"
+
+namespace k3 {
+
+// ------------------------------------------------------------------ finishing kernels
+// Output column c of the reduce runs over the segments' outputs in order;
+// segment s contributes cols[s] columns read from partial rows starting at
+// rows_before[s]. SkOut modes:
+//   BF16:   y[t][j]  = bf16(sum)                       (ldy)
+//   F32:    y[t][j]  = sum (+ bias[j])                 (ldy), fp32
+//   SWIGLU: h[t][j]  = bf16(silu(sum_gate j) * sum_up j), gate row j and up
+//           row I + j of the segment (cols = I)
+//   RESID:  v = r[t][j] + sum; r[t][j] = bf16(v) in place (y = r), h32[t][j] = v
+struct SkOutSeg {
+    int mode;  // 0 BF16, 1 F32, 2 SWIGLU, 3 RESID
+    int cols;
+    int rows_before;
+    void *y;
+    int64_t ldy;
+    const float *bias;
+    float *h32;
+};
+struct SkOuts {
+    SkOutSeg s[3];
+    int nseg;
+    int cols_total;
+};
+
+__device__ __forceinline__ float sk_sum(const float *part, int ks, int64_t stride, int64_t i) {
+    float v = part[i];
+    for (int r = 1; r < ks; ++r)
+        v += part[i + r * stride];
+    return v;
+}
+
+__device__ __forceinline__ void sk_finish_one(const float *__restrict__ part, int ks, int T,
+                                              int64_t ldp, const SkOuts &O, int64_t i) {
+    const int t = (int)(i / O.cols_total);
+    int c = (int)(i - (int64_t)t * O.cols_total);
+    int s = 0;
+    while (s < O.nseg - 1 && c >= O.s[s].cols) {
+        c -= O.s[s].cols;
+        ++s;
+    }
+    const SkOutSeg &q = O.s[s];
+    const int64_t stride = (int64_t)T * ldp;
+    const int64_t base = (int64_t)t * ldp + q.rows_before;
+    if (q.mode == 2) {
+        const float g = sk_sum(part, ks, stride, base + c);
+        const float u = sk_sum(part, ks, stride, base + q.cols + c);
+        ((uint16_t *)q.y)[(int64_t)t * q.ldy + c] = f32_to_bf16(silu(g) * u);
+    } else {
+        const float v = sk_sum(part, ks, stride, base + c);
+        const int64_t o = (int64_t)t * q.ldy + c;
+        if (q.mode == 0) {
+            ((uint16_t *)q.y)[o] = f32_to_bf16(v);
+        } else if (q.mode == 1) {
+            ((float *)q.y)[o] = q.bias ? v + q.bias[c] : v;
+        } else {
+            uint16_t *r = (uint16_t *)q.y;
+            const float h = bf16_to_f32(r[o]) + v;
+            r[o] = f32_to_bf16(h);
+            q.h32[o] = h;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kBlock)
+k_sk_finish(const float *__restrict__ part, int ks, int T, int64_t ldp, SkOuts O) {
+    const int64_t n = (int64_t)T * O.cols_total;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock)
+        sk_finish_one(part, ks, T, ldp, O, i);
+}
+
+// ------------------------------------------------------------------ launchers
+int sk_tile_count(int N) { return (N + kSkRows - 1) / kSkRows; }
+
+// K ranges of a K-wide projection: a function of K alone (about four chunks
+// per range, at most kSkMaxSplit ranges), so every call that streams the
+// same rows against the same tokens sums them in the same order, whichever
+// other rows share its launch.
+int sk_ksplit(int K) {
+    const int nchunks = (K + kSkKc - 1) / kSkKc;
+    const int ks = nchunks / 4;
+    return ks < 1 ? 1 : (ks > kSkMaxSplit ? kSkMaxSplit : ks);
+}
+
+int sk_mt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+
+size_t sk_partial_bytes(int T, int rows) {
+    return align_up((size_t)kSkMaxSplit * T * rows * sizeof(float), 256);
+}
+
+// Partial sums of up to three row segments against the same tokens:
+// part[(ks * T + t) * rows_total + n]. Returns the number of K ranges used.
+int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, const uint16_t *x,
+                      int64_t ldx, int T, float *part, int cu_budget, hipStream_t s) {
+    SkDense J{};
+    int tiles = 0, rows = 0;
+    for (int i = 0; i < 3; ++i) {
+        J.W[i] = i < nseg ? W[i] : W[0];
+        J.N[i] = i < nseg ? N[i] : 0;
+        J.tiles_before[i] = tiles;
+        J.rows_before[i] = rows;
+        if (i < nseg) {
+            tiles += sk_tile_count(N[i]);
+            rows += N[i];
+        }
+    }
+    J.tiles_before[3] = tiles;
+    J.K = K;
+    J.x = x;
+    J.ldx = ldx;
+    J.T = T;
+    J.part = part;
+    J.ldp = rows;
+    const int ks = sk_ksplit(K);
+    const int grid = budget_grid(tiles * ks, cu_budget, 2);
+    switch (sk_mt(T)) {
+    case 1:
+        k_sk_gemm<1, SkDense><<<grid, kBlock, 0, s>>>(J, K, ks);
+        break;
+    case 2:
+        k_sk_gemm<2, SkDense><<<grid, kBlock, 0, s>>>(J, K, ks);
+        break;
+    default:
+        k_sk_gemm<4, SkDense><<<grid, kBlock, 0, s>>>(J, K, ks);
+        break;
+    }
+    return ks;
+}
+
+void sk_finish(const float *part, int ks, int T, int64_t ldp, const SkOuts &O, int cu_budget,
+               hipStream_t s) {
+    const int64_t n = (int64_t)T * O.cols_total;
+    const int want = (int)((n + kBlock - 1) / kBlock);
+    k_sk_finish<<<budget_grid(want, cu_budget, 8), kBlock, 0, s>>>(part, ks, T, ldp, O);
+}
+
+SkOuts sk_outs1(int mode, int cols, void *y, int64_t ldy, const float *bias) {
+    SkOuts O{};
+    O.s[0] = SkOutSeg{mode, cols, 0, y, ldy, bias, nullptr};
+    O.nseg = 1;
+    O.cols_total = cols;
+    return O;
+}
+
+// y[t][n] = bf16(x . W^T) through partials.
+void sk_proj_bf16(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
+                  uint16_t *y, int64_t ldy, float *part, hipStream_t s) {
+    const int ks = sk_dense_partials(&W, &N, 1, K, x, ldx, T, part, 0, s);
+    sk_finish(part, ks, T, N, sk_outs1(0, N, y, ldy, nullptr), 0, s);
+}
+
+// y[t][n] = x . W^T in fp32 (the shared expert's down projection).
+void sk_proj_f32(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
+                 float *y, int64_t ldy, float *part, int cu_budget, hipStream_t s) {
+    const int ks = sk_dense_partials(&W, &N, 1, K, x, ldx, T, part, cu_budget, s);
+    sk_finish(part, ks, T, N, sk_outs1(1, N, y, ldy, nullptr), cu_budget, s);
+}
+
+// logits[t][e] = x . W_r^T (+ bias), fp32.
+void sk_logits(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int E, int K,
+               const float *bias, float *logits, float *part, hipStream_t s) {
+    const int ks = sk_dense_partials(&W, &E, 1, K, x, ldx, T, part, 0, s);
+    sk_finish(part, ks, T, E, sk_outs1(1, E, logits, E, bias), 0, s);
+}
+
+// Router logits and latent projection in one pass over x.
+void sk_logits_latent(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r, int E,
+                      const float *bias, float *logits, const uint16_t *W_lat, int d_lat,
+                      uint16_t *z, int64_t ldz, float *part, hipStream_t s) {
+    const uint16_t *W[2] = {W_r, W_lat};
+    const int N[2] = {E, d_lat};
+    const int ks = sk_dense_partials(W, N, 2, K, x, ldx, T, part, 0, s);
+    SkOuts O{};
+    O.s[0] = SkOutSeg{1, E, 0, logits, E, bias, nullptr};
+    O.s[1] = SkOutSeg{0, d_lat, E, z, ldz, nullptr, nullptr};
+    O.nseg = 2;
+    O.cols_total = E + d_lat;
+    sk_finish(part, ks, T, E + d_lat, O, 0, s);
+}
+
+// Router logits, latent projection and the shared expert's gate/up + SwiGLU
+// in one pass over x.
+void sk_router_latent_shared(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r,
+                             int E, const float *bias, float *logits, const uint16_t *W_lat,
+                             int d_lat, uint16_t *z, int64_t ldz, const uint16_t *W13_s, int I_s,
+                             uint16_t *hs, float *part, hipStream_t s) {
+    const uint16_t *W[3] = {W_r, W_lat, W13_s};
+    const int N[3] = {E, d_lat, 2 * I_s};
+    const int ks = sk_dense_partials(W, N, 3, K, x, ldx, T, part, 0, s);
+    SkOuts O{};
+    O.s[0] = SkOutSeg{1, E, 0, logits, E, bias, nullptr};
+    O.s[1] = SkOutSeg{0, d_lat, E, z, ldz, nullptr, nullptr};
+    O.s[2] = SkOutSeg{2, I_s, E + d_lat, hs, I_s, nullptr, nullptr};
+    O.nseg = 3;
+    O.cols_total = E + d_lat + I_s;
+    sk_finish(part, ks, T, E + d_lat + 2 * I_s, O, 0, s);
+}
+
+// Shared expert's gate/up + SwiGLU: hs[t][j] (bf16, row stride I).
+void sk_swiglu(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W13, int I,
+               uint16_t *hs, float *part, int cu_budget, hipStream_t s) {
+    const int N = 2 * I;
+    const int ks = sk_dense_partials(&W13, &N, 1, K, x, ldx, T, part, cu_budget, s);
+    sk_finish(part, ks, T, N, sk_outs1(2, I, hs, I, nullptr), cu_budget, s);
+}
+
+// Output projection + residual: residual <- bf16(residual + a . W_o^T) in
+// place and h32 = the fp32 sum (the RMSNorm kernel reads it).
+void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
+                       uint16_t *residual, float *h32, float *part, hipStream_t s) {
+    const int ks = sk_dense_partials(&W_o, &d, 1, K, a, lda, T, part, 0, s);
+    SkOuts O{};
+    O.s[0] = SkOutSeg{3, d, 0, residual, d, nullptr, h32};
+    O.nseg = 1;
+    O.cols_total = d;
+    sk_finish(part, ks, T, d, O, 0, s);
+}
+
+}  // namespace k3

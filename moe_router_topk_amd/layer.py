@@ -48,7 +48,8 @@ class DecodeLayer:
         I_s = moe["w13_s"].shape[0] // 2
         self.E, self.d, self.d_lat, self.I, self.I_s, self.b_max = E, d, d_lat, I, I_s, b_max
         u8 = dict(dtype=torch.uint8, device=dev)
-        self.ws_router = torch.empty(workspace_size("router_topk", b=b_max, E=E), **u8)
+        self.ws_router = torch.empty(
+            workspace_size("router_topk_latent", b=b_max, E=E, d_lat=d_lat), **u8)
         self.ws_moe = torch.empty(
             workspace_size("moe_experts", b=b_max, d_in=d_lat, E=E, k=k, I=I, d_out=d), **u8)
         self.ws_shared = torch.empty(workspace_size("shared_expert", b=b_max, d=d, I=I_s), **u8)
@@ -66,6 +67,8 @@ class DecodeLayer:
             self.x_moe = torch.empty((b_max, d), dtype=torch.bfloat16, device=dev)
             self.ws_oproj = torch.empty(
                 workspace_size("oproj_residual", b=b_max, K=self.k_o, d=d), **u8)
+            self.ws_proj = torch.empty(
+                workspace_size("proj_skinny", b=b_max, K=d, N=n_in), **u8)
         self.side = torch.cuda.Stream(device=dev)
         self.pf_stream = torch.cuda.Stream(device=dev)
         self.ev_in = torch.cuda.Event()
@@ -113,7 +116,7 @@ class DecodeLayer:
         c = self.chain_w
         b = x.shape[0]
         q = self.q[:b]
-        k3_proj_skinny(x, c["w_in"], y=q)
+        k3_proj_skinny(x, c["w_in"], y=q, workspace=self.ws_proj)
         x_moe = self.x_moe[:b]
         k3_oproj_residual(q[:, :self.k_o], c["w_o"], residual, c["gamma"], self.eps,
                           y_norm=x_moe, workspace=self.ws_oproj)

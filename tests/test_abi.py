@@ -75,7 +75,11 @@ def test_force_variant_validation(L):
 def test_workspace_sizes(L):
     import moe_router_topk_amd as k3
     assert k3.workspace_size("router_topk", b=64, E=384) >= 64 * 384 * 4
-    assert k3.workspace_size("proj_skinny", b=64, K=7168, N=12288) == 0
+    assert k3.workspace_size("proj_skinny", b=64, K=7168, N=12288) >= 4 * 64 * 12288 * 4
+    assert k3.workspace_size("router_topk_latent", b=64, E=384, d_lat=7168) >= \
+        k3.workspace_size("router_topk", b=64, E=384) + 4 * 64 * 7168 * 4
+    assert k3.workspace_size("moe_block", b=64, d=7168, E=384, k=8, d_lat=7168, I=2048,
+                             I_s=2048) >= 4 * 64 * (384 + 7168 + 4096) * 4
     assert k3.workspace_size("moe_experts", b=64, d_in=7168, E=384, k=8, I=2048,
                              d_out=7168) >= 512 * 2048 * 2 + 512 * 7168 * 4
     assert k3.workspace_size("shared_expert", b=64, d=7168, I=2048) >= 64 * 2048 * 2
@@ -124,6 +128,9 @@ def test_router_topk_latent_validation(L):
     assert _router_latent(L, wl=MIS) == UNSUP
     assert _router_latent(L, k=9) == UNSUP
     assert _router_latent(L, ws=None) == WORKSPACE
+    # the router-only workspace is too small once the latent rows join the pass
+    small = L.k3_router_topk_workspace_size(64, 8)
+    assert _router_latent(L, b=64, wsb=small) == WORKSPACE
 
 
 def _block(L, **kw):
@@ -166,8 +173,8 @@ def test_proj_skinny_validation(L):
     assert _proj(L, b=65) == UNSUP
     assert _proj(L, K=252, ldx=256) == UNSUP
     assert _proj(L, w=MIS) == UNSUP
-    # MFMA needs K % 128 == 0 above 8 tokens; dot2 stops at 8 tokens
-    assert _proj(L, b=16, K=264, ldx=264) == UNSUP
+    # above 4 tokens the split-K MFMA variant keeps its partial sums in the workspace
+    assert _proj(L, b=16, K=264, ldx=264) == WORKSPACE
     assert L.k3_force_variant(1, 1) == K3_OK
     try:
         assert _proj(L, b=9) == UNSUP
