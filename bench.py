@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_moe_up_b1_traffic.json")
-DOMINANT_SOURCES = ["moe_router_topk_amd/csrc/experts.hip", "moe_router_topk_amd/csrc/k3_device.h"]
+DOMINANT_SOURCES = ["moe_router_topk_amd/csrc/moe_b1.hip", "moe_router_topk_amd/csrc/k3_device.h"]
 
 
 def log(msg: str) -> None:

@@ -71,4 +71,18 @@ void sk_swiglu(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W13
 void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
                        uint16_t *residual, float *h32, float *part, hipStream_t s);
 
+// Batch-1 routed experts (moe_b1.hip). up_b1: routed gate/up + SwiGLU into
+// hbuf [k][I]; with `topk` the selection from logits happens in the kernel
+// (ids/weights written out), and with w2s the shared expert's down rows
+// (y_s) stream first. down_b1: y = bf16(y_add + sum_j w_j w2[ids[j]] . h_j).
+bool up_b1_fits(int d, int Is);
+void launch_up_b1(bool topk, const uint16_t *z, int d, const uint16_t *w13, int I, int E, int k,
+                  const int32_t *ids_in, const float *logits, int32_t *ids_out, float *w_out,
+                  const uint16_t *hs, int Is, const uint16_t *w2s, int d_s, float *y_s,
+                  uint16_t *hbuf, int cu_budget, hipStream_t s);
+bool down_b1_fits(int k, int I, int d_out, int cu_budget);
+void launch_down_b1(const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
+                    const int32_t *ids, const float *wts, int k, int E, const float *y_add,
+                    uint16_t *y, int cu_budget, hipStream_t s);
+
 }  // namespace k3
