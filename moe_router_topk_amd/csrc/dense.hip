@@ -448,13 +448,15 @@ extern "C" int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
     float *logits = (float *)((char *)workspace + router_logits_offset());
     float *part = (float *)((char *)workspace + router_partial_offset(b, E));
     trace_begin(K3_OP_ROUTER_TOPK, s);
-    if (variant == K3_VARIANT_DOT2)
+    if (variant == K3_VARIANT_DOT2) {
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, nullptr, 0, nullptr, 0, nullptr, 0,
                    nullptr, s);
-    else
-        sk_logits(x, ldx, b, w_router, E, d, bias, logits, part, s);
-    trace_end(K3_OP_ROUTER_TOPK, s);
-    launch_topk(logits, b, E, k, topk_ids, topk_w, s);
+        trace_end(K3_OP_ROUTER_TOPK, s);
+        launch_topk(logits, b, E, k, topk_ids, topk_w, s);
+    } else {
+        sk_router_topk(x, ldx, b, w_router, E, d, bias, k, logits, topk_ids, topk_w, part, s);
+        trace_end(K3_OP_ROUTER_TOPK, s);
+    }
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_ROUTER_TOPK, variant);
@@ -483,13 +485,16 @@ extern "C" int k3_router_topk_latent(const uint16_t *x, int64_t ldx, int b, int 
     float *logits = (float *)((char *)workspace + router_logits_offset());
     float *part = (float *)((char *)workspace + router_partial_offset(b, E));
     trace_begin(K3_OP_ROUTER_LATENT, s);
-    if (variant == K3_VARIANT_DOT2)
+    if (variant == K3_VARIANT_DOT2) {
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, nullptr, 0,
                    nullptr, s);
-    else
-        sk_logits_latent(x, ldx, b, d, w_router, E, bias, logits, w_lat, d_lat, z, ldz, part, s);
-    trace_end(K3_OP_ROUTER_LATENT, s);
-    launch_topk(logits, b, E, k, topk_ids, topk_w, s);
+        trace_end(K3_OP_ROUTER_LATENT, s);
+        launch_topk(logits, b, E, k, topk_ids, topk_w, s);
+    } else {
+        sk_router_topk_latent(x, ldx, b, d, w_router, E, bias, k, logits, topk_ids, topk_w,
+                              w_lat, d_lat, z, ldz, part, s);
+        trace_end(K3_OP_ROUTER_LATENT, s);
+    }
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_ROUTER_LATENT, variant);

@@ -328,15 +328,15 @@ struct SkExperts {
             wr = base + (int64_t)(n > 0 ? r0 : 0) * K;
         }
     }
-    // Branch-free, so the token-row loads of an item all go out together:
+    __device__ const uint16_t *xbase(const Job &jb) const { return jb.extra ? x_x : x; }
+    // Branch-free, so the token-row lookups of an item all go out together:
     // sorted_token[p] is read unconditionally (p < b k for every job).
-    __device__ const uint16_t *xrow(const Job &jb, int t) const {
+    __device__ uint32_t xrow(const Job &jb, int t) const {
         const int p = jb.p0 + t;
         const int tok = L.token(p);
         const int row = jb.extra ? t : (gather ? tok : p);
-        const uint16_t *base = jb.extra ? x_x : x;
         const int64_t ld = jb.extra ? ldx_x : ldx;
-        return base + (int64_t)row * ld;
+        return (uint32_t)((int64_t)row * ld);
     }
     template <int MT>
     __device__ void store(const Job &jb, int tile, int, int wq, const f32x4 (&acc)[MT],
@@ -578,19 +578,20 @@ struct OutDense {  // y_s[t][r] = s (positions are tokens for the dense list)
     __device__ void operator()(int p, int r, float s) const { y[(int64_t)p * d + r] = s; }
 };
 
-// Heavy-expert launch: up to `items` (job, tile) items; surplus workgroups
-// exit at once when fewer experts are heavy.
+// Heavy-expert launch: up to `items` (job, tile) items, fewer when fewer
+// experts are heavy.
 void launch_sk_experts(const SkExperts &J, int b, int items, int cu_budget, hipStream_t s) {
-    const int grid = budget_grid(items < 1 ? 1 : items, cu_budget, 64);
+    // two workgroups per compute unit, each streaming its items back to back
+    const int grid = budget_grid(items < 1 ? 1 : items, cu_budget, 2);
     switch (sk_mt(b)) {
     case 1:
-        k_sk_gemm<1, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        k_sk_gemm_stream<1, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
         break;
     case 2:
-        k_sk_gemm<2, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        k_sk_gemm_stream<2, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
         break;
     default:
-        k_sk_gemm<4, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        k_sk_gemm_stream<4, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
         break;
     }
 }
@@ -598,10 +599,21 @@ void launch_sk_experts(const SkExperts &J, int b, int items, int cu_budget, hipS
 // The routed experts after validation: batch 1 reads the ids directly; larger
 // batches permute, then run light experts on dot2 rows and heavy ones on MFMA
 // tiles; y = y_add + the weighted expert outputs.
+// A dense job the heavy down launch can carry: y_x[t][n] = w_x[n] . x_x[t]
+// (fp32), t < xT, n < d_out, K = I (the shared expert's down projection).
+struct DownExtra {
+    const uint16_t *w_x;
+    const uint16_t *x_x;
+    int64_t ldx_x;
+    int xT;
+    float *out_x;
+};
+
 void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int32_t *topk_ids,
                      const float *topk_w, int k, const uint16_t *w13, const uint16_t *w2, int E,
                      int I, int d_out, const float *y_add, hipEvent_t y_add_ready, uint16_t *y,
-                     int cu_budget, char *ws, int trace_op, hipStream_t s) {
+                     int cu_budget, char *ws, int trace_op, hipStream_t s,
+                     const DownExtra *extra = nullptr) {
     const MoeWorkspace L = moe_workspace_layout(b, E, k, I, d_out);
     uint16_t *hbuf = (uint16_t *)(ws + L.hbuf);
     float *part = (float *)(ws + L.part);
@@ -655,7 +667,7 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
         }
         trace_end(trace_op, s);
         launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
-        if (any_heavy) {
+        if (any_heavy || extra) {
             SkExperts J{};
             J.L = heavy;
             J.w = w2;
@@ -665,7 +677,15 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
             J.x = hbuf;
             J.ldx = I;
             J.out = part;
-            launch_sk_experts(J, b, max_heavy * ((d_out + kSkRows - 1) / kSkRows), cu_budget, s);
+            if (extra) {
+                J.w_x = extra->w_x;
+                J.x_x = extra->x_x;
+                J.ldx_x = extra->ldx_x;
+                J.xT = extra->xT;
+                J.out_x = extra->out_x;
+            }
+            const int jobs = (any_heavy ? max_heavy : 0) + (extra ? 1 : 0);
+            launch_sk_experts(J, b, jobs * ((d_out + kSkRows - 1) / kSkRows), cu_budget, s);
         }
         if (y_add_ready)
             (void)hipStreamWaitEvent(s, y_add_ready, 0);
@@ -691,7 +711,7 @@ void run_shared_expert(int variant, const uint16_t *x, int64_t ldx, int b, int d
     } else {
         sk_swiglu(x, ldx, b, d, w13, I, hbuf, part, cu_budget, s);
         trace_end(trace_op, s);
-        sk_proj_f32(hbuf, I, b, w2, d, I, y_s, d, part, cu_budget, s);
+        sk_proj_f32_direct(hbuf, I, b, w2, d, I, y_s, d, cu_budget, s);
     }
 }
 
@@ -846,11 +866,21 @@ extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
         // router, latent and shared gate/up rows in one split-K pass over x;
         // the shared down projection follows the selection
         float *part = (float *)(ws + L.part);
-        sk_router_latent_shared(x, ldx, b, d, w_router, E, bias, logits, w_lat, d_lat, z, ldz,
-                                w13_s, I_s, hs, part, s);
+        sk_router_latent_shared(x, ldx, b, d, w_router, E, bias, k, logits, topk_ids, topk_w,
+                                w_lat, d_lat, z, ldz, w13_s, I_s, hs, part, s);
         trace_end(K3_OP_MOE_BLOCK, s);
-        launch_topk(logits, b, E, k, topk_ids, topk_w, s);
-        sk_proj_f32(hs, I_s, b, w2_s, d, I_s, y_s, d, part, 0, s);
+        // the shared down projection rides in the routed down launch of the
+        // heavy experts when it has their shape; else it runs on its own
+        if (b > kDot2MaxTokens && I_s == I) {
+            const DownExtra ex{w2_s, hs, I_s, b, y_s};
+            run_moe_experts(z, ldz, b, d_lat, topk_ids, topk_w, k, w13, w2, E, I, d, y_s, nullptr,
+                            y, 0, ws + L.moe, K3_OP_MOE_EXPERTS, s, &ex);
+            const int st = launch_status();
+            if (st == K3_OK)
+                record_dispatch(K3_OP_MOE_BLOCK, variant);
+            return st;
+        }
+        sk_proj_f32_direct(hs, I_s, b, w2_s, d, I_s, y_s, d, 0, s);
     }
     // 3-4. routed gate/up, down and combine with the shared output added
     run_moe_experts(z, ldz, b, d_lat, topk_ids, topk_w, k, w13, w2, E, I, d, y_s, nullptr, y, 0,

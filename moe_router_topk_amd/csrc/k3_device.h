@@ -41,6 +41,18 @@ __device__ __forceinline__ u32x4 ld_weight16(rsrc_t r, uint32_t off) {
 // An offset past every range: the load returns zeros.
 constexpr uint32_t kOffNone = 0x80000000u;
 
+// Activations (re-read by many workgroups, so cached normally) through a
+// buffer resource: a masked lane passes kOffNone and reads zeros without a
+// memory access or a branch.
+__device__ __forceinline__ rsrc_t act_range(const uint16_t *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0,
+                                             (int)(kOffNone - 16u), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld_act16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 // Index of the calling wave in its workgroup, known uniform to the compiler.
 __device__ __forceinline__ int wave_in_block() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));

@@ -57,15 +57,20 @@ void sk_proj_bf16(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int 
                   uint16_t *y, int64_t ldy, float *part, hipStream_t s);
 void sk_proj_f32(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
                  float *y, int64_t ldy, float *part, int cu_budget, hipStream_t s);
-void sk_logits(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int E, int K,
-               const float *bias, float *logits, float *part, hipStream_t s);
-void sk_logits_latent(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r, int E,
-                      const float *bias, float *logits, const uint16_t *W_lat, int d_lat,
-                      uint16_t *z, int64_t ldz, float *part, hipStream_t s);
+void sk_proj_f32_direct(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
+                        float *y, int64_t ldy, int cu_budget, hipStream_t s);
+void sk_router_topk(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int E, int K,
+                    const float *bias, int k, float *logits, int32_t *ids, float *wts,
+                    float *part, hipStream_t s);
+void sk_router_topk_latent(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r,
+                           int E, const float *bias, int k, float *logits, int32_t *ids,
+                           float *wts, const uint16_t *W_lat, int d_lat, uint16_t *z,
+                           int64_t ldz, float *part, hipStream_t s);
 void sk_router_latent_shared(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r,
-                             int E, const float *bias, float *logits, const uint16_t *W_lat,
-                             int d_lat, uint16_t *z, int64_t ldz, const uint16_t *W13_s, int I_s,
-                             uint16_t *hs, float *part, hipStream_t s);
+                             int E, const float *bias, int k, float *logits, int32_t *ids,
+                             float *wts, const uint16_t *W_lat, int d_lat, uint16_t *z,
+                             int64_t ldz, const uint16_t *W13_s, int I_s, uint16_t *hs,
+                             float *part, hipStream_t s);
 void sk_swiglu(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W13, int I,
                uint16_t *hs, float *part, int cu_budget, hipStream_t s);
 void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,

@@ -28,8 +28,11 @@ constexpr int kSkMaxTokens = 64;
 //   Job  job(a)                           what the item needs of job a, read once:
 //                                         it has a member T (tokens; 0 skips the job)
 //   void wave_rows(jb, tile, wq, w, n)    first weight row of wave wq's 16 and how many are valid
-//   const uint16_t *xrow(jb, t)           token row t of the job (t < T)
+//   const uint16_t *xbase(jb)             the job's token matrix (wave-uniform)
+//   uint32_t xrow(jb, t)                  element offset of token row t in it (t < T)
 //   void store(jb, tile, ks, wq, acc, xch)   epilogue (may hold a block barrier)
+// One item per loop iteration (the pipeline is filled per item): for dense
+// projections, whose items are many and uniform.
 template <int MT, class Jobs>
 __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
     __shared__ u32x4 xs[MT * 16][kSkKq + 1];  // +1 vector per row keeps the MFMA reads conflict-free
@@ -57,15 +60,16 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         const uint32_t wbytes =
             (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u;
         // This thread stages vectors q = tid + j * 256 of each chunk: token
-        // q / kSkKq, vector q % kSkKq. Rows past T load token 0 and are
-        // zeroed, so the loads carry no branch.
-        const uint16_t *xr[SQ];
+        // q / kSkKq, vector q % kSkKq. Rows past T read zeros through the
+        // buffer range (no branch, no memory access).
+        const uint16_t *xb = uniform_ptr(J.xbase(jb));
+        uint32_t xo[SQ];
         bool xv[SQ];
 #pragma unroll
         for (int j = 0; j < SQ; ++j) {
             const int t = (threadIdx.x + j * kBlock) / kSkKq;
             xv[j] = t < T;
-            xr[j] = J.xrow(jb, xv[j] ? t : 0);
+            xo[j] = J.xrow(jb, xv[j] ? t : 0);
         }
         const int vq = threadIdx.x % kSkKq;
         int c0, c1;
@@ -79,13 +83,12 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
             }
         };
         auto aload = [&](u32x4 (&st)[SQ], int c) {
+            const rsrc_t rx = act_range(xb);
             const int k = c * kSkKc + 8 * vq;
             const bool kv = k < K;
 #pragma unroll
-            for (int j = 0; j < SQ; ++j) {
-                const u32x4 v = ld_act16(xr[j] + (kv ? k : 0));
-                st[j] = (xv[j] && kv) ? v : zero16();
-            }
+            for (int j = 0; j < SQ; ++j)
+                st[j] = ld_act16(rx, (xv[j] && kv) ? (xo[j] + (uint32_t)k) * 2u : kOffNone);
         };
         auto astore = [&](u32x4 (&st)[SQ]) {
 #pragma unroll
@@ -144,6 +147,172 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
     }
 }
 
+// For lists of jobs (the heavy experts), whose workgroups stream several
+// items each.
+template <int MT, class Jobs>
+struct SkItem {
+    static constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
+    bool valid;
+    int next;  // the next item index of this workgroup to look at
+    int tile, ks, c0, c1, T, mt_n;
+    typename Jobs::Job jb;
+    const uint16_t *wbase;
+    uint32_t wbytes;
+    const uint16_t *xb;
+    uint32_t xo[SQ];
+    bool xv[SQ];
+};
+
+// The workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...; their
+// (item, chunk) units form one stream, so the next item's first chunk is
+// already in flight while the current item finishes (a workgroup does not
+// drain and refill the pipeline between tiles).
+template <int MT, class Jobs>
+__device__ __forceinline__ void sk_open_item(const Jobs &J, int from, int items, int per_job,
+                                             int ksplit, int nchunks, int K, int wq,
+                                             SkItem<MT, Jobs> &c) {
+    constexpr int SQ = SkItem<MT, Jobs>::SQ;
+    c.valid = false;
+    for (int it = from; it < items; it += gridDim.x) {
+        const int a = it / per_job, rem = it - a * per_job;
+        c.jb = J.job(a);
+        if (c.jb.T <= 0)
+            continue;  // uniform over the workgroup
+        c.next = it + gridDim.x;
+        c.tile = rem / ksplit;
+        c.ks = rem - c.tile * ksplit;
+        c.T = c.jb.T;
+        c.mt_n = min((c.T + 15) >> 4, MT);
+        split_range(nchunks, ksplit, c.ks, c.c0, c.c1);
+        const uint16_t *wr;
+        int nvalid;
+        J.wave_rows(c.jb, c.tile, wq, wr, nvalid);
+        c.wbase = uniform_ptr(wr);
+        c.wbytes = (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u;
+        // this thread stages vectors q = tid + j * 256 of each chunk: token
+        // q / kSkKq, vector q % kSkKq; rows past T read zeros
+        c.xb = uniform_ptr(J.xbase(c.jb));
+#pragma unroll
+        for (int j = 0; j < SQ; ++j) {
+            const int t = (threadIdx.x + j * kBlock) / kSkKq;
+            c.xv[j] = t < c.T;
+            c.xo[j] = J.xrow(c.jb, c.xv[j] ? t : 0);
+        }
+        c.valid = c.c0 < c.c1;
+        if (c.valid)
+            return;
+    }
+}
+
+template <int MT, class Jobs>
+__global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ksplit) {
+    __shared__ u32x4 xs[MT * 16][kSkKq + 1];  // +1 vector per row keeps the MFMA reads conflict-free
+    __shared__ float xch[2][MT][4][kWave];     // epilogue exchange between waves
+    using Item = SkItem<MT, Jobs>;
+    constexpr int SQ = Item::SQ;
+    const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
+    const int g = lane >> 4, rl = lane & 15;
+    const int nchunks = (K + kSkKc - 1) / kSkKc;
+    const int per_job = J.tiles() * ksplit;
+    const int items = J.count() * per_job;
+    const int vq = threadIdx.x % kSkKq;
+
+    auto wload = [&](u32x4 (&buf)[kSkKb], const Item &it, int c) {
+        const rsrc_t rw = weight_range(it.wbase, it.wbytes);
+#pragma unroll
+        for (int u = 0; u < kSkKb; ++u) {
+            const int k = c * kSkKc + 32 * u + 8 * g;
+            buf[u] = ld_weight16(rw, k < K ? (uint32_t)(rl * K + k) * 2u : kOffNone);
+        }
+    };
+    auto aload = [&](u32x4 (&st)[SQ], const Item &it, int c) {
+        const rsrc_t rx = act_range(it.xb);
+        const int k = c * kSkKc + 8 * vq;
+        const bool kv = k < K;
+#pragma unroll
+        for (int j = 0; j < SQ; ++j)
+            st[j] = ld_act16(rx, (it.xv[j] && kv) ? (it.xo[j] + (uint32_t)k) * 2u : kOffNone);
+    };
+    auto astore = [&](u32x4 (&st)[SQ]) {
+#pragma unroll
+        for (int j = 0; j < SQ; ++j) {
+            const int q = threadIdx.x + j * kBlock;
+            xs[q / kSkKq][q % kSkKq] = st[j];
+        }
+    };
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](u32x4 (&buf)[kSkKb], int mt_n) {
+#pragma unroll
+        for (int u = 0; u < kSkKb; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                if (mt < mt_n)
+                    acc[mt] = mfma16x16x32(xs[mt * 16 + rl][4 * u + g], buf[u], acc[mt]);
+    };
+
+    // cur: the item being multiplied (chunk cc); nx: the item of the next
+    // unit to load (chunk nc).
+    Item cur, nx;
+    sk_open_item<MT>(J, blockIdx.x, items, per_job, ksplit, nchunks, K, wq, cur);
+    if (!cur.valid)
+        return;
+    nx = cur;
+    int cc = cur.c0, nc = cur.c0;
+    auto advance = [&]() {  // nx/nc -> the unit after it
+        if (++nc >= nx.c1) {
+            sk_open_item<MT>(J, nx.next, items, per_job, ksplit, nchunks, K, wq, nx);
+            nc = nx.c0;
+        }
+    };
+    // Weights of the next unit and its tokens are in flight while the current
+    // unit is multiplied; the token loads go out first, so waiting for them
+    // never waits for the weights issued after them.
+    u32x4 A[kSkKb], B[kSkKb], st[SQ];
+    wload(A, nx, nc);
+    aload(st, nx, nc);
+    astore(st);
+    __syncthreads();
+    advance();
+    // one step: multiply `buf` (unit cur/cc) while the next unit loads into `nbuf`
+    auto step = [&](u32x4 (&buf)[kSkKb], u32x4 (&nbuf)[kSkKb]) -> bool {
+        const bool more = nx.valid;
+        if (more) {
+            aload(st, nx, nc);
+            wload(nbuf, nx, nc);
+        }
+        compute(buf, cur.mt_n);
+        if (cc + 1 >= cur.c1) {
+            // acc[mt][i] = out[token 16 mt + 4 g + i][row rl of this wave's 16]
+            J.store(cur.jb, cur.tile, cur.ks, wq, acc, xch);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();  // every wave is done with xs (and xch)
+        if (!more)
+            return false;
+        astore(st);
+        __syncthreads();
+        if (cc + 1 >= cur.c1) {
+            cur = nx;
+            cc = nc;
+        } else {
+            ++cc;
+        }
+        advance();
+        return true;
+    };
+    while (true) {
+        if (!step(A, B))
+            break;
+        if (!step(B, A))
+            break;
+    }
+}
+
 // One dense projection made of up to three row segments (e.g. router,
 // latent and shared gate/up rows, all against the same tokens). Segment s
 // has N[s] rows (a multiple of 16) of W[s]; its rows are numbered after the
@@ -176,7 +345,8 @@ struct SkDense {
         n = max(0, min(16, N[s] - r0));
         w = W[s] + (int64_t)(n > 0 ? r0 : 0) * K;
     }
-    __device__ const uint16_t *xrow(const Job &, int t) const { return x + (int64_t)t * ldx; }
+    __device__ const uint16_t *xbase(const Job &) const { return x; }
+    __device__ uint32_t xrow(const Job &, int t) const { return (uint32_t)((int64_t)t * ldx); }
     template <int MT>
     __device__ void store(const Job &, int tile, int ks, int wq, const f32x4 (&acc)[MT],
                           float (*)[MT][4][kWave]) const {

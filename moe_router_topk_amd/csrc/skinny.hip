@@ -101,8 +101,11 @@ size_t sk_partial_bytes(int T, int rows) {
 
 // Partial sums of up to three row segments against the same tokens:
 // part[(ks * T + t) * rows_total + n]. Returns the number of K ranges used.
+// ks_force > 0 fixes the number of K ranges (1: part is the output itself,
+// row stride ldp_force).
 int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, const uint16_t *x,
-                      int64_t ldx, int T, float *part, int cu_budget, hipStream_t s) {
+                      int64_t ldx, int T, float *part, int cu_budget, hipStream_t s,
+                      int ks_force = 0, int64_t ldp_force = 0) {
     SkDense J{};
     int tiles = 0, rows = 0;
     for (int i = 0; i < 3; ++i) {
@@ -121,8 +124,8 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
     J.ldx = ldx;
     J.T = T;
     J.part = part;
-    J.ldp = rows;
-    const int ks = sk_ksplit(K);
+    J.ldp = ldp_force > 0 ? ldp_force : rows;
+    const int ks = ks_force > 0 ? ks_force : sk_ksplit(K);
     const int grid = budget_grid(tiles * ks, cu_budget, 2);
     switch (sk_mt(T)) {
     case 1:
@@ -142,7 +145,8 @@ void sk_finish(const float *part, int ks, int T, int64_t ldp, const SkOuts &O, i
                hipStream_t s) {
     const int64_t n = (int64_t)T * O.cols_total;
     const int want = (int)((n + kBlock - 1) / kBlock);
-    k_sk_finish<<<budget_grid(want, cu_budget, 8), kBlock, 0, s>>>(part, ks, T, ldp, O);
+    k_sk_finish<<<budget_grid(want < 1 ? 1 : want, cu_budget, 8), kBlock, 0, s>>>(part, ks, T,
+                                                                                  ldp, O);
 }
 
 SkOuts sk_outs1(int mode, int cols, void *y, int64_t ldy, const float *bias) {
@@ -167,17 +171,28 @@ void sk_proj_f32(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N
     sk_finish(part, ks, T, N, sk_outs1(1, N, y, ldy, nullptr), cu_budget, s);
 }
 
-// logits[t][e] = x . W_r^T (+ bias), fp32.
-void sk_logits(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int E, int K,
-               const float *bias, float *logits, float *part, hipStream_t s) {
-    const int ks = sk_dense_partials(&W, &E, 1, K, x, ldx, T, part, 0, s);
-    sk_finish(part, ks, T, E, sk_outs1(1, E, logits, E, bias), 0, s);
+// y[t][n] = x . W^T in fp32 with one K range: the engine's epilogue writes
+// the outputs directly (no partials, no finishing kernel).
+void sk_proj_f32_direct(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
+                        float *y, int64_t ldy, int cu_budget, hipStream_t s) {
+    sk_dense_partials(&W, &N, 1, K, x, ldx, T, y, cu_budget, s, 1, ldy);
 }
 
-// Router logits and latent projection in one pass over x.
-void sk_logits_latent(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r, int E,
-                      const float *bias, float *logits, const uint16_t *W_lat, int d_lat,
-                      uint16_t *z, int64_t ldz, float *part, hipStream_t s) {
+// Router scores and top-k: logits (fp32, + bias) from the router rows'
+// partials, then the selection kernel.
+void sk_router_topk(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int E, int K,
+                    const float *bias, int k, float *logits, int32_t *ids, float *wts,
+                    float *part, hipStream_t s) {
+    const int ks = sk_dense_partials(&W, &E, 1, K, x, ldx, T, part, 0, s);
+    sk_finish(part, ks, T, E, sk_outs1(1, E, logits, E, bias), 0, s);
+    launch_topk(logits, T, E, k, ids, wts, s);
+}
+
+// Router top-k and latent projection in one pass over x.
+void sk_router_topk_latent(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r,
+                           int E, const float *bias, int k, float *logits, int32_t *ids,
+                           float *wts, const uint16_t *W_lat, int d_lat, uint16_t *z,
+                           int64_t ldz, float *part, hipStream_t s) {
     const uint16_t *W[2] = {W_r, W_lat};
     const int N[2] = {E, d_lat};
     const int ks = sk_dense_partials(W, N, 2, K, x, ldx, T, part, 0, s);
@@ -187,14 +202,16 @@ void sk_logits_latent(const uint16_t *x, int64_t ldx, int T, int K, const uint16
     O.nseg = 2;
     O.cols_total = E + d_lat;
     sk_finish(part, ks, T, E + d_lat, O, 0, s);
+    launch_topk(logits, T, E, k, ids, wts, s);
 }
 
-// Router logits, latent projection and the shared expert's gate/up + SwiGLU
+// Router top-k, latent projection and the shared expert's gate/up + SwiGLU
 // in one pass over x.
 void sk_router_latent_shared(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W_r,
-                             int E, const float *bias, float *logits, const uint16_t *W_lat,
-                             int d_lat, uint16_t *z, int64_t ldz, const uint16_t *W13_s, int I_s,
-                             uint16_t *hs, float *part, hipStream_t s) {
+                             int E, const float *bias, int k, float *logits, int32_t *ids,
+                             float *wts, const uint16_t *W_lat, int d_lat, uint16_t *z,
+                             int64_t ldz, const uint16_t *W13_s, int I_s, uint16_t *hs,
+                             float *part, hipStream_t s) {
     const uint16_t *W[3] = {W_r, W_lat, W13_s};
     const int N[3] = {E, d_lat, 2 * I_s};
     const int ks = sk_dense_partials(W, N, 3, K, x, ldx, T, part, 0, s);
@@ -205,6 +222,7 @@ void sk_router_latent_shared(const uint16_t *x, int64_t ldx, int T, int K, const
     O.nseg = 3;
     O.cols_total = E + d_lat + I_s;
     sk_finish(part, ks, T, E + d_lat + 2 * I_s, O, 0, s);
+    launch_topk(logits, T, E, k, ids, wts, s);
 }
 
 // Shared expert's gate/up + SwiGLU: hs[t][j] (bf16, row stride I).
