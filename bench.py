@@ -118,6 +118,78 @@ def traffic_per_launch():
     return t.get("traffic_bytes_per_launch")
 
 
+PMC_RUNS = {
+    "fetch": ("FETCH_SIZE", "--steps 5 --warmup 2 --eager-only --layers 2"),
+    "write": ("WRITE_SIZE", "--steps 5 --warmup 2 --eager-only --layers 2"),
+    "copy_fetch": ("FETCH_SIZE", "--copy-mb 256"),
+    "copy_write": ("WRITE_SIZE", "--copy-mb 256"),
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_MB = 256
+
+
+def pmc_values(run_dir: str, counter: str, name_part: str):
+    """Per-dispatch values (KiB) of one counter for kernels whose name holds
+    name_part, from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    vals = []
+    for f in sorted(glob.glob(os.path.join(run_dir, "*counter_collection.csv"))):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def write_traffic_summary(pmc_dir: str) -> int:
+    """Reduce the four counter runs under pmc_dir (pmc_fetch, pmc_write,
+    pmc_copy_fetch, pmc_copy_write, made by the commands recorded in the
+    output) to HBM bytes per launch of the dominant kernel at b = 1."""
+    import synth
+    name = "k_moe_up_b1<true>"
+    fetch = pmc_values(os.path.join(pmc_dir, "pmc_fetch"), "FETCH_SIZE", name)
+    write = pmc_values(os.path.join(pmc_dir, "pmc_write"), "WRITE_SIZE", name)
+    cf = pmc_values(os.path.join(pmc_dir, "pmc_copy_fetch"), "FETCH_SIZE", COPY_KERNEL)
+    cw = pmc_values(os.path.join(pmc_dir, "pmc_copy_write"), "WRITE_SIZE", COPY_KERNEL)
+    if not (fetch and write and cf and cw):
+        print("bench.py: counter runs missing under " + pmc_dir, file=sys.stderr)
+        return 2
+    copied = COPY_MB << 20
+    # the copy reads and writes `copied` bytes; take its largest dispatch
+    fetch_scale = copied / (max(cf) * 1024)
+    write_scale = copied / (max(cw) * 1024)
+    f_kib = sum(fetch) / len(fetch)
+    w_kib = sum(write) / len(write)
+    traffic = int(round(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale))
+    algo = gateup_bytes(synth.MOE_CONFIGS["b1"], 1, synth.MOE_CONFIGS["b1"].k)
+    out = {
+        "kernel": "k3::k_moe_up_b1<true> (expert selection + shared down projection + routed "
+                  "gate/up + SwiGLU), batch 1, d=7168, E=384, k=8, I=I_s=2048",
+        "commands": [
+            f"rocprofv3 --pmc {ctr} --output-format csv -d gpurun_out/pmc_{key} -o c -- "
+            f"python3 -u bench.py {args}" for key, (ctr, args) in PMC_RUNS.items()
+        ] + ["python3 bench.py --traffic-summary gpurun_out"],
+        "dispatches_averaged": {"FETCH_SIZE": len(fetch), "WRITE_SIZE": len(write)},
+        "fetch_kib_per_dispatch": round(f_kib, 1),
+        "write_kib_per_dispatch": round(w_kib, 1),
+        "copy_calibration": {
+            "bytes_copied": copied, "kernel": COPY_KERNEL,
+            "fetch_kib": round(max(cf), 1), "write_kib": round(max(cw), 1),
+            "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+        },
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": round(traffic / algo, 4),
+        "source_sha256": sources_digest(DOMINANT_SOURCES),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=2)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
 # ------------------------------------------------------------------ timing helpers
 def capture(torch, fn, n: int):
     """Capture fn(i) for i < n into one graph."""
@@ -191,7 +263,12 @@ def main() -> int:
                          "for profiler counter runs")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-summary", metavar="DIR", default="",
+                    help="no GPU work: reduce the rocprofv3 counter runs under DIR to the "
+                         "dominant kernel's HBM bytes per launch (written under profiles/)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return write_traffic_summary(args.traffic_summary)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -445,7 +522,7 @@ def cpu_baseline(torch, layer, cfg, cc, pool, b, seconds):
         return experts[e]
 
     done, spent, i, nbytes = 0, 0.0, 0, 0
-    while done < 50 and (done == 0 or spent < seconds):
+    while done < 2000 and (done == 0 or spent < seconds):
         inp = pool[i % len(pool)]
         x, r = inp["x"][:b].cpu(), inp["r"][:b].cpu()
         # host copies of what this step reads (outside the timed part)

@@ -22,6 +22,59 @@ constexpr int kSkKb = kSkKc / 32;     // MFMA k-steps per chunk
 constexpr int kSkMaxSplit = 4;        // most K ranges a projection is split into
 constexpr int kSkMaxTokens = 64;
 
+// Weight operand loads. One load instruction covers 8 rows x 128 bytes: lane
+// l reads row 8h + l % 8 (h the instruction's half of the wave's 16 rows) at
+// bytes 16 (l / 8) of a 128-byte piece, so each row is fetched in whole
+// 128-byte lines. (Loading the MFMA operand order directly, 16 rows x 64
+// bytes per instruction, streams about a quarter slower.) Load 2p + h of a
+// chunk holds piece p of the rows of half h.
+__device__ __forceinline__ void sk_wload(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K, int lane) {
+    const int r8 = lane & 7, q = lane >> 3;
+#pragma unroll
+    for (int u = 0; u < kSkKb; ++u) {
+        const int row = 8 * (u & 1) + r8;
+        const int k = c * kSkKc + 64 * (u >> 1) + 8 * q;
+        // past K: the sign bit of K - 1 - k moves the offset out of the range
+        // (reads zero); arithmetic rather than a select, which the compiler
+        // would turn into a branch and a wait around the load
+        const uint32_t past = (uint32_t)(K - 1 - k) & 0x80000000u;
+        buf[u] = ld_weight16(rw, ((uint32_t)(row * K + k) * 2u) | past);
+    }
+}
+
+// The two loads of one piece (x: rows 0-7, y: rows 8-15) -> the B operands of
+// its two MFMA k-steps, row l % 16 in lane l: lanes l and l ^ 8 trade one
+// vector (row_ror:8 within each 16-lane row, written into half the banks).
+// Step 0 then holds elements 16g .. 16g + 7 of the piece in lane group
+// g = l / 16, step 1 elements 16g + 8 .. 16g + 15.
+__device__ __forceinline__ void sk_pair(const u32x4 &x, const u32x4 &y, u32x4 &s0, u32x4 &s1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s0[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)x[i], (int)y[i], 0x128, 0xf, 0xc, false);
+        s1[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)y[i], (int)x[i], 0x128, 0xf, 0x3, false);
+    }
+}
+
+// acc[mt] += tokens 16 mt .. 16 mt + 15 (staged chunk xs) x the wave's 16
+// rows (loads buf of the same chunk).
+template <int MT>
+__device__ __forceinline__ void sk_mfma_chunk(f32x4 (&acc)[MT], const u32x4 (&buf)[kSkKb],
+                                              const u32x4 (&xs)[MT * 16][kSkKq + 1], int mt_n,
+                                              int lane) {
+    const int g = lane >> 4, rl = lane & 15;
+#pragma unroll
+    for (int p = 0; p < kSkKb / 2; ++p) {
+        u32x4 b0, b1;
+        sk_pair(buf[2 * p], buf[2 * p + 1], b0, b1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            if (mt < mt_n) {
+                acc[mt] = mfma16x16x32(xs[mt * 16 + rl][8 * p + 2 * g], b0, acc[mt]);
+                acc[mt] = mfma16x16x32(xs[mt * 16 + rl][8 * p + 2 * g + 1], b1, acc[mt]);
+            }
+    }
+}
+
 // Jobs policy (see SkDense and the expert jobs in experts.hip):
 //   int  count()                          jobs in this launch (may read device memory)
 //   int  tiles()                          tile slots per job
@@ -39,7 +92,6 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
     __shared__ float xch[2][MT][4][kWave];     // epilogue exchange between waves
     constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
-    const int g = lane >> 4, rl = lane & 15;
     const int nchunks = (K + kSkKc - 1) / kSkKc;
     const int per_job = J.tiles() * ksplit;
     const int items = J.count() * per_job;
@@ -75,12 +127,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         int c0, c1;
         split_range(nchunks, ksplit, ks, c0, c1);
         auto wload = [&](u32x4 (&buf)[kSkKb], int c) {
-            const rsrc_t rw = weight_range(wbase, wbytes);
-#pragma unroll
-            for (int u = 0; u < kSkKb; ++u) {
-                const int k = c * kSkKc + 32 * u + 8 * g;
-                buf[u] = ld_weight16(rw, k < K ? (uint32_t)(rl * K + k) * 2u : kOffNone);
-            }
+            sk_wload(buf, weight_range(wbase, wbytes), c, K, lane);
         };
         auto aload = [&](u32x4 (&st)[SQ], int c) {
             const rsrc_t rx = act_range(xb);
@@ -101,14 +148,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](u32x4 (&buf)[kSkKb]) {
-#pragma unroll
-            for (int u = 0; u < kSkKb; ++u)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    if (mt < mt_n)
-                        acc[mt] = mfma16x16x32(xs[mt * 16 + rl][4 * u + g], buf[u], acc[mt]);
-        };
+        auto compute = [&](u32x4 (&buf)[kSkKb]) { sk_mfma_chunk<MT>(acc, buf, xs, mt_n, lane); };
         // Weights of chunk c + 1 and the tokens of chunk c + 1 are in flight
         // while chunk c is multiplied; the token loads go out first, so
         // waiting for them never waits for the weights issued after them.
@@ -211,19 +251,13 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     using Item = SkItem<MT, Jobs>;
     constexpr int SQ = Item::SQ;
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
-    const int g = lane >> 4, rl = lane & 15;
     const int nchunks = (K + kSkKc - 1) / kSkKc;
     const int per_job = J.tiles() * ksplit;
     const int items = J.count() * per_job;
     const int vq = threadIdx.x % kSkKq;
 
     auto wload = [&](u32x4 (&buf)[kSkKb], const Item &it, int c) {
-        const rsrc_t rw = weight_range(it.wbase, it.wbytes);
-#pragma unroll
-        for (int u = 0; u < kSkKb; ++u) {
-            const int k = c * kSkKc + 32 * u + 8 * g;
-            buf[u] = ld_weight16(rw, k < K ? (uint32_t)(rl * K + k) * 2u : kOffNone);
-        }
+        sk_wload(buf, weight_range(it.wbase, it.wbytes), c, K, lane);
     };
     auto aload = [&](u32x4 (&st)[SQ], const Item &it, int c) {
         const rsrc_t rx = act_range(it.xb);
@@ -245,12 +279,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](u32x4 (&buf)[kSkKb], int mt_n) {
-#pragma unroll
-        for (int u = 0; u < kSkKb; ++u)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                if (mt < mt_n)
-                    acc[mt] = mfma16x16x32(xs[mt * 16 + rl][4 * u + g], buf[u], acc[mt]);
+        sk_mfma_chunk<MT>(acc, buf, xs, mt_n, lane);
     };
 
     // cur: the item being multiplied (chunk cc); nx: the item of the next
