@@ -25,17 +25,19 @@
 namespace k3 {
 
 constexpr int kDot2MaxTokens = 4;
+constexpr int kAllMfmaMin = 5;  // batches from which light experts join the MFMA launches
 
 // ------------------------------------------------------------------ expert lists
 struct ExpertList {  // a compacted list written by the permutation kernel
     const int *n;
     const int *expert, *start, *ntok;
     const int *sorted_token;
-    __device__ int count() const { return *n; }
+    // a is the same in every lane: the entries come through the scalar cache
+    __device__ int count() const { return ld_scalar(n); }
     __device__ void get(int a, int &e, int &p0, int &na) const {
-        e = expert[a];
-        p0 = start[a];
-        na = ntok[a];
+        e = ld_scalar(expert + a);
+        p0 = ld_scalar(start + a);
+        na = ld_scalar(ntok + a);
     }
     __device__ int token(int p) const { return sorted_token[p]; }
 };
@@ -276,6 +278,7 @@ k_down_dot2(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict
 // job after the list: the shared expert's down projection into y_s.
 struct SkExperts {
     ExpertList L;
+    ExpertList L2;  // a second list after L (its n may be null: none)
     const uint16_t *w;  // expert e: w + e * w_stride, [rows][K] (gate/up: [2I][K])
     int64_t w_stride;
     int K;
@@ -299,15 +302,26 @@ struct SkExperts {
         int p0;      // first position (list jobs)
         bool extra;  // the extra dense job
     };
-    __device__ int nlist() const { return *L.n; }
+    // List entries are read once per workgroup and taken from lane 0, so the
+    // compiler keeps the item state (and the ranges built from it) in scalar
+    // registers.
+    __device__ int n1() const { return __builtin_amdgcn_readfirstlane(L.count()); }
+    __device__ int nlist() const {
+        return n1() + (L2.n ? __builtin_amdgcn_readfirstlane(L2.count()) : 0);
+    }
     __device__ int count() const { return nlist() + (w_x ? 1 : 0); }
     __device__ int tiles() const { return pair ? I / 32 : (rows + kSkRows - 1) / kSkRows; }
     __device__ Job job(int a) const {
         if (w_x && a == nlist())
             return Job{xT, 0, 0, true};
         int e, p0, na;
-        L.get(a, e, p0, na);
-        return Job{na, e, p0, false};
+        const int m = n1();
+        if (a < m)
+            L.get(a, e, p0, na);
+        else
+            L2.get(a - m, e, p0, na);
+        return Job{__builtin_amdgcn_readfirstlane(na), __builtin_amdgcn_readfirstlane(e),
+                   __builtin_amdgcn_readfirstlane(p0), false};
     }
     __device__ void wave_rows(const Job &jb, int tile, int wq, const uint16_t *&wr,
                               int &n) const {
@@ -329,15 +343,16 @@ struct SkExperts {
         }
     }
     __device__ const uint16_t *xbase(const Job &jb) const { return jb.extra ? x_x : x; }
-    // Branch-free, so the token-row lookups of an item all go out together:
-    // sorted_token[p] is read unconditionally (p < b k for every job).
-    __device__ uint32_t xrow(const Job &jb, int t) const {
-        const int p = jb.p0 + t;
-        const int tok = L.token(p);
-        const int row = jb.extra ? t : (gather ? tok : p);
-        const int64_t ld = jb.extra ? ldx_x : ldx;
-        return (uint32_t)((int64_t)row * ld);
+    // The choice is uniform; on the gathering path the looked-up row is the
+    // result itself, so nothing waits for the lookup until the row is used.
+    __device__ int xrow(const Job &jb, int t) const {
+        if (jb.extra)
+            return t;
+        if (!gather)
+            return jb.p0 + t;
+        return L.token(jb.p0 + t);
     }
+    __device__ int xld(const Job &jb) const { return (int)(jb.extra ? ldx_x : ldx); }
     template <int MT>
     __device__ void store(const Job &jb, int tile, int, int wq, const f32x4 (&acc)[MT],
                           float (*xch)[MT][4][kWave]) const {
@@ -647,13 +662,23 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
             (int *)(ws + L.light_ntok), n_heavy, (int *)(ws + L.heavy_expert),
             (int *)(ws + L.heavy_start), (int *)(ws + L.heavy_ntok), (int *)(ws + L.sorted_token),
             slot_pos);
-        launch_gateup_dot2(kDot2MaxTokens, z, ldz, d_in, w13, I, light, hbuf, cu_budget, s);
+        // Above kAllMfmaMin tokens every expert runs in the MFMA launches
+        // (heavy list first, then the light one); below, light experts run
+        // on dot2 rows.
+        const bool all_mfma = b >= kAllMfmaMin;
+        const ExpertList none{nullptr, nullptr, nullptr, nullptr, nullptr};
+        if (!all_mfma)
+            launch_gateup_dot2(kDot2MaxTokens, z, ldz, d_in, w13, I, light, hbuf, cu_budget, s);
         const bool any_heavy = b > kDot2MaxTokens;
-        const int max_heavy = (b * k) / (kDot2MaxTokens + 1) < E ? (b * k) / (kDot2MaxTokens + 1)
-                                                                 : E;
+        const int pairs = b * k < E ? b * k : E;
+        const int max_heavy = all_mfma ? pairs
+                                       : ((b * k) / (kDot2MaxTokens + 1) < E
+                                              ? (b * k) / (kDot2MaxTokens + 1)
+                                              : E);
         if (any_heavy) {
             SkExperts J{};
             J.L = heavy;
+            J.L2 = all_mfma ? light : none;
             J.w = w13;
             J.w_stride = (int64_t)2 * I * d_in;
             J.K = d_in;
@@ -666,10 +691,12 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
             launch_sk_experts(J, b, max_heavy * (I / 32), cu_budget, s);
         }
         trace_end(trace_op, s);
-        launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
+        if (!all_mfma)
+            launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
         if (any_heavy || extra) {
             SkExperts J{};
             J.L = heavy;
+            J.L2 = all_mfma ? light : none;
             J.w = w2;
             J.w_stride = (int64_t)d_out * I;
             J.K = I;

@@ -58,6 +58,15 @@ __device__ __forceinline__ int wave_in_block() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
 }
 
+// A load through the scalar data cache (s_load): the address must be the
+// same in every lane and the memory must not change while the kernel runs
+// (e.g. lists an earlier kernel wrote). Scalar loads count separately from
+// vector loads, so waiting for one never waits for the weight loads in
+// flight (vector loads retire in order).
+__device__ __forceinline__ int ld_scalar(const int *p) {
+    return *(const __attribute__((address_space(4))) int *)p;
+}
+
 // A pointer every lane of the wave holds (e.g. read from LDS), made known
 // uniform to the compiler so that a range built from it stays scalar.
 template <class T>

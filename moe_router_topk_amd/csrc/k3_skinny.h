@@ -55,6 +55,12 @@ __device__ __forceinline__ void sk_pair(const u32x4 &x, const u32x4 &y, u32x4 &s
     }
 }
 
+// The compiler may not move instructions across this point: it keeps a
+// chunk's prefetch loads ahead of the multiplies of the chunk before (left
+// to itself it sinks them below, to save registers, which leaves one chunk
+// in flight instead of two).
+__device__ __forceinline__ void sk_keep_order() { __builtin_amdgcn_sched_barrier(0); }
+
 // acc[mt] += tokens 16 mt .. 16 mt + 15 (staged chunk xs) x the wave's 16
 // rows (loads buf of the same chunk).
 template <int MT>
@@ -82,13 +88,16 @@ __device__ __forceinline__ void sk_mfma_chunk(f32x4 (&acc)[MT], const u32x4 (&bu
 //                                         it has a member T (tokens; 0 skips the job)
 //   void wave_rows(jb, tile, wq, w, n)    first weight row of wave wq's 16 and how many are valid
 //   const uint16_t *xbase(jb)             the job's token matrix (wave-uniform)
-//   uint32_t xrow(jb, t)                  element offset of token row t in it (t < T)
+//   int  xrow(jb, t)                      row of token t in it (t < T; may read memory)
+//   int  xld(jb)                          its row stride in elements
 //   void store(jb, tile, ks, wq, acc, xch)   epilogue (may hold a block barrier)
 // One item per loop iteration (the pipeline is filled per item): for dense
 // projections, whose items are many and uniform.
 template <int MT, class Jobs>
 __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
-    __shared__ u32x4 xs[MT * 16][kSkKq + 1];  // +1 vector per row keeps the MFMA reads conflict-free
+    // two token buffers (chunks alternate); +1 vector per row keeps the MFMA
+    // reads conflict-free
+    __shared__ u32x4 xs[2][MT * 16][kSkKq + 1];
     __shared__ float xch[2][MT][4][kWave];     // epilogue exchange between waves
     constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
@@ -115,71 +124,73 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         // q / kSkKq, vector q % kSkKq. Rows past T read zeros through the
         // buffer range (no branch, no memory access).
         const uint16_t *xb = uniform_ptr(J.xbase(jb));
+        const uint32_t xld = (uint32_t)J.xld(jb);
         uint32_t xo[SQ];
         bool xv[SQ];
 #pragma unroll
         for (int j = 0; j < SQ; ++j) {
             const int t = (threadIdx.x + j * kBlock) / kSkKq;
             xv[j] = t < T;
-            xo[j] = J.xrow(jb, xv[j] ? t : 0);
+            xo[j] = (uint32_t)J.xrow(jb, xv[j] ? t : 0) * xld;
         }
         const int vq = threadIdx.x % kSkKq;
         int c0, c1;
         split_range(nchunks, ksplit, ks, c0, c1);
+        // Loads of a chunk past the item's range read nothing (an empty
+        // range, offsets out of range): every load is issued on every path,
+        // so the waits for a buffer count exactly the loads issued after it.
         auto wload = [&](u32x4 (&buf)[kSkKb], int c) {
-            sk_wload(buf, weight_range(wbase, wbytes), c, K, lane);
+            sk_wload(buf, weight_range(wbase, c < c1 ? wbytes : 0u), c, K, lane);
         };
         auto aload = [&](u32x4 (&st)[SQ], int c) {
             const rsrc_t rx = act_range(xb);
             const int k = c * kSkKc + 8 * vq;
-            const bool kv = k < K;
+            const bool kv = k < K && c < c1;
 #pragma unroll
             for (int j = 0; j < SQ; ++j)
                 st[j] = ld_act16(rx, (xv[j] && kv) ? (xo[j] + (uint32_t)k) * 2u : kOffNone);
         };
-        auto astore = [&](u32x4 (&st)[SQ]) {
+        auto astore = [&](u32x4 (&st)[SQ], int b) {
 #pragma unroll
             for (int j = 0; j < SQ; ++j) {
                 const int q = threadIdx.x + j * kBlock;
-                xs[q / kSkKq][q % kSkKq] = st[j];
+                xs[b][q / kSkKq][q % kSkKq] = st[j];
             }
         };
         f32x4 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](u32x4 (&buf)[kSkKb]) { sk_mfma_chunk<MT>(acc, buf, xs, mt_n, lane); };
-        // Weights of chunk c + 1 and the tokens of chunk c + 1 are in flight
-        // while chunk c is multiplied; the token loads go out first, so
-        // waiting for them never waits for the weights issued after them.
+        auto compute = [&](u32x4 (&buf)[kSkKb], int b) {
+            sk_mfma_chunk<MT>(acc, buf, xs[b], mt_n, lane);
+        };
+        // Chunk c (the item's chunks alternate between token buffers 0 and 1):
+        // the weights of chunk c + 1 go out, chunk c is multiplied, the tokens
+        // of chunk c + 1 (loaded one step earlier) go to the other buffer and
+        // the tokens of chunk c + 2 go out; one barrier per chunk. A token
+        // load thus has a whole step to arrive, and each wait is for loads
+        // issued a step before. Chunks run in pairs; an odd count ends with
+        // an empty chunk (zero weights and tokens, adding +0), so the loop has
+        // one exit and every load is issued on every path.
         u32x4 A[kSkKb], B[kSkKb], st[SQ];
-        if (c0 < c1) {
-            wload(A, c0);
-            aload(st, c0);
-            astore(st);
+        aload(st, c0);
+        wload(A, c0);
+        astore(st, 0);
+        aload(st, c0 + 1);
+        __syncthreads();
+        for (int c = c0; c < c1; c += 2) {
+            wload(B, c + 1);
+            sk_keep_order();
+            compute(A, 0);
+            astore(st, 1);
+            aload(st, c + 2);
             __syncthreads();
-            for (int c = c0; c < c1; c += 2) {
-                if (c + 1 < c1) {
-                    aload(st, c + 1);
-                    wload(B, c + 1);
-                }
-                compute(A);
-                __syncthreads();
-                if (c + 1 >= c1)
-                    break;
-                astore(st);
-                __syncthreads();
-                if (c + 2 < c1) {
-                    aload(st, c + 2);
-                    wload(A, c + 2);
-                }
-                compute(B);
-                __syncthreads();
-                if (c + 2 >= c1)
-                    break;
-                astore(st);
-                __syncthreads();
-            }
+            wload(A, c + 2);
+            sk_keep_order();
+            compute(B, 1);
+            astore(st, 0);
+            aload(st, c + 3);
+            __syncthreads();
         }
         // acc[mt][i] = out[token 16 mt + 4 g + i][row rl of this wave's 16]
         J.store(jb, tile, ks, wq, acc, xch);
@@ -188,158 +199,175 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
 }
 
 // For lists of jobs (the heavy experts), whose workgroups stream several
-// items each.
-template <int MT, class Jobs>
-struct SkItem {
-    static constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
+// items each. The workgroup's units are (item, chunk) pairs: items
+// blockIdx.x, blockIdx.x + gridDim.x, ... that have tokens, each over its
+// chunk range. Three cursors walk that one sequence: the unit being
+// multiplied, the unit whose weights are loading (one ahead) and the unit
+// whose tokens are loading (two ahead), so the pipeline never drains at an
+// item boundary. A step is one unit with one barrier; steps run in pairs and
+// a sequence of odd length ends with an empty step (every load out of range,
+// no multiply), so the loop has one exit and every load is issued on every
+// path.
+template <class Job>
+struct SkCursor {
+    int it;     // this workgroup's item index
+    int c, c1;  // current chunk, end of the item's chunk range
+    int tile, ks;
+    Job jb;
     bool valid;
-    int next;  // the next item index of this workgroup to look at
-    int tile, ks, c0, c1, T, mt_n;
-    typename Jobs::Job jb;
-    const uint16_t *wbase;
-    uint32_t wbytes;
-    const uint16_t *xb;
-    uint32_t xo[SQ];
-    bool xv[SQ];
 };
-
-// The workgroup's items are blockIdx.x, blockIdx.x + gridDim.x, ...; their
-// (item, chunk) units form one stream, so the next item's first chunk is
-// already in flight while the current item finishes (a workgroup does not
-// drain and refill the pipeline between tiles).
-template <int MT, class Jobs>
-__device__ __forceinline__ void sk_open_item(const Jobs &J, int from, int items, int per_job,
-                                             int ksplit, int nchunks, int K, int wq,
-                                             SkItem<MT, Jobs> &c) {
-    constexpr int SQ = SkItem<MT, Jobs>::SQ;
-    c.valid = false;
-    for (int it = from; it < items; it += gridDim.x) {
-        const int a = it / per_job, rem = it - a * per_job;
-        c.jb = J.job(a);
-        if (c.jb.T <= 0)
-            continue;  // uniform over the workgroup
-        c.next = it + gridDim.x;
-        c.tile = rem / ksplit;
-        c.ks = rem - c.tile * ksplit;
-        c.T = c.jb.T;
-        c.mt_n = min((c.T + 15) >> 4, MT);
-        split_range(nchunks, ksplit, c.ks, c.c0, c.c1);
-        const uint16_t *wr;
-        int nvalid;
-        J.wave_rows(c.jb, c.tile, wq, wr, nvalid);
-        c.wbase = uniform_ptr(wr);
-        c.wbytes = (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u;
-        // this thread stages vectors q = tid + j * 256 of each chunk: token
-        // q / kSkKq, vector q % kSkKq; rows past T read zeros
-        c.xb = uniform_ptr(J.xbase(c.jb));
-#pragma unroll
-        for (int j = 0; j < SQ; ++j) {
-            const int t = (threadIdx.x + j * kBlock) / kSkKq;
-            c.xv[j] = t < c.T;
-            c.xo[j] = J.xrow(c.jb, c.xv[j] ? t : 0);
-        }
-        c.valid = c.c0 < c.c1;
-        if (c.valid)
-            return;
-    }
-}
 
 template <int MT, class Jobs>
 __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ksplit) {
-    __shared__ u32x4 xs[MT * 16][kSkKq + 1];  // +1 vector per row keeps the MFMA reads conflict-free
-    __shared__ float xch[2][MT][4][kWave];     // epilogue exchange between waves
-    using Item = SkItem<MT, Jobs>;
-    constexpr int SQ = Item::SQ;
+    // two token buffers (units alternate); +1 vector per row keeps the MFMA
+    // reads conflict-free
+    __shared__ u32x4 xs[2][MT * 16][kSkKq + 1];
+    __shared__ float xch[2][MT][4][kWave];  // epilogue exchange between waves
+    constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
+    using Job = typename Jobs::Job;
+    using Cur = SkCursor<Job>;
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
     const int nchunks = (K + kSkKc - 1) / kSkKc;
     const int per_job = J.tiles() * ksplit;
     const int items = J.count() * per_job;
     const int vq = threadIdx.x % kSkKq;
 
-    auto wload = [&](u32x4 (&buf)[kSkKb], const Item &it, int c) {
-        sk_wload(buf, weight_range(it.wbase, it.wbytes), c, K, lane);
+    auto open = [&](Cur &u, int from) {
+        u.valid = false;
+        u.c = 0;
+        u.c1 = 0;
+        u.tile = 0;
+        u.ks = 0;
+        u.jb = Job{};
+        for (int it = from; it < items; it += gridDim.x) {
+            const int a = it / per_job, rem = it - a * per_job;
+            const Job jb = J.job(a);
+            if (jb.T <= 0)
+                continue;  // uniform over the workgroup
+            u.it = it;
+            u.jb = jb;
+            u.tile = rem / ksplit;
+            u.ks = rem - u.tile * ksplit;
+            split_range(nchunks, ksplit, u.ks, u.c, u.c1);
+            if (u.c < u.c1) {
+                u.valid = true;
+                return;
+            }
+        }
     };
-    auto aload = [&](u32x4 (&st)[SQ], const Item &it, int c) {
-        const rsrc_t rx = act_range(it.xb);
-        const int k = c * kSkKc + 8 * vq;
-        const bool kv = k < K;
+    auto next = [&](Cur &u) {
+        if (u.valid && ++u.c >= u.c1)
+            open(u, u.it + gridDim.x);
+    };
+
+    // token cursor: this thread stages vectors q = tid + j * 256 of each
+    // chunk (token q / kSkKq, vector q % kSkKq); rows past T read zeros
+    // xr holds the rows as read: they are first used by the next token load,
+    // a step later, so waiting for a row lookup never waits for the weight
+    // loads issued after it
+    int xr[SQ];
+    bool xv[SQ];
+    const uint16_t *xb = nullptr;
+    uint32_t xld = 0;
+    auto set_rows = [&](const Cur &u) {
+        xb = u.valid ? J.xbase(u.jb) : nullptr;
+        xld = u.valid ? (uint32_t)J.xld(u.jb) : 0u;
+#pragma unroll
+        for (int j = 0; j < SQ; ++j) {
+            const int t = (threadIdx.x + j * kBlock) / kSkKq;
+            xv[j] = u.valid && t < u.jb.T;
+            xr[j] = J.xrow(u.jb, xv[j] ? t : 0);  // an empty cursor has T = 0: row 0
+        }
+    };
+    auto wload = [&](u32x4 (&buf)[kSkKb], const Cur &u) {
+        const uint16_t *wr;
+        int nvalid;
+        J.wave_rows(u.jb, u.tile, wq, wr, nvalid);
+        // range parts from lane 0: the cursor passes through joins the
+        // compiler cannot prove uniform, and a range in vector registers
+        // turns every load into a loop over lanes
+        const uint32_t wbytes =
+            u.valid ? (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u : 0u;
+        sk_wload(buf, weight_range(uniform_ptr(wr), wbytes), u.c, K, lane);
+    };
+    auto aload = [&](u32x4 (&st)[SQ], const Cur &u) {
+        const rsrc_t rx = act_range(uniform_ptr(xb));
+        const int k = u.c * kSkKc + 8 * vq;
+        const bool kv = u.valid && k < K;
 #pragma unroll
         for (int j = 0; j < SQ; ++j)
-            st[j] = ld_act16(rx, (it.xv[j] && kv) ? (it.xo[j] + (uint32_t)k) * 2u : kOffNone);
+            st[j] = ld_act16(rx, (xv[j] && kv) ? ((uint32_t)xr[j] * xld + (uint32_t)k) * 2u
+                                               : kOffNone);
     };
-    auto astore = [&](u32x4 (&st)[SQ]) {
+    auto astore = [&](u32x4 (&st)[SQ], int b) {
 #pragma unroll
         for (int j = 0; j < SQ; ++j) {
             const int q = threadIdx.x + j * kBlock;
-            xs[q / kSkKq][q % kSkKq] = st[j];
+            xs[b][q / kSkKq][q % kSkKq] = st[j];
         }
     };
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](u32x4 (&buf)[kSkKb], int mt_n) {
-        sk_mfma_chunk<MT>(acc, buf, xs, mt_n, lane);
-    };
 
-    // cur: the item being multiplied (chunk cc); nx: the item of the next
-    // unit to load (chunk nc).
-    Item cur, nx;
-    sk_open_item<MT>(J, blockIdx.x, items, per_job, ksplit, nchunks, K, wq, cur);
-    if (!cur.valid)
+    Cur C, W, A;  // multiply, weights (one ahead), tokens (two ahead)
+    open(C, blockIdx.x);
+    if (!C.valid)
         return;
-    nx = cur;
-    int cc = cur.c0, nc = cur.c0;
-    auto advance = [&]() {  // nx/nc -> the unit after it
-        if (++nc >= nx.c1) {
-            sk_open_item<MT>(J, nx.next, items, per_job, ksplit, nchunks, K, wq, nx);
-            nc = nx.c0;
-        }
-    };
-    // Weights of the next unit and its tokens are in flight while the current
-    // unit is multiplied; the token loads go out first, so waiting for them
-    // never waits for the weights issued after them.
-    u32x4 A[kSkKb], B[kSkKb], st[SQ];
-    wload(A, nx, nc);
-    aload(st, nx, nc);
-    astore(st);
+    W = C;
+    A = C;
+    u32x4 Bx[kSkKb], By[kSkKb], st[SQ];
+    set_rows(A);
+    aload(st, A);
+    wload(Bx, W);
+    astore(st, 0);
+    {
+        const int it0 = A.it;
+        next(A);
+        if (!A.valid || A.it != it0)
+            set_rows(A);
+    }
+    aload(st, A);
+    next(W);
+    {
+        const int it0 = A.it;
+        next(A);
+        if (!A.valid || A.it != it0)
+            set_rows(A);
+    }
     __syncthreads();
-    advance();
-    // one step: multiply `buf` (unit cur/cc) while the next unit loads into `nbuf`
-    auto step = [&](u32x4 (&buf)[kSkKb], u32x4 (&nbuf)[kSkKb]) -> bool {
-        const bool more = nx.valid;
-        if (more) {
-            aload(st, nx, nc);
-            wload(nbuf, nx, nc);
-        }
-        compute(buf, cur.mt_n);
-        if (cc + 1 >= cur.c1) {
+
+    // one unit: C multiplies from token buffer b, W's weights go out into
+    // nbuf, A's tokens (already staged in st for unit C + 1) go to buffer
+    // b ^ 1 and the tokens of the unit after go out
+    auto step = [&](u32x4 (&buf)[kSkKb], u32x4 (&nbuf)[kSkKb], int b) {
+        wload(nbuf, W);
+        sk_keep_order();
+        const int mt_n = C.valid ? min((C.jb.T + 15) >> 4, MT) : 0;
+        sk_mfma_chunk<MT>(acc, buf, xs[b], mt_n, lane);
+        if (C.valid && C.c + 1 >= C.c1) {
             // acc[mt][i] = out[token 16 mt + 4 g + i][row rl of this wave's 16]
-            J.store(cur.jb, cur.tile, cur.ks, wq, acc, xch);
+            J.store(C.jb, C.tile, C.ks, wq, acc, xch);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();  // every wave is done with xs (and xch)
-        if (!more)
-            return false;
-        astore(st);
+        astore(st, b ^ 1);
+        aload(st, A);
+        next(C);
+        next(W);
+        const int it0 = A.it;
+        const bool was = A.valid;
+        next(A);
+        if (was && (!A.valid || A.it != it0))
+            set_rows(A);
         __syncthreads();
-        if (cc + 1 >= cur.c1) {
-            cur = nx;
-            cc = nc;
-        } else {
-            ++cc;
-        }
-        advance();
-        return true;
     };
-    while (true) {
-        if (!step(A, B))
-            break;
-        if (!step(B, A))
-            break;
-    }
+    do {
+        step(Bx, By, 0);
+        step(By, Bx, 1);
+    } while (C.valid);
 }
 
 // One dense projection made of up to three row segments (e.g. router,
@@ -375,7 +403,8 @@ struct SkDense {
         w = W[s] + (int64_t)(n > 0 ? r0 : 0) * K;
     }
     __device__ const uint16_t *xbase(const Job &) const { return x; }
-    __device__ uint32_t xrow(const Job &, int t) const { return (uint32_t)((int64_t)t * ldx); }
+    __device__ int xrow(const Job &, int t) const { return t; }
+    __device__ int xld(const Job &) const { return (int)ldx; }
     template <int MT>
     __device__ void store(const Job &, int tile, int ks, int wq, const f32x4 (&acc)[MT],
                           float (*)[MT][4][kWave]) const {
