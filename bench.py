@@ -6,9 +6,10 @@ A step is one pass of the whole hot path over one batch of synthetic tokens
 output projection 8192 -> 7168 with residual add and RMSNorm, router scores
 over E = 384 experts with top-8 renormalised softmax, latent projection
 7168 -> 7168, the 8 routed SwiGLU experts (I = 2048) behind the token
-permutation, the shared expert on a second stream, and the side-stream
-prefetch. Weights are bf16, synthetic and seeded; they and the inputs are
-resident in HBM before timing starts.
+permutation and the shared expert (folded into the routed kernels; the
+two-stream form and the side-stream prefetch are timed beside the step).
+Weights are bf16, synthetic and seeded; they and the inputs are resident in
+HBM before timing starts.
 
 Cold-cache discipline: steps rotate over --layers independent copies of the
 layer's weights (about 35 GB each) and a pool of 16 token batches, so no
@@ -94,7 +95,9 @@ def gateup_kernel_name(b: int) -> str:
     if b == 1:
         return ("k_moe_up_b1<true> (expert selection + shared down projection + "
                 "routed gate/up + SwiGLU)")
-    return "routed gate/up + SwiGLU (dot2 rows for light experts, MFMA tiles for heavy)"
+    if b <= 4:
+        return "routed gate/up + SwiGLU (dot2 rows for light experts, MFMA tiles for heavy)"
+    return "routed gate/up + SwiGLU, every expert on MFMA tiles (k_sk_gemm_stream)"
 
 
 def sources_digest(paths) -> str:
