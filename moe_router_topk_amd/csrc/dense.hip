@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include "k3_device.h"
+#include "k3_gemv.h"
 #include "k3_internal.h"
 
 namespace k3 {
@@ -151,15 +152,18 @@ k_rls_dot2(const uint16_t *__restrict__ x, int64_t ldx, int b, int d,
 template <int TM, int CB>
 __global__ void __launch_bounds__(kBlock)
 k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t *__restrict__ Wo,
-             int d, int K, int rpw, uint16_t *res, float *__restrict__ h32) {
+             int d, int K, int rows_blk, uint16_t *res, float *__restrict__ h32) {
     extern __shared__ u32x4 xs[];
     const int nv = K >> 3;
-    const int rows_blk = rpw * (kBlock / kWave);
-    const int rblk = blockIdx.x * rows_blk;
-    float *rs = reinterpret_cast<float *>(xs + b * nv);  // [b][rows_blk]
+    // the rows split evenly over the workgroups (every compute unit streams
+    // the same share), then over the block's waves
+    int rblk, rend;
+    split_range(d, gridDim.x, blockIdx.x, rblk, rend);
+    float *rs = reinterpret_cast<float *>(xs + b * nv);  // [b][rows_blk], rows_blk >= rend - rblk
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * (kBlock / kWave) + wave_in_block();
-    const int r0 = wave * rpw, r1 = min(d, r0 + rpw);
+    int q0, q1;
+    split_range(rend - rblk, kBlock / kWave, wave_in_block(), q0, q1);
+    const int r0 = rblk + q0, r1 = rblk + q1;
     stream_rows<TM, 16 / CB, CB>(
         r0, r1, nv, xs, nv, b, [&](int r) { return Wo + (int64_t)r * K; },
         [&](int r, int t, float s) {
@@ -174,7 +178,7 @@ k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t 
             stage_rows(xs, nv, b, nv, [&](int t) { return a + (int64_t)t * lda; });
             for (int i = threadIdx.x; i < b * rows_blk; i += kBlock) {
                 const int t = i / rows_blk, r = rblk + (i - t * rows_blk);
-                rs[i] = r < d ? bf16_to_f32(res[(int64_t)t * d + r]) : 0.0f;
+                rs[i] = r < rend ? bf16_to_f32(res[(int64_t)t * d + r]) : 0.0f;
             }
             __syncthreads();
         });
@@ -225,6 +229,162 @@ k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gam
     }
 }
 
+// ------------------------------------------------------------------ batch 1 (k3_gemv.h)
+// Shares of the rows per workgroup and the LDS layout of the 8-row engine:
+// x (K / 8 vectors), then the four quarters' partial sums [4][ps_stride],
+// then (o-proj) the residuals of the share.
+struct GemvGeom {
+    int grid, ps_stride;
+    size_t lds;
+};
+
+static GemvGeom gemv_geom(int N, int K, bool resid) {
+    GemvGeom g;
+    g.grid = budget_grid(N, 0, 2);
+    const int rows = (N + g.grid - 1) / g.grid;
+    g.ps_stride = (rows + 7) / 8 * 8;
+    g.lds = (size_t)K * 2 + (size_t)(4 + (resid ? 1 : 0)) * g.ps_stride * sizeof(float);
+    return g;
+}
+
+// The 8-row engine takes K in 64-element pieces.
+static bool gemv_fits(int K) { return K % 64 == 0 && K <= 8192; }
+
+// y[n] = epi(x . W[n]) for one token.
+template <int U, class Epi>
+__global__ void __launch_bounds__(kBlock)
+k_gemv1(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, int N, int K,
+        int ps_stride, Epi epi) {
+    extern __shared__ u32x4 xs[];
+    float *ps = reinterpret_cast<float *>(xs + (K >> 3));
+    int r0, r1;
+    split_range(N, gridDim.x, blockIdx.x, r0, r1);
+    gemv8_stream<U>(
+        (r1 - r0 + 7) >> 3, K,
+        [&](int g, const uint16_t *&base, int &nr, int &skip) {
+            base = W + (int64_t)(r0 + 8 * g) * K;
+            nr = min(8, r1 - r0 - 8 * g);
+            skip = 0;
+        },
+        [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
+        [&]() {
+            stage_rows(xs, K >> 3, 1, K >> 3, [&](int) { return x; });
+            __syncthreads();
+        });
+    for (int i = threadIdx.x; i < r1 - r0; i += kBlock)
+        epi(0, r0 + i, gv_total(ps, ps_stride, i));
+}
+
+// Output projection + residual for one token: h = r + a . Wo^T, written as
+// fp32 (for the norm) and bf16 (back into r). The share's residuals are
+// staged beside a while the first weights load.
+template <int U>
+__global__ void __launch_bounds__(kBlock)
+k_oproj_gemv1(const uint16_t *__restrict__ a, const uint16_t *__restrict__ Wo, int d, int K,
+              int ps_stride, uint16_t *res, float *__restrict__ h32) {
+    extern __shared__ u32x4 xs[];
+    float *ps = reinterpret_cast<float *>(xs + (K >> 3));
+    float *rs = ps + 4 * ps_stride;
+    int r0, r1;
+    split_range(d, gridDim.x, blockIdx.x, r0, r1);
+    gemv8_stream<U>(
+        (r1 - r0 + 7) >> 3, K,
+        [&](int g, const uint16_t *&base, int &nr, int &skip) {
+            base = Wo + (int64_t)(r0 + 8 * g) * K;
+            nr = min(8, r1 - r0 - 8 * g);
+            skip = 0;
+        },
+        [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
+        [&]() {
+            stage_rows(xs, K >> 3, 1, K >> 3, [&](int) { return a; });
+            for (int i = threadIdx.x; i < r1 - r0; i += kBlock)
+                rs[i] = bf16_to_f32(res[r0 + i]);
+            __syncthreads();
+        });
+    for (int i = threadIdx.x; i < r1 - r0; i += kBlock) {
+        const float h = rs[i] + gv_total(ps, ps_stride, i);
+        h32[r0 + i] = h;
+        res[r0 + i] = f32_to_bf16(h);
+    }
+}
+
+// One token's pass over x for every row set that reads it (as k_rls_dot2):
+// E router rows (fp32 logits + bias), NL latent rows (z, bf16) and Is shared
+// gate/up row pairs (h_s = silu(gate) * up, bf16). The rows form one
+// sequence of 8-row groups -- router, latent, then shared pair groups (gate
+// rows 4q .. 4q + 3 with up rows Is + 4q .. Is + 4q + 3) -- split evenly
+// over the workgroups. Each row is summed in the same order as k_gemv1, so
+// logits and z match the separate calls bit for bit.
+template <int U>
+__global__ void __launch_bounds__(kBlock)
+k_rls_gemv1(const uint16_t *__restrict__ x, int d, const uint16_t *__restrict__ Wr,
+            const float *__restrict__ bias, int E, float *__restrict__ logits,
+            const uint16_t *__restrict__ Wl, int NL, uint16_t *__restrict__ z,
+            const uint16_t *__restrict__ W13s, int Is, uint16_t *__restrict__ hs,
+            int ps_stride) {
+    extern __shared__ u32x4 xs[];
+    float *ps = reinterpret_cast<float *>(xs + (d >> 3));
+    float *bs = ps + 4 * ps_stride;
+    const int Gr = (E + 7) >> 3, Gl = (NL + 7) >> 3, Gs = Is >> 2;
+    int g0, g1;
+    split_range(Gr + Gl + Gs, gridDim.x, blockIdx.x, g0, g1);
+    gemv8_stream<U>(
+        g1 - g0, d,
+        [&](int g, const uint16_t *&base, int &nr, int &skip) {
+            const int vg = g0 + g;
+            skip = 0;
+            if (vg < Gr) {
+                base = Wr + (int64_t)(8 * vg) * d;
+                nr = min(8, E - 8 * vg);
+            } else if (vg < Gr + Gl) {
+                const int r = 8 * (vg - Gr);
+                base = Wl + (int64_t)r * d;
+                nr = min(8, NL - r);
+            } else {
+                base = W13s + (int64_t)(4 * (vg - Gr - Gl)) * d;
+                nr = 8;
+                skip = Is - 4;
+            }
+        },
+        [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
+        [&]() {
+            stage_rows(xs, d >> 3, 1, d >> 3, [&](int) { return x; });
+            for (int e = threadIdx.x; e < E; e += kBlock)
+                bs[e] = bias ? bias[e] : 0.0f;
+            __syncthreads();
+        });
+    for (int i = threadIdx.x; i < 8 * (g1 - g0); i += kBlock) {
+        const int vg = g0 + (i >> 3), r = i & 7;
+        if (vg < Gr) {
+            const int e = 8 * vg + r;
+            if (e < E)
+                logits[e] = gv_total(ps, ps_stride, i) + bs[e];
+        } else if (vg < Gr + Gl) {
+            const int n = 8 * (vg - Gr) + r;
+            if (n < NL)
+                z[n] = f32_to_bf16(gv_total(ps, ps_stride, i));
+        } else if (r < 4) {
+            hs[4 * (vg - Gr - Gl) + r] =
+                f32_to_bf16(silu(gv_total(ps, ps_stride, i)) * gv_total(ps, ps_stride, i + 4));
+        }
+    }
+}
+
+static int rls_gemv_ps_stride(int E, int NL, int Is, int grid) {
+    const int total = (E + 7) / 8 + (NL + 7) / 8 + Is / 4;
+    return 8 * ((total + grid - 1) / grid);
+}
+
+template <class Epi>
+static void launch_gemv1(const uint16_t *x, const uint16_t *W, int N, int K, Epi epi,
+                         hipStream_t s) {
+    const GemvGeom g = gemv_geom(N, K, false);
+    if (gv_unit_pieces(K) == 7)
+        k_gemv1<7, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
+    else
+        k_gemv1<8, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
+}
+
 // ------------------------------------------------------------------ launchers
 // Launch geometry of the dot2 engine: one workgroup (four waves) per compute
 // unit by default; each wave streams an even share of the rows.
@@ -266,7 +426,9 @@ static void launch_dense_dot2_t(const uint16_t *x, int64_t ldx, int b, const uin
 template <class Epi>
 static void launch_dense_dot2(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N,
                               int K, Epi epi, hipStream_t s) {
-    if (b == 1)
+    if (b == 1 && gemv_fits(K) && gemv_geom(N, K, false).lds <= 65536)
+        launch_gemv1(x, W, N, K, epi, s);
+    else if (b == 1)
         launch_dense_dot2_t<1>(x, ldx, b, W, N, K, epi, s);
     else
         launch_dense_dot2_t<kDot2MaxTokens>(x, ldx, b, W, N, K, epi, s);
@@ -342,6 +504,21 @@ void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
                 hipStream_t s) {
+    if (b == 1 && gemv_fits(d) && Is % 4 == 0) {
+        const int total = (E + 7) / 8 + (NL + 7) / 8 + Is / 4;
+        const int grid = budget_grid(total, 0, 2);
+        const int ps_stride = rls_gemv_ps_stride(E, NL, Is, grid);
+        const size_t lds = (size_t)d * 2 + ((size_t)4 * ps_stride + E) * sizeof(float);
+        if (lds <= 65536) {
+            if (gv_unit_pieces(d) == 7)
+                k_rls_gemv1<7><<<grid, kBlock, lds, s>>>(x, d, w_router, bias, E, logits, w_lat,
+                                                         NL, z, w13s, Is, hs, ps_stride);
+            else
+                k_rls_gemv1<8><<<grid, kBlock, lds, s>>>(x, d, w_router, bias, E, logits, w_lat,
+                                                         NL, z, w13s, Is, hs, ps_stride);
+            return;
+        }
+    }
     const int cus = budget_grid(1 << 30, 0, 2);
     const int grid = (NL > 0 || Is > 0) ? cus : (E + kBlock / kWave - 1) / (kBlock / kWave);
     const size_t lds = (size_t)b * d * sizeof(uint16_t) + (size_t)E * sizeof(float);
@@ -517,9 +694,12 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         return K3_ERR_WORKSPACE;
     int variant = pick_dense_variant(K3_OP_OPROJ_RESIDUAL, b, K);
     Dot2Geom g{};
+    int rows_blk = 0;
     if (variant == K3_VARIANT_DOT2) {
         g = dot2_geom(d, K, b, 0);
-        g.lds += (size_t)b * g.rpw * (kBlock / kWave) * sizeof(float);  // staged residuals
+        g.grid = budget_grid(d, 0, 2);  // two workgroups per compute unit, even row shares
+        rows_blk = (d + g.grid - 1) / g.grid;
+        g.lds += (size_t)b * rows_blk * sizeof(float);  // staged residuals
         if (g.lds > 65536) {
             if (forced_variant(K3_OP_OPROJ_RESIDUAL) == K3_VARIANT_DOT2)
                 return K3_ERR_UNSUPPORTED;
@@ -531,10 +711,21 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
     hipStream_t s = (hipStream_t)stream;
     float *h32 = (float *)((char *)workspace + oproj_h32_offset());
     trace_begin(K3_OP_OPROJ_RESIDUAL, s);
-    if (variant == K3_VARIANT_DOT2) {
+    if (variant == K3_VARIANT_DOT2 && b == 1 && gemv_fits(K) &&
+        gemv_geom(d, K, true).lds <= 65536) {
+        const GemvGeom gg = gemv_geom(d, K, true);
+        if (gv_unit_pieces(K) == 7)
+            k_oproj_gemv1<7><<<gg.grid, kBlock, gg.lds, s>>>(a, w_o, d, K, gg.ps_stride, residual,
+                                                             h32);
+        else
+            k_oproj_gemv1<8><<<gg.grid, kBlock, gg.lds, s>>>(a, w_o, d, K, gg.ps_stride, residual,
+                                                             h32);
+        trace_end(K3_OP_OPROJ_RESIDUAL, s);
+        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
+    } else if (variant == K3_VARIANT_DOT2) {
 #define K3_OPROJ(TM_, CB_)                                                                     \
-    k_oproj_dot2<TM_, CB_><<<g.grid, kBlock, g.lds, s>>>(a, lda, b, w_o, d, K, g.rpw, residual, \
-                                                         h32)
+    k_oproj_dot2<TM_, CB_><<<g.grid, kBlock, g.lds, s>>>(a, lda, b, w_o, d, K, rows_blk, \
+                                                         residual, h32)
         if (b == 1 && g.cb == 16)
             K3_OPROJ(1, 16);
         else if (b == 1 && g.cb == 4)
