@@ -42,7 +42,9 @@ __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv,
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
     int p0, p1;
     split_range(K >> 6, kBlock / kWave, wq, p0, p1);
-    const int upg = (p1 - p0 + U - 1) / U;  // units per group
+    // units per group; a wave whose quarter is empty (K < 256) still runs
+    // one masked unit per group, so its partial sums are written as zeros
+    const int upg = max(1, (p1 - p0 + U - 1) / U);
     const int nunits = ngroups * upg;
     const int rl = lane >> 3, el = (lane & 7) * 8;
     auto load = [&](u32x4 (&b)[U], int u) {

@@ -10,6 +10,7 @@
 #include <math.h>
 
 #include "k3_device.h"
+#include "k3_gemv.h"
 #include "k3_internal.h"
 
 namespace k3 {
@@ -176,115 +177,86 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
         !TOPK || ns > 0);
 }
 
-// Down projection at batch 1 with the weighted combine folded in. Workgroup
-// g owns an even share of the output rows; its units are (slot, four
-// consecutive rows of w2[ids[slot]]), taken slot-major and split evenly over
-// its four waves, so each wave streams long contiguous runs of one expert.
-// Row sums land in LDS; once all are in, y[r] = bf16(y_add[r] + sum_j w_j
-// o_j[r]) in slot order. The h rows of all k slots sit in LDS. Slots with an
-// id outside [0, E) are skipped.
-template <int CPS>
+// Down projection at batch 1 with the weighted combine folded in, on the
+// 8-row engine (k3_gemv.h). Workgroup g owns an even share of the output
+// rows; its groups are (slot j, 8 consecutive rows of w2[ids[j]]), slot-major,
+// and every wave streams its K-quarter of each. Once all partial sums are in
+// LDS, y[r] = bf16(y_add[r] + sum_j w_j o_j[r]) in slot order. The h rows of
+// all k slots sit in LDS. Slots with an id outside [0, E) read no weights and
+// are skipped in the sum.
+template <int U>
 __global__ void __launch_bounds__(kBlock)
 k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__ w2, int d_out,
           const int32_t *__restrict__ ids, const float *__restrict__ topk_w, int k, int E,
-          const float *__restrict__ y_add, uint16_t *__restrict__ y) {
-    constexpr int RB = 4;
-    extern __shared__ u32x4 hs[];  // k rows of h, then o[k][rows], then y_add[rows]
-    __shared__ const uint16_t *sbase[K3_MAX_TOPK];
+          const float *__restrict__ y_add, uint16_t *__restrict__ y, int ps_stride) {
+    extern __shared__ u32x4 hs[];  // k rows of h, then ps[4][ps_stride], then y_add[rows]
     __shared__ float sw[K3_MAX_TOPK];
+    __shared__ int sv[K3_MAX_TOPK];
     const int nv = I >> 3;
-    if (threadIdx.x < k) {
-        const int e = ids[threadIdx.x];
-        const bool ok = e >= 0 && e < E;
-        sbase[threadIdx.x] = ok ? w2 + (int64_t)e * d_out * I : nullptr;
-        sw[threadIdx.x] = ok ? topk_w[threadIdx.x] : 0.0f;
-    }
+    float *ps = reinterpret_cast<float *>(hs + k * nv);
+    float *ya = ps + 4 * ps_stride;
     int rb0, rb1;
     split_range(d_out, gridDim.x, blockIdx.x, rb0, rb1);
-    const int rows = rb1 - rb0;
-    const int chunks = (rows + RB - 1) / RB;
-    float *o = reinterpret_cast<float *>(hs + k * nv);
-    float *ya = o + k * rows;
-    const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
-    int u0, u1;
-    split_range(k * chunks, kBlock / kWave, wq, u0, u1);
-    __syncthreads();  // the first unit's loads read sbase
-    stream_units<RB * CPS>(
-        u0, u1,
-        [&](u32x4 (&buf)[RB * CPS], int u) {
-            // rows r .. r + RB - 1 of w2[ids[j]] as one range
-            const int j = u / chunks, r = rb0 + (u - j * chunks) * RB;
-            const uint16_t *base = uniform_ptr(sbase[j]);
-            const int nr = base ? min(RB, rb1 - r) : 0;
-            const rsrc_t rs = weight_range(base ? base + (int64_t)r * I : w2, (uint32_t)nr * I * 2);
-#pragma unroll
-            for (int i = 0; i < RB; ++i)
-#pragma unroll
-                for (int c = 0; c < CPS; ++c) {
-                    const int v = c * kWave + lane;
-                    buf[i * CPS + c] =
-                        ld_weight16(rs, v < nv ? (uint32_t)(i * I + v * 8) * 2 : kOffNone);
-                }
+    const int rows = rb1 - rb0, gps = (rows + 7) >> 3;
+    gemv8_stream<U>(
+        k * gps, I,
+        [&](int g, const uint16_t *&base, int &nr, int &skip) {
+            const int j = g / gps, gg = g - j * gps;
+            const int e = ld_scalar(ids + j);  // the same in every lane
+            const bool ok = e >= 0 && e < E;
+            base = w2 + (ok ? (int64_t)e * d_out * I : 0) + (int64_t)(rb0 + 8 * gg) * I;
+            nr = ok ? min(8, rows - 8 * gg) : 0;
+            skip = 0;
         },
-        [&](u32x4 (&buf)[RB * CPS], int u) {
-            const int j = u / chunks, rl = (u - j * chunks) * RB;
-            float acc[RB];
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                acc[i] = 0.0f;
-#pragma unroll
-                for (int c = 0; c < CPS; ++c) {
-                    const int v = c * kWave + lane;
-                    if (v < nv)
-                        acc[i] = dot8(buf[i * CPS + c], hs[j * nv + v], acc[i]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                const float sum = wave_sum(acc[i]);
-                if (lane == 0 && rl + i < rows)
-                    o[j * rows + rl + i] = sum;
-            }
-        },
+        [&](int g, int kv) { return hs[min(g / gps, k - 1) * nv + kv]; }, ps, ps_stride,
         [&]() {
             stage_rows(hs, nv, k, nv, [&](int j) { return hbuf + (int64_t)j * I; });
             for (int i = threadIdx.x; i < rows; i += kBlock)
                 ya[i] = y_add ? y_add[rb0 + i] : 0.0f;
+            if (threadIdx.x < k) {
+                const int e = ids[threadIdx.x];
+                sv[threadIdx.x] = e >= 0 && e < E;
+                sw[threadIdx.x] = topk_w[threadIdx.x];
+            }
             __syncthreads();
         });
-    __syncthreads();
     for (int i = threadIdx.x; i < rows; i += kBlock) {
         float acc = ya[i];
         for (int j = 0; j < k; ++j)
-            if (sbase[j])
-                acc += sw[j] * o[j * rows + i];
+            if (sv[j])
+                acc += sw[j] * gv_total(ps, ps_stride, 8 * j * gps + i);
         y[rb0 + i] = f32_to_bf16(acc);
     }
 }
 
 // ------------------------------------------------------------------ launchers
-static int down_b1_grid(int cu_budget) { return budget_grid(1 << 30, cu_budget, 2); }
+static int down_b1_grid(int d_out, int cu_budget) { return budget_grid(d_out, cu_budget, 2); }
 
-static size_t down_b1_lds(int k, int I, int d_out, int grid) {
+// LDS of the down kernel: k rows of h, the partial sums, y_add of the share.
+static size_t down_b1_lds(int k, int I, int d_out, int grid, int &ps_stride) {
     const int rows = (d_out + grid - 1) / grid;
-    return (size_t)k * I * sizeof(uint16_t) + (size_t)(k + 1) * rows * sizeof(float);
+    ps_stride = 8 * k * ((rows + 7) / 8);
+    return (size_t)k * I * sizeof(uint16_t) + ((size_t)4 * ps_stride + rows) * sizeof(float);
 }
 
 bool down_b1_fits(int k, int I, int d_out, int cu_budget) {
-    return I <= 2048 && down_b1_lds(k, I, d_out, down_b1_grid(cu_budget)) <= 65536;
+    int ps_stride;
+    return I <= 2048 && I % 64 == 0 &&
+           down_b1_lds(k, I, d_out, down_b1_grid(d_out, cu_budget), ps_stride) <= 65536;
 }
 
 void launch_down_b1(const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
                     const int32_t *ids, const float *wts, int k, int E, const float *y_add,
                     uint16_t *y, int cu_budget, hipStream_t s) {
-    const int grid = down_b1_grid(cu_budget);
-    const size_t lds = down_b1_lds(k, I, d_out, grid);
-    if (I > 1024)
-        k_down_b1<4><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y);
-    else if (I > 512)
-        k_down_b1<2><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y);
+    const int grid = down_b1_grid(d_out, cu_budget);
+    int ps_stride;
+    const size_t lds = down_b1_lds(k, I, d_out, grid, ps_stride);
+    if (gv_unit_pieces(I) == 7)
+        k_down_b1<7><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y,
+                                              ps_stride);
     else
-        k_down_b1<1><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y);
+        k_down_b1<8><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, ids, wts, k, E, y_add, y,
+                                              ps_stride);
 }
 
 // The fused batch-1 gate/up kernel: d <= 7168 and, with the shared down
