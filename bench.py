@@ -42,7 +42,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_moe_up_b1_traffic.json")
-DOMINANT_SOURCES = ["moe_router_topk_amd/csrc/moe_b1.hip", "moe_router_topk_amd/csrc/k3_device.h"]
+DOMINANT_SOURCES = ["moe_router_topk_amd/csrc/moe_b1.hip", "moe_router_topk_amd/csrc/k3_gemv.h",
+                    "moe_router_topk_amd/csrc/k3_device.h"]
 
 
 def log(msg: str) -> None:
@@ -79,22 +80,20 @@ def chain_bytes(cc, b: int) -> int:
 
 
 def gateup_bytes(cfg, b: int, n_active: int) -> int:
-    """Per launch of the kernel traced as the routed experts' gate/up pass.
-    Always: n_active experts' [2I x d_lat] weights, the z rows it reads and the
-    h rows it writes. At batch 1 that kernel (k_moe_up_b1) also selects the
-    experts and streams the shared expert's down projection: + the [d x I_s]
-    weights, the logits and shared h it reads, y_s, ids and weights it writes."""
-    d, dl, I, Is, E, k = cfg.d, cfg.d_lat, cfg.I, cfg.I_s, cfg.E, cfg.k
+    """Per launch of the kernel traced as the routed experts' gate/up pass:
+    n_active experts' [2I x d_lat] weights, the z rows it reads and the h rows
+    it writes. At batch 1 that kernel (k_moe_up_b1) also selects the experts:
+    + the logits it reads, the ids and weights it writes."""
+    dl, I, E, k = cfg.d_lat, cfg.I, cfg.E, cfg.k
     n = 2 * n_active * 2 * I * dl + 2 * b * dl + 2 * b * k * I
     if b == 1:
-        n += 2 * d * Is + 4 * E + 2 * Is + 4 * d + 8 * k
+        n += 4 * E + 8 * k
     return n
 
 
 def gateup_kernel_name(b: int) -> str:
     if b == 1:
-        return ("k_moe_up_b1<true> (expert selection + shared down projection + "
-                "routed gate/up + SwiGLU)")
+        return "k_moe_up_b1<true> (expert selection + routed gate/up + SwiGLU)"
     if b <= 4:
         return "routed gate/up + SwiGLU (dot2 rows for light experts, MFMA tiles for heavy)"
     return "routed gate/up + SwiGLU, every expert on MFMA tiles (k_sk_gemm_stream)"
@@ -167,8 +166,8 @@ def write_traffic_summary(pmc_dir: str) -> int:
     traffic = int(round(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale))
     algo = gateup_bytes(synth.MOE_CONFIGS["b1"], 1, synth.MOE_CONFIGS["b1"].k)
     out = {
-        "kernel": "k3::k_moe_up_b1<true> (expert selection + shared down projection + routed "
-                  "gate/up + SwiGLU), batch 1, d=7168, E=384, k=8, I=I_s=2048",
+        "kernel": "k3::k_moe_up_b1<true> (expert selection + routed gate/up + SwiGLU), "
+                  "batch 1, d=7168, E=384, k=8, I=2048",
         "commands": [
             f"rocprofv3 --pmc {ctr} --output-format csv -d gpurun_out/pmc_{key} -o c -- "
             f"python3 -u bench.py {args}" for key, (ctr, args) in PMC_RUNS.items()

@@ -238,9 +238,9 @@ struct GemvGeom {
     size_t lds;
 };
 
-static GemvGeom gemv_geom(int N, int K, bool resid) {
+static GemvGeom gemv_geom(int N, int K, bool resid, int cu_budget = 0) {
     GemvGeom g;
-    g.grid = budget_grid(N, 0, 2);
+    g.grid = budget_grid(N, cu_budget, 2);
     const int rows = (N + g.grid - 1) / g.grid;
     g.ps_stride = (rows + 7) / 8 * 8;
     g.lds = (size_t)K * 2 + (size_t)(4 + (resid ? 1 : 0)) * g.ps_stride * sizeof(float);
@@ -377,12 +377,22 @@ static int rls_gemv_ps_stride(int E, int NL, int Is, int grid) {
 
 template <class Epi>
 static void launch_gemv1(const uint16_t *x, const uint16_t *W, int N, int K, Epi epi,
-                         hipStream_t s) {
-    const GemvGeom g = gemv_geom(N, K, false);
+                         hipStream_t s, int cu_budget = 0) {
+    const GemvGeom g = gemv_geom(N, K, false, cu_budget);
     if (gv_unit_pieces(K) == 7)
         k_gemv1<7, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
     else
         k_gemv1<8, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
+}
+
+bool gemv1_f32_fits(int N, int K) {
+    return gemv_fits(K) && gemv_geom(N, K, false).lds <= 65536;
+}
+
+// One token, y[n] = x . W[n] in fp32 (the shared expert's down projection).
+void launch_gemv1_f32(const uint16_t *x, const uint16_t *W, int N, int K, float *y, int cu_budget,
+                      hipStream_t s) {
+    launch_gemv1(x, W, N, K, EpiLogits{y, N, nullptr}, s, cu_budget);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -503,10 +513,10 @@ bool rls_fits(int b, int d, int E) {
 void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
-                hipStream_t s) {
+                hipStream_t s, int cu_budget) {
     if (b == 1 && gemv_fits(d) && Is % 4 == 0) {
         const int total = (E + 7) / 8 + (NL + 7) / 8 + Is / 4;
-        const int grid = budget_grid(total, 0, 2);
+        const int grid = budget_grid(total, cu_budget, 2);
         const int ps_stride = rls_gemv_ps_stride(E, NL, Is, grid);
         const size_t lds = (size_t)d * 2 + ((size_t)4 * ps_stride + E) * sizeof(float);
         if (lds <= 65536) {

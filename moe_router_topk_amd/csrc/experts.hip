@@ -637,16 +637,17 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
     trace_begin(trace_op, s);
     if (b == 1) {
         const SlotList sl{topk_ids, k, E};
-        if (up_b1_fits(d_in, 0))
-            launch_up_b1(false, z, d_in, w13, I, E, k, topk_ids, nullptr, nullptr, nullptr,
-                         nullptr, 0, nullptr, 0, nullptr, hbuf, cu_budget, s);
+        if (up_b1_fits(d_in, k, I, cu_budget))
+            launch_up_b1(false, z, d_in, w13, I, E, k, topk_ids, nullptr, nullptr, nullptr, hbuf,
+                         cu_budget, s);
         else
             launch_gateup_dot2(1, z, ldz, d_in, w13, I, sl, hbuf, cu_budget, s);
         trace_end(trace_op, s);
         if (y_add_ready)
             (void)hipStreamWaitEvent(s, y_add_ready, 0);
-        if (down_b1_fits(k, I, d_out, cu_budget)) {
-            launch_down_b1(hbuf, I, w2, d_out, topk_ids, topk_w, k, E, y_add, y, cu_budget, s);
+        if (down_b1_fits(k, I, d_out, false, cu_budget)) {
+            launch_down_b1(hbuf, I, w2, d_out, topk_ids, topk_w, k, E, y_add, nullptr, nullptr,
+                           nullptr, y, cu_budget, s);
             return;
         }
         launch_down_dot2(1, hbuf, I, w2, d_out, sl, out, cu_budget, s);
@@ -730,7 +731,16 @@ void run_shared_expert(int variant, const uint16_t *x, int64_t ldx, int b, int d
     const DenseList dl{b};
     const OutDense out{y_s, d};
     trace_begin(trace_op, s);
-    if (variant == K3_VARIANT_DOT2) {
+    if (variant == K3_VARIANT_DOT2 && b == 1 && rls_fits(1, d, 0) && I % 4 == 0 &&
+        gemv1_f32_fits(d, I)) {
+        // the 8-row engine, summing in the same order as the fused block's
+        // shared rows (gate/up in the router+latent pass, down in the routed
+        // down kernel)
+        launch_rls(x, ldx, 1, d, nullptr, nullptr, 0, nullptr, nullptr, 0, nullptr, 0, w13, I, hbuf,
+                   s, cu_budget);
+        trace_end(trace_op, s);
+        launch_gemv1_f32(hbuf, w2, d, I, y_s, cu_budget, s);
+    } else if (variant == K3_VARIANT_DOT2) {
         const int tm = b == 1 ? 1 : kDot2MaxTokens;
         launch_gateup_dot2(tm, x, ldx, d, w13, I, dl, hbuf, cu_budget, s);
         trace_end(trace_op, s);
@@ -845,20 +855,19 @@ extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
     float *logits = (float *)(ws + L.logits);
     uint16_t *hs = (uint16_t *)(ws + L.hs);
     trace_begin(K3_OP_MOE_BLOCK, s);
-    if (variant == K3_VARIANT_DOT2 && b == 1 && up_b1_fits(d_lat, I_s) &&
-        down_b1_fits(k, I, d, 0)) {
+    if (variant == K3_VARIANT_DOT2 && b == 1 && I_s == I &&
+        up_b1_fits(d_lat, k, I, 0) && down_b1_fits(k, I, d, true, 0)) {
         // 1. router, latent and shared gate/up rows in one pass over x;
-        // 2. expert selection, shared down rows and routed gate/up;
-        // 3. routed down rows with the combine and the shared output added
+        // 2. expert selection and routed gate/up;
+        // 3. routed and shared down rows with the combine
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, w13_s, I_s, hs,
                    s);
         trace_end(K3_OP_MOE_BLOCK, s);
         uint16_t *hbuf = (uint16_t *)(ws + L.moe + moe_workspace_layout(b, E, k, I, d).hbuf);
         trace_begin(K3_OP_MOE_EXPERTS, s);
-        launch_up_b1(true, z, d_lat, w13, I, E, k, nullptr, logits, topk_ids, topk_w, hs, I_s,
-                     w2_s, d, y_s, hbuf, 0, s);
+        launch_up_b1(true, z, d_lat, w13, I, E, k, nullptr, logits, topk_ids, topk_w, hbuf, 0, s);
         trace_end(K3_OP_MOE_EXPERTS, s);
-        launch_down_b1(hbuf, I, w2, d, topk_ids, topk_w, k, E, y_s, y, 0, s);
+        launch_down_b1(hbuf, I, w2, d, topk_ids, topk_w, k, E, nullptr, hs, w2_s, y_s, y, 0, s);
         const int st = launch_status();
         if (st == K3_OK)
             record_dispatch(K3_OP_MOE_BLOCK, variant);

@@ -43,7 +43,11 @@ bool rls_fits(int b, int d, int E);
 void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
-                hipStream_t s);
+                hipStream_t s, int cu_budget = 0);
+// One token on the 8-row engine: y[n] = x . W[n] in fp32, n < N (K % 64 == 0).
+bool gemv1_f32_fits(int N, int K);
+void launch_gemv1_f32(const uint16_t *x, const uint16_t *W, int N, int K, float *y, int cu_budget,
+                      hipStream_t s);
 void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *wts,
                  hipStream_t s);
 
@@ -78,16 +82,17 @@ void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint1
 
 // Batch-1 routed experts (moe_b1.hip). up_b1: routed gate/up + SwiGLU into
 // hbuf [k][I]; with `topk` the selection from logits happens in the kernel
-// (ids/weights written out), and with w2s the shared expert's down rows
-// (y_s) stream first. down_b1: y = bf16(y_add + sum_j w_j w2[ids[j]] . h_j).
-bool up_b1_fits(int d, int Is);
+// (ids/weights written out). down_b1: y = bf16(base + sum_j w_j w2[ids[j]] .
+// h_j) with base = y_add, or, with w2s, the shared expert's down projection
+// of hs (also written to y_s).
+bool up_b1_fits(int d, int k, int I, int cu_budget);
 void launch_up_b1(bool topk, const uint16_t *z, int d, const uint16_t *w13, int I, int E, int k,
                   const int32_t *ids_in, const float *logits, int32_t *ids_out, float *w_out,
-                  const uint16_t *hs, int Is, const uint16_t *w2s, int d_s, float *y_s,
                   uint16_t *hbuf, int cu_budget, hipStream_t s);
-bool down_b1_fits(int k, int I, int d_out, int cu_budget);
+bool down_b1_fits(int k, int I, int d_out, bool shared, int cu_budget);
 void launch_down_b1(const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
                     const int32_t *ids, const float *wts, int k, int E, const float *y_add,
-                    uint16_t *y, int cu_budget, hipStream_t s);
+                    const uint16_t *hs, const uint16_t *w2s, float *y_s, uint16_t *y,
+                    int cu_budget, hipStream_t s);
 
 }  // namespace k3
