@@ -115,6 +115,7 @@ size_t k3_moe_experts_workspace_size(int b, int d_in, int E, int k, int I, int d
 size_t k3_shared_expert_workspace_size(int b, int d, int I);
 size_t k3_oproj_residual_workspace_size(int b, int K, int d);
 size_t k3_moe_block_workspace_size(int b, int d, int E, int k, int d_lat, int I, int I_s);
+size_t k3_moe_block_rmsnorm_workspace_size(int b, int d, int E, int k, int d_lat, int I, int I_s);
 
 /* ------------------------------------------------------------ entry points */
 
@@ -265,6 +266,30 @@ int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w
                  int64_t ldz, float *y_s, uint16_t *y, void *workspace, size_t ws_bytes,
                  void *stream);
 
+/* The MoE block on the normalised hidden state, normalising it itself (the
+ * RMSNorm that k3_oproj_residual applies, moved into the block's first
+ * kernel at batch 1, so the step has one kernel boundary less):
+ *
+ *   x[t][n] = bf16( h32[t][n] / sqrt( (1/d) sum_m h32[t][m]^2 + eps ) * gamma[n] )
+ *
+ * then exactly k3_moe_block on x (same outputs, bit for bit the same as
+ * k3_oproj_residual's y_norm fed to k3_moe_block).
+ *
+ * h32      device, [b x d] fp32, row stride d (e.g. k3_oproj_residual_h32)
+ * gamma    device, [d] bf16
+ * x_out    device, [b x d] bf16 (output), or NULL: receives x
+ * The other arguments are k3_moe_block's (x and ldx replaced by the above).
+ * workspace: >= k3_moe_block_rmsnorm_workspace_size(b, d, E, k, d_lat, I, I_s)
+ * bytes. Limits: k3_moe_block's, and eps >= 0.
+ */
+int k3_moe_block_rmsnorm(const float *h32, int b, int d, const uint16_t *gamma, float eps,
+                         uint16_t *x_out, const uint16_t *w_router, const float *bias, int E,
+                         int k, const uint16_t *w_lat, int d_lat, const uint16_t *w13,
+                         const uint16_t *w2, int I, const uint16_t *w13_s, const uint16_t *w2_s,
+                         int I_s, int32_t *topk_ids, float *topk_w, uint16_t *z, int64_t ldz,
+                         float *y_s, uint16_t *y, void *workspace, size_t ws_bytes,
+                         void *stream);
+
 /* Attention output projection with residual add and RMSNorm (Part 1
  * section 2, "Overlap computation and communication": the output
  * projection is fused with the attention residual that follows it).
@@ -278,7 +303,9 @@ int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w
  * residual device, [b x d] bf16, row stride d: read as r, overwritten with
  *          bf16(h) (in place)
  * gamma    device, [d] bf16
- * y_norm   device, [b x d] bf16 (output); must not overlap residual or a
+ * y_norm   device, [b x d] bf16 (output); must not overlap residual or a;
+ *          or NULL: the norm is skipped (gamma may then be NULL too) and
+ *          the fp32 h stays in the workspace for k3_moe_block_rmsnorm
  * The norm is taken over fp32 h, before h is rounded for the store.
  * workspace: >= k3_oproj_residual_workspace_size(b, K, d) bytes.
  * Limits: 1 <= b <= 64, d % 8 == 0, eps >= 0.
@@ -287,6 +314,11 @@ int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
                       const uint16_t *w_o, int d, uint16_t *residual,
                       const uint16_t *gamma, float eps, uint16_t *y_norm,
                       void *workspace, size_t ws_bytes, void *stream);
+
+/* Where k3_oproj_residual leaves the fp32 h ([b x d], row stride d) in its
+ * workspace: valid after the call on the same stream, until the workspace
+ * is reused. Pure pointer arithmetic; NULL for a NULL workspace. */
+const float *k3_oproj_residual_h32(const void *workspace);
 
 /* Weight prefetch (Part 1 section 4, "Prefetching upcoming weights into
  * cache"): reads [p, p + bytes) once, so the next operator that reads those

@@ -18,6 +18,7 @@ __all__ = [
     "K3Error", "lib", "library_path",
     "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
     "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_moe_block",
+    "k3_moe_block_rmsnorm", "oproj_h32_view",
     "k3_get_last_dispatch", "k3_force_variant",
     "k3_trace_events", "HipEvent",
     "k3_status_string", "k3_version", "workspace_size",
@@ -39,8 +40,10 @@ EXPORTED_SYMBOLS = [
     "k3_router_topk_latent_workspace_size", "k3_proj_skinny_workspace_size",
     "k3_moe_experts_workspace_size", "k3_shared_expert_workspace_size",
     "k3_oproj_residual_workspace_size", "k3_moe_block_workspace_size",
+    "k3_moe_block_rmsnorm_workspace_size",
     "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
     "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_moe_block",
+    "k3_moe_block_rmsnorm", "k3_oproj_residual_h32",
 ]
 
 _vp = ctypes.c_void_p
@@ -87,11 +90,19 @@ def lib():
     L.k3_shared_expert_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_oproj_residual_workspace_size.argtypes = [_i32, _i32, _i32]
     L.k3_moe_block_workspace_size.argtypes = [_i32] * 7
+    L.k3_moe_block_rmsnorm_workspace_size.argtypes = [_i32] * 7
     for f in ("k3_router_topk_workspace_size", "k3_router_topk_latent_workspace_size",
               "k3_proj_skinny_workspace_size",
               "k3_moe_experts_workspace_size", "k3_shared_expert_workspace_size",
-              "k3_oproj_residual_workspace_size", "k3_moe_block_workspace_size"):
+              "k3_oproj_residual_workspace_size", "k3_moe_block_workspace_size",
+              "k3_moe_block_rmsnorm_workspace_size"):
         getattr(L, f).restype = _sz
+    L.k3_moe_block_rmsnorm.argtypes = [_vp, _i32, _i32, _vp, ctypes.c_float, _vp, _vp, _vp, _i32,
+                                       _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
+                                       _vp, _i64, _vp, _vp, _vp, _sz, _vp]
+    L.k3_moe_block_rmsnorm.restype = _i32
+    L.k3_oproj_residual_h32.argtypes = [_vp]
+    L.k3_oproj_residual_h32.restype = _vp
     L.k3_moe_block.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp,
                                _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]
     L.k3_moe_block.restype = _i32
@@ -242,6 +253,9 @@ def workspace_size(op: str, **kw) -> int:
         return L.k3_shared_expert_workspace_size(kw["b"], kw["d"], kw["I"])
     if op == "oproj_residual":
         return L.k3_oproj_residual_workspace_size(kw["b"], kw["K"], kw["d"])
+    if op == "moe_block_rmsnorm":
+        return L.k3_moe_block_rmsnorm_workspace_size(kw["b"], kw["d"], kw["E"], kw["k"],
+                                                     kw["d_lat"], kw["I"], kw["I_s"])
     if op == "moe_block":
         return L.k3_moe_block_workspace_size(kw["b"], kw["d"], kw["E"], kw["k"], kw["d_lat"],
                                              kw["I"], kw["I_s"])
@@ -344,13 +358,16 @@ def k3_shared_expert(x, w13, w2, y_s=None, cu_budget=0, workspace=None, stream=N
     return y_s
 
 
-def k3_oproj_residual(a, w_o, residual, gamma, eps, y_norm=None, workspace=None, stream=None):
-    """In place: residual <- bf16(residual + a . w_o^T); returns y_norm = RMSNorm(h) * gamma."""
+def k3_oproj_residual(a, w_o, residual, gamma, eps, y_norm=None, workspace=None, stream=None,
+                      norm=True):
+    """In place: residual <- bf16(residual + a . w_o^T); returns y_norm = RMSNorm(h) * gamma.
+    With norm=False the norm is skipped (returns None); the fp32 h stays in the workspace
+    (oproj_h32_view)."""
     dev = _dev(a)
     b, K = a.shape
     d = w_o.shape[0]
     assert residual.is_contiguous() and residual.shape == (b, d)
-    if y_norm is None:
+    if y_norm is None and norm:
         y_norm = torch.empty((b, d), dtype=torch.bfloat16, device=dev)
     nbytes = lib().k3_oproj_residual_workspace_size(b, K, d)
     ws = workspace if workspace is not None else _workspace(dev, nbytes, "oproj_residual")
@@ -385,6 +402,44 @@ def k3_moe_block(x, w_router, bias, k, w_lat, w13, w2, w13_s, w2_s, topk_ids=Non
         _ptr(x), _ld(x), b, d, _ptr(w_router), _ptr(bias), E, k, _ptr(w_lat), d_lat, _ptr(w13),
         _ptr(w2), I, _ptr(w13_s), _ptr(w2_s), I_s, _ptr(topk_ids), _ptr(topk_w), _ptr(z), _ld(z),
         _ptr(y_s), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+    return y, topk_ids, topk_w, z, y_s
+
+
+def oproj_h32_view(workspace, b, d):
+    """The fp32 h [b x d] that k3_oproj_residual left in `workspace` (a view, no copy)."""
+    off = lib().k3_oproj_residual_h32(_ptr(workspace)) - workspace.data_ptr()
+    return workspace[off:off + 4 * b * d].view(torch.float32).view(b, d)
+
+
+def k3_moe_block_rmsnorm(h32, gamma, eps, w_router, bias, k, w_lat, w13, w2, w13_s, w2_s,
+                         x_out=None, topk_ids=None, topk_w=None, z=None, y_s=None, y=None,
+                         workspace=None, stream=None):
+    """The MoE block on x = RMSNorm(h32) * gamma (normalised inside the block):
+    returns (y, topk_ids, topk_w, z, y_s); x_out, if given, receives x."""
+    dev = _dev(h32)
+    b, d = h32.shape
+    assert h32.dtype == torch.float32 and h32.is_contiguous()
+    E = w_router.shape[0]
+    d_lat = w_lat.shape[0]
+    I = w13.shape[1] // 2
+    I_s = w13_s.shape[0] // 2
+    if topk_ids is None:
+        topk_ids = torch.empty((b, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((b, k), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((b, d_lat), dtype=torch.bfloat16, device=dev)
+    if y_s is None:
+        y_s = torch.empty((b, d), dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((b, d), dtype=torch.bfloat16, device=dev)
+    nbytes = lib().k3_moe_block_rmsnorm_workspace_size(b, d, E, k, d_lat, I, I_s)
+    ws = workspace if workspace is not None else _workspace(dev, nbytes, "moe_block_rmsnorm")
+    _check("k3_moe_block_rmsnorm", lib().k3_moe_block_rmsnorm(
+        _ptr(h32), b, d, _ptr(gamma), float(eps), _ptr(x_out), _ptr(w_router), _ptr(bias), E, k,
+        _ptr(w_lat), d_lat, _ptr(w13), _ptr(w2), I, _ptr(w13_s), _ptr(w2_s), I_s,
+        _ptr(topk_ids), _ptr(topk_w), _ptr(z), _ld(z), _ptr(y_s), _ptr(y), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
     return y, topk_ids, topk_w, z, y_s
 
 

@@ -184,49 +184,64 @@ k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t 
         });
 }
 
-// One workgroup per token: y = h / sqrt(mean(h^2) + eps) * gamma, the mean in
-// fp32 with a fixed reduction order (d % 4 == 0, d <= 8192). Every load of
-// h and gamma is issued before the first is used (indexes clamped, no
-// branches), so the kernel costs about one memory latency, not several.
+// One token's RMSNorm by one workgroup: y = h / sqrt(mean(h^2) + eps) *
+// gamma, the mean in fp32 with a fixed reduction order (d % 4 == 0,
+// d <= 8192). load() issues every load of h and gamma (indexes clamped, no
+// branches), finish() waits for them, reduces (one barrier) and hands
+// element e of y to out(e, bf16).
 constexpr int kNormVec = 8;
+struct RmsRow {
+    f32x4 v[kNormVec];
+    uint16_t gm[kNormVec][4];
+    __device__ __forceinline__ void load(const float *__restrict__ h32, int d,
+                                         const uint16_t *__restrict__ gamma) {
+        const f32x4 *h = reinterpret_cast<const f32x4 *>(h32);
+        const int n4 = d >> 2;
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j) {
+            const int i = threadIdx.x + j * kBlock;
+            const int ic = i < n4 ? i : 0;
+            v[j] = h[ic];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                gm[j][q] = gamma[4 * ic + q];
+        }
+    }
+    template <class Out>
+    __device__ __forceinline__ void finish(int d, float eps, Out out) const {
+        __shared__ float part[kBlock / kWave];
+        const int n4 = d >> 2;
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j)
+            if (threadIdx.x + j * kBlock < n4)
+                ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+        ss = wave_sum(ss);
+        if ((threadIdx.x & (kWave - 1)) == 0)
+            part[threadIdx.x / kWave] = ss;
+        __syncthreads();
+        const float inv =
+            1.0f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)d + eps);
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j) {
+            const int i = threadIdx.x + j * kBlock;
+            if (i < n4)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    out(4 * i + q, f32_to_bf16(v[j][q] * inv * bf16_to_f32(gm[j][q])));
+        }
+    }
+};
+
+// One workgroup per token.
 __global__ void __launch_bounds__(kBlock)
 k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gamma, float eps,
           uint16_t *__restrict__ y) {
-    __shared__ float part[kBlock / kWave];
     const int t = blockIdx.x;
-    const f32x4 *h = reinterpret_cast<const f32x4 *>(h32 + (int64_t)t * d);
-    const int n4 = d >> 2;
-    f32x4 v[kNormVec];
-    uint16_t gm[kNormVec][4];
-#pragma unroll
-    for (int j = 0; j < kNormVec; ++j) {
-        const int i = threadIdx.x + j * kBlock;
-        const int ic = i < n4 ? i : 0;
-        v[j] = h[ic];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            gm[j][q] = gamma[4 * ic + q];
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kNormVec; ++j)
-        if (threadIdx.x + j * kBlock < n4)
-            ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-    ss = wave_sum(ss);
-    if ((threadIdx.x & (kWave - 1)) == 0)
-        part[threadIdx.x / kWave] = ss;
-    __syncthreads();
-    const float inv = 1.0f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)d + eps);
-#pragma unroll
-    for (int j = 0; j < kNormVec; ++j) {
-        const int i = threadIdx.x + j * kBlock;
-        if (i < n4) {
-            uint16_t *o = y + (int64_t)t * d + 4 * i;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                o[q] = f32_to_bf16(v[j][q] * inv * bf16_to_f32(gm[j][q]));
-        }
-    }
+    uint16_t *yt = y + (int64_t)t * d;
+    RmsRow rr;
+    rr.load(h32 + (int64_t)t * d, d, gamma);
+    rr.finish(d, eps, [&](int e, uint16_t v) { yt[e] = v; });
 }
 
 // ------------------------------------------------------------------ batch 1 (k3_gemv.h)
@@ -259,6 +274,7 @@ k_gemv1(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, int N, i
     float *ps = reinterpret_cast<float *>(xs + (K >> 3));
     int r0, r1;
     split_range(N, gridDim.x, blockIdx.x, r0, r1);
+    GvStage<4> st;  // K <= 8192
     gemv8_stream<U>(
         (r1 - r0 + 7) >> 3, K,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
@@ -266,9 +282,9 @@ k_gemv1(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, int N, i
             nr = min(8, r1 - r0 - 8 * g);
             skip = 0;
         },
-        [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
+        [&](int, int kv) { return xs[kv]; }, ps, ps_stride, [&]() { st.load(x, K >> 3); },
         [&]() {
-            stage_rows(xs, K >> 3, 1, K >> 3, [&](int) { return x; });
+            st.store(xs, K >> 3);
             __syncthreads();
         });
     for (int i = threadIdx.x; i < r1 - r0; i += kBlock)
@@ -287,6 +303,8 @@ k_oproj_gemv1(const uint16_t *__restrict__ a, const uint16_t *__restrict__ Wo, i
     float *rs = ps + 4 * ps_stride;
     int r0, r1;
     split_range(d, gridDim.x, blockIdx.x, r0, r1);
+    GvStage<4> st;  // K <= 8192
+    uint16_t rv = 0;  // this thread's residual (thread i < the share's rows)
     gemv8_stream<U>(
         (r1 - r0 + 7) >> 3, K,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
@@ -296,9 +314,13 @@ k_oproj_gemv1(const uint16_t *__restrict__ a, const uint16_t *__restrict__ Wo, i
         },
         [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
         [&]() {
-            stage_rows(xs, K >> 3, 1, K >> 3, [&](int) { return a; });
-            for (int i = threadIdx.x; i < r1 - r0; i += kBlock)
-                rs[i] = bf16_to_f32(res[r0 + i]);
+            st.load(a, K >> 3);
+            rv = res[r0 + min((int)threadIdx.x, r1 - r0 - 1)];
+        },
+        [&]() {
+            st.store(xs, K >> 3);
+            if ((int)threadIdx.x < r1 - r0)
+                rs[threadIdx.x] = bf16_to_f32(rv);
             __syncthreads();
         });
     for (int i = threadIdx.x; i < r1 - r0; i += kBlock) {
@@ -315,19 +337,26 @@ k_oproj_gemv1(const uint16_t *__restrict__ a, const uint16_t *__restrict__ Wo, i
 // rows 4q .. 4q + 3 with up rows Is + 4q .. Is + 4q + 3) -- split evenly
 // over the workgroups. Each row is summed in the same order as k_gemv1, so
 // logits and z match the separate calls bit for bit.
-template <int U>
+// With NORM the input is x = RMSNorm(h32) * gamma (as k_rmsnorm computes it),
+// normalised by every workgroup while its first weights load; workgroup 0
+// also writes x to x_out when that is not null.
+template <int U, bool NORM>
 __global__ void __launch_bounds__(kBlock)
 k_rls_gemv1(const uint16_t *__restrict__ x, int d, const uint16_t *__restrict__ Wr,
             const float *__restrict__ bias, int E, float *__restrict__ logits,
             const uint16_t *__restrict__ Wl, int NL, uint16_t *__restrict__ z,
             const uint16_t *__restrict__ W13s, int Is, uint16_t *__restrict__ hs,
-            int ps_stride) {
+            int ps_stride, const float *__restrict__ h32, const uint16_t *__restrict__ gamma,
+            float eps, uint16_t *__restrict__ x_out) {
     extern __shared__ u32x4 xs[];
     float *ps = reinterpret_cast<float *>(xs + (d >> 3));
     float *bs = ps + 4 * ps_stride;
     const int Gr = (E + 7) >> 3, Gl = (NL + 7) >> 3, Gs = Is >> 2;
     int g0, g1;
     split_range(Gr + Gl + Gs, gridDim.x, blockIdx.x, g0, g1);
+    GvStage<4> st;  // d <= 8192
+    RmsRow rr;
+    float bv[4];    // router bias, E <= 1024
     gemv8_stream<U>(
         g1 - g0, d,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
@@ -348,9 +377,34 @@ k_rls_gemv1(const uint16_t *__restrict__ x, int d, const uint16_t *__restrict__ 
         },
         [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
         [&]() {
-            stage_rows(xs, d >> 3, 1, d >> 3, [&](int) { return x; });
-            for (int e = threadIdx.x; e < E; e += kBlock)
-                bs[e] = bias ? bias[e] : 0.0f;
+            if (NORM)
+                rr.load(h32, d, gamma);
+            else
+                st.load(x, d >> 3);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = threadIdx.x + j * kBlock;
+                bv[j] = bias ? bias[e < E ? e : 0] : 0.0f;
+            }
+        },
+        [&]() {
+            if (NORM) {
+                uint16_t *x16 = reinterpret_cast<uint16_t *>(xs);
+                const bool pub = x_out && blockIdx.x == 0;
+                rr.finish(d, eps, [&](int e, uint16_t v) {
+                    x16[e] = v;
+                    if (pub)
+                        x_out[e] = v;
+                });
+            } else {
+                st.store(xs, d >> 3);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = threadIdx.x + j * kBlock;
+                if (e < E)
+                    bs[e] = bv[j];
+            }
             __syncthreads();
         });
     for (int i = threadIdx.x; i < 8 * (g1 - g0); i += kBlock) {
@@ -383,6 +437,11 @@ static void launch_gemv1(const uint16_t *x, const uint16_t *W, int N, int K, Epi
         k_gemv1<7, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
     else
         k_gemv1<8, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
+}
+
+void launch_rmsnorm(const float *h32, int b, int d, const uint16_t *gamma, float eps, uint16_t *y,
+                    hipStream_t s) {
+    k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y);
 }
 
 bool gemv1_f32_fits(int N, int K) {
@@ -489,6 +548,10 @@ static size_t oproj_part_offset(int b, int d) {
     return kHeadBytes + align_up((size_t)b * d * sizeof(float), 256);
 }
 
+extern "C" const float *k3_oproj_residual_h32(const void *workspace) {
+    return workspace ? (const float *)((const char *)workspace + oproj_h32_offset()) : nullptr;
+}
+
 extern "C" size_t k3_oproj_residual_workspace_size(int b, int K, int d) {
     (void)K;
     if (b <= 0 || d <= 0)
@@ -510,24 +573,50 @@ bool rls_fits(int b, int d, int E) {
     return dot2_fits(b, d) && (size_t)b * d * 2 + (size_t)E * 4 <= 65536;
 }
 
+static size_t rls_gemv_lds(int d, int E, int NL, int Is, int grid, int &ps_stride) {
+    ps_stride = rls_gemv_ps_stride(E, NL, Is, grid);
+    return (size_t)d * 2 + ((size_t)4 * ps_stride + E) * sizeof(float);
+}
+
+static int rls_gemv_grid(int E, int NL, int Is, int cu_budget) {
+    return budget_grid((E + 7) / 8 + (NL + 7) / 8 + Is / 4, cu_budget, 2);
+}
+
+bool rls_gemv_fits(int d, int E, int NL, int Is) {
+    int ps_stride;
+    return gemv_fits(d) && Is % 4 == 0 && d % 4 == 0 &&
+           rls_gemv_lds(d, E, NL, Is, rls_gemv_grid(E, NL, Is, 0), ps_stride) <= 65536;
+}
+
 void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
-                hipStream_t s, int cu_budget) {
-    if (b == 1 && gemv_fits(d) && Is % 4 == 0) {
-        const int total = (E + 7) / 8 + (NL + 7) / 8 + Is / 4;
-        const int grid = budget_grid(total, cu_budget, 2);
-        const int ps_stride = rls_gemv_ps_stride(E, NL, Is, grid);
-        const size_t lds = (size_t)d * 2 + ((size_t)4 * ps_stride + E) * sizeof(float);
-        if (lds <= 65536) {
-            if (gv_unit_pieces(d) == 7)
-                k_rls_gemv1<7><<<grid, kBlock, lds, s>>>(x, d, w_router, bias, E, logits, w_lat,
-                                                         NL, z, w13s, Is, hs, ps_stride);
+                hipStream_t s, int cu_budget, const NormIn *norm) {
+    if (b == 1 && rls_gemv_fits(d, E, NL, Is)) {
+        const int grid = rls_gemv_grid(E, NL, Is, cu_budget);
+        int ps_stride;
+        const size_t lds = rls_gemv_lds(d, E, NL, Is, grid, ps_stride);
+        const float *h32 = norm ? norm->h32 : nullptr;
+        const uint16_t *gamma = norm ? norm->gamma : nullptr;
+        const float eps = norm ? norm->eps : 0.0f;
+        uint16_t *x_out = norm ? norm->x_out : nullptr;
+#define K3_RLSG(U_, N_)                                                                        \
+    k_rls_gemv1<U_, N_><<<grid, kBlock, lds, s>>>(x, d, w_router, bias, E, logits, w_lat, NL, z, \
+                                                  w13s, Is, hs, ps_stride, h32, gamma, eps,     \
+                                                  x_out)
+        if (gv_unit_pieces(d) == 7) {
+            if (norm)
+                K3_RLSG(7, true);
             else
-                k_rls_gemv1<8><<<grid, kBlock, lds, s>>>(x, d, w_router, bias, E, logits, w_lat,
-                                                         NL, z, w13s, Is, hs, ps_stride);
-            return;
+                K3_RLSG(7, false);
+        } else {
+            if (norm)
+                K3_RLSG(8, true);
+            else
+                K3_RLSG(8, false);
         }
+#undef K3_RLSG
+        return;
     }
     const int cus = budget_grid(1 << 30, 0, 2);
     const int grid = (NL > 0 || Is > 0) ? cus : (E + kBlock / kWave - 1) / (kBlock / kWave);
@@ -692,7 +781,7 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
                                  const uint16_t *w_o, int d, uint16_t *residual,
                                  const uint16_t *gamma, float eps, uint16_t *y_norm,
                                  void *workspace, size_t ws_bytes, void *stream) {
-    if (!a || !w_o || !residual || !gamma || !y_norm)
+    if (!a || !w_o || !residual || (y_norm && !gamma))
         return K3_ERR_INVALID_ARG;
     if (b <= 0 || K <= 0 || d <= 0 || lda < K || !(eps >= 0.0f))
         return K3_ERR_INVALID_ARG;
@@ -731,7 +820,8 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
             k_oproj_gemv1<8><<<gg.grid, kBlock, gg.lds, s>>>(a, w_o, d, K, gg.ps_stride, residual,
                                                              h32);
         trace_end(K3_OP_OPROJ_RESIDUAL, s);
-        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
+        if (y_norm)
+            k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     } else if (variant == K3_VARIANT_DOT2) {
 #define K3_OPROJ(TM_, CB_)                                                                     \
     k_oproj_dot2<TM_, CB_><<<g.grid, kBlock, g.lds, s>>>(a, lda, b, w_o, d, K, rows_blk, \
@@ -750,12 +840,14 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
             K3_OPROJ(kDot2MaxTokens, 1);
 #undef K3_OPROJ
         trace_end(K3_OP_OPROJ_RESIDUAL, s);
-        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
+        if (y_norm)
+            k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     } else {
         sk_oproj_residual(a, lda, b, K, w_o, d, residual, h32,
                           (float *)((char *)workspace + oproj_part_offset(b, d)), s);
         trace_end(K3_OP_OPROJ_RESIDUAL, s);
-        k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
+        if (y_norm)
+            k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
     }
     const int st = launch_status();
     if (st == K3_OK)

@@ -819,28 +819,36 @@ extern "C" int k3_shared_expert(const uint16_t *x, int64_t ldx, int b, int d, co
     return st;
 }
 
-extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
-                            const uint16_t *w_router, const float *bias, int E, int k,
-                            const uint16_t *w_lat, int d_lat, const uint16_t *w13,
-                            const uint16_t *w2, int I, const uint16_t *w13_s,
-                            const uint16_t *w2_s, int I_s, int32_t *topk_ids, float *topk_w,
-                            uint16_t *z, int64_t ldz, float *y_s, uint16_t *y, void *workspace,
-                            size_t ws_bytes, void *stream) {
-    if (!x || !w_router || !w_lat || !w13 || !w2 || !w13_s || !w2_s || !topk_ids || !topk_w ||
-        !z || !y_s || !y)
+// The block on x, or, with nin, on x = RMSNorm(nin->h32) * gamma (x is then
+// nin->x_out when that is not null, else xbuf in the workspace).
+static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int b, int d,
+                         const uint16_t *w_router, const float *bias, int E, int k,
+                         const uint16_t *w_lat, int d_lat, const uint16_t *w13,
+                         const uint16_t *w2, int I, const uint16_t *w13_s, const uint16_t *w2_s,
+                         int I_s, int32_t *topk_ids, float *topk_w, uint16_t *z, int64_t ldz,
+                         float *y_s, uint16_t *y, void *workspace, size_t ws_bytes,
+                         void *stream) {
+    if ((!x && !nin) || !w_router || !w_lat || !w13 || !w2 || !w13_s || !w2_s || !topk_ids ||
+        !topk_w || !z || !y_s || !y)
         return K3_ERR_INVALID_ARG;
+    if (nin && (!nin->h32 || !nin->gamma || !(nin->eps >= 0.0f)))
+        return K3_ERR_INVALID_ARG;
+    if (nin)
+        ldx = d;
     if (b <= 0 || d <= 0 || E <= 0 || k <= 0 || d_lat <= 0 || I <= 0 || I_s <= 0 || ldx < d ||
         ldz < d_lat)
         return K3_ERR_INVALID_ARG;
     const int chk = check_moe_shapes(b, d_lat, k, E, I, d, ldz);
     if (chk != K3_OK)
         return chk;
-    if (d % 128 || d > 8192 || I_s % 128 || I_s > 8192 || ldx % 8 || !aligned16(x) ||
+    if (d % 128 || d > 8192 || I_s % 128 || I_s > 8192 || ldx % 8 || (x && !aligned16(x)) ||
         !aligned16(w_router) || !aligned16(w_lat) || !aligned16(w13) || !aligned16(w2) ||
-        !aligned16(w13_s) || !aligned16(w2_s) || !aligned16(z))
+        !aligned16(w13_s) || !aligned16(w2_s) || !aligned16(z) ||
+        (nin && (!aligned16(nin->h32) || (nin->x_out && !aligned16(nin->x_out)))))
         return K3_ERR_UNSUPPORTED;
     const BlockWorkspace L = block_workspace_layout(b, E, k, I, d, d_lat, I_s);
-    if (!workspace || ws_bytes < L.total || !aligned16(workspace))
+    const size_t need = L.total + (nin ? align_up((size_t)b * d * sizeof(uint16_t), 256) : 0);
+    if (!workspace || ws_bytes < need || !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     int variant = forced_variant(K3_OP_MOE_BLOCK);
     const bool fits = b <= kDot2MaxTokens && rls_fits(b, d, E) &&
@@ -854,14 +862,23 @@ extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
     char *ws = (char *)workspace;
     float *logits = (float *)(ws + L.logits);
     uint16_t *hs = (uint16_t *)(ws + L.hs);
+    const bool fast = variant == K3_VARIANT_DOT2 && b == 1 && I_s == I &&
+                      up_b1_fits(d_lat, k, I, 0) && down_b1_fits(k, I, d, true, 0);
+    const bool norm_in_pass = nin && fast && rls_gemv_fits(d, E, d_lat, I_s);
+    if (nin && !norm_in_pass) {
+        // the norm as its own kernel, into x_out or the workspace
+        uint16_t *xb = nin->x_out ? nin->x_out : (uint16_t *)(ws + L.total);
+        launch_rmsnorm(nin->h32, b, d, nin->gamma, nin->eps, xb, s);
+        x = xb;
+    }
     trace_begin(K3_OP_MOE_BLOCK, s);
-    if (variant == K3_VARIANT_DOT2 && b == 1 && I_s == I &&
-        up_b1_fits(d_lat, k, I, 0) && down_b1_fits(k, I, d, true, 0)) {
-        // 1. router, latent and shared gate/up rows in one pass over x;
+    if (fast) {
+        // 1. router, latent and shared gate/up rows in one pass over x (with
+        //    the norm of its input folded in when it comes as h32);
         // 2. expert selection and routed gate/up;
         // 3. routed and shared down rows with the combine
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, w13_s, I_s, hs,
-                   s);
+                   s, 0, norm_in_pass ? nin : nullptr);
         trace_end(K3_OP_MOE_BLOCK, s);
         uint16_t *hbuf = (uint16_t *)(ws + L.moe + moe_workspace_layout(b, E, k, I, d).hbuf);
         trace_begin(K3_OP_MOE_EXPERTS, s);
@@ -925,4 +942,38 @@ extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
     if (st == K3_OK)
         record_dispatch(K3_OP_MOE_BLOCK, variant);
     return st;
+}
+
+extern "C" int k3_moe_block(const uint16_t *x, int64_t ldx, int b, int d,
+                            const uint16_t *w_router, const float *bias, int E, int k,
+                            const uint16_t *w_lat, int d_lat, const uint16_t *w13,
+                            const uint16_t *w2, int I, const uint16_t *w13_s,
+                            const uint16_t *w2_s, int I_s, int32_t *topk_ids, float *topk_w,
+                            uint16_t *z, int64_t ldz, float *y_s, uint16_t *y, void *workspace,
+                            size_t ws_bytes, void *stream) {
+    if (!x)
+        return K3_ERR_INVALID_ARG;
+    return moe_block_run(x, ldx, nullptr, b, d, w_router, bias, E, k, w_lat, d_lat, w13, w2, I,
+                         w13_s, w2_s, I_s, topk_ids, topk_w, z, ldz, y_s, y, workspace, ws_bytes,
+                         stream);
+}
+
+extern "C" size_t k3_moe_block_rmsnorm_workspace_size(int b, int d, int E, int k, int d_lat,
+                                                      int I, int I_s) {
+    const size_t w = k3_moe_block_workspace_size(b, d, E, k, d_lat, I, I_s);
+    return w ? w + align_up((size_t)b * d * sizeof(uint16_t), 256) : 0;
+}
+
+extern "C" int k3_moe_block_rmsnorm(const float *h32, int b, int d, const uint16_t *gamma,
+                                    float eps, uint16_t *x_out, const uint16_t *w_router,
+                                    const float *bias, int E, int k, const uint16_t *w_lat,
+                                    int d_lat, const uint16_t *w13, const uint16_t *w2, int I,
+                                    const uint16_t *w13_s, const uint16_t *w2_s, int I_s,
+                                    int32_t *topk_ids, float *topk_w, uint16_t *z, int64_t ldz,
+                                    float *y_s, uint16_t *y, void *workspace, size_t ws_bytes,
+                                    void *stream) {
+    const NormIn nin{h32, gamma, eps, x_out};
+    return moe_block_run(nullptr, d, &nin, b, d, w_router, bias, E, k, w_lat, d_lat, w13, w2, I,
+                         w13_s, w2_s, I_s, topk_ids, topk_w, z, ldz, y_s, y, workspace, ws_bytes,
+                         stream);
 }

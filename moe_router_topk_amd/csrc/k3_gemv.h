@@ -28,17 +28,45 @@ __device__ __forceinline__ float gv_red8(float v) {
 // pieces (K % 256 == 0); 7 or 8 divide the common widths exactly.
 constexpr int gv_unit_pieces(int K) { return (K / 256) % 8 == 0 ? 8 : ((K / 256) % 7 == 0 ? 7 : 8); }
 
+// Two-phase staging of n 16-byte vectors of one buffer into LDS: load()
+// issues all the loads at once (vectors past n read nothing: their offsets
+// leave the range), store() writes them. A kernel issues the loads before
+// its first weight loads and stores them after: vector loads retire in
+// order, so waiting for these then never waits for the weights.
+template <int M>
+struct GvStage {
+    u32x4 v[M];
+    __device__ __forceinline__ void load(const uint16_t *base, int n) {
+        const rsrc_t r = act_range(uniform_ptr(base));
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const int i = threadIdx.x + j * kBlock;
+            // past n: the sign bit of n - 1 - i (arithmetic, so no branch)
+            v[j] = ld_act16(r, ((uint32_t)i * 16u) | ((uint32_t)(n - 1 - i) & 0x80000000u));
+        }
+    }
+    __device__ __forceinline__ void store(u32x4 *dst, int n) const {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const int i = threadIdx.x + j * kBlock;
+            if (i < n)
+                dst[i] = v[j];
+        }
+    }
+};
+
 // Streams the workgroup's groups. grp(g, base, nrows, skip): the 8-row
 // group g starts at base, rows K elements apart, and has nrows valid rows
 // (<= 8); rows 4..7 sit skip rows further on (a gate/up pair group: four
 // gate rows, then the four matching up rows of the same columns).
 // xv(g, kv): the activation vector kv (8 elements) group g multiplies.
 // ps[w * ps_stride + 8 g + r]: wave w's partial sum of row r of group g.
-// pre(): runs once after the first loads are issued (stage activations
-// there; the caller's barrier follows) -- it must end with __syncthreads().
-template <int U, class Grp, class XV, class Pre>
+// first(): runs before the first weight loads are issued (issue the
+// activation loads there, GvStage::load); pre(): runs right after them (store
+// the activations to LDS) and must end with __syncthreads().
+template <int U, class Grp, class XV, class First, class Pre>
 __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv, float *ps,
-                                             int ps_stride, Pre pre) {
+                                             int ps_stride, First first, Pre pre) {
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
     int p0, p1;
     split_range(K >> 6, kBlock / kWave, wq, p0, p1);
@@ -92,6 +120,7 @@ __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv,
     // masked activations), so the loop has a single exit and every load is
     // issued on every path: the waits then count exactly the loads behind.
     u32x4 A[U], B[U];
+    first();
     load(A, 0);
     pre();
     for (int u = 0; u < nunits; u += 2) {

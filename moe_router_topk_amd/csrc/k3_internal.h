@@ -40,10 +40,23 @@ MoeWorkspace moe_workspace_layout(int b, int E, int k, int I, int d_out);
 
 // Dense launchers defined in dense.hip, shared with the fused MoE block.
 bool rls_fits(int b, int d, int E);
+// The router+latent+shared pass may normalise its input itself: x =
+// RMSNorm(h32) * gamma, written to x_out too when that is not null (one
+// token, only where rls_gemv_fits).
+struct NormIn {
+    const float *h32;
+    const uint16_t *gamma;
+    float eps;
+    uint16_t *x_out;
+};
+bool rls_gemv_fits(int d, int E, int NL, int Is);
 void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
-                hipStream_t s, int cu_budget = 0);
+                hipStream_t s, int cu_budget = 0, const NormIn *norm = nullptr);
+// y[t] = RMSNorm(h32[t]) * gamma, bf16, one workgroup per token.
+void launch_rmsnorm(const float *h32, int b, int d, const uint16_t *gamma, float eps, uint16_t *y,
+                    hipStream_t s);
 // One token on the 8-row engine: y[n] = x . W[n] in fp32, n < N (K % 64 == 0).
 bool gemv1_f32_fits(int N, int K);
 void launch_gemv1_f32(const uint16_t *x, const uint16_t *W, int N, int K, float *y, int cu_budget,

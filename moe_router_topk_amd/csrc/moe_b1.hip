@@ -69,7 +69,7 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
             nr = e >= 0 ? 8 : 0;
             skip = I - 4;
         },
-        [&](int, int kv) { return zs[kv]; }, ps, ps_stride, [&]() {});
+        [&](int, int kv) { return zs[kv]; }, ps, ps_stride, [&]() {}, [&]() {});
     for (int i = threadIdx.x; i < 8 * (g1 - g0); i += kBlock) {
         const int r = i & 7, vg = g0 + (i >> 3), a = vg / gpe, j = 4 * (vg - a * gpe) + r;
         if (r < 4 && sid[a] >= 0)
@@ -103,6 +103,13 @@ k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__
     int rb0, rb1;
     split_range(d_out, gridDim.x, blockIdx.x, rb0, rb1);
     const int rows = rb1 - rb0, gps = (rows + 7) >> 3;
+    // the slots' h rows: the k routed rows are contiguous in hbuf (staged in
+    // registers before the first weight loads when they fit), the shared one
+    // is hs
+    const bool early = k * nv <= 8 * kBlock && nv <= kBlock;
+    GvStage<8> sr;
+    GvStage<1> ss;
+    float yv = 0.0f;
     gemv8_stream<U>(
         ns * gps, I,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
@@ -120,10 +127,30 @@ k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__
         },
         [&](int g, int kv) { return hl[min(g / gps, ns - 1) * nv + kv]; }, ps, ps_stride,
         [&]() {
-            stage_rows(hl, nv, ns, nv,
-                       [&](int j) { return j < k ? hbuf + (int64_t)j * I : hs; });
-            for (int i = threadIdx.x; i < rows; i += kBlock)
-                ya[i] = y_add ? y_add[rb0 + i] : 0.0f;
+            if (early) {
+                sr.load(hbuf, k * nv);
+                if (w2s)
+                    ss.load(hs, nv);
+            }
+            if (y_add && rows <= kBlock)
+                yv = y_add[rb0 + min((int)threadIdx.x, rows - 1)];
+        },
+        [&]() {
+            if (early) {
+                sr.store(hl, k * nv);
+                if (w2s)
+                    ss.store(hl + k * nv, nv);
+            } else {
+                stage_rows(hl, nv, ns, nv,
+                           [&](int j) { return j < k ? hbuf + (int64_t)j * I : hs; });
+            }
+            if (rows <= kBlock) {
+                if ((int)threadIdx.x < rows)
+                    ya[threadIdx.x] = yv;
+            } else {
+                for (int i = threadIdx.x; i < rows; i += kBlock)
+                    ya[i] = y_add ? y_add[rb0 + i] : 0.0f;
+            }
             if (threadIdx.x < k) {
                 const int e = ids[threadIdx.x];
                 sv[threadIdx.x] = e >= 0 && e < E;

@@ -3,7 +3,8 @@
 "Hyper Optimizing Kimi K3 in vLLM", Part 1:
   section 1 -- attention input projection (k3_proj_skinny);
   section 2 -- output projection fused with the attention residual
-               (k3_oproj_residual, here with the RMSNorm that feeds the MoE);
+               (k3_oproj_residual; the RMSNorm that feeds the MoE runs in the
+               block's first kernel, k3_moe_block_rmsnorm);
   section 3 -- router scores and latent projection from the same input, then
                the routed experts; the shared expert on a separate stream,
                overlapping routing and the routed experts, with a bounded
@@ -20,8 +21,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (k3_moe_block, k3_moe_experts, k3_oproj_residual, k3_prefetch, k3_proj_skinny,
-               k3_router_topk_latent, k3_shared_expert, workspace_size)
+from . import (k3_moe_block, k3_moe_block_rmsnorm, k3_moe_experts, k3_oproj_residual,
+               k3_prefetch, k3_proj_skinny, k3_router_topk_latent, k3_shared_expert,
+               oproj_h32_view, workspace_size)
 
 
 class DecodeLayer:
@@ -53,7 +55,8 @@ class DecodeLayer:
         self.ws_moe = torch.empty(
             workspace_size("moe_experts", b=b_max, d_in=d_lat, E=E, k=k, I=I, d_out=d), **u8)
         self.ws_shared = torch.empty(workspace_size("shared_expert", b=b_max, d=d, I=I_s), **u8)
-        self.ws_block = torch.empty(workspace_size("moe_block", b=b_max, d=d, E=E, k=k,
+        # sized for the block that normalises its own input (the larger one)
+        self.ws_block = torch.empty(workspace_size("moe_block_rmsnorm", b=b_max, d=d, E=E, k=k,
                                                    d_lat=d_lat, I=I, I_s=I_s), **u8)
         self.ids = torch.empty((b_max, k), dtype=torch.int32, device=dev)
         self.wts = torch.empty((b_max, k), dtype=torch.float32, device=dev)
@@ -122,6 +125,30 @@ class DecodeLayer:
                           y_norm=x_moe, workspace=self.ws_oproj)
         return x_moe
 
+    def attn_chain_h32(self, x: torch.Tensor, residual: torch.Tensor) -> torch.Tensor:
+        """As attn_chain without the norm: returns the fp32 h (a view into the
+        o-projection's workspace) for moe_block_rmsnorm."""
+        c = self.chain_w
+        b = x.shape[0]
+        q = self.q[:b]
+        k3_proj_skinny(x, c["w_in"], y=q, workspace=self.ws_proj)
+        k3_oproj_residual(q[:, :self.k_o], c["w_o"], residual, None, self.eps,
+                          workspace=self.ws_oproj, norm=False)
+        return oproj_h32_view(self.ws_oproj, b, self.d)
+
+    def moe_block_rmsnorm(self, h32: torch.Tensor) -> torch.Tensor:
+        """The MoE block on RMSNorm(h32) * gamma, normalised inside the block
+        (k3_moe_block_rmsnorm); the normalised input lands in x_moe."""
+        b = h32.shape[0]
+        assert b <= self.b_max
+        m = self.moe
+        y, _, _, _, _ = k3_moe_block_rmsnorm(
+            h32, self.chain_w["gamma"], self.eps, m["w_router"], m["bias"], self.k, m["w_lat"],
+            m["w13"], m["w2"], m["w13_s"], m["w2_s"], x_out=self.x_moe[:b],
+            topk_ids=self.ids[:b], topk_w=self.wts[:b], z=self.z[:b], y_s=self.y_s[:b],
+            y=self.y[:b], workspace=self.ws_block)
+        return y
+
     PREFETCH_KEYS = ("w_router", "w_lat")
 
     def step(self, x: torch.Tensor, residual: torch.Tensor, prefetch: bool = False):
@@ -137,8 +164,9 @@ class DecodeLayer:
             for key in self.PREFETCH_KEYS:
                 k3_prefetch(self.moe[key], cu_budget=self.prefetch_cu, stream=self.pf_stream)
             self.ev_side_done.record(self.pf_stream)
-        h = self.attn_chain(x, residual)
-        y = self.moe_block(h)
+        # the chain leaves the fp32 h; the block normalises it in its first
+        # kernel (one kernel boundary less than attn_chain + moe_block)
+        y = self.moe_block_rmsnorm(self.attn_chain_h32(x, residual))
         if prefetch:
             main.wait_event(self.ev_side_done)
         return y

@@ -521,6 +521,41 @@ def test_moe_block_matches_stream_composition(k3, full, b, zipf):
     assert torch.equal(y2, y1)
 
 
+@pytest.mark.parametrize("b", [1, 3, 16])
+def test_moe_block_rmsnorm_matches_composition(k3, full, chain_w, b):
+    """k3_moe_block_rmsnorm on the o-projection's fp32 h gives the same bits
+    as k3_oproj_residual's y_norm fed to k3_moe_block (batch 1 folds the norm
+    into the block's first kernel; larger batches run it on its own)."""
+    cfg, w = full
+    d, K = cfg.d, chain_w["w_o"].shape[1]
+    a = synth.randn_bf16((b, K), 1.0, 4, "bn_a", b, device=DEV)
+    r = synth.randn_bf16((b, d), 1.0, 4, "bn_r", b, device=DEV)
+    g = chain_w["gamma"]
+    r1, r2 = r.clone(), r.clone()
+    y_norm = k3.k3_oproj_residual(a, chain_w["w_o"], r1, g, 1e-6)
+    y1, ids1, wts1, z1, ys1 = k3.k3_moe_block(y_norm, w["w_router"], None, cfg.k, w["w_lat"],
+                                              w["w13"], w["w2"], w["w13_s"], w["w2_s"])
+    ws = torch.empty(k3.workspace_size("oproj_residual", b=b, K=K, d=d), dtype=torch.uint8,
+                     device=DEV)
+    assert k3.k3_oproj_residual(a, chain_w["w_o"], r2, None, 1e-6, workspace=ws,
+                                norm=False) is None
+    h32 = k3.oproj_h32_view(ws, b, d)
+    x_out = torch.empty((b, d), dtype=torch.bfloat16, device=DEV)
+    y2, ids2, wts2, z2, ys2 = k3.k3_moe_block_rmsnorm(
+        h32, g, 1e-6, w["w_router"], None, cfg.k, w["w_lat"], w["w13"], w["w2"], w["w13_s"],
+        w["w2_s"], x_out=x_out)
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2)
+    assert torch.equal(x_out, y_norm)
+    assert torch.equal(ids1, ids2) and torch.equal(wts1, wts2) and torch.equal(z1, z2)
+    assert torch.equal(ys1, ys2) and torch.equal(y1, y2)
+    # without x_out the block keeps x in its workspace
+    y3 = k3.k3_moe_block_rmsnorm(h32, g, 1e-6, w["w_router"], None, cfg.k, w["w_lat"], w["w13"],
+                                 w["w2"], w["w13_s"], w["w2_s"])[0]
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y1)
+
+
 def test_layer_step_chain_then_moe(k3, full, chain_w):
     """Chain + MoE block at b = 1, the benchmark's step, against the oracle."""
     from moe_router_topk_amd.layer import DecodeLayer
