@@ -149,7 +149,7 @@ def write_traffic_summary(pmc_dir: str) -> int:
     pmc_copy_fetch, pmc_copy_write, made by the commands recorded in the
     output) to HBM bytes per launch of the dominant kernel at b = 1."""
     import synth
-    name = "k_moe_up_b1<true>"
+    name = "k_moe_up_b1<true"
     fetch = pmc_values(os.path.join(pmc_dir, "pmc_fetch"), "FETCH_SIZE", name)
     write = pmc_values(os.path.join(pmc_dir, "pmc_write"), "WRITE_SIZE", name)
     cf = pmc_values(os.path.join(pmc_dir, "pmc_copy_fetch"), "FETCH_SIZE", COPY_KERNEL)
