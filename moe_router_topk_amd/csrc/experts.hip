@@ -277,6 +277,7 @@ k_down_dot2(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict
 // rows; the sums go to part[p][n]. A down launch may carry one extra dense
 // job after the list: the shared expert's down projection into y_s.
 struct SkExperts {
+    int tpw = 1;  // 16-row tiles per wave of the launch (a wave streams 16 tpw rows)
     ExpertList L;
     ExpertList L2;  // a second list after L (its n may be null: none)
     const uint16_t *w;  // expert e: w + e * w_stride, [rows][K] (gate/up: [2I][K])
@@ -310,7 +311,9 @@ struct SkExperts {
         return n1() + (L2.n ? __builtin_amdgcn_readfirstlane(L2.count()) : 0);
     }
     __device__ int count() const { return nlist() + (w_x ? 1 : 0); }
-    __device__ int tiles() const { return pair ? I / 32 : (rows + kSkRows - 1) / kSkRows; }
+    __device__ int tiles() const {
+        return pair ? I / (32 * tpw) : (rows + 64 * tpw - 1) / (64 * tpw);
+    }
     __device__ Job job(int a) const {
         if (w_x && a == nlist())
             return Job{xT, 0, 0, true};
@@ -325,20 +328,23 @@ struct SkExperts {
     }
     __device__ void wave_rows(const Job &jb, int tile, int wq, const uint16_t *&wr,
                               int &n) const {
+        const int wr_rows = 16 * tpw;  // the wave's rows (tpw tiles of 16)
         if (jb.extra) {
-            const int r0 = tile * kSkRows + wq * 16;
-            n = max(0, min(16, rows - r0));
+            const int r0 = tile * 4 * wr_rows + wq * wr_rows;
+            n = max(0, min(wr_rows, rows - r0));
             wr = w_x + (int64_t)(n > 0 ? r0 : 0) * K;
             return;
         }
         const uint16_t *base = w + (int64_t)jb.e * w_stride;
         if (pair) {
-            const int r = wq < 2 ? 32 * tile + 16 * wq : I + 32 * tile + 16 * (wq - 2);
-            n = 16;
+            // waves 0-1 stream gate rows j, waves 2-3 the matching up rows I + j
+            const int j0 = 2 * wr_rows * tile;
+            const int r = wq < 2 ? j0 + wr_rows * wq : I + j0 + wr_rows * (wq - 2);
+            n = wr_rows;
             wr = base + (int64_t)r * K;
         } else {
-            const int r0 = tile * kSkRows + wq * 16;
-            n = max(0, min(16, rows - r0));
+            const int r0 = tile * 4 * wr_rows + wq * wr_rows;
+            n = max(0, min(wr_rows, rows - r0));
             wr = base + (int64_t)(n > 0 ? r0 : 0) * K;
         }
     }
@@ -353,12 +359,14 @@ struct SkExperts {
         return L.token(jb.p0 + t);
     }
     __device__ int xld(const Job &jb) const { return (int)(jb.extra ? ldx_x : ldx); }
+    // Epilogue of tile tt of the wave's tpw tiles.
     template <int MT>
-    __device__ void store(const Job &jb, int tile, int, int wq, const f32x4 (&acc)[MT],
+    __device__ void store(const Job &jb, int tile, int, int wq, int tt, const f32x4 (&acc)[MT],
                           float (*xch)[MT][4][kWave]) const {
         const int lane = threadIdx.x & (kWave - 1);
         const int g = lane >> 4, rl = lane & 15;
         const int T = jb.T;
+        const int wr_rows = 16 * tpw;
         if (pair) {
             if (wq >= 2)
 #pragma unroll
@@ -368,7 +376,7 @@ struct SkExperts {
                         xch[wq - 2][mt][i][lane] = acc[mt][i];
             __syncthreads();
             if (wq < 2) {
-                const int j = 32 * tile + 16 * wq + rl;
+                const int j = 2 * wr_rows * tile + wr_rows * wq + 16 * tt + rl;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -379,9 +387,10 @@ struct SkExperts {
                                 f32_to_bf16(silu(acc[mt][i]) * xch[wq][mt][i][lane]);
                     }
             }
+            __syncthreads();  // xch is read before the next tile's exchange
             return;
         }
-        const int n = tile * kSkRows + wq * 16 + rl;
+        const int n = tile * 4 * wr_rows + wq * wr_rows + 16 * tt + rl;
         if (n >= rows)
             return;
         float *o = jb.extra ? out_x : out + (int64_t)jb.p0 * rows;
@@ -593,20 +602,25 @@ struct OutDense {  // y_s[t][r] = s (positions are tokens for the dense list)
     __device__ void operator()(int p, int r, float s) const { y[(int64_t)p * d + r] = s; }
 };
 
-// Heavy-expert launch: up to `items` (job, tile) items, fewer when fewer
-// experts are heavy.
-void launch_sk_experts(const SkExperts &J, int b, int items, int cu_budget, hipStream_t s) {
+// Expert launch over at most max_jobs jobs. At 64 tokens a wave streams two
+// 16-row tiles per chunk (half the token staging and token reads per weight
+// byte); below, one.
+void launch_sk_experts(SkExperts J, int b, int max_jobs, int cu_budget, hipStream_t s) {
+    const int mt = sk_mt(b);
+    J.tpw = mt == 4 ? 2 : 1;
+    const int tiles = J.pair ? J.I / (32 * J.tpw) : (J.rows + 64 * J.tpw - 1) / (64 * J.tpw);
+    const int items = max_jobs * tiles;
     // two workgroups per compute unit, each streaming its items back to back
     const int grid = budget_grid(items < 1 ? 1 : items, cu_budget, 2);
-    switch (sk_mt(b)) {
+    switch (mt) {
     case 1:
-        k_sk_gemm_stream<1, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        k_sk_gemm_stream<1, SkExperts, 1><<<grid, kBlock, 0, s>>>(J, J.K, 1);
         break;
     case 2:
-        k_sk_gemm_stream<2, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        k_sk_gemm_stream<2, SkExperts, 1><<<grid, kBlock, 0, s>>>(J, J.K, 1);
         break;
     default:
-        k_sk_gemm_stream<4, SkExperts><<<grid, kBlock, 0, s>>>(J, J.K, 1);
+        k_sk_gemm_stream<4, SkExperts, 2><<<grid, kBlock, 0, s>>>(J, J.K, 1);
         break;
     }
 }
@@ -689,7 +703,7 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
             J.ldx = ldz;
             J.gather = true;
             J.h = hbuf;
-            launch_sk_experts(J, b, max_heavy * (I / 32), cu_budget, s);
+            launch_sk_experts(J, b, max_heavy, cu_budget, s);
         }
         trace_end(trace_op, s);
         if (!all_mfma)
@@ -713,7 +727,7 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
                 J.out_x = extra->out_x;
             }
             const int jobs = (any_heavy ? max_heavy : 0) + (extra ? 1 : 0);
-            launch_sk_experts(J, b, jobs * ((d_out + kSkRows - 1) / kSkRows), cu_budget, s);
+            launch_sk_experts(J, b, jobs, cu_budget, s);
         }
         if (y_add_ready)
             (void)hipStreamWaitEvent(s, y_add_ready, 0);

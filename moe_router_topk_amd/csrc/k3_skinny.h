@@ -81,6 +81,51 @@ __device__ __forceinline__ void sk_mfma_chunk(f32x4 (&acc)[MT], const u32x4 (&bu
     }
 }
 
+// The same with TPW 16-row tiles per wave (the wave's 16 TPW contiguous
+// rows) over a K chunk of kSkKc / TPW: load u holds tile u / (8 / TPW),
+// piece (u / 2) % (4 / TPW), half u % 2. With TPW = 2 a staged token chunk
+// and each token operand read from LDS serve twice the weight rows.
+template <int TPW>
+__device__ __forceinline__ void sk_wload_t(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K,
+                                           int lane) {
+    constexpr int KC = kSkKc / TPW, PP = KC / 64;
+    const int r8 = lane & 7, q = lane >> 3;
+#pragma unroll
+    for (int u = 0; u < kSkKb; ++u) {
+        const int tt = u / (2 * PP), p = (u / 2) % PP;
+        const int row = 16 * tt + 8 * (u & 1) + r8;
+        const int k = c * KC + 64 * p + 8 * q;
+        const uint32_t past = (uint32_t)(K - 1 - k) & 0x80000000u;
+        buf[u] = ld_weight16(rw, ((uint32_t)(row * K + k) * 2u) | past);
+    }
+}
+
+template <int MT, int TPW>
+__device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32x4 (&buf)[kSkKb],
+                                                const u32x4 (&xs)[MT * 16][kSkKc / TPW / 8 + 1],
+                                                int mt_n, int lane) {
+    constexpr int PP = kSkKc / TPW / 64;
+    const int g = lane >> 4, rl = lane & 15;
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+        u32x4 b0[TPW], b1[TPW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+            sk_pair(buf[tt * 2 * PP + 2 * p], buf[tt * 2 * PP + 2 * p + 1], b0[tt], b1[tt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            if (mt < mt_n) {
+                const u32x4 a0 = xs[mt * 16 + rl][8 * p + 2 * g];
+                const u32x4 a1 = xs[mt * 16 + rl][8 * p + 2 * g + 1];
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt) {
+                    acc[tt][mt] = mfma16x16x32(a0, b0[tt], acc[tt][mt]);
+                    acc[tt][mt] = mfma16x16x32(a1, b1[tt], acc[tt][mt]);
+                }
+            }
+    }
+}
+
 // Jobs policy (see SkDense and the expert jobs in experts.hip):
 //   int  count()                          jobs in this launch (may read device memory)
 //   int  tiles()                          tile slots per job
@@ -217,20 +262,24 @@ struct SkCursor {
     bool valid;
 };
 
-template <int MT, class Jobs>
+// TPW 16-row tiles per wave (1 or 2; J.tpw must equal it): chunks of
+// kSkKc / TPW, every staged token chunk serving 64 TPW weight rows.
+template <int MT, class Jobs, int TPW = 1>
 __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ksplit) {
+    constexpr int KC = kSkKc / TPW;  // K per chunk
+    constexpr int KQ = KC / 8;       // 16-byte vectors per token row of a chunk
     // two token buffers (units alternate); +1 vector per row keeps the MFMA
     // reads conflict-free
-    __shared__ u32x4 xs[2][MT * 16][kSkKq + 1];
+    __shared__ u32x4 xs[2][MT * 16][KQ + 1];
     __shared__ float xch[2][MT][4][kWave];  // epilogue exchange between waves
-    constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
+    constexpr int SQ = MT * 16 * KQ / kBlock;  // staged vectors per thread per chunk
     using Job = typename Jobs::Job;
     using Cur = SkCursor<Job>;
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
-    const int nchunks = (K + kSkKc - 1) / kSkKc;
+    const int nchunks = (K + KC - 1) / KC;
     const int per_job = J.tiles() * ksplit;
     const int items = J.count() * per_job;
-    const int vq = threadIdx.x % kSkKq;
+    const int vq = threadIdx.x % KQ;
 
     auto open = [&](Cur &u, int from) {
         u.valid = false;
@@ -261,7 +310,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     };
 
     // token cursor: this thread stages vectors q = tid + j * 256 of each
-    // chunk (token q / kSkKq, vector q % kSkKq); rows past T read zeros
+    // chunk (token q / KQ, vector q % KQ); rows past T read zeros
     // xr holds the rows as read: they are first used by the next token load,
     // a step later, so waiting for a row lookup never waits for the weight
     // loads issued after it
@@ -274,7 +323,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
         xld = u.valid ? (uint32_t)J.xld(u.jb) : 0u;
 #pragma unroll
         for (int j = 0; j < SQ; ++j) {
-            const int t = (threadIdx.x + j * kBlock) / kSkKq;
+            const int t = (threadIdx.x + j * kBlock) / KQ;
             xv[j] = u.valid && t < u.jb.T;
             xr[j] = J.xrow(u.jb, xv[j] ? t : 0);  // an empty cursor has T = 0: row 0
         }
@@ -288,11 +337,11 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
         // turns every load into a loop over lanes
         const uint32_t wbytes =
             u.valid ? (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u : 0u;
-        sk_wload(buf, weight_range(uniform_ptr(wr), wbytes), u.c, K, lane);
+        sk_wload_t<TPW>(buf, weight_range(uniform_ptr(wr), wbytes), u.c, K, lane);
     };
     auto aload = [&](u32x4 (&st)[SQ], const Cur &u) {
         const rsrc_t rx = act_range(uniform_ptr(xb));
-        const int k = u.c * kSkKc + 8 * vq;
+        const int k = u.c * KC + 8 * vq;
         const bool kv = u.valid && k < K;
 #pragma unroll
         for (int j = 0; j < SQ; ++j)
@@ -303,13 +352,15 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
 #pragma unroll
         for (int j = 0; j < SQ; ++j) {
             const int q = threadIdx.x + j * kBlock;
-            xs[b][q / kSkKq][q % kSkKq] = st[j];
+            xs[b][q / KQ][q % KQ] = st[j];
         }
     };
-    f32x4 acc[MT];
+    f32x4 acc[TPW][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Cur C, W, A;  // multiply, weights (one ahead), tokens (two ahead)
     open(C, blockIdx.x);
@@ -345,13 +396,17 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
         wload(nbuf, W);
         sk_keep_order();
         const int mt_n = C.valid ? min((C.jb.T + 15) >> 4, MT) : 0;
-        sk_mfma_chunk<MT>(acc, buf, xs[b], mt_n, lane);
+        sk_mfma_chunk_t<MT, TPW>(acc, buf, xs[b], mt_n, lane);
         if (C.valid && C.c + 1 >= C.c1) {
-            // acc[mt][i] = out[token 16 mt + 4 g + i][row rl of this wave's 16]
-            J.store(C.jb, C.tile, C.ks, wq, acc, xch);
+            // acc[tt][mt][i] = out[token 16 mt + 4 g + i][row rl of the
+            // wave's tile tt]
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < TPW; ++tt) {
+                J.store(C.jb, C.tile, C.ks, wq, tt, acc[tt], xch);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
         astore(st, b ^ 1);
         aload(st, A);
