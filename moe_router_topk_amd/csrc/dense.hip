@@ -247,117 +247,139 @@ k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gam
 // ------------------------------------------------------------------ batch 1 (k3_gemv.h)
 // Shares of the rows per workgroup and the LDS layout of the 8-row engine:
 // x (K / 8 vectors), then the four quarters' partial sums [4][ps_stride],
-// then (o-proj) the residuals of the share.
+// then (o-proj) the residuals of the share, for nt tokens.
 struct GemvGeom {
     int grid, ps_stride;
     size_t lds;
 };
 
-static GemvGeom gemv_geom(int N, int K, bool resid, int cu_budget = 0) {
+static GemvGeom gemv_geom(int N, int K, bool resid, int cu_budget = 0, int nt = 1) {
     GemvGeom g;
     g.grid = budget_grid(N, cu_budget, 2);
     const int rows = (N + g.grid - 1) / g.grid;
     g.ps_stride = (rows + 7) / 8 * 8;
-    g.lds = (size_t)K * 2 + (size_t)(4 + (resid ? 1 : 0)) * g.ps_stride * sizeof(float);
+    g.lds = (size_t)nt * K * 2 + (size_t)(4 + (resid ? 1 : 0)) * nt * g.ps_stride * sizeof(float);
     return g;
 }
 
 // The 8-row engine takes K in 64-element pieces.
 static bool gemv_fits(int K) { return K % 64 == 0 && K <= 8192; }
 
-// y[n] = epi(x . W[n]) for one token.
-template <int U, class Epi>
+// y[t][n] = epi(t, n, x[t] . W[n]) for NT (1..4) tokens, rows ldx apart.
+template <int U, int NT, class Epi>
 __global__ void __launch_bounds__(kBlock)
-k_gemv1(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, int N, int K,
-        int ps_stride, Epi epi) {
-    extern __shared__ u32x4 xs[];
-    float *ps = reinterpret_cast<float *>(xs + (K >> 3));
+k_gemv(const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ W, int N,
+       int K, int ps_stride, Epi epi) {
+    extern __shared__ u32x4 xs[];  // NT token rows, then ps[4][NT][ps_stride]
+    const int nv = K >> 3;
+    float *ps = reinterpret_cast<float *>(xs + NT * nv);
     int r0, r1;
     split_range(N, gridDim.x, blockIdx.x, r0, r1);
-    GvStage<4> st;  // K <= 8192
-    gemv8_stream<U>(
+    GvStage<4> st[NT];  // K <= 8192
+    gemv8_stream<U, NT>(
         (r1 - r0 + 7) >> 3, K,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
             base = W + (int64_t)(r0 + 8 * g) * K;
             nr = min(8, r1 - r0 - 8 * g);
             skip = 0;
         },
-        [&](int, int kv) { return xs[kv]; }, ps, ps_stride, [&]() { st.load(x, K >> 3); },
+        [&](int, int kv, int t) { return xs[t * nv + kv]; }, ps, ps_stride,
         [&]() {
-            st.store(xs, K >> 3);
-            __syncthreads();
-        });
-    for (int i = threadIdx.x; i < r1 - r0; i += kBlock)
-        epi(0, r0 + i, gv_total(ps, ps_stride, i));
-}
-
-// Output projection + residual for one token: h = r + a . Wo^T, written as
-// fp32 (for the norm) and bf16 (back into r). The share's residuals are
-// staged beside a while the first weights load.
-template <int U>
-__global__ void __launch_bounds__(kBlock)
-k_oproj_gemv1(const uint16_t *__restrict__ a, const uint16_t *__restrict__ Wo, int d, int K,
-              int ps_stride, uint16_t *res, float *__restrict__ h32) {
-    extern __shared__ u32x4 xs[];
-    float *ps = reinterpret_cast<float *>(xs + (K >> 3));
-    float *rs = ps + 4 * ps_stride;
-    int r0, r1;
-    split_range(d, gridDim.x, blockIdx.x, r0, r1);
-    GvStage<4> st;  // K <= 8192
-    uint16_t rv = 0;  // this thread's residual (thread i < the share's rows)
-    gemv8_stream<U>(
-        (r1 - r0 + 7) >> 3, K,
-        [&](int g, const uint16_t *&base, int &nr, int &skip) {
-            base = Wo + (int64_t)(r0 + 8 * g) * K;
-            nr = min(8, r1 - r0 - 8 * g);
-            skip = 0;
-        },
-        [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
-        [&]() {
-            st.load(a, K >> 3);
-            rv = res[r0 + min((int)threadIdx.x, r1 - r0 - 1)];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                st[t].load(x + (int64_t)t * ldx, nv);
         },
         [&]() {
-            st.store(xs, K >> 3);
-            if ((int)threadIdx.x < r1 - r0)
-                rs[threadIdx.x] = bf16_to_f32(rv);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                st[t].store(xs + t * nv, nv);
             __syncthreads();
         });
-    for (int i = threadIdx.x; i < r1 - r0; i += kBlock) {
-        const float h = rs[i] + gv_total(ps, ps_stride, i);
-        h32[r0 + i] = h;
-        res[r0 + i] = f32_to_bf16(h);
+    const int rows = r1 - r0;
+    for (int q = threadIdx.x; q < NT * rows; q += kBlock) {
+        const int t = q / rows, i = q - t * rows;
+        epi(t, r0 + i, gv_total(ps, ps_stride, i, NT, t));
     }
 }
 
-// One token's pass over x for every row set that reads it (as k_rls_dot2):
+// Output projection + residual for NT (1..4) tokens: h = r + a . Wo^T,
+// written as fp32 (for the norm) and bf16 (back into r). The share's
+// residuals are staged beside a while the first weights load (thread q
+// holds residual q of the NT x rows share; NT * rows <= the block size).
+template <int U, int NT>
+__global__ void __launch_bounds__(kBlock)
+k_oproj_gemv(const uint16_t *__restrict__ a, int64_t lda, const uint16_t *__restrict__ Wo,
+             int d, int K, int ps_stride, uint16_t *res, float *__restrict__ h32) {
+    extern __shared__ u32x4 xs[];  // NT rows of a, ps[4][NT][ps_stride], rs[NT * rows]
+    const int nv = K >> 3;
+    float *ps = reinterpret_cast<float *>(xs + NT * nv);
+    float *rs = ps + 4 * NT * ps_stride;
+    int r0, r1;
+    split_range(d, gridDim.x, blockIdx.x, r0, r1);
+    const int rows = r1 - r0;
+    GvStage<4> st[NT];  // K <= 8192
+    uint16_t rv = 0;
+    gemv8_stream<U, NT>(
+        (rows + 7) >> 3, K,
+        [&](int g, const uint16_t *&base, int &nr, int &skip) {
+            base = Wo + (int64_t)(r0 + 8 * g) * K;
+            nr = min(8, rows - 8 * g);
+            skip = 0;
+        },
+        [&](int, int kv, int t) { return xs[t * nv + kv]; }, ps, ps_stride,
+        [&]() {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                st[t].load(a + (int64_t)t * lda, nv);
+            const int q = min((int)threadIdx.x, NT * rows - 1), t = q / rows;
+            rv = res[(int64_t)t * d + r0 + (q - t * rows)];
+        },
+        [&]() {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                st[t].store(xs + t * nv, nv);
+            if ((int)threadIdx.x < NT * rows)
+                rs[threadIdx.x] = bf16_to_f32(rv);
+            __syncthreads();
+        });
+    for (int q = threadIdx.x; q < NT * rows; q += kBlock) {
+        const int t = q / rows, i = q - t * rows;
+        const float h = rs[q] + gv_total(ps, ps_stride, i, NT, t);
+        h32[(int64_t)t * d + r0 + i] = h;
+        res[(int64_t)t * d + r0 + i] = f32_to_bf16(h);
+    }
+}
+
+// The pass of NT (1..4) tokens over x for every row set that reads it (as
+// k_rls_dot2):
 // E router rows (fp32 logits + bias), NL latent rows (z, bf16) and Is shared
 // gate/up row pairs (h_s = silu(gate) * up, bf16). The rows form one
 // sequence of 8-row groups -- router, latent, then shared pair groups (gate
 // rows 4q .. 4q + 3 with up rows Is + 4q .. Is + 4q + 3) -- split evenly
-// over the workgroups. Each row is summed in the same order as k_gemv1, so
+// over the workgroups. Each row is summed in the same order as k_gemv, so
 // logits and z match the separate calls bit for bit.
-// With NORM the input is x = RMSNorm(h32) * gamma (as k_rmsnorm computes it),
-// normalised by every workgroup while its first weights load; workgroup 0
-// also writes x to x_out when that is not null.
-template <int U, bool NORM>
+// With NORM (one token) the input is x = RMSNorm(h32) * gamma (as k_rmsnorm
+// computes it), normalised by every workgroup while its first weights load;
+// workgroup 0 also writes x to x_out when that is not null.
+template <int U, int NT, bool NORM>
 __global__ void __launch_bounds__(kBlock)
-k_rls_gemv1(const uint16_t *__restrict__ x, int d, const uint16_t *__restrict__ Wr,
+k_rls_gemv(const uint16_t *__restrict__ x, int64_t ldx, int d, const uint16_t *__restrict__ Wr,
             const float *__restrict__ bias, int E, float *__restrict__ logits,
             const uint16_t *__restrict__ Wl, int NL, uint16_t *__restrict__ z,
             const uint16_t *__restrict__ W13s, int Is, uint16_t *__restrict__ hs,
             int ps_stride, const float *__restrict__ h32, const uint16_t *__restrict__ gamma,
-            float eps, uint16_t *__restrict__ x_out) {
-    extern __shared__ u32x4 xs[];
-    float *ps = reinterpret_cast<float *>(xs + (d >> 3));
-    float *bs = ps + 4 * ps_stride;
+            float eps, uint16_t *__restrict__ x_out, int64_t ldz) {
+    extern __shared__ u32x4 xs[];  // NT token rows, then ps[4][NT][ps_stride], then bias
+    const int nv = d >> 3;
+    float *ps = reinterpret_cast<float *>(xs + NT * nv);
+    float *bs = ps + 4 * NT * ps_stride;
     const int Gr = (E + 7) >> 3, Gl = (NL + 7) >> 3, Gs = Is >> 2;
     int g0, g1;
     split_range(Gr + Gl + Gs, gridDim.x, blockIdx.x, g0, g1);
-    GvStage<4> st;  // d <= 8192
+    GvStage<4> st[NT];  // d <= 8192
     RmsRow rr;
     float bv[4];    // router bias, E <= 1024
-    gemv8_stream<U>(
+    gemv8_stream<U, NT>(
         g1 - g0, d,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
             const int vg = g0 + g;
@@ -375,12 +397,15 @@ k_rls_gemv1(const uint16_t *__restrict__ x, int d, const uint16_t *__restrict__ 
                 skip = Is - 4;
             }
         },
-        [&](int, int kv) { return xs[kv]; }, ps, ps_stride,
+        [&](int, int kv, int t) { return xs[t * nv + kv]; }, ps, ps_stride,
         [&]() {
-            if (NORM)
+            if (NORM) {
                 rr.load(h32, d, gamma);
-            else
-                st.load(x, d >> 3);
+            } else {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    st[t].load(x + (int64_t)t * ldx, nv);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int e = threadIdx.x + j * kBlock;
@@ -397,7 +422,9 @@ k_rls_gemv1(const uint16_t *__restrict__ x, int d, const uint16_t *__restrict__ 
                         x_out[e] = v;
                 });
             } else {
-                st.store(xs, d >> 3);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    st[t].store(xs + t * nv, nv);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -407,19 +434,22 @@ k_rls_gemv1(const uint16_t *__restrict__ x, int d, const uint16_t *__restrict__ 
             }
             __syncthreads();
         });
-    for (int i = threadIdx.x; i < 8 * (g1 - g0); i += kBlock) {
+    const int nrow = 8 * (g1 - g0);
+    for (int q = threadIdx.x; q < NT * nrow; q += kBlock) {
+        const int t = q / nrow, i = q - t * nrow;
         const int vg = g0 + (i >> 3), r = i & 7;
         if (vg < Gr) {
             const int e = 8 * vg + r;
             if (e < E)
-                logits[e] = gv_total(ps, ps_stride, i) + bs[e];
+                logits[(int64_t)t * E + e] = gv_total(ps, ps_stride, i, NT, t) + bs[e];
         } else if (vg < Gr + Gl) {
             const int n = 8 * (vg - Gr) + r;
             if (n < NL)
-                z[n] = f32_to_bf16(gv_total(ps, ps_stride, i));
+                z[(int64_t)t * ldz + n] = f32_to_bf16(gv_total(ps, ps_stride, i, NT, t));
         } else if (r < 4) {
-            hs[4 * (vg - Gr - Gl) + r] =
-                f32_to_bf16(silu(gv_total(ps, ps_stride, i)) * gv_total(ps, ps_stride, i + 4));
+            hs[(int64_t)t * Is + 4 * (vg - Gr - Gl) + r] =
+                f32_to_bf16(silu(gv_total(ps, ps_stride, i, NT, t)) *
+                            gv_total(ps, ps_stride, i + 4, NT, t));
         }
     }
 }
@@ -429,14 +459,59 @@ static int rls_gemv_ps_stride(int E, int NL, int Is, int grid) {
     return 8 * ((total + grid - 1) / grid);
 }
 
-template <class Epi>
-static void launch_gemv1(const uint16_t *x, const uint16_t *W, int N, int K, Epi epi,
-                         hipStream_t s, int cu_budget = 0) {
-    const GemvGeom g = gemv_geom(N, K, false, cu_budget);
+// The 8-row engine serves b tokens while their rows (and the partial sums)
+// fit 64 KB of LDS; the o-projection also needs b x rows <= the block size.
+static bool gemv_fits_b(int b, int N, int K, bool resid, int cu_budget = 0) {
+    if (b < 1 || b > kDot2MaxTokens || !gemv_fits(K))
+        return false;
+    const GemvGeom g = gemv_geom(N, K, resid, cu_budget, b);
+    return g.lds <= 65536 && (!resid || b * g.ps_stride <= kBlock);
+}
+
+template <int NT, class Epi>
+static void launch_gemv_nt(const uint16_t *x, int64_t ldx, const uint16_t *W, int N, int K,
+                           Epi epi, hipStream_t s, int cu_budget) {
+    const GemvGeom g = gemv_geom(N, K, false, cu_budget, NT);
     if (gv_unit_pieces(K) == 7)
-        k_gemv1<7, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
+        k_gemv<7, NT, Epi><<<g.grid, kBlock, g.lds, s>>>(x, ldx, W, N, K, g.ps_stride, epi);
     else
-        k_gemv1<8, Epi><<<g.grid, kBlock, g.lds, s>>>(x, W, N, K, g.ps_stride, epi);
+        k_gemv<8, NT, Epi><<<g.grid, kBlock, g.lds, s>>>(x, ldx, W, N, K, g.ps_stride, epi);
+}
+
+// y[t][n] = epi(t, n, x[t] . W[n]) for b <= 4 tokens (gemv_fits_b).
+template <class Epi>
+static void launch_gemv(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N, int K,
+                        Epi epi, hipStream_t s, int cu_budget = 0) {
+    if (b == 1)
+        launch_gemv_nt<1>(x, ldx, W, N, K, epi, s, cu_budget);
+    else if (b == 2)
+        launch_gemv_nt<2>(x, ldx, W, N, K, epi, s, cu_budget);
+    else if (b == 3)
+        launch_gemv_nt<3>(x, ldx, W, N, K, epi, s, cu_budget);
+    else
+        launch_gemv_nt<4>(x, ldx, W, N, K, epi, s, cu_budget);
+}
+
+template <int NT>
+static void launch_oproj_gemv_nt(const uint16_t *a, int64_t lda, const uint16_t *W, int d, int K,
+                                 uint16_t *res, float *h32, hipStream_t s) {
+    const GemvGeom g = gemv_geom(d, K, true, 0, NT);
+    if (gv_unit_pieces(K) == 7)
+        k_oproj_gemv<7, NT><<<g.grid, kBlock, g.lds, s>>>(a, lda, W, d, K, g.ps_stride, res, h32);
+    else
+        k_oproj_gemv<8, NT><<<g.grid, kBlock, g.lds, s>>>(a, lda, W, d, K, g.ps_stride, res, h32);
+}
+
+static void launch_oproj_gemv(const uint16_t *a, int64_t lda, int b, const uint16_t *W, int d,
+                              int K, uint16_t *res, float *h32, hipStream_t s) {
+    if (b == 1)
+        launch_oproj_gemv_nt<1>(a, lda, W, d, K, res, h32, s);
+    else if (b == 2)
+        launch_oproj_gemv_nt<2>(a, lda, W, d, K, res, h32, s);
+    else if (b == 3)
+        launch_oproj_gemv_nt<3>(a, lda, W, d, K, res, h32, s);
+    else
+        launch_oproj_gemv_nt<4>(a, lda, W, d, K, res, h32, s);
 }
 
 void launch_rmsnorm(const float *h32, int b, int d, const uint16_t *gamma, float eps, uint16_t *y,
@@ -444,14 +519,12 @@ void launch_rmsnorm(const float *h32, int b, int d, const uint16_t *gamma, float
     k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y);
 }
 
-bool gemv1_f32_fits(int N, int K) {
-    return gemv_fits(K) && gemv_geom(N, K, false).lds <= 65536;
-}
+bool gemv1_f32_fits(int N, int K) { return gemv_fits_b(1, N, K, false); }
 
 // One token, y[n] = x . W[n] in fp32 (the shared expert's down projection).
 void launch_gemv1_f32(const uint16_t *x, const uint16_t *W, int N, int K, float *y, int cu_budget,
                       hipStream_t s) {
-    launch_gemv1(x, W, N, K, EpiLogits{y, N, nullptr}, s, cu_budget);
+    launch_gemv(x, K, 1, W, N, K, EpiLogits{y, N, nullptr}, s, cu_budget);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -495,8 +568,8 @@ static void launch_dense_dot2_t(const uint16_t *x, int64_t ldx, int b, const uin
 template <class Epi>
 static void launch_dense_dot2(const uint16_t *x, int64_t ldx, int b, const uint16_t *W, int N,
                               int K, Epi epi, hipStream_t s) {
-    if (b == 1 && gemv_fits(K) && gemv_geom(N, K, false).lds <= 65536)
-        launch_gemv1(x, W, N, K, epi, s);
+    if (gemv_fits_b(b, N, K, false))
+        launch_gemv(x, ldx, b, W, N, K, epi, s);
     else if (b == 1)
         launch_dense_dot2_t<1>(x, ldx, b, W, N, K, epi, s);
     else
@@ -573,48 +646,54 @@ bool rls_fits(int b, int d, int E) {
     return dot2_fits(b, d) && (size_t)b * d * 2 + (size_t)E * 4 <= 65536;
 }
 
-static size_t rls_gemv_lds(int d, int E, int NL, int Is, int grid, int &ps_stride) {
+static size_t rls_gemv_lds(int nt, int d, int E, int NL, int Is, int grid, int &ps_stride) {
     ps_stride = rls_gemv_ps_stride(E, NL, Is, grid);
-    return (size_t)d * 2 + ((size_t)4 * ps_stride + E) * sizeof(float);
+    return (size_t)nt * d * 2 + ((size_t)4 * nt * ps_stride + E) * sizeof(float);
 }
 
 static int rls_gemv_grid(int E, int NL, int Is, int cu_budget) {
     return budget_grid((E + 7) / 8 + (NL + 7) / 8 + Is / 4, cu_budget, 2);
 }
 
-bool rls_gemv_fits(int d, int E, int NL, int Is) {
+bool rls_gemv_fits(int b, int d, int E, int NL, int Is) {
     int ps_stride;
-    return gemv_fits(d) && Is % 4 == 0 && d % 4 == 0 &&
-           rls_gemv_lds(d, E, NL, Is, rls_gemv_grid(E, NL, Is, 0), ps_stride) <= 65536;
+    return b >= 1 && b <= kDot2MaxTokens && gemv_fits(d) && Is % 4 == 0 && d % 4 == 0 &&
+           rls_gemv_lds(b, d, E, NL, Is, rls_gemv_grid(E, NL, Is, 0), ps_stride) <= 65536;
 }
 
 void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,
                 hipStream_t s, int cu_budget, const NormIn *norm) {
-    if (b == 1 && rls_gemv_fits(d, E, NL, Is)) {
+    if (rls_gemv_fits(b, d, E, NL, Is) && (b == 1 || !norm)) {
         const int grid = rls_gemv_grid(E, NL, Is, cu_budget);
         int ps_stride;
-        const size_t lds = rls_gemv_lds(d, E, NL, Is, grid, ps_stride);
+        const size_t lds = rls_gemv_lds(b, d, E, NL, Is, grid, ps_stride);
         const float *h32 = norm ? norm->h32 : nullptr;
         const uint16_t *gamma = norm ? norm->gamma : nullptr;
         const float eps = norm ? norm->eps : 0.0f;
         uint16_t *x_out = norm ? norm->x_out : nullptr;
-#define K3_RLSG(U_, N_)                                                                        \
-    k_rls_gemv1<U_, N_><<<grid, kBlock, lds, s>>>(x, d, w_router, bias, E, logits, w_lat, NL, z, \
-                                                  w13s, Is, hs, ps_stride, h32, gamma, eps,     \
-                                                  x_out)
+#define K3_RLSG(U_, T_, N_)                                                                    \
+    k_rls_gemv<U_, T_, N_><<<grid, kBlock, lds, s>>>(x, ldx, d, w_router, bias, E, logits,     \
+                                                      w_lat, NL, z, w13s, Is, hs, ps_stride,   \
+                                                      h32, gamma, eps, x_out, ldz)
+#define K3_RLSB(U_)                                                                            \
+    if (b == 1 && norm)                                                                        \
+        K3_RLSG(U_, 1, true);                                                                  \
+    else if (b == 1)                                                                           \
+        K3_RLSG(U_, 1, false);                                                                 \
+    else if (b == 2)                                                                           \
+        K3_RLSG(U_, 2, false);                                                                 \
+    else if (b == 3)                                                                           \
+        K3_RLSG(U_, 3, false);                                                                 \
+    else                                                                                       \
+        K3_RLSG(U_, 4, false)
         if (gv_unit_pieces(d) == 7) {
-            if (norm)
-                K3_RLSG(7, true);
-            else
-                K3_RLSG(7, false);
+            K3_RLSB(7);
         } else {
-            if (norm)
-                K3_RLSG(8, true);
-            else
-                K3_RLSG(8, false);
+            K3_RLSB(8);
         }
+#undef K3_RLSB
 #undef K3_RLSG
         return;
     }
@@ -810,15 +889,8 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
     hipStream_t s = (hipStream_t)stream;
     float *h32 = (float *)((char *)workspace + oproj_h32_offset());
     trace_begin(K3_OP_OPROJ_RESIDUAL, s);
-    if (variant == K3_VARIANT_DOT2 && b == 1 && gemv_fits(K) &&
-        gemv_geom(d, K, true).lds <= 65536) {
-        const GemvGeom gg = gemv_geom(d, K, true);
-        if (gv_unit_pieces(K) == 7)
-            k_oproj_gemv1<7><<<gg.grid, kBlock, gg.lds, s>>>(a, w_o, d, K, gg.ps_stride, residual,
-                                                             h32);
-        else
-            k_oproj_gemv1<8><<<gg.grid, kBlock, gg.lds, s>>>(a, w_o, d, K, gg.ps_stride, residual,
-                                                             h32);
+    if (variant == K3_VARIANT_DOT2 && gemv_fits_b(b, d, K, true)) {
+        launch_oproj_gemv(a, lda, b, w_o, d, K, residual, h32, s);
         trace_end(K3_OP_OPROJ_RESIDUAL, s);
         if (y_norm)
             k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);

@@ -745,15 +745,18 @@ void run_shared_expert(int variant, const uint16_t *x, int64_t ldx, int b, int d
     const DenseList dl{b};
     const OutDense out{y_s, d};
     trace_begin(trace_op, s);
-    if (variant == K3_VARIANT_DOT2 && b == 1 && rls_fits(1, d, 0) && I % 4 == 0 &&
-        gemv1_f32_fits(d, I)) {
-        // the 8-row engine, summing in the same order as the fused block's
-        // shared rows (gate/up in the router+latent pass, down in the routed
-        // down kernel)
-        launch_rls(x, ldx, 1, d, nullptr, nullptr, 0, nullptr, nullptr, 0, nullptr, 0, w13, I, hbuf,
+    if (variant == K3_VARIANT_DOT2 && rls_fits(b, d, 0) && rls_gemv_fits(b, d, 0, 0, I) &&
+        (b > 1 || gemv1_f32_fits(d, I))) {
+        // gate/up on the 8-row engine, summing in the same order as the
+        // fused block's router+latent+shared pass; the down rows as the
+        // block sums them (one token: in the routed down kernel's order)
+        launch_rls(x, ldx, b, d, nullptr, nullptr, 0, nullptr, nullptr, 0, nullptr, 0, w13, I, hbuf,
                    s, cu_budget);
         trace_end(trace_op, s);
-        launch_gemv1_f32(hbuf, w2, d, I, y_s, cu_budget, s);
+        if (b == 1)
+            launch_gemv1_f32(hbuf, w2, d, I, y_s, cu_budget, s);
+        else
+            launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d, dl, out, cu_budget, s);
     } else if (variant == K3_VARIANT_DOT2) {
         const int tm = b == 1 ? 1 : kDot2MaxTokens;
         launch_gateup_dot2(tm, x, ldx, d, w13, I, dl, hbuf, cu_budget, s);
@@ -878,7 +881,7 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
     uint16_t *hs = (uint16_t *)(ws + L.hs);
     const bool fast = variant == K3_VARIANT_DOT2 && b == 1 && I_s == I &&
                       up_b1_fits(d_lat, k, I, 0) && down_b1_fits(k, I, d, true, 0);
-    const bool norm_in_pass = nin && fast && rls_gemv_fits(d, E, d_lat, I_s);
+    const bool norm_in_pass = nin && fast && rls_gemv_fits(1, d, E, d_lat, I_s);
     if (nin && !norm_in_pass) {
         // the norm as its own kernel, into x_out or the workspace
         uint16_t *xb = nin->x_out ? nin->x_out : (uint16_t *)(ws + L.total);

@@ -64,7 +64,9 @@ struct GvStage {
 // first(): runs before the first weight loads are issued (issue the
 // activation loads there, GvStage::load); pre(): runs right after them (store
 // the activations to LDS) and must end with __syncthreads().
-template <int U, class Grp, class XV, class First, class Pre>
+// NT tokens (1..4): xv(g, kv, t) is token t's vector; the partial sums of
+// token t sit at ps[(w * NT + t) * ps_stride + 8 g + r].
+template <int U, int NT = 1, class Grp, class XV, class First, class Pre>
 __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv, float *ps,
                                              int ps_stride, First first, Pre pre) {
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
@@ -96,7 +98,10 @@ __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv,
             b[i] = ld_weight16(r, ((uint32_t)(row * K + p * 64 + el) * 2u) | past);
         }
     };
-    float acc = 0.0f;
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        acc[t] = 0.0f;
     auto fin = [&](u32x4 (&b)[U], int u) {
         const int g = u / upg, c = u - g * upg;
 #pragma unroll
@@ -106,14 +111,21 @@ __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv,
             // make the compiler wait for every load in flight)
             const int p = p0 + c * U + i;
             const uint32_t m = (p < p1 && u < nunits) ? 0xffffffffu : 0u;
-            const u32x4 xa = xv(g, min(p, p1 - 1) * 8 + (lane & 7));
-            acc = dot8(b[i], u32x4{xa.x & m, xa.y & m, xa.z & m, xa.w & m}, acc);
+            const int kv = min(p, p1 - 1) * 8 + (lane & 7);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const u32x4 xa = xv(g, kv, t);
+                acc[t] = dot8(b[i], u32x4{xa.x & m, xa.y & m, xa.z & m, xa.w & m}, acc[t]);
+            }
         }
         if (c == upg - 1) {
-            const float s = gv_red8(acc);
-            acc = 0.0f;
-            if (g < ngroups && (lane & 7) == 0)
-                ps[wq * ps_stride + 8 * g + rl] = s;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float s = gv_red8(acc[t]);
+                acc[t] = 0.0f;
+                if (g < ngroups && (lane & 7) == 0)
+                    ps[(wq * NT + t) * ps_stride + 8 * g + rl] = s;
+            }
         }
     };
     // Units run in pairs; an odd count ends with an empty unit (no weights,
@@ -134,9 +146,12 @@ __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv,
     __syncthreads();  // every quarter's partials are in ps
 }
 
-// The four quarter sums of row i of the share, in wave order.
-__device__ __forceinline__ float gv_total(const float *ps, int ps_stride, int i) {
-    return ((ps[i] + ps[ps_stride + i]) + ps[2 * ps_stride + i]) + ps[3 * ps_stride + i];
+// The four quarter sums of row i of the share, in wave order (token t of NT).
+__device__ __forceinline__ float gv_total(const float *ps, int ps_stride, int i, int NT = 1,
+                                          int t = 0) {
+    const float *q = ps + (int64_t)t * ps_stride + i;
+    const int64_t w = (int64_t)NT * ps_stride;
+    return ((q[0] + q[w]) + q[2 * w]) + q[3 * w];
 }
 
 }  // namespace k3

@@ -43,13 +43,14 @@ bool rls_fits(int b, int d, int E);
 // The router+latent+shared pass may normalise its input itself: x =
 // RMSNorm(h32) * gamma, written to x_out too when that is not null (one
 // token, only where rls_gemv_fits).
+// rls_gemv_fits: the pass runs on the 8-row engine for these b (<= 4) tokens.
 struct NormIn {
     const float *h32;
     const uint16_t *gamma;
     float eps;
     uint16_t *x_out;
 };
-bool rls_gemv_fits(int d, int E, int NL, int Is);
+bool rls_gemv_fits(int b, int d, int E, int NL, int Is);
 void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_router,
                 const float *bias, int E, float *logits, const uint16_t *w_lat, int NL,
                 uint16_t *z, int64_t ldz, const uint16_t *w13s, int Is, uint16_t *hs,

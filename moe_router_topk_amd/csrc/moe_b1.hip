@@ -69,7 +69,7 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
             nr = e >= 0 ? 8 : 0;
             skip = I - 4;
         },
-        [&](int, int kv) { return zs[kv]; }, ps, ps_stride, [&]() {}, [&]() {});
+        [&](int, int kv, int) { return zs[kv]; }, ps, ps_stride, [&]() {}, [&]() {});
     for (int i = threadIdx.x; i < 8 * (g1 - g0); i += kBlock) {
         const int r = i & 7, vg = g0 + (i >> 3), a = vg / gpe, j = 4 * (vg - a * gpe) + r;
         if (r < 4 && sid[a] >= 0)
@@ -125,7 +125,7 @@ k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__
                 nr = min(8, rows - 8 * gg);
             }
         },
-        [&](int g, int kv) { return hl[min(g / gps, ns - 1) * nv + kv]; }, ps, ps_stride,
+        [&](int g, int kv, int) { return hl[min(g / gps, ns - 1) * nv + kv]; }, ps, ps_stride,
         [&]() {
             if (early) {
                 sr.load(hbuf, k * nv);

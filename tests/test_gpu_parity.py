@@ -178,20 +178,22 @@ def test_proj_skinny_ragged(k3, variant, b, K, N):
     assert_rel_close(y.cpu(), oracle.linear(x.cpu(), W.cpu()), "y")
 
 
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
 @pytest.mark.parametrize("K,N", [(64, 24), (128, 40), (192, 17), (320, 9), (7168, 13),
                                  (8192, 1000)])
-def test_batch1_engine_short_and_uneven_rows(k3, K, N):
-    """One token on the 8-row engine: K-quarters that are empty (K < 256) or
-    uneven (K / 64 not a multiple of 4), partial 8-row groups, and fewer rows
-    than workgroups."""
-    x = synth.randn_bf16((1, K), 1.0, 9, "b1e_x", K * 100 + N, device=DEV)
+def test_row_engine_short_and_uneven_rows(k3, K, N, b):
+    """1..4 tokens on the 8-row engine: K-quarters that are empty (K < 256)
+    or uneven (K / 64 not a multiple of 4), partial 8-row groups, and fewer
+    rows than workgroups; token rows ldx apart."""
+    xb = synth.randn_bf16((b, K + 64), 1.0, 9, "b1e_x", K * 100 + N + b, device=DEV)
+    x = xb[:, 32:32 + K]
     W = synth.randn_bf16((N, K), 1 / math.sqrt(K), 9, "b1e_w", K * 100 + N, device=DEV)
     y = k3.k3_proj_skinny(x, W)
     torch.cuda.synchronize()
     assert k3.k3_get_last_dispatch("proj_skinny") == "dot2"
     assert_rel_close(y.cpu(), oracle.linear(x.cpu(), W.cpu()), "y")
     # the o-projection with residual and RMSNorm on the same shapes (d = N)
-    r = synth.randn_bf16((1, N), 1.0, 9, "b1e_r", K * 100 + N, device=DEV)
+    r = synth.randn_bf16((b, N), 1.0, 9, "b1e_r", K * 100 + N + b, device=DEV)
     g = (synth.randn_bf16((N,), 0.1, 9, "b1e_g", K * 100 + N, device=DEV).float() + 1).to(
         torch.bfloat16)
     r0 = r.clone()
@@ -219,7 +221,7 @@ def test_proj_skinny_strided_output(k3, chain_w):
 
 
 # ---------------------------------------------------------------- shared expert
-@pytest.mark.parametrize("b", [1, 2, 16, 64])
+@pytest.mark.parametrize("b", [1, 2, 4, 16, 64])
 def test_shared_expert_full(k3, full, b):
     cfg, w = full
     x = synth.make_tokens(cfg, device=DEV, index=300 + b, b=b)
