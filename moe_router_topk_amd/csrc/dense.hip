@@ -22,6 +22,7 @@
 #include "k3_device.h"
 #include "k3_gemv.h"
 #include "k3_internal.h"
+#include "k3_skinny.h"
 
 namespace k3 {
 
@@ -191,8 +192,19 @@ k_oproj_dot2(const uint16_t *__restrict__ a, int64_t lda, int b, const uint16_t 
 // element e of y to out(e, bf16).
 constexpr int kNormVec = 8;
 struct RmsRow {
-    f32x4 v[kNormVec];
+    f32x4 v[kNormVec];  // thread i holds elements 4 (i + 256 j) .. + 3
     uint16_t gm[kNormVec][4];
+    __device__ __forceinline__ void load_gamma(int d, const uint16_t *__restrict__ gamma) {
+        const int n4 = d >> 2;
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j) {
+            const int i = threadIdx.x + j * kBlock;
+            const int ic = i < n4 ? i : 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                gm[j][q] = gamma[4 * ic + q];
+        }
+    }
     __device__ __forceinline__ void load(const float *__restrict__ h32, int d,
                                          const uint16_t *__restrict__ gamma) {
         const f32x4 *h = reinterpret_cast<const f32x4 *>(h32);
@@ -200,12 +212,9 @@ struct RmsRow {
 #pragma unroll
         for (int j = 0; j < kNormVec; ++j) {
             const int i = threadIdx.x + j * kBlock;
-            const int ic = i < n4 ? i : 0;
-            v[j] = h[ic];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                gm[j][q] = gamma[4 * ic + q];
+            v[j] = h[i < n4 ? i : 0];
         }
+        load_gamma(d, gamma);
     }
     template <class Out>
     __device__ __forceinline__ void finish(int d, float eps, Out out) const {
@@ -241,6 +250,56 @@ k_rmsnorm(const float *__restrict__ h32, int d, const uint16_t *__restrict__ gam
     uint16_t *yt = y + (int64_t)t * d;
     RmsRow rr;
     rr.load(h32 + (int64_t)t * d, d, gamma);
+    rr.finish(d, eps, [&](int e, uint16_t v) { yt[e] = v; });
+}
+
+// The o-projection's finish fused with the norm, one workgroup per token:
+// h = r + the K ranges' fp32 partial sums (added in range order, as
+// k_sk_finish adds them), r <- bf16(h), h32 <- h, y = RMSNorm(h) * gamma (as
+// k_rmsnorm computes it). part[(ks * T + t) * d + n]; d % 4 == 0.
+__global__ void __launch_bounds__(kBlock)
+k_oproj_finish_rmsnorm(const float *__restrict__ part, int ks, int T, int d, uint16_t *res,
+                       float *__restrict__ h32, const uint16_t *__restrict__ gamma, float eps,
+                       uint16_t *__restrict__ y) {
+    const int t = blockIdx.x, n4 = d >> 2;
+    const int64_t stride = (int64_t)T * d / 4;  // one K range, in 16-byte vectors
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(part + (int64_t)t * d);
+    uint2 *r = reinterpret_cast<uint2 *>(res + (int64_t)t * d);
+    f32x4 *h = reinterpret_cast<f32x4 *>(h32 + (int64_t)t * d);
+    RmsRow rr;
+    f32x4 pv[kNormVec][kSkMaxSplit];
+    uint2 rv[kNormVec];
+#pragma unroll
+    for (int j = 0; j < kNormVec; ++j) {
+        const int i = threadIdx.x + j * kBlock;
+        const int ic = i < n4 ? i : 0;
+        rv[j] = r[ic];
+#pragma unroll
+        for (int q = 0; q < kSkMaxSplit; ++q)
+            pv[j][q] = p[ic + (q < ks ? q : 0) * stride];
+    }
+    rr.load_gamma(d, gamma);
+#pragma unroll
+    for (int j = 0; j < kNormVec; ++j) {
+        f32x4 v = pv[j][0];
+#pragma unroll
+        for (int q = 1; q < kSkMaxSplit; ++q)
+            if (q < ks)
+                v += pv[j][q];
+        const uint32_t lo = rv[j].x, hi = rv[j].y;
+        v.x += bf16_to_f32((uint16_t)(lo & 0xffffu));
+        v.y += bf16_to_f32((uint16_t)(lo >> 16));
+        v.z += bf16_to_f32((uint16_t)(hi & 0xffffu));
+        v.w += bf16_to_f32((uint16_t)(hi >> 16));
+        rr.v[j] = v;
+        const int i = threadIdx.x + j * kBlock;
+        if (i < n4) {
+            h[i] = v;
+            r[i] = uint2{(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                         (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+        }
+    }
+    uint16_t *yt = y + (int64_t)t * d;
     rr.finish(d, eps, [&](int e, uint16_t v) { yt[e] = v; });
 }
 
@@ -914,6 +973,13 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         trace_end(K3_OP_OPROJ_RESIDUAL, s);
         if (y_norm)
             k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
+    } else if (y_norm && d % 4 == 0 && d <= 4 * kNormVec * kBlock) {
+        // partial sums, then the finish and the norm in one kernel
+        float *part = (float *)((char *)workspace + oproj_part_offset(b, d));
+        const int ks = sk_oproj_partials(a, lda, b, K, w_o, d, part, s);
+        k_oproj_finish_rmsnorm<<<b, kBlock, 0, s>>>(part, ks, b, d, residual, h32, gamma, eps,
+                                                    y_norm);
+        trace_end(K3_OP_OPROJ_RESIDUAL, s);
     } else {
         sk_oproj_residual(a, lda, b, K, w_o, d, residual, h32,
                           (float *)((char *)workspace + oproj_part_offset(b, d)), s);

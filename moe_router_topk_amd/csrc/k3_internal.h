@@ -91,6 +91,8 @@ void sk_router_latent_shared(const uint16_t *x, int64_t ldx, int T, int K, const
                              float *part, hipStream_t s);
 void sk_swiglu(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W13, int I,
                uint16_t *hs, float *part, int cu_budget, hipStream_t s);
+int sk_oproj_partials(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
+                      float *part, hipStream_t s);
 void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
                        uint16_t *residual, float *h32, float *part, hipStream_t s);
 

@@ -235,6 +235,12 @@ void sk_swiglu(const uint16_t *x, int64_t ldx, int T, int K, const uint16_t *W13
 
 // Output projection + residual: residual <- bf16(residual + a . W_o^T) in
 // place and h32 = the fp32 sum (the RMSNorm kernel reads it).
+// The o-projection's partial sums alone; returns the number of K ranges.
+int sk_oproj_partials(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
+                      float *part, hipStream_t s) {
+    return sk_dense_partials(&W_o, &d, 1, K, a, lda, T, part, 0, s);
+}
+
 void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
                        uint16_t *residual, float *h32, float *part, hipStream_t s) {
     const int ks = sk_dense_partials(&W_o, &d, 1, K, a, lda, T, part, 0, s);

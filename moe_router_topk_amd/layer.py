@@ -164,9 +164,13 @@ class DecodeLayer:
             for key in self.PREFETCH_KEYS:
                 k3_prefetch(self.moe[key], cu_budget=self.prefetch_cu, stream=self.pf_stream)
             self.ev_side_done.record(self.pf_stream)
-        # the chain leaves the fp32 h; the block normalises it in its first
-        # kernel (one kernel boundary less than attn_chain + moe_block)
-        y = self.moe_block_rmsnorm(self.attn_chain_h32(x, residual))
+        # one token: the chain leaves the fp32 h and the block normalises it in
+        # its first kernel; more tokens: the o-projection's finishing kernel
+        # normalises (each saves a kernel boundary)
+        if x.shape[0] == 1:
+            y = self.moe_block_rmsnorm(self.attn_chain_h32(x, residual))
+        else:
+            y = self.moe_block(self.attn_chain(x, residual))
         if prefetch:
             main.wait_event(self.ev_side_done)
         return y

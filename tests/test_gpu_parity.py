@@ -558,25 +558,27 @@ def test_moe_block_rmsnorm_matches_composition(k3, full, chain_w, b):
     assert torch.equal(y3, y1)
 
 
-def test_layer_step_chain_then_moe(k3, full, chain_w):
-    """Chain + MoE block at b = 1, the benchmark's step, against the oracle."""
+@pytest.mark.parametrize("b", [1, 8])
+def test_layer_step_chain_then_moe(k3, full, chain_w, b):
+    """Chain + MoE block, the benchmark's step (b = 1; at b = 8 the norm runs
+    in the o-projection's finishing kernel), against the oracle."""
     from moe_router_topk_amd.layer import DecodeLayer
     cfg, w = full
-    layer = DecodeLayer(w, cfg.k, b_max=1, chain=chain_w)
-    inp = synth.make_chain_inputs(synth.CHAIN_CONFIG, 1, device=DEV)
+    layer = DecodeLayer(w, cfg.k, b_max=b, chain=chain_w)
+    inp = synth.make_chain_inputs(synth.CHAIN_CONFIG, b, device=DEV)
     r0 = inp["r"].clone()
     y = layer.step(inp["x"], inp["r"], prefetch=True)
     torch.cuda.synchronize()
     c = oracle.chain(inp["x"].cpu(), r0.cpu(), chain_w["w_in"].cpu(), chain_w["w_o"].cpu(),
                      chain_w["gamma"].cpu(), 1e-6)
-    assert_rel_close(layer.x_moe[:1].cpu(), c["y"], "x_moe")
+    assert_rel_close(layer.x_moe[:b].cpu(), c["y"], "x_moe")
     # the MoE block continues from the bf16 hidden state the GPU produced
     wc = {key: w[key].cpu() for key in ("w_router", "w_lat", "w13_s", "w2_s")}
     wc["bias"] = None
-    xm = layer.x_moe[:1].cpu()
+    xm = layer.x_moe[:b].cpu()
     logits = oracle.router_logits(xm, wc["w_router"])
     ids, wt = oracle.topk_softmax(logits, cfg.k)
-    check_ids(layer.ids[:1], ids, logits, cfg.k)
+    check_ids(layer.ids[:b], ids, logits, cfg.k)
     z = oracle.linear(xm, wc["w_lat"])
     y_s = oracle.shared_expert(xm, wc["w13_s"], wc["w2_s"])
     ref = oracle.moe_experts(z, ids, wt, _experts_on_host(w), cfg.E, y_add=y_s)
