@@ -14,7 +14,24 @@ std::atomic<void *> g_trace_begin[8];
 std::atomic<void *> g_trace_end[8];
 std::mutex g_cu_mutex;
 int g_cu_count[64];
+int g_max_lds[64];
 }  // namespace
+
+size_t device_max_lds() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 65536;
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (g_max_lds[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess ||
+            n <= 0)
+            n = 65536;
+        g_max_lds[dev] = n;
+    }
+    return (size_t)g_max_lds[dev];
+}
 
 int device_cu_count() {
     int dev = 0;

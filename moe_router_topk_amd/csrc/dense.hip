@@ -518,13 +518,20 @@ static int rls_gemv_ps_stride(int E, int NL, int Is, int grid) {
     return 8 * ((total + grid - 1) / grid);
 }
 
+// LDS of one 8-row-engine workgroup: two of them per compute unit share its
+// 160 KB (and the device's per-workgroup limit applies).
+static size_t gemv_lds_cap() {
+    const size_t cap = device_max_lds();
+    return cap < 81920 ? cap : 81920;
+}
+
 // The 8-row engine serves b tokens while their rows (and the partial sums)
-// fit 64 KB of LDS; the o-projection also needs b x rows <= the block size.
+// fit gemv_lds_cap(); the o-projection also needs b x rows <= the block size.
 static bool gemv_fits_b(int b, int N, int K, bool resid, int cu_budget = 0) {
     if (b < 1 || b > kDot2MaxTokens || !gemv_fits(K))
         return false;
     const GemvGeom g = gemv_geom(N, K, resid, cu_budget, b);
-    return g.lds <= 65536 && (!resid || b * g.ps_stride <= kBlock);
+    return g.lds <= gemv_lds_cap() && (!resid || b * g.ps_stride <= kBlock);
 }
 
 template <int NT, class Epi>
@@ -932,7 +939,7 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
     int variant = pick_dense_variant(K3_OP_OPROJ_RESIDUAL, b, K);
     Dot2Geom g{};
     int rows_blk = 0;
-    if (variant == K3_VARIANT_DOT2) {
+    if (variant == K3_VARIANT_DOT2 && !gemv_fits_b(b, d, K, true)) {
         g = dot2_geom(d, K, b, 0);
         g.grid = budget_grid(d, 0, 2);  // two workgroups per compute unit, even row shares
         rows_blk = (d + g.grid - 1) / g.grid;

@@ -14,6 +14,8 @@ int device_cu_count();
 // Grid size for a kernel that wants `want` workgroups of 256 threads, at most
 // `per_cu` resident per compute unit, on min(cu_budget, all) compute units.
 int budget_grid(int want, int cu_budget, int per_cu);
+// LDS a workgroup may allocate on the current device (bytes).
+size_t device_max_lds();
 
 // Variant bookkeeping for k3_get_last_dispatch / k3_force_variant.
 void record_dispatch(int op, int variant);
