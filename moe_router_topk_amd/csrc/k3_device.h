@@ -347,9 +347,12 @@ __device__ __forceinline__ void topk_keys(const float (&lv)[kTopkPer], int E,
 // lane j keeps the j-th pick. The weights are the softmax over the k picked
 // logits (the full softmax renormalised over the selection), written by
 // lanes j < k to ids[j], wts[j].
+// Only the first ceil(E / 64) keys of a lane can be non-empty; the rest are
+// skipped (a wave-uniform bound: E is the same in every lane).
 __device__ __forceinline__ void topk_select(uint32_t (&key)[kTopkPer], int k, int32_t *ids,
-                                            float *wts) {
+                                            float *wts, int E = K3_MAX_EXPERTS) {
     const int lane = threadIdx.x & (kWave - 1);
+    const int per = __builtin_amdgcn_readfirstlane((E + kWave - 1) / kWave);
     uint32_t sel_key = 0u, top_key = 0u;
     int sel_e = 0;
     for (int j = 0; j < k; ++j) {
@@ -357,16 +360,17 @@ __device__ __forceinline__ void topk_select(uint32_t (&key)[kTopkPer], int k, in
         int bi = 0;
 #pragma unroll
         for (int i = 0; i < kTopkPer; ++i) {
-            if (key[i] > bk) {
+            if (i < per && key[i] > bk) {
                 bk = key[i];
                 bi = i;
             }
         }
         const uint32_t m = wave_max_u32(bk);
         const uint32_t w = wave_min_u32(bk == m ? (uint32_t)(bi * kWave + lane) : 0xffffffffu);
+        const int wi = (int)(w >> 6);
 #pragma unroll
         for (int i = 0; i < kTopkPer; ++i)
-            if ((int)(w >> 6) == i && (int)(w & (kWave - 1)) == lane)
+            if (i < per && wi == i && (int)(w & (kWave - 1)) == lane)
                 key[i] = 0u;
         if (lane == j) {
             sel_key = m;
@@ -391,7 +395,7 @@ __device__ __forceinline__ void topk_wave(const float *logits, int E, int k, int
     uint32_t key[kTopkPer];
     topk_load(logits, E, lv);
     topk_keys(lv, E, key);
-    topk_select(key, k, ids, wts);
+    topk_select(key, k, ids, wts, E);
 }
 
 }  // namespace k3

@@ -39,13 +39,18 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
     const int nv = d >> 3;
     float *ps = reinterpret_cast<float *>(zs + nv);
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
+    // wave 0 issues the logit loads, then every wave its z loads; the
+    // selection waits for the logits only and z arrives meanwhile
+    float lv[kTopkPer];
+    if (TOPK && wq == 0)
+        topk_load(logits, E, lv);
+    GvStage<4> zst;  // d <= 8192
+    zst.load(z, nv);
     if (TOPK) {
         if (wq == 0) {
-            float lv[kTopkPer];
-            topk_load(logits, E, lv);
             uint32_t key[kTopkPer];
             topk_keys(lv, E, key);
-            topk_select(key, k, sid, swt);
+            topk_select(key, k, sid, swt, E);
             if (blockIdx.x == 0 && lane < k) {
                 ids_out[lane] = sid[lane];
                 w_out[lane] = swt[lane];
@@ -55,7 +60,7 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
         const int e = ids_in[threadIdx.x];
         sid[threadIdx.x] = (e >= 0 && e < E) ? e : -1;
     }
-    stage_rows(zs, nv, 1, nv, [&](int) { return z; });
+    zst.store(zs, nv);
     __syncthreads();
     const int gpe = I >> 2;  // groups per expert
     int g0, g1;
