@@ -410,7 +410,8 @@ def main() -> int:
              "eager_step_us_p90": round(pct(per, 0.9) * 1e3, 2),
              "bytes_per_step": int(bytes_step), "n_active_mean": mean_act}
 
-    # ---- sweep: MoE block at b = 4, 16, 32 (uniform) and 64 (Zipf bias); chain b = 1..64
+    # ---- sweep: MoE block and layer step at b = 4, 16, 32 (uniform) and 64 (Zipf
+    # bias); chain b = 1..64
     if not args.no_sweep:
         sweep = []
         S = 40
@@ -433,6 +434,24 @@ def main() -> int:
                           "GBps": round(by / us / 1e3, 1),
                           "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)})
             log(f"MoE block b={bb} {'zipf' if zipf else 'uniform'}: {us:.1f} us, "
+                f"n_active {na:.1f}, {by / us / 1e3:.0f} GB/s")
+            # the whole layer step at this batch: chain, then the block on its output
+            acts = []
+            for i in range(NX):
+                step(i, bb)
+                acts.append(int(torch.unique(layers[i % len(layers)].ids[:bb]).numel()))
+            g = capture(torch, lambda i: step(i, bb), S)
+            ts, _ = replay_timed(torch, g, S)
+            del g
+            us = ts * 1e3
+            na = sum(acts[i % NX] for i in range(S)) / S
+            by = moe_bytes(synth.MOE_CONFIGS["b64zipf" if zipf else "b16"], bb, na) + \
+                chain_bytes(cc, bb)
+            sweep.append({"what": "layer_step", "b": bb,
+                          "routing": "zipf1.1" if zipf else "uniform", "us": round(us, 1),
+                          "n_active_mean": na, "GBps": round(by / us / 1e3, 1),
+                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)})
+            log(f"layer step b={bb} {'zipf' if zipf else 'uniform'}: {us:.1f} us, "
                 f"n_active {na:.1f}, {by / us / 1e3:.0f} GB/s")
         for lay in layers:
             lay.moe["bias"] = None
