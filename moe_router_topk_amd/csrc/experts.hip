@@ -651,7 +651,10 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
     trace_begin(trace_op, s);
     if (b == 1) {
         const SlotList sl{topk_ids, k, E};
-        if (up_b1_fits(d_in, k, I, cu_budget))
+        // the batch-1 pair shares its own h layout: both kernels or neither
+        const bool b1 = up_b1_fits(d_in, k, I, cu_budget) &&
+                        down_b1_fits(k, I, d_out, false, cu_budget);
+        if (b1)
             launch_up_b1(false, z, d_in, w13, I, E, k, topk_ids, nullptr, nullptr, nullptr, hbuf,
                          cu_budget, s);
         else
@@ -659,7 +662,7 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
         trace_end(trace_op, s);
         if (y_add_ready)
             (void)hipStreamWaitEvent(s, y_add_ready, 0);
-        if (down_b1_fits(k, I, d_out, false, cu_budget)) {
+        if (b1) {
             launch_down_b1(hbuf, I, w2, d_out, topk_ids, topk_w, k, E, y_add, nullptr, nullptr,
                            nullptr, y, cu_budget, s);
             return;

@@ -53,6 +53,12 @@ __device__ __forceinline__ u32x4 ld_act16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// 8 bytes at byte offset off of the range.
+__device__ __forceinline__ uint2 ld_act8(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return uint2{(uint32_t)v[0], (uint32_t)v[1]};
+}
+
 // Index of the calling wave in its workgroup, known uniform to the compiler.
 __device__ __forceinline__ int wave_in_block() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -337,25 +343,35 @@ __device__ __forceinline__ void topk_load(const float *logits, int E, float (&lv
 __device__ __forceinline__ void topk_keys(const float (&lv)[kTopkPer], int E,
                                           uint32_t (&key)[kTopkPer]) {
     const int lane = threadIdx.x & (kWave - 1);
+    // masked rather than selected: a branch here lets the compiler sink a
+    // logit load into it and wait there for every load issued after it
 #pragma unroll
     for (int i = 0; i < kTopkPer; ++i)
-        key[i] = i * kWave + lane < E ? order_key(lv[i]) : 0u;
+        key[i] = order_key(lv[i]) & (i * kWave + lane < E ? 0xffffffffu : 0u);
 }
 
-// One wave picks k experts from the keys topk_load gave it: k rounds of a
-// wave-wide maximum of the keys, then the smallest expert index holding it;
-// lane j keeps the j-th pick. The weights are the softmax over the k picked
-// logits (the full softmax renormalised over the selection), written by
-// lanes j < k to ids[j], wts[j].
-// Only the first ceil(E / 64) keys of a lane can be non-empty; the rest are
-// skipped (a wave-uniform bound: E is the same in every lane).
-__device__ __forceinline__ void topk_select(uint32_t (&key)[kTopkPer], int k, int32_t *ids,
-                                            float *wts, int E = K3_MAX_EXPERTS) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int per = __builtin_amdgcn_readfirstlane((E + kWave - 1) / kWave);
-    uint32_t sel_key = 0u, top_key = 0u;
-    int sel_e = 0;
-    for (int j = 0; j < k; ++j) {
+// One wave picks experts from the keys topk_load gave it, one per next():
+// the wave-wide maximum of the keys, then the smallest expert index holding
+// it; lane j keeps the j-th pick. finish(k) turns the k picks into weights,
+// the softmax over the k picked logits (the full softmax renormalised over
+// the selection), written by lanes j < k to ids[j], wts[j]. Only the first
+// ceil(E / 64) keys of a lane can be non-empty; the rest are skipped (a
+// wave-uniform bound: E is the same in every lane).
+struct TopkPicker {
+    uint32_t key[kTopkPer];
+    int per;  // key slots that can hold logits
+    int n;    // picks so far
+    uint32_t sel_key, top_key;
+    int sel_e;
+    __device__ __forceinline__ void init(int E) {
+        per = __builtin_amdgcn_readfirstlane((E + kWave - 1) / kWave);
+        n = 0;
+        sel_key = top_key = 0u;
+        sel_e = 0;
+    }
+    // The next pick's expert (the same in every lane).
+    __device__ __forceinline__ int next() {
+        const int lane = threadIdx.x & (kWave - 1);
         uint32_t bk = 0u;
         int bi = 0;
 #pragma unroll
@@ -372,21 +388,39 @@ __device__ __forceinline__ void topk_select(uint32_t (&key)[kTopkPer], int k, in
         for (int i = 0; i < kTopkPer; ++i)
             if (i < per && wi == i && (int)(w & (kWave - 1)) == lane)
                 key[i] = 0u;
-        if (lane == j) {
+        if (lane == n) {
             sel_key = m;
             sel_e = (int)w;
         }
-        if (j == 0)
+        if (n == 0)
             top_key = m;
+        ++n;
+        return (int)w;
     }
-    const float sel_v = key_value(sel_key), top = key_value(top_key);
-    const float dl = (sel_v == top) ? 0.0f : sel_v - top;
-    const float p = lane < k ? expf(dl) : 0.0f;
-    const float sum = wave_sum(p);
-    if (lane < k) {
-        ids[lane] = sel_e;
-        wts[lane] = p / sum;
+    __device__ __forceinline__ void finish(int k, int32_t *ids, float *wts) const {
+        const int lane = threadIdx.x & (kWave - 1);
+        const float sel_v = key_value(sel_key), top = key_value(top_key);
+        const float dl = (sel_v == top) ? 0.0f : sel_v - top;
+        const float p = lane < k ? expf(dl) : 0.0f;
+        const float sum = wave_sum(p);
+        if (lane < k) {
+            ids[lane] = sel_e;
+            wts[lane] = p / sum;
+        }
     }
+};
+
+// All k picks at once.
+__device__ __forceinline__ void topk_select(uint32_t (&key)[kTopkPer], int k, int32_t *ids,
+                                            float *wts, int E = K3_MAX_EXPERTS) {
+    TopkPicker pk;
+#pragma unroll
+    for (int i = 0; i < kTopkPer; ++i)
+        pk.key[i] = key[i];
+    pk.init(E);
+    for (int j = 0; j < k; ++j)
+        pk.next();
+    pk.finish(k, ids, wts);
 }
 
 __device__ __forceinline__ void topk_wave(const float *logits, int E, int k, int32_t *ids,

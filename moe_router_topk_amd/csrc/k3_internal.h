@@ -99,10 +99,11 @@ void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint1
                        uint16_t *residual, float *h32, float *part, hipStream_t s);
 
 // Batch-1 routed experts (moe_b1.hip). up_b1: routed gate/up + SwiGLU into
-// hbuf [k][I]; with `topk` the selection from logits happens in the kernel
-// (ids/weights written out). down_b1: y = bf16(base + sum_j w_j w2[ids[j]] .
-// h_j) with base = y_add, or, with w2s, the shared expert's down projection
-// of hs (also written to y_s).
+// hbuf, k x I values in the pair's own layout ([I / 4][k][4], read only by
+// down_b1: launch both or neither); with `topk` the selection from logits
+// happens in the kernel (ids/weights written out). down_b1: y = bf16(base +
+// sum_j w_j w2[ids[j]] . h_j) with base = y_add, or, with w2s, the shared
+// expert's down projection of hs (also written to y_s).
 bool up_b1_fits(int d, int k, int I, int cu_budget);
 void launch_up_b1(bool topk, const uint16_t *z, int d, const uint16_t *w13, int I, int E, int k,
                   const int32_t *ids_in, const float *logits, int32_t *ids_out, float *w_out,

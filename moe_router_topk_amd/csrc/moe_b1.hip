@@ -4,9 +4,11 @@
 // "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 3 ("Improve MoE
 // scheduling and overlap"): the routed experts follow the router and the
 // latent projection; the shared expert's work fills the gap the routing
-// leaves. Here that gap is the expert selection itself: every workgroup of
-// the gate/up kernel selects the experts while its first units -- rows of
-// the shared expert's down projection -- are in flight.
+// leaves. Here the shared expert's rows ride in the passes around the
+// routed ones (gate/up with the router and latent rows, down as one more
+// slot of the routed down kernel), and the expert selection itself runs
+// while the routed weights stream: each pick is made just before its
+// expert's rows are needed.
 #include <math.h>
 
 #include "k3_device.h"
@@ -19,13 +21,24 @@ namespace k3 {
 // Both kernels run on the 8-row engine of k3_gemv.h. At batch 1 the slots are
 // the experts (k distinct ids).
 
+// The batch-1 routed h: h[a][j] (slot a, column j) sits at hbuf[((j / 4) k
+// + a) 4 + j % 4], i.e. [column block][slot][4]. The gate/up kernel's
+// workgroups own column blocks of every slot, so each writes one contiguous
+// piece; the down kernel gathers the 8-byte pieces into its LDS rows.
+__device__ __forceinline__ int64_t hb1_index(int a, int j, int k) {
+    return ((int64_t)(j >> 2) * k + a) * 4 + (j & 3);
+}
+
 // Routed gate/up at batch 1, optionally with the expert selection folded in.
-// The groups are (slot a, columns j0 .. j0 + 3): the gate rows j0 .. j0 + 3
-// and the up rows I + j0 .. I + j0 + 3 of w13[ids[a]], so one group holds
-// both halves of its four outputs: hbuf[a][j] = bf16(silu(gate . z) *
-// (up . z)). With TOPK, wave 0 of every workgroup selects the experts from
-// the router logits while all threads stage z (workgroup 0 publishes ids and
-// weights); without it the ids come from ids_in and slots outside [0, E)
+// A group is (slot a, columns 4c .. 4c + 3): the gate rows 4c .. 4c + 3 and
+// the up rows I + 4c .. I + 4c + 3 of w13[ids[a]], so one group holds both
+// halves of its four outputs: h[a][j] = bf16(silu(gate . z) * (up . z)).
+// Workgroup w takes the same column blocks (an even share of the I / 4) of
+// every slot, slot 0 first. With TOPK every wave picks the experts itself
+// from the router logits, one pick just before it first needs that slot's
+// expert: the first weight loads wait for one pick only, and the later picks
+// run while earlier loads are in flight (workgroup 0 publishes ids and
+// weights). Without TOPK the ids come from ids_in and slots outside [0, E)
 // are skipped.
 template <bool TOPK, int U>
 __global__ void __launch_bounds__(kBlock)
@@ -34,52 +47,68 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
             int32_t *__restrict__ ids_out, float *__restrict__ w_out,
             uint16_t *__restrict__ hbuf, int ps_stride) {
     extern __shared__ u32x4 zs[];  // z (d / 8 vectors), then ps[4][ps_stride]
-    __shared__ int sid[K3_MAX_TOPK];
-    __shared__ float swt[K3_MAX_TOPK];
     const int nv = d >> 3;
     float *ps = reinterpret_cast<float *>(zs + nv);
-    const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
-    // wave 0 issues the logit loads, then every wave its z loads; the
-    // selection waits for the logits only and z arrives meanwhile
+    const int gpe = I >> 2;  // column blocks (groups) per slot
+    int c0, c1;
+    split_range(gpe, gridDim.x, blockIdx.x, c0, c1);
+    const int cps = c1 - c0;  // this workgroup's groups per slot
+    // the expert of the slot the stream is on (slots come in order)
+    TopkPicker pk;
     float lv[kTopkPer];
-    if (TOPK && wq == 0)
-        topk_load(logits, E, lv);
-    GvStage<4> zst;  // d <= 8192
-    zst.load(z, nv);
-    if (TOPK) {
-        if (wq == 0) {
-            uint32_t key[kTopkPer];
-            topk_keys(lv, E, key);
-            topk_select(key, k, sid, swt, E);
-            if (blockIdx.x == 0 && lane < k) {
-                ids_out[lane] = sid[lane];
-                w_out[lane] = swt[lane];
+    int cur_a = -1, cur_e = -1;
+    auto slot_expert = [&](int a) {
+        while (cur_a < a) {
+            ++cur_a;
+            if (TOPK) {
+                cur_e = pk.next();
+            } else {
+                const int e = ld_scalar(ids_in + cur_a);
+                cur_e = (e >= 0 && e < E) ? e : -1;
             }
         }
-    } else if (threadIdx.x < k) {
-        const int e = ids_in[threadIdx.x];
-        sid[threadIdx.x] = (e >= 0 && e < E) ? e : -1;
-    }
-    zst.store(zs, nv);
-    __syncthreads();
-    const int gpe = I >> 2;  // groups per expert
-    int g0, g1;
-    split_range(k * gpe, gridDim.x, blockIdx.x, g0, g1);
+        return cur_e;
+    };
+    GvStage<4> zst;  // d <= 8192
     gemv8_stream<U>(
-        g1 - g0, d,
+        k * cps, d,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
-            const int vg = g0 + g, a = vg / gpe, j0 = 4 * (vg - a * gpe);
-            const int e = __builtin_amdgcn_readfirstlane(sid[a]);
-            base = w13 + ((int64_t)(e < 0 ? 0 : e) * 2 * I + j0) * d;
+            const int a = g / cps, c = c0 + (g - a * cps);
+            const int e = slot_expert(a);
+            base = w13 + ((int64_t)(e < 0 ? 0 : e) * 2 * I + 4 * c) * d;
             nr = e >= 0 ? 8 : 0;
             skip = I - 4;
         },
-        [&](int, int kv, int) { return zs[kv]; }, ps, ps_stride, [&]() {}, [&]() {});
-    for (int i = threadIdx.x; i < 8 * (g1 - g0); i += kBlock) {
-        const int r = i & 7, vg = g0 + (i >> 3), a = vg / gpe, j = 4 * (vg - a * gpe) + r;
-        if (r < 4 && sid[a] >= 0)
-            hbuf[(int64_t)a * I + j] =
+        [&](int, int kv, int) { return zs[kv]; }, ps, ps_stride,
+        [&]() {
+            // the logits first: the first pick waits for them, not for z
+            if (TOPK) {
+                topk_load(logits, E, lv);
+                pk.init(E);
+            }
+            zst.load(z, nv);
+            if (TOPK)
+                topk_keys(lv, E, pk.key);
+        },
+        [&]() {
+            zst.store(zs, nv);
+            __syncthreads();
+        });
+    for (int i = threadIdx.x; i < 8 * k * cps; i += kBlock) {
+        const int r = i & 7, g = i >> 3, a = g / cps, j = 4 * (c0 + g - a * cps) + r;
+        bool ok = true;
+        if (!TOPK) {
+            const int e = ids_in[a];
+            ok = e >= 0 && e < E;
+        }
+        if (r < 4 && ok)
+            hbuf[hb1_index(a, j, k)] =
                 f32_to_bf16(silu(gv_total(ps, ps_stride, i)) * gv_total(ps, ps_stride, i + 4));
+    }
+    if (TOPK && blockIdx.x == 0 && threadIdx.x < kWave) {
+        while (pk.n < k)
+            pk.next();
+        pk.finish(k, ids_out, w_out);
     }
 }
 
@@ -108,12 +137,21 @@ k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__
     int rb0, rb1;
     split_range(d_out, gridDim.x, blockIdx.x, rb0, rb1);
     const int rows = rb1 - rb0, gps = (rows + 7) >> 3;
-    // the slots' h rows: the k routed rows are contiguous in hbuf (staged in
-    // registers before the first weight loads when they fit), the shared one
-    // is hs
-    const bool early = k * nv <= 8 * kBlock && nv <= kBlock;
-    GvStage<8> sr;
+    // the slots' h rows: the k routed rows are gathered from hbuf's 8-byte
+    // pieces (loaded before the first weight loads when they fit), the shared
+    // one is hs
+    const int npc = 2 * k * nv;  // 8-byte pieces of the routed rows
+    const bool early = npc <= 16 * kBlock && nv <= kBlock;
+    uint2 hp[16];
     GvStage<1> ss;
+    int e_ld = 0;
+    float w_ld = 0.0f;
+    uint2 *hl8 = reinterpret_cast<uint2 *>(hl);
+    // piece p = (column block c, slot a) goes to half c % 2 of LDS vector (a, c / 2)
+    auto put = [&](int p, uint2 v) {
+        const int c = p / k, a = p - c * k;
+        hl8[(a * nv + (c >> 1)) * 2 + (c & 1)] = v;
+    };
     float yv = 0.0f;
     gemv8_stream<U>(
         ns * gps, I,
@@ -133,21 +171,40 @@ k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__
         [&](int g, int kv, int) { return hl[min(g / gps, ns - 1) * nv + kv]; }, ps, ps_stride,
         [&]() {
             if (early) {
-                sr.load(hbuf, k * nv);
+                const rsrc_t r = act_range(uniform_ptr(hbuf));
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int p = threadIdx.x + q * kBlock;
+                    // past npc: the sign bit of npc - 1 - p (arithmetic, no branch)
+                    hp[q] = ld_act8(r, ((uint32_t)p * 8u) | ((uint32_t)(npc - 1 - p) & 0x80000000u));
+                }
                 if (w2s)
                     ss.load(hs, nv);
             }
             if (y_add && rows <= kBlock)
                 yv = y_add[rb0 + min((int)threadIdx.x, rows - 1)];
+            // the slots' ids and weights too (clamped, unconditional loads)
+            const int ti = min((int)threadIdx.x, k - 1);
+            e_ld = ids[ti];
+            w_ld = topk_w[ti];
         },
         [&]() {
             if (early) {
-                sr.store(hl, k * nv);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int p = threadIdx.x + q * kBlock;
+                    if (p < npc)
+                        put(p, hp[q]);
+                }
                 if (w2s)
                     ss.store(hl + k * nv, nv);
             } else {
-                stage_rows(hl, nv, ns, nv,
-                           [&](int j) { return j < k ? hbuf + (int64_t)j * I : hs; });
+                const uint2 *h8 = reinterpret_cast<const uint2 *>(hbuf);
+                for (int p = threadIdx.x; p < npc; p += kBlock)
+                    put(p, h8[p]);
+                if (w2s)
+                    for (int i = threadIdx.x; i < nv; i += kBlock)
+                        hl[k * nv + i] = ld_act16(hs + 8 * i);
             }
             if (rows <= kBlock) {
                 if ((int)threadIdx.x < rows)
@@ -157,9 +214,8 @@ k_down_b1(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__
                     ya[i] = y_add ? y_add[rb0 + i] : 0.0f;
             }
             if (threadIdx.x < k) {
-                const int e = ids[threadIdx.x];
-                sv[threadIdx.x] = e >= 0 && e < E;
-                sw[threadIdx.x] = topk_w[threadIdx.x];
+                sv[threadIdx.x] = e_ld >= 0 && e_ld < E;
+                sw[threadIdx.x] = w_ld;
             }
             __syncthreads();
         });
@@ -209,24 +265,26 @@ void launch_down_b1(const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
                                               y_s, y, ps_stride);
 }
 
-// LDS of the gate/up kernel: z, then the partial sums of the share.
+// LDS of the gate/up kernel: z, then the partial sums of the share (k
+// slots x the workgroup's column blocks).
 static size_t up_b1_lds(int d, int k, int I, int grid, int &ps_stride) {
-    const int groups = k * (I / 4);
-    ps_stride = 8 * ((groups + grid - 1) / grid);
+    ps_stride = 8 * k * ((I / 4 + grid - 1) / grid);
     return (size_t)d * sizeof(uint16_t) + (size_t)4 * ps_stride * sizeof(float);
 }
 
+// One workgroup per column block of I / 4 at most, two per compute unit.
+static int up_b1_grid(int I, int cu_budget) { return budget_grid(I / 4, cu_budget, 2); }
+
 bool up_b1_fits(int d, int k, int I, int cu_budget) {
     int ps_stride;
-    const int grid = budget_grid(k * (I / 4), cu_budget, 2);
-    return d % 64 == 0 && d <= 8192 && I % 4 == 0 &&
-           up_b1_lds(d, k, I, grid, ps_stride) <= 65536;
+    return d % 64 == 0 && d <= 8192 && I % 4 == 0 && I >= 4 &&
+           up_b1_lds(d, k, I, up_b1_grid(I, cu_budget), ps_stride) <= 65536;
 }
 
 void launch_up_b1(bool topk, const uint16_t *z, int d, const uint16_t *w13, int I, int E, int k,
                   const int32_t *ids_in, const float *logits, int32_t *ids_out, float *w_out,
                   uint16_t *hbuf, int cu_budget, hipStream_t s) {
-    const int grid = budget_grid(k * (I / 4), cu_budget, 2);
+    const int grid = up_b1_grid(I, cu_budget);
     int ps_stride;
     const size_t lds = up_b1_lds(d, k, I, grid, ps_stride);
 #define K3_UP(T_, U_)                                                                          \
