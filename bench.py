@@ -410,13 +410,13 @@ def main() -> int:
              "eager_step_us_p90": round(pct(per, 0.9) * 1e3, 2),
              "bytes_per_step": int(bytes_step), "n_active_mean": mean_act}
 
-    # ---- sweep: MoE block and layer step at b = 4, 16, 32 (uniform) and 64 (Zipf
+    # ---- sweep: MoE block and layer step at b = 4, 8, 16, 32 (uniform) and 64 (Zipf
     # bias); chain b = 1..64
     if not args.no_sweep:
         sweep = []
         S = 40
         bias = synth.zipf_router_bias(cfg.E, 1.1, cfg.seed).to(dev)
-        for bb, zipf in ((4, False), (16, False), (32, False), (64, True)):
+        for bb, zipf in ((4, False), (8, False), (16, False), (32, False), (64, True)):
             for lay in layers:
                 lay.moe["bias"] = bias if zipf else None
             acts = []

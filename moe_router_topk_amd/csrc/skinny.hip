@@ -33,10 +33,19 @@ struct SkOuts {
     int cols_total;
 };
 
+// The K ranges' partials of element i, added in range order. Every range's
+// load is issued up front (ranges past ks re-read range 0 and are not
+// added), so the sum waits for one memory latency, not ks of them.
 __device__ __forceinline__ float sk_sum(const float *part, int ks, int64_t stride, int64_t i) {
-    float v = part[i];
-    for (int r = 1; r < ks; ++r)
-        v += part[i + r * stride];
+    float p[kSkMaxSplit];
+#pragma unroll
+    for (int r = 0; r < kSkMaxSplit; ++r)
+        p[r] = part[i + (r < ks ? r : 0) * stride];
+    float v = p[0];
+#pragma unroll
+    for (int r = 1; r < kSkMaxSplit; ++r)
+        if (r < ks)
+            v += p[r];
     return v;
 }
 
