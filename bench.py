@@ -192,6 +192,35 @@ def write_traffic_summary(pmc_dir: str) -> int:
     return 0
 
 
+def print_counter_summary(pmc_dir: str) -> int:
+    """Per-kernel means (per dispatch) of every counter in the rocprofv3 --pmc
+    csv files under pmc_dir, printed as a markdown table."""
+    import csv
+    import glob
+    acc = {}
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].split("(")[0]
+                if "k3::" not in name:
+                    continue
+                key = (name, r["Counter_Name"])
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    if not acc:
+        print("bench.py: no k3 counter rows under " + pmc_dir, file=sys.stderr)
+        return 2
+    counters = sorted({c for _, c in acc})
+    print("| Kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for name in sorted({n for n, _ in acc}):
+        vals = [acc.get((name, c)) for c in counters]
+        n = max(len(v) for v in vals if v)
+        cells = [f"{sum(v) / len(v):.4g}" if v else "" for v in vals]
+        print(f"| `{name}` | {n} | " + " | ".join(cells) + " |")
+    return 0
+
+
 # ------------------------------------------------------------------ timing helpers
 def capture(torch, fn, n: int):
     """Capture fn(i) for i < n into one graph."""
@@ -251,6 +280,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--zipf", type=float, default=0.0,
+                    help="Zipf exponent of the router bias for the main step (0: none)")
     ap.add_argument("--layers", type=int, default=2, help="weight copies rotated per step")
     ap.add_argument("--prefetch", action="store_true",
                     help="run the side-stream prefetch inside the timed step")
@@ -268,9 +299,14 @@ def main() -> int:
     ap.add_argument("--traffic-summary", metavar="DIR", default="",
                     help="no GPU work: reduce the rocprofv3 counter runs under DIR to the "
                          "dominant kernel's HBM bytes per launch (written under profiles/)")
+    ap.add_argument("--counter-summary", metavar="DIR", default="",
+                    help="no GPU work: per-kernel means of every counter in the rocprofv3 "
+                         "--pmc csv files under DIR, as a markdown table")
     args = ap.parse_args()
     if args.traffic_summary:
         return write_traffic_summary(args.traffic_summary)
+    if args.counter_summary:
+        return print_counter_summary(args.counter_summary)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -312,6 +348,11 @@ def main() -> int:
         layers.append(DecodeLayer(mw, cfg.k, b_max=64, chain=cw, eps=cc.eps,
                                   cu_shared=args.cu_shared, prefetch_cu=args.prefetch_cu))
         log(f"layer {li}: weights generated")
+    if args.zipf > 0:
+        zbias = synth.zipf_router_bias(cfg.E, args.zipf, cfg.seed).to(dev)
+        for lay in layers:
+            lay.moe["bias"] = zbias
+        cfg = synth.MOE_CONFIGS["b64zipf"]  # the same layer with the bias counted
     NX = 16
     pool = [synth.make_chain_inputs(cc, 64, device=dev, index=i) for i in range(NX)]
     torch.cuda.synchronize()
@@ -496,11 +537,12 @@ def main() -> int:
         "data": "synthetic (seeded bf16 weights and tokens, rotated over "
                 f"{args.layers} weight copies and {NX} token batches)",
         "config": {
-            "workload": ("decode layer step at batch 1: attention in-proj 7168->12288, "
+            "workload": (f"decode layer step at batch {b}: attention in-proj 7168->12288, "
                          "o-proj 8192->7168 + residual + RMSNorm, router E=384 top-8 "
                          "renormalised softmax, latent 7168->7168, 8 routed + 1 shared "
                          "SwiGLU experts I=2048 (gate/up [4096x7168], down [7168x2048]), "
-                         "side-stream prefetch " + ("on" if prefetch else "off")),
+                         "side-stream prefetch " + ("on" if prefetch else "off")
+                         + (f", Zipf({args.zipf}) router bias" if args.zipf > 0 else "")),
             "batch": b, "d": cfg.d, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
             "prefetch": prefetch, "hip_graph": not args.eager_only,
             "layers_rotated": args.layers,

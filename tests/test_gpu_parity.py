@@ -205,6 +205,19 @@ def test_row_engine_short_and_uneven_rows(k3, K, N, b):
         assert_rel_close(yn.cpu(), y_ref, "y_norm")
 
 
+@pytest.mark.parametrize("b", list(synth.CHAIN_BATCHES))
+def test_proj_skinny_chain_in(k3, chain_w, b):
+    """The attention input projection 7168 -> 12288 at every chain batch the
+    benchmark times; sampled output columns."""
+    inp = synth.make_chain_inputs(synth.CHAIN_CONFIG, b, device=DEV, index=300 + b)
+    q = k3.k3_proj_skinny(inp["x"], chain_w["w_in"])
+    torch.cuda.synchronize()
+    cols = torch.arange(0, 12288, 11)
+    ref = oracle.linear(inp["x"].cpu(), chain_w["w_in"][cols].cpu())
+    assert_rel_close(q[:, cols].cpu(), ref, "q")
+    assert k3.k3_get_last_dispatch("proj_skinny") == ("dot2" if b <= 4 else "mfma")
+
+
 def test_proj_skinny_strided_output(k3, chain_w):
     """x and y as column slices of wider buffers (row strides > width)."""
     w = chain_w
