@@ -488,10 +488,18 @@ def main() -> int:
             na = sum(acts[i % NX] for i in range(S)) / S
             by = moe_bytes(synth.MOE_CONFIGS["b64zipf" if zipf else "b16"], bb, na) + \
                 chain_bytes(cc, bb)
-            sweep.append({"what": "layer_step", "b": bb,
-                          "routing": "zipf1.1" if zipf else "uniform", "us": round(us, 1),
-                          "n_active_mean": na, "GBps": round(by / us / 1e3, 1),
-                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)})
+            entry = {"what": "layer_step", "b": bb,
+                     "routing": "zipf1.1" if zipf else "uniform", "us": round(us, 1),
+                     "n_active_mean": na, "GBps": round(by / us / 1e3, 1),
+                     "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)}
+            if not args.no_cpu_baseline:
+                # the oracle beside it: one layer step at this batch on the host cores
+                cfg_b = synth.MOE_CONFIGS["b64zipf" if zipf else "b16"]
+                oms, othr, oby = oracle_step(layers[0], cfg_b, cc, pool[0], bb)
+                entry["oracle"] = {"ms_per_step": round(oms, 1), "cores": othr,
+                                   "GBps": round(oby / oms / 1e6, 3), "steps": 1}
+                log(f"oracle layer step b={bb}: {oms:.0f} ms on {othr} threads")
+            sweep.append(entry)
             log(f"layer step b={bb} {'zipf' if zipf else 'uniform'}: {us:.1f} us, "
                 f"n_active {na:.1f}, {by / us / 1e3:.0f} GB/s")
         for lay in layers:
@@ -608,6 +616,32 @@ def cpu_baseline(torch, layer, cfg, cc, pool, b, seconds):
             "kind": "oracle", "ms_per_step": round(sec * 1e3, 2),
             "sample": f"{done} whole layer steps at batch {b} (chain + MoE block, "
                       f"{cfg.k} routed experts each), fp64 C oracle with OpenMP"}
+
+
+def oracle_step(layer, cfg, cc, inp, b):
+    """One whole layer step of the oracle (plain fp64 C, all host cores) at
+    batch b: (ms, threads, bytes of the step). The experts it reads are copied
+    to the host before the clock starts."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.threads()
+    host = {k: (v.cpu() if v is not None else None) for k, v in layer.moe.items()
+            if k not in ("w13", "w2")}
+    ch = {k: v.cpu() for k, v in layer.chain_w.items()}
+    x, r = inp["x"][:b].cpu(), inp["r"][:b].cpu()
+    hm = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)["y"]
+    ids, _ = oracle.topk_softmax(oracle.router_logits(hm, host["w_router"], host["bias"]),
+                                 cfg.k)
+    experts = {int(e): (layer.moe["w13"][int(e)].cpu(), layer.moe["w2"][int(e)].cpu())
+               for e in np.unique(ids)}
+    t0 = time.perf_counter()
+    c = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)
+    oracle.moe_block(c["y"], host, cfg.k, expert_weights=lambda e: experts[e])
+    dt = time.perf_counter() - t0
+    nbytes = moe_bytes(cfg, b, len(experts)) + chain_bytes(cc, b)
+    return dt * 1e3, threads, nbytes
 
 
 if __name__ == "__main__":
