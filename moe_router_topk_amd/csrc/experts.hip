@@ -68,16 +68,26 @@ struct DenseList {  // the shared expert: one expert, every token in order
 };
 
 // ------------------------------------------------------------------ permutation
+// Where the permutation writes: the two compacted expert lists (light: at
+// most kDot2MaxTokens tokens, heavy: more), the tokens sorted by expert and
+// every (token, slot)'s position.
+struct PermuteOut {
+    int *n_light, *light_expert, *light_start, *light_ntok;
+    int *n_heavy, *heavy_expert, *heavy_start, *heavy_ntok;
+    int *sorted_token, *slot_pos;
+};
+
 // One workgroup. Token t's choice of expert e sets bit t of mask[e]; an
 // expert's token count is the popcount, so every (expert, token) pair gets
 // exactly one position and all positions [0, total) are written. Ids outside
 // [0, E) are dropped (slot_pos = -1). Exclusive scans over the experts give
 // the positions and the two compacted lists.
-__global__ void __launch_bounds__(kBlock)
-k_moe_permute(const int32_t *__restrict__ ids, int b, int k, int E, int *n_light,
-              int *light_expert, int *light_start, int *light_ntok, int *n_heavy,
-              int *heavy_expert, int *heavy_start, int *heavy_ntok, int *sorted_token,
-              int *slot_pos) {
+__device__ __forceinline__ void moe_permute_block(const int32_t *__restrict__ ids, int b, int k,
+                                                  int E, const PermuteOut &o) {
+    int *n_light = o.n_light, *light_expert = o.light_expert, *light_start = o.light_start;
+    int *light_ntok = o.light_ntok, *n_heavy = o.n_heavy, *heavy_expert = o.heavy_expert;
+    int *heavy_start = o.heavy_start, *heavy_ntok = o.heavy_ntok;
+    int *sorted_token = o.sorted_token, *slot_pos = o.slot_pos;
     __shared__ unsigned long long mask[K3_MAX_EXPERTS];
     __shared__ int start[K3_MAX_EXPERTS];
     __shared__ int wsum[3][kBlock / kWave];
@@ -162,6 +172,11 @@ k_moe_permute(const int32_t *__restrict__ ids, int b, int k, int E, int *n_light
         }
         slot_pos[i] = pos;
     }
+}
+
+__global__ void __launch_bounds__(kBlock)
+k_moe_permute(const int32_t *__restrict__ ids, int b, int k, int E, PermuteOut o) {
+    moe_permute_block(ids, b, k, E, o);
 }
 
 // ------------------------------------------------------------------ dot2 gate/up
@@ -444,19 +459,25 @@ __global__ void k_slot_identity(const int32_t *__restrict__ ids, int k, int E, i
 
 // ------------------------------------------------------------------ top-k + shared down
 // Second kernel of the fused MoE block: workgroup 0 picks every token's
-// experts from the logits the first kernel wrote (one wave per token); the
-// other workgroups stream the shared expert's down projection meanwhile, so
-// the selection's latency hides under useful weight reads.
+// experts from the logits the first kernel wrote (one wave per token) and,
+// with `permute`, sorts the (token, slot) pairs by expert right after (the
+// permutation kernel's work, one launch fewer); the other workgroups stream
+// the shared expert's down projection meanwhile, so the selection's latency
+// hides under useful weight reads.
 template <int TM, int CB>
 __global__ void __launch_bounds__(kBlock)
 k_topk_shared_down(const float *__restrict__ logits, int E, int k, int b,
                    int32_t *__restrict__ ids, float *__restrict__ wts,
                    const uint16_t *__restrict__ hs, int Is, const uint16_t *__restrict__ W2s,
-                   int d, float *__restrict__ y_s) {
+                   int d, float *__restrict__ y_s, bool permute, PermuteOut po) {
     const int wq = wave_in_block();
     if (blockIdx.x == 0) {
         for (int t = wq; t < b; t += kBlock / kWave)
             topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k);
+        if (permute) {
+            __syncthreads();  // every token's ids are written (and visible to the block)
+            moe_permute_block(ids, b, k, E, po);
+        }
         return;
     }
     extern __shared__ u32x4 xs[];
@@ -638,11 +659,20 @@ struct DownExtra {
     float *out_x;
 };
 
+// The permutation's outputs in a routed-experts workspace.
+PermuteOut permute_out(const MoeWorkspace &L, char *ws) {
+    return PermuteOut{(int *)(ws + L.n_light),      (int *)(ws + L.light_expert),
+                      (int *)(ws + L.light_start),  (int *)(ws + L.light_ntok),
+                      (int *)(ws + L.n_heavy),      (int *)(ws + L.heavy_expert),
+                      (int *)(ws + L.heavy_start),  (int *)(ws + L.heavy_ntok),
+                      (int *)(ws + L.sorted_token), (int *)(ws + L.slot_pos)};
+}
+
 void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int32_t *topk_ids,
                      const float *topk_w, int k, const uint16_t *w13, const uint16_t *w2, int E,
                      int I, int d_out, const float *y_add, hipEvent_t y_add_ready, uint16_t *y,
                      int cu_budget, char *ws, int trace_op, hipStream_t s,
-                     const DownExtra *extra = nullptr) {
+                     const DownExtra *extra = nullptr, bool permuted = false) {
     const MoeWorkspace L = moe_workspace_layout(b, E, k, I, d_out);
     uint16_t *hbuf = (uint16_t *)(ws + L.hbuf);
     float *part = (float *)(ws + L.part);
@@ -675,11 +705,10 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
                                (int *)(ws + L.light_ntok), (int *)(ws + L.sorted_token)};
         const ExpertList heavy{n_heavy, (int *)(ws + L.heavy_expert), (int *)(ws + L.heavy_start),
                                (int *)(ws + L.heavy_ntok), (int *)(ws + L.sorted_token)};
-        k_moe_permute<<<1, kBlock, 0, s>>>(
-            topk_ids, b, k, E, n_light, (int *)(ws + L.light_expert), (int *)(ws + L.light_start),
-            (int *)(ws + L.light_ntok), n_heavy, (int *)(ws + L.heavy_expert),
-            (int *)(ws + L.heavy_start), (int *)(ws + L.heavy_ntok), (int *)(ws + L.sorted_token),
-            slot_pos);
+        // the lists come from the permutation kernel, or were written by the
+        // selection kernel before this call (permuted)
+        if (!permuted)
+            k_moe_permute<<<1, kBlock, 0, s>>>(topk_ids, b, k, E, permute_out(L, ws));
         // Above kAllMfmaMin tokens every expert runs in the MFMA launches
         // (heavy list first, then the light one); below, light experts run
         // on dot2 rows.
@@ -910,18 +939,22 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
             record_dispatch(K3_OP_MOE_BLOCK, variant);
         return st;
     }
+    bool permuted = false;  // the selection kernel wrote the expert lists too
     if (variant == K3_VARIANT_DOT2) {
         // 1. router, latent and shared gate/up rows in one pass over x
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, w13_s, I_s, hs,
                    s);
         trace_end(K3_OP_MOE_BLOCK, s);
-        // 2. top-k in workgroup 0, the shared down projection in the others
+        // 2. top-k (and, above one token, the permutation) in workgroup 0,
+        //    the shared down projection in the others
         const int grid = dot2_grid(0);
         const size_t lds = (size_t)b * I_s * sizeof(uint16_t);
         const int cb = I_s > 2048 ? 16 : (I_s > 512 ? 4 : 1);
+        permuted = b > 1;
+        const PermuteOut po = permute_out(moe_workspace_layout(b, E, k, I, d), ws + L.moe);
 #define K3_TSD(TM_, CB_)                                                                       \
     k_topk_shared_down<TM_, CB_><<<grid, kBlock, lds, s>>>(logits, E, k, b, topk_ids, topk_w, \
-                                                           hs, I_s, w2_s, d, y_s)
+                                                           hs, I_s, w2_s, d, y_s, permuted, po)
         if (b == 1 && cb == 16)
             K3_TSD(1, 16);
         else if (b == 1 && cb == 4)
@@ -957,7 +990,7 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
     }
     // 3-4. routed gate/up, down and combine with the shared output added
     run_moe_experts(z, ldz, b, d_lat, topk_ids, topk_w, k, w13, w2, E, I, d, y_s, nullptr, y, 0,
-                    ws + L.moe, K3_OP_MOE_EXPERTS, s);
+                    ws + L.moe, K3_OP_MOE_EXPERTS, s, nullptr, permuted);
     const int st = launch_status();
     if (st == K3_OK)
         record_dispatch(K3_OP_MOE_BLOCK, variant);
