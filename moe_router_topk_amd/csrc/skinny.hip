@@ -89,6 +89,41 @@ k_sk_finish(const float *__restrict__ part, int ks, int T, int64_t ldp, SkOuts O
         sk_finish_one(part, ks, T, ldp, O, i);
 }
 
+// The finish of a pass whose first segment is the router (fp32 logits, +
+// bias) fused with the expert selection: workgroup t < T sums token t's
+// logits (exactly as k_sk_finish does), writes them out, keeps them in LDS,
+// and its first wave picks the token's experts from there (as the top-k
+// kernel would from memory); the other workgroups finish every other column
+// of every token. One launch instead of two.
+__global__ void __launch_bounds__(kBlock)
+k_sk_finish_topk(const float *__restrict__ part, int ks, int T, int64_t ldp, SkOuts O, int k,
+                 int32_t *__restrict__ ids, float *__restrict__ wts) {
+    const SkOutSeg &r = O.s[0];
+    const int E = r.cols;
+    if ((int)blockIdx.x < T) {
+        __shared__ float lg[K3_MAX_EXPERTS];
+        const int t = blockIdx.x;
+        const int64_t stride = (int64_t)T * ldp;
+        for (int c = threadIdx.x; c < E; c += kBlock) {
+            const float v = sk_sum(part, ks, stride, (int64_t)t * ldp + c);
+            const float l = r.bias ? v + r.bias[c] : v;
+            ((float *)r.y)[(int64_t)t * r.ldy + c] = l;
+            lg[c] = l;
+        }
+        __syncthreads();
+        if (threadIdx.x < kWave)
+            topk_wave(lg, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k);
+        return;
+    }
+    const int rest = O.cols_total - E;
+    const int64_t n = (int64_t)T * rest;
+    for (int64_t i = (int64_t)(blockIdx.x - T) * kBlock + threadIdx.x; i < n;
+         i += (int64_t)(gridDim.x - T) * kBlock) {
+        const int t = (int)(i / rest);
+        sk_finish_one(part, ks, T, ldp, O, (int64_t)t * O.cols_total + E + (i - (int64_t)t * rest));
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 int sk_tile_count(int N) { return (N + kSkRows - 1) / kSkRows; }
 
@@ -158,6 +193,17 @@ void sk_finish(const float *part, int ks, int T, int64_t ldp, const SkOuts &O, i
                                                                                   ldp, O);
 }
 
+// The finish of a pass whose segment 0 is the router, with the selection
+// (k_sk_finish_topk): T workgroups for the tokens' logits and picks, then
+// enough for the other columns.
+void sk_finish_topk(const float *part, int ks, int T, int64_t ldp, const SkOuts &O, int k,
+                    int32_t *ids, float *wts, hipStream_t s) {
+    const int64_t n = (int64_t)T * (O.cols_total - O.s[0].cols);
+    const int want = (int)((n + kBlock - 1) / kBlock);
+    const int grid = T + (want > 0 ? budget_grid(want, 0, 8) : 0);
+    k_sk_finish_topk<<<grid, kBlock, 0, s>>>(part, ks, T, ldp, O, k, ids, wts);
+}
+
 SkOuts sk_outs1(int mode, int cols, void *y, int64_t ldy, const float *bias) {
     SkOuts O{};
     O.s[0] = SkOutSeg{mode, cols, 0, y, ldy, bias, nullptr};
@@ -188,13 +234,12 @@ void sk_proj_f32_direct(const uint16_t *x, int64_t ldx, int T, const uint16_t *W
 }
 
 // Router scores and top-k: logits (fp32, + bias) from the router rows'
-// partials, then the selection kernel.
+// partials, finished together with the selection.
 void sk_router_topk(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int E, int K,
                     const float *bias, int k, float *logits, int32_t *ids, float *wts,
                     float *part, hipStream_t s) {
     const int ks = sk_dense_partials(&W, &E, 1, K, x, ldx, T, part, 0, s);
-    sk_finish(part, ks, T, E, sk_outs1(1, E, logits, E, bias), 0, s);
-    launch_topk(logits, T, E, k, ids, wts, s);
+    sk_finish_topk(part, ks, T, E, sk_outs1(1, E, logits, E, bias), k, ids, wts, s);
 }
 
 // Router top-k and latent projection in one pass over x.
@@ -210,8 +255,7 @@ void sk_router_topk_latent(const uint16_t *x, int64_t ldx, int T, int K, const u
     O.s[1] = SkOutSeg{0, d_lat, E, z, ldz, nullptr, nullptr};
     O.nseg = 2;
     O.cols_total = E + d_lat;
-    sk_finish(part, ks, T, E + d_lat, O, 0, s);
-    launch_topk(logits, T, E, k, ids, wts, s);
+    sk_finish_topk(part, ks, T, E + d_lat, O, k, ids, wts, s);
 }
 
 // Router top-k, latent projection and the shared expert's gate/up + SwiGLU
@@ -230,8 +274,7 @@ void sk_router_latent_shared(const uint16_t *x, int64_t ldx, int T, int K, const
     O.s[2] = SkOutSeg{2, I_s, E + d_lat, hs, I_s, nullptr, nullptr};
     O.nseg = 3;
     O.cols_total = E + d_lat + I_s;
-    sk_finish(part, ks, T, E + d_lat + 2 * I_s, O, 0, s);
-    launch_topk(logits, T, E, k, ids, wts, s);
+    sk_finish_topk(part, ks, T, E + d_lat + 2 * I_s, O, k, ids, wts, s);
 }
 
 // Shared expert's gate/up + SwiGLU: hs[t][j] (bf16, row stride I).
