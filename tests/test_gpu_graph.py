@@ -32,10 +32,10 @@ def _tiny_layer(prefetch_cu=8):
         "w_o": synth.randn_bf16((256, 256), 1 / math.sqrt(256), 3, "g_w_o", device=DEV),
         "gamma": torch.ones(256, dtype=torch.bfloat16, device=DEV),
     }
-    return DecodeLayer(w, cfg.k, b_max=4, chain=chain, prefetch_cu=prefetch_cu)
+    return DecodeLayer(w, cfg.k, b_max=64, chain=chain, prefetch_cu=prefetch_cu)
 
 
-@pytest.mark.parametrize("b", [1, 4])
+@pytest.mark.parametrize("b", [1, 4, 8, 64])
 def test_step_graph_replays_match_eager(k3, b):
     layer = _tiny_layer()
     x = synth.randn_bf16((b, 256), 1.0, 5, "g_x", b, device=DEV)
