@@ -222,6 +222,21 @@ def print_counter_summary(pmc_dir: str) -> int:
 
 
 # ------------------------------------------------------------------ timing helpers
+def read_ceiling(torch, k3, t, nbytes: int, reps: int = 7) -> float:
+    """GB/s of k3_stream_read over the first nbytes of t: the median of reps
+    event-timed reads."""
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        k3.k3_stream_read(t, nbytes)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return nbytes / (pct(ts, 0.5) * 1e-3) / 1e9
+
+
 def capture(torch, fn, n: int):
     """Capture fn(i) for i < n into one graph."""
     g = torch.cuda.CUDAGraph()
@@ -360,6 +375,12 @@ def main() -> int:
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
     prefetch = args.prefetch
 
+    # the measured streaming-read ceiling: 4 GiB of expert weights read once
+    # with the weight streams' non-temporal loads (k3_stream_read)
+    ceil_bytes = min(4 << 30, layers[0].moe["w13"].numel() * 2)
+    ceiling = read_ceiling(torch, k3, layers[0].moe["w13"], ceil_bytes)
+    log(f"streaming-read ceiling: {ceiling:.0f} GB/s over {ceil_bytes / 2**30:.1f} GiB")
+
     def step(i, bb=b):
         lay = layers[i % len(layers)]
         inp = pool[i % NX]
@@ -445,6 +466,7 @@ def main() -> int:
                  round(alt_ms * 1e3, 2),
              "moe_block_two_stream_us": round(streams_ms * 1e3, 2),
              "moe_block_frac_of_peak": round(moe_gbs / PEAK_GBS, 4),
+             "moe_block_frac_of_read_ceiling": round(moe_gbs / ceiling, 4),
              "eager_step_us": round(eager_ms * 1e3, 2),
              "eager_step_us_median": round(pct(per, 0.5) * 1e3, 2),
              "eager_step_us_p10": round(pct(per, 0.1) * 1e3, 2),
@@ -473,7 +495,8 @@ def main() -> int:
             sweep.append({"what": "moe_block", "b": bb, "routing": "zipf1.1" if zipf else "uniform",
                           "us": round(us, 1), "n_active_mean": na,
                           "GBps": round(by / us / 1e3, 1),
-                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)})
+                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
+                          "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4)})
             log(f"MoE block b={bb} {'zipf' if zipf else 'uniform'}: {us:.1f} us, "
                 f"n_active {na:.1f}, {by / us / 1e3:.0f} GB/s")
             # the whole layer step at this batch: chain, then the block on its output
@@ -491,7 +514,8 @@ def main() -> int:
             entry = {"what": "layer_step", "b": bb,
                      "routing": "zipf1.1" if zipf else "uniform", "us": round(us, 1),
                      "n_active_mean": na, "GBps": round(by / us / 1e3, 1),
-                     "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)}
+                     "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
+                     "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4)}
             if not args.no_cpu_baseline:
                 # the oracle beside it: one layer step at this batch on the host cores
                 cfg_b = synth.MOE_CONFIGS["b64zipf" if zipf else "b16"]
@@ -519,7 +543,8 @@ def main() -> int:
             by = chain_bytes(cc, bb)
             sweep.append({"what": "chain", "b": bb, "us": round(us, 1),
                           "GBps": round(by / us / 1e3, 1),
-                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4)})
+                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
+                          "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4)})
             log(f"chain b={bb}: {us:.1f} us, {by / us / 1e3:.0f} GB/s")
         extra["sweep"] = sweep
 
@@ -538,6 +563,10 @@ def main() -> int:
         "ms_per_step": round(ms, 5),
         "us_per_step": round(ms * 1e3, 2),
         "frac_of_peak": round(gbs / PEAK_GBS, 4),
+        "frac_of_read_ceiling": round(gbs / ceiling, 4),
+        "read_ceiling": {"GBps": round(ceiling, 1), "bytes": int(ceil_bytes),
+                         "kernel": "k3_stream_read: non-temporal 128-bit loads, one workgroup "
+                                   "per compute unit"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -562,6 +591,7 @@ def main() -> int:
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gu_gbs / PEAK_GBS, 4),
+            "frac_of_read_ceiling": round(gu_gbs / ceiling, 4),
             "traffic": traffic_per_launch() if b == 1 else None,
             "bytes_per_launch": int(gu_bytes),
             "avg_launch_us": round(kern_avg * 1e3, 2),

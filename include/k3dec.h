@@ -331,6 +331,17 @@ const float *k3_oproj_residual_h32(const void *workspace);
  */
 int k3_prefetch(const void *p, size_t bytes, int cu_budget, void *stream);
 
+/* Streaming-read reference (a measurement aid, not a step of the path):
+ * reads [p, p + bytes) once with the non-temporal 128-bit loads the weight
+ * streams use, one workgroup per compute unit, and discards the data. Its
+ * rate over a few GB is the device's measured streaming-read ceiling, which
+ * the path's kernels are compared with beside the 8 TB/s specification.
+ *
+ * p device, 16-byte aligned; bytes a multiple of 16 (0 is a no-op).
+ * Errors as k3_prefetch. Asynchronous on `stream`.
+ */
+int k3_stream_read(const void *p, size_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "K3Error", "lib", "library_path",
     "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
-    "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_moe_block",
+    "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_stream_read", "k3_moe_block",
     "k3_moe_block_rmsnorm", "oproj_h32_view",
     "k3_get_last_dispatch", "k3_force_variant",
     "k3_trace_events", "HipEvent",
@@ -43,7 +43,7 @@ EXPORTED_SYMBOLS = [
     "k3_moe_block_rmsnorm_workspace_size",
     "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
     "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_moe_block",
-    "k3_moe_block_rmsnorm", "k3_oproj_residual_h32",
+    "k3_moe_block_rmsnorm", "k3_oproj_residual_h32", "k3_stream_read",
 ]
 
 _vp = ctypes.c_void_p
@@ -118,8 +118,9 @@ def lib():
     L.k3_oproj_residual.argtypes = [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, ctypes.c_float,
                                     _vp, _vp, _sz, _vp]
     L.k3_prefetch.argtypes = [_vp, _sz, _i32, _vp]
+    L.k3_stream_read.argtypes = [_vp, _sz, _vp]
     for f in ("k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
-              "k3_shared_expert", "k3_oproj_residual", "k3_prefetch"):
+              "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_stream_read"):
         getattr(L, f).restype = _i32
     _lib = L
     return _lib
@@ -447,3 +448,10 @@ def k3_prefetch(t, nbytes=None, cu_budget=0, stream=None):
     """Read the first nbytes of tensor t (default: all of it) into the MALL."""
     nbytes = t.numel() * t.element_size() if nbytes is None else int(nbytes)
     _check("k3_prefetch", lib().k3_prefetch(_ptr(t), nbytes, int(cu_budget), _stream(stream)))
+
+
+def k3_stream_read(t, nbytes=None, stream=None):
+    """Read the first nbytes of tensor t (default: all of it) with the weight
+    streams' non-temporal loads and discard them (streaming-read ceiling)."""
+    nbytes = t.numel() * t.element_size() if nbytes is None else int(nbytes)
+    _check("k3_stream_read", lib().k3_stream_read(_ptr(t), nbytes, _stream(stream)))

@@ -16,7 +16,9 @@ namespace k3 {
 
 __device__ uint32_t g_prefetch_sink;
 
-template <int U>
+// NT: non-temporal loads (the weight streams' kind) instead of allocating
+// ones; k3_stream_read uses them to measure the streaming-read ceiling.
+template <int U, bool NT = false>
 __global__ void __launch_bounds__(kBlock)
 k_prefetch(const u32x4 *__restrict__ p, size_t n, uint32_t never) {
     const size_t stride = (size_t)gridDim.x * kBlock * U;
@@ -26,7 +28,7 @@ k_prefetch(const u32x4 *__restrict__ p, size_t n, uint32_t never) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t i = base + (size_t)u * kBlock;
-            v[u] = i < n ? p[i] : zero16();
+            v[u] = i < n ? (NT ? __builtin_nontemporal_load(p + i) : p[i]) : zero16();
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -64,4 +66,20 @@ extern "C" int k3_prefetch(const void *p, size_t bytes, int cu_budget, void *str
     if (st == K3_OK)
         record_dispatch(K3_OP_PREFETCH, K3_VARIANT_STREAM);
     return st;
+}
+
+extern "C" int k3_stream_read(const void *p, size_t bytes, void *stream) {
+    if (bytes == 0)
+        return K3_OK;
+    if (!p)
+        return K3_ERR_INVALID_ARG;
+    if (!aligned16(p) || bytes % 16)
+        return K3_ERR_UNSUPPORTED;
+    const size_t n = bytes / 16;
+    const size_t per_block = (size_t)kBlock * 8;
+    const size_t want = (n + per_block - 1) / per_block;
+    const int grid = budget_grid(want > (1u << 30) ? (1 << 30) : (int)want, 0, 1);
+    k_prefetch<8, true><<<grid, kBlock, 0, (hipStream_t)stream>>>((const u32x4 *)p, n,
+                                                                  0x9e3779b9u);
+    return launch_status();
 }

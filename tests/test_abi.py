@@ -251,6 +251,13 @@ def test_prefetch_validation(L):
     assert L.k3_prefetch(P, 24, 0, None) == UNSUP
 
 
+def test_stream_read_validation(L):
+    assert L.k3_stream_read(P, 0, None) == K3_OK  # nothing to read: no launch
+    assert L.k3_stream_read(None, 16, None) == INVALID
+    assert L.k3_stream_read(MIS, 16, None) == UNSUP
+    assert L.k3_stream_read(P, 24, None) == UNSUP
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import moe_router_topk_amd as k3
     monkeypatch.setattr(k3, "_lib", None)

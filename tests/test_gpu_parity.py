@@ -452,6 +452,18 @@ def test_prefetch_reads_only(k3):
     assert k3.k3_get_last_dispatch("prefetch") == "stream"
 
 
+def test_stream_read_reads_only(k3):
+    t = synth.randn_bf16((1 << 20,), 1.0, 0, "sr", device=DEV)
+    t0 = t.clone()
+    k3.k3_stream_read(t)
+    k3.k3_stream_read(t, nbytes=16)
+    k3.k3_stream_read(t, nbytes=0)
+    torch.cuda.synchronize()
+    assert torch.equal(t, t0)
+    with pytest.raises(k3.K3Error):
+        k3.k3_stream_read(t, nbytes=24)
+
+
 # ---------------------------------------------------------------- whole block / layer
 def test_tiny_layer_end_to_end(k3):
     from moe_router_topk_amd.layer import DecodeLayer
