@@ -80,20 +80,23 @@ def test_router_topk_full(k3, full, b, zipf):
     assert k3.k3_get_last_dispatch("router_topk") == want
 
 
-def test_router_topk_ties(k3):
-    """x = 0 makes every logit 0: ids 0..k-1 and weights 1/k."""
-    x = torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV)
+@pytest.mark.parametrize("b", [2, 8])
+def test_router_topk_ties(k3, b):
+    """x = 0 makes every logit 0: ids 0..k-1 and weights 1/k (row engine at
+    2 tokens, the MFMA pass with its finish-and-select kernel at 8)."""
+    x = torch.zeros((b, 256), dtype=torch.bfloat16, device=DEV)
     wr = synth.uniform_bf16((8, 256), 0.1, 0, "tie", device=DEV)
     ids, wts = k3.k3_router_topk(x, wr, None, 3)
     torch.cuda.synchronize()
-    assert ids.cpu().tolist() == [[0, 1, 2], [0, 1, 2]]
+    assert ids.cpu().tolist() == [[0, 1, 2]] * b
     np.testing.assert_allclose(wts.cpu().numpy(), 1 / 3, rtol=1e-6)
 
 
-def test_router_topk_k_equals_E(k3):
+@pytest.mark.parametrize("b", [4, 8, 33])
+def test_router_topk_k_equals_E(k3, b):
     cfg = synth.MOE_CONFIGS["tiny"]
     w = synth.make_moe_weights(cfg, device=DEV)
-    x = synth.make_tokens(cfg, device=DEV, b=4)
+    x = synth.make_tokens(cfg, device=DEV, b=b)
     ids, wts = k3.k3_router_topk(x, w["w_router"], None, cfg.E)
     torch.cuda.synchronize()
     logits = oracle.router_logits(x.cpu(), w["w_router"].cpu())
