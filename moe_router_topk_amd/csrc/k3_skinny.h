@@ -137,16 +137,22 @@ __device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32
 //   int  xld(jb)                          its row stride in elements
 //   void store(jb, tile, ks, wq, acc, xch)   epilogue (may hold a block barrier)
 // One item per loop iteration (the pipeline is filled per item): for dense
-// projections, whose items are many and uniform.
-template <int MT, class Jobs>
+// projections, whose items are many and uniform. TPW 16-row tiles per wave
+// (J.tpw must equal it) over K chunks of kSkKc / TPW: with TPW = 2 a staged
+// token chunk serves twice the weight rows, which halves the token staging
+// per weight byte (at 64 tokens it would otherwise equal the weight bytes).
+// The K-steps run in the same order for either TPW, so the sums are the same.
+template <int MT, class Jobs, int TPW = 1>
 __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
+    constexpr int KC = kSkKc / TPW;  // K per chunk
+    constexpr int KQ = KC / 8;       // 16-byte vectors per token row of a chunk
     // two token buffers (chunks alternate); +1 vector per row keeps the MFMA
     // reads conflict-free
-    __shared__ u32x4 xs[2][MT * 16][kSkKq + 1];
+    __shared__ u32x4 xs[2][MT * 16][KQ + 1];
     __shared__ float xch[2][MT][4][kWave];     // epilogue exchange between waves
-    constexpr int SQ = MT * 16 * kSkKq / kBlock;  // staged vectors per thread per chunk
+    constexpr int SQ = MT * 16 * KQ / kBlock;  // staged vectors per thread per chunk
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
-    const int nchunks = (K + kSkKc - 1) / kSkKc;
+    const int nchunks = (K + KC - 1) / KC;
     const int per_job = J.tiles() * ksplit;
     const int items = J.count() * per_job;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
@@ -166,30 +172,30 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         const uint32_t wbytes =
             (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u;
         // This thread stages vectors q = tid + j * 256 of each chunk: token
-        // q / kSkKq, vector q % kSkKq. Rows past T read zeros through the
-        // buffer range (no branch, no memory access).
+        // q / KQ, vector q % KQ. Rows past T read zeros through the buffer
+        // range (no branch, no memory access).
         const uint16_t *xb = uniform_ptr(J.xbase(jb));
         const uint32_t xld = (uint32_t)J.xld(jb);
         uint32_t xo[SQ];
         bool xv[SQ];
 #pragma unroll
         for (int j = 0; j < SQ; ++j) {
-            const int t = (threadIdx.x + j * kBlock) / kSkKq;
+            const int t = (threadIdx.x + j * kBlock) / KQ;
             xv[j] = t < T;
             xo[j] = (uint32_t)J.xrow(jb, xv[j] ? t : 0) * xld;
         }
-        const int vq = threadIdx.x % kSkKq;
+        const int vq = threadIdx.x % KQ;
         int c0, c1;
         split_range(nchunks, ksplit, ks, c0, c1);
         // Loads of a chunk past the item's range read nothing (an empty
         // range, offsets out of range): every load is issued on every path,
         // so the waits for a buffer count exactly the loads issued after it.
         auto wload = [&](u32x4 (&buf)[kSkKb], int c) {
-            sk_wload(buf, weight_range(wbase, c < c1 ? wbytes : 0u), c, K, lane);
+            sk_wload_t<TPW>(buf, weight_range(wbase, c < c1 ? wbytes : 0u), c, K, lane);
         };
         auto aload = [&](u32x4 (&st)[SQ], int c) {
             const rsrc_t rx = act_range(xb);
-            const int k = c * kSkKc + 8 * vq;
+            const int k = c * KC + 8 * vq;
             const bool kv = k < K && c < c1;
 #pragma unroll
             for (int j = 0; j < SQ; ++j)
@@ -199,15 +205,17 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
 #pragma unroll
             for (int j = 0; j < SQ; ++j) {
                 const int q = threadIdx.x + j * kBlock;
-                xs[b][q / kSkKq][q % kSkKq] = st[j];
+                xs[b][q / KQ][q % KQ] = st[j];
             }
         };
-        f32x4 acc[MT];
+        f32x4 acc[TPW][MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto compute = [&](u32x4 (&buf)[kSkKb], int b) {
-            sk_mfma_chunk<MT>(acc, buf, xs[b], mt_n, lane);
+            sk_mfma_chunk_t<MT, TPW>(acc, buf, xs[b], mt_n, lane);
         };
         // Chunk c (the item's chunks alternate between token buffers 0 and 1):
         // the weights of chunk c + 1 go out, chunk c is multiplied, the tokens
@@ -237,8 +245,10 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
             aload(st, c + 3);
             __syncthreads();
         }
-        // acc[mt][i] = out[token 16 mt + 4 g + i][row rl of this wave's 16]
-        J.store(jb, tile, ks, wq, acc, xch);
+        // acc[tt][mt][i] = out[token 16 mt + 4 g + i][row rl of the wave's tile tt]
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+            J.store(jb, tile, ks, wq, tt, acc[tt], xch);
         __syncthreads();  // xs and xch are reused by the next item
     }
 }
@@ -428,8 +438,9 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
 // One dense projection made of up to three row segments (e.g. router,
 // latent and shared gate/up rows, all against the same tokens). Segment s
 // has N[s] rows (a multiple of 16) of W[s]; its rows are numbered after the
-// previous segments' rows in the output. The epilogue writes fp32 partials
-// part[(ks * T + t) * ldp + n], n the row in that numbering.
+// previous segments' rows in the output. A tile is 64 tpw rows (16 tpw per
+// wave). The epilogue writes fp32 partials part[(ks * T + t) * ldp + n], n
+// the row in that numbering.
 struct SkDense {
     const uint16_t *W[3];
     int N[3];
@@ -441,6 +452,7 @@ struct SkDense {
     int T;
     float *part;
     int64_t ldp;
+    int tpw;  // 16-row tiles per wave
 
     struct Job {
         int T;
@@ -453,19 +465,21 @@ struct SkDense {
     }
     __device__ void wave_rows(const Job &, int tile, int wq, const uint16_t *&w, int &n) const {
         const int s = seg(tile);
-        const int r0 = (tile - tiles_before[s]) * kSkRows + wq * 16;
-        n = max(0, min(16, N[s] - r0));
+        const int r0 = (tile - tiles_before[s]) * kSkRows * tpw + wq * 16 * tpw;
+        n = max(0, min(16 * tpw, N[s] - r0));
         w = W[s] + (int64_t)(n > 0 ? r0 : 0) * K;
     }
     __device__ const uint16_t *xbase(const Job &) const { return x; }
     __device__ int xrow(const Job &, int t) const { return t; }
     __device__ int xld(const Job &) const { return (int)ldx; }
+    // Epilogue of tile tt of the wave's tpw tiles.
     template <int MT>
-    __device__ void store(const Job &, int tile, int ks, int wq, const f32x4 (&acc)[MT],
+    __device__ void store(const Job &, int tile, int ks, int wq, int tt, const f32x4 (&acc)[MT],
                           float (*)[MT][4][kWave]) const {
         const int lane = threadIdx.x & (kWave - 1);
         const int s = seg(tile);
-        const int r = (tile - tiles_before[s]) * kSkRows + wq * 16 + (lane & 15);
+        const int r =
+            (tile - tiles_before[s]) * kSkRows * tpw + wq * 16 * tpw + 16 * tt + (lane & 15);
         if (r >= N[s])
             return;
         const int n = rows_before[s] + r;

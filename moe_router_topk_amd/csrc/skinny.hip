@@ -125,8 +125,6 @@ k_sk_finish_topk(const float *__restrict__ part, int ks, int T, int64_t ldp, SkO
 }
 
 // ------------------------------------------------------------------ launchers
-int sk_tile_count(int N) { return (N + kSkRows - 1) / kSkRows; }
-
 // K ranges of a K-wide projection: a function of K alone (about four chunks
 // per range, at most kSkMaxSplit ranges), so every call that streams the
 // same rows against the same tokens sums them in the same order, whichever
@@ -151,6 +149,10 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
                       int64_t ldx, int T, float *part, int cu_budget, hipStream_t s,
                       int ks_force = 0, int64_t ldp_force = 0) {
     SkDense J{};
+    // at 33-64 tokens each wave streams two 16-row tiles (half the token
+    // staging per weight byte); below, one
+    const int mt = sk_mt(T);
+    J.tpw = mt == 4 ? 2 : 1;
     int tiles = 0, rows = 0;
     for (int i = 0; i < 3; ++i) {
         J.W[i] = i < nseg ? W[i] : W[0];
@@ -158,7 +160,7 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
         J.tiles_before[i] = tiles;
         J.rows_before[i] = rows;
         if (i < nseg) {
-            tiles += sk_tile_count(N[i]);
+            tiles += (N[i] + kSkRows * J.tpw - 1) / (kSkRows * J.tpw);
             rows += N[i];
         }
     }
@@ -171,15 +173,15 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
     J.ldp = ldp_force > 0 ? ldp_force : rows;
     const int ks = ks_force > 0 ? ks_force : sk_ksplit(K);
     const int grid = budget_grid(tiles * ks, cu_budget, 2);
-    switch (sk_mt(T)) {
+    switch (mt) {
     case 1:
-        k_sk_gemm<1, SkDense><<<grid, kBlock, 0, s>>>(J, K, ks);
+        k_sk_gemm<1, SkDense, 1><<<grid, kBlock, 0, s>>>(J, K, ks);
         break;
     case 2:
-        k_sk_gemm<2, SkDense><<<grid, kBlock, 0, s>>>(J, K, ks);
+        k_sk_gemm<2, SkDense, 1><<<grid, kBlock, 0, s>>>(J, K, ks);
         break;
     default:
-        k_sk_gemm<4, SkDense><<<grid, kBlock, 0, s>>>(J, K, ks);
+        k_sk_gemm<4, SkDense, 2><<<grid, kBlock, 0, s>>>(J, K, ks);
         break;
     }
     return ks;
