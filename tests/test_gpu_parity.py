@@ -105,6 +105,23 @@ def test_router_topk_k_equals_E(k3, b):
     assert_rel_close(wts.cpu(), ref_w, "topk_w")
 
 
+@pytest.mark.parametrize("b", [1, 3, 8, 40])
+def test_router_topk_many_experts(k3, b):
+    """E = 1000 experts (near the 1024 limit, not a multiple of the wave),
+    k = 16, with a bias: every engine's selection against the oracle."""
+    E, d, k = 1000, 512, 16
+    wr = synth.uniform_bf16((E, d), math.sqrt(3.0 / d), 0, "many_wr", device=DEV)
+    bias = synth.zipf_router_bias(E, 1.1, 0).to(DEV)
+    x = synth.randn_bf16((b, d), 1.0, 0, "many_x", b, device=DEV)
+    ids, wts = k3.k3_router_topk(x, wr, bias, k)
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(x.cpu(), wr.cpu(), bias.cpu())
+    ref_ids, ref_w = oracle.topk_softmax(logits, k)
+    differ = check_ids(ids, ref_ids, logits, k)
+    keep = [t for t in range(b) if t not in differ]
+    assert_rel_close(wts.cpu().numpy()[keep], ref_w[keep], "topk_w")
+
+
 @pytest.mark.parametrize("b,zipf", [(1, 0.0), (2, 0.0), (4, 1.1), (16, 0.0), (64, 1.1)])
 def test_router_topk_latent_full(k3, full, b, zipf):
     """The fused router + latent pass: ids and weights as k3_router_topk, z as
