@@ -102,20 +102,35 @@ __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv,
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         acc[t] = 0.0f;
+    // When the quarter is a non-empty whole number of units every piece of a
+    // unit lies inside it and needs no mask; the sums of the empty units at
+    // the end belong to groups past the last and are never stored. (An empty
+    // quarter, K < 256, takes the masked path: its one unit per group must
+    // add nothing.)
+    const bool exact = p1 > p0 && (p1 - p0) % U == 0;
     auto fin = [&](u32x4 (&b)[U], int u) {
         const int g = u / upg, c = u - g * upg;
+        if (exact) {
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            // a piece past the quarter has zero weights; its activations are
-            // masked to zero too (no branch: a skipped wait at a join would
-            // make the compiler wait for every load in flight)
-            const int p = p0 + c * U + i;
-            const uint32_t m = (p < p1 && u < nunits) ? 0xffffffffu : 0u;
-            const int kv = min(p, p1 - 1) * 8 + (lane & 7);
+            for (int i = 0; i < U; ++i) {
+                const int kv = (p0 + c * U + i) * 8 + (lane & 7);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const u32x4 xa = xv(g, kv, t);
-                acc[t] = dot8(b[i], u32x4{xa.x & m, xa.y & m, xa.z & m, xa.w & m}, acc[t]);
+                for (int t = 0; t < NT; ++t)
+                    acc[t] = dot8(b[i], xv(g, kv, t), acc[t]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                // a piece past the quarter has zero weights; its activations
+                // are masked to zero too (a mask, not a branch around loads)
+                const int p = p0 + c * U + i;
+                const uint32_t m = (p < p1 && u < nunits) ? 0xffffffffu : 0u;
+                const int kv = min(p, p1 - 1) * 8 + (lane & 7);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const u32x4 xa = xv(g, kv, t);
+                    acc[t] = dot8(b[i], u32x4{xa.x & m, xa.y & m, xa.z & m, xa.w & m}, acc[t]);
+                }
             }
         }
         if (c == upg - 1) {
