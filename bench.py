@@ -169,9 +169,9 @@ def write_traffic_summary(pmc_dir: str) -> int:
         "kernel": "k3::k_moe_up_b1<true> (expert selection + routed gate/up + SwiGLU), "
                   "batch 1, d=7168, E=384, k=8, I=2048",
         "commands": [
-            f"rocprofv3 --pmc {ctr} --output-format csv -d gpurun_out/pmc_{key} -o c -- "
+            f"rocprofv3 --pmc {ctr} --output-format csv -d {pmc_dir}/pmc_{key} -o c -- "
             f"python3 -u bench.py {args}" for key, (ctr, args) in PMC_RUNS.items()
-        ] + ["python3 bench.py --traffic-summary gpurun_out"],
+        ] + [f"python3 bench.py --traffic-summary {pmc_dir}"],
         "dispatches_averaged": {"FETCH_SIZE": len(fetch), "WRITE_SIZE": len(write)},
         "fetch_kib_per_dispatch": round(f_kib, 1),
         "write_kib_per_dispatch": round(w_kib, 1),
