@@ -51,7 +51,7 @@ extern "C" {
 #define K3_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than the size query says */
 #define K3_ERR_HIP (-4)          /* the HIP runtime reported an error at launch */
 
-/* Limits of this build. */
+/* Limits of the library (argument checks return K3_ERR_UNSUPPORTED beyond them). */
 #define K3_MAX_BATCH 64      /* tokens per call */
 #define K3_MAX_EXPERTS 1024  /* routed experts E */
 #define K3_MAX_TOPK 32       /* experts per token k */
