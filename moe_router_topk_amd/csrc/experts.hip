@@ -326,6 +326,10 @@ struct SkExperts {
         return n1() + (L2.n ? __builtin_amdgcn_readfirstlane(L2.count()) : 0);
     }
     __device__ int count() const { return nlist() + (w_x ? 1 : 0); }
+    // Down launches group each XCD's items (measured: 16-token down 480-486
+    // against 502-508 us, no change at 8 or 64 tokens); gate/up launches keep
+    // the plain interleave, which was faster for them at 8-64 tokens.
+    __device__ bool xcd_grouped() const { return !pair; }
     __device__ int tiles() const {
         return pair ? I / (32 * tpw) : (rows + 64 * tpw - 1) / (64 * tpw);
     }

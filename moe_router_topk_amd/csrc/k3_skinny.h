@@ -136,6 +136,7 @@ __device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32
 //   int  xrow(jb, t)                      row of token t in it (t < T; may read memory)
 //   int  xld(jb)                          its row stride in elements
 //   void store(jb, tile, ks, wq, acc, xch)   epilogue (may hold a block barrier)
+//   bool xcd_grouped()                    (stream kernel) give each XCD consecutive items
 // One item per loop iteration (the pipeline is filled per item): for dense
 // projections, whose items are many and uniform. TPW 16-row tiles per wave
 // (J.tpw must equal it) over K chunks of kSkKc / TPW: with TPW = 2 a staged
@@ -373,7 +374,13 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
             acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Cur C, W, A;  // multiply, weights (one ahead), tokens (two ahead)
-    open(C, blockIdx.x);
+    // Workgroups are dispatched to the 8 XCDs in turn, so consecutive items
+    // (the tiles of one expert) normally run on 8 XCDs. Grouped, workgroup b
+    // takes the items of virtual index (b % 8) G / 8 + b / 8: each XCD takes a
+    // consecutive block of every round, and one expert's token rows stay in
+    // one L2. Either way every item has exactly one workgroup.
+    const int G = gridDim.x, bx = blockIdx.x;
+    open(C, (J.xcd_grouped() && G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx);
     if (!C.valid)
         return;
     W = C;
