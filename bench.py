@@ -42,6 +42,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_moe_up_b1_traffic.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "layer_step_b1_kernel_trace.json")
+TRACE_MD = os.path.join(ROOT, "profiles", "layer_step_b1_kernel_stats.md")
+NX = 16  # token batches rotated through the steps
 DOMINANT_SOURCES = ["moe_router_topk_amd/csrc/moe_b1.hip", "moe_router_topk_amd/csrc/k3_gemv.h",
                     "moe_router_topk_amd/csrc/k3_device.h"]
 
@@ -105,6 +108,138 @@ def sources_digest(paths) -> str:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def trace_in_graph():
+    """The dominant kernel's average duration inside the graph-replayed timed
+    region, from the committed rocprofv3 kernel-trace summary, or None when it
+    is missing or the kernel changed since."""
+    try:
+        with open(TRACE_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sources_digest(DOMINANT_SOURCES):
+        return None
+    return t.get("dominant_timed_region_avg_us")
+
+
+# the kernels of one batch-1 layer step, once each, in launch order
+STEP_B1_KERNELS = ["k_gemv<7, 1,", "k_oproj_gemv<", "k_rls_gemv<7, 1, true>",
+                   "k_moe_up_b1<true", "k_down_b1<"]
+
+
+def write_trace_summary(trace_dir: str, warmup: int, steps: int, out_json: str = TRACE_FILE,
+                        out_md: str = TRACE_MD) -> int:
+    """Reduce the kernel trace of a default bench run (rocprofv3 --kernel-trace,
+    csv) to per-kernel statistics over all dispatches and over the timed
+    region: the K steps of the one graph replay the line's time comes from.
+    Each step kernel runs once per step, and before the timed replay come the
+    warm-up steps, the NX routing-statistics steps and the K eager steps, so
+    dispatches [warmup + NX + K, warmup + NX + 2K) of each are the replay's."""
+    import csv
+    import glob
+    import statistics as st
+    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"),
+                             recursive=True))
+    if not files:
+        print("bench.py: no kernel_trace.csv under " + trace_dir, file=sys.stderr)
+        return 2
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    allk = {}
+    for r in rows:
+        name = r["Kernel_Name"].split("(")[0]
+        if "k3::" in name:
+            allk.setdefault(name, []).append(r)
+    i0 = warmup + NX + steps
+    region = {}
+    for pat in STEP_B1_KERNELS:
+        hits = [n for n in allk if pat in n]
+        if len(hits) != 1 or len(allk[hits[0]]) < i0 + steps:
+            print(f"bench.py: step kernel {pat} not found {i0 + steps} times", file=sys.stderr)
+            return 2
+        region[hits[0]] = allk[hits[0]][i0:i0 + steps]
+
+    def dur(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+
+    first = region[[n for n in region if STEP_B1_KERNELS[0] in n][0]][0]
+    last = region[[n for n in region if STEP_B1_KERNELS[-1] in n][0]][-1]
+    span_us = (int(last["End_Timestamp"]) - int(first["Start_Timestamp"])) / 1000.0
+    dom = [n for n in region if STEP_B1_KERNELS[3] in n][0]
+    dom_d = [dur(r) for r in region[dom]]
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o kt -- "
+           f"python3 -u bench.py --steps {steps} --warmup {warmup} --no-sweep "
+           f"--no-cpu-baseline")
+    out = {
+        "command": cmd,
+        "summary_command": f"python3 bench.py --trace-summary {trace_dir} --steps {steps} "
+                           f"--warmup {warmup}",
+        "timed_region_steps": steps,
+        "timed_region_us_per_step": round(span_us / steps, 2),
+        "dominant_kernel": dom,
+        "dominant_timed_region_avg_us": round(sum(dom_d) / len(dom_d), 2),
+        "dominant_timed_region_median_us": round(st.median(dom_d), 2),
+        "dominant_all_dispatches_avg_us": round(
+            sum(dur(r) for r in allk[dom]) / len(allk[dom]), 2),
+        "source_sha256": sources_digest(DOMINANT_SOURCES),
+    }
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=2)
+        f.write("\n")
+    lines = [
+        "# Kernel trace of the batch-1 layer step (rocprofv3)",
+        "",
+        "Command (on the GPU box, from the repository root):",
+        "",
+        "    " + cmd,
+        "    " + out["summary_command"],
+        "",
+        f"Timed region: the {steps} graph-replayed steps the bench line's time comes from "
+        f"(dispatches {i0}..{i0 + steps - 1} of each step kernel; warm-up {warmup}, "
+        f"{NX} routing-statistics steps and {steps} eager steps come first). Trace span "
+        f"from the first step's input projection to the last step's down projection: "
+        f"{span_us / steps:.2f} us per step.",
+        "",
+        "| Kernel (timed region) | dispatches | avg us | median us | min us | max us |",
+        "|---|---|---|---|---|---|",
+    ]
+    for n in region:
+        d = [dur(r) for r in region[n]]
+        lines.append(f"| `{n}` | {len(d)} | {sum(d) / len(d):.2f} | {st.median(d):.2f} | "
+                     f"{min(d):.2f} | {max(d):.2f} |")
+    lines += ["", "| Kernel (every dispatch of the run: eager and graph-replayed) | dispatches "
+              "| avg us | median us |", "|---|---|---|---|"]
+    for n, rs in sorted(allk.items(), key=lambda kv: -sum(dur(r) for r in kv[1])):
+        d = [dur(r) for r in rs]
+        lines.append(f"| `{n}` | {len(d)} | {sum(d) / len(d):.2f} | {st.median(d):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out))
+    return 0
+
+
+def host_info() -> dict:
+    """What the oracle's timings ran on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "nproc": nproc,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def traffic_per_launch():
@@ -302,13 +437,13 @@ def main() -> int:
                     help="run the side-stream prefetch inside the timed step")
     ap.add_argument("--cu-shared", type=int, default=0, help="CU budget of the shared expert")
     ap.add_argument("--prefetch-cu", type=int, default=32, help="CU budget of the prefetch")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the b = 1..64 sweep")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the b = 2..64 sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager-only", action="store_true",
-                    help="time host-launched steps only (no graph, sweep or CPU leg); "
-                         "for profiler counter runs")
+                    help="host-launched steps on one stream only: no HIP graph is captured, "
+                         "no side stream runs, no sweep or CPU leg; for profiler counter runs")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     ap.add_argument("--traffic-summary", metavar="DIR", default="",
@@ -317,11 +452,17 @@ def main() -> int:
     ap.add_argument("--counter-summary", metavar="DIR", default="",
                     help="no GPU work: per-kernel means of every counter in the rocprofv3 "
                          "--pmc csv files under DIR, as a markdown table")
+    ap.add_argument("--trace-summary", metavar="DIR", default="",
+                    help="no GPU work: reduce the rocprofv3 kernel trace of a default run "
+                         "(same --steps/--warmup) to per-kernel statistics of its timed "
+                         "region (written under profiles/)")
     args = ap.parse_args()
     if args.traffic_summary:
         return write_traffic_summary(args.traffic_summary)
     if args.counter_summary:
         return print_counter_summary(args.counter_summary)
+    if args.trace_summary:
+        return write_trace_summary(args.trace_summary, args.warmup, args.steps)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -331,6 +472,11 @@ def main() -> int:
     if not 1 <= args.steps <= 2000:
         print("bench.py: --steps must be in 1..2000", file=sys.stderr)
         return 2
+    if args.eager_only:
+        args.no_sweep = args.no_cpu_baseline = True
+        if args.prefetch:
+            print("bench.py: --eager-only runs one stream; drop --prefetch", file=sys.stderr)
+            return 2
 
     import torch
 
@@ -368,7 +514,6 @@ def main() -> int:
         for lay in layers:
             lay.moe["bias"] = zbias
         cfg = synth.MOE_CONFIGS["b64zipf"]  # the same layer with the bias counted
-    NX = 16
     pool = [synth.make_chain_inputs(cc, 64, device=dev, index=i) for i in range(NX)]
     torch.cuda.synchronize()
     log(f"weights + inputs ready in {time.perf_counter() - t_gen:.1f} s "
@@ -406,7 +551,6 @@ def main() -> int:
     # ---- timed region: exactly K steps in one graph, one replay
     if args.eager_only:
         ms, wall = eager_ms, float("nan")
-        args.no_sweep = args.no_cpu_baseline = True
     else:
         g = capture(torch, step, K)
         ms, wall = replay_timed(torch, g, K)
@@ -440,31 +584,7 @@ def main() -> int:
     log(f"MoE block b={b}: {moe_ms * 1e3:.1f} us, {moe_gbs:.0f} GB/s "
         f"({100 * moe_gbs / PEAK_GBS:.1f}% of peak)")
 
-    # the other configurations, for comparison (graph-timed like the step)
-    def step_alt(i):
-        lay = layers[i % len(layers)]
-        return lay.step(pool[i % NX]["x"][:b], pool[i % NX]["r"][:b], prefetch=not prefetch)
-
-    step_alt(0)
-    g = capture(torch, step_alt, K)
-    alt_ms, _ = replay_timed(torch, g, K)
-    del g
-
-    def block_streams(i, bb=b):
-        lay = layers[i % len(layers)]
-        return lay.moe_block_streams(pool[i % NX]["x"][:bb])
-
-    block_streams(0)
-    g = capture(torch, block_streams, K)
-    streams_ms, _ = replay_timed(torch, g, K)
-    del g
-    log(f"step with prefetch {'off' if prefetch else 'on'}: {alt_ms * 1e3:.1f} us; "
-        f"MoE block as two-stream composition: {streams_ms * 1e3:.1f} us")
-
     extra = {"moe_block_us": round(moe_ms * 1e3, 2), "moe_block_GBps": round(moe_gbs, 1),
-             ("step_us_prefetch_off" if prefetch else "step_us_prefetch_on"):
-                 round(alt_ms * 1e3, 2),
-             "moe_block_two_stream_us": round(streams_ms * 1e3, 2),
              "moe_block_frac_of_peak": round(moe_gbs / PEAK_GBS, 4),
              "moe_block_frac_of_read_ceiling": round(moe_gbs / ceiling, 4),
              "eager_step_us": round(eager_ms * 1e3, 2),
@@ -473,32 +593,99 @@ def main() -> int:
              "eager_step_us_p90": round(pct(per, 0.9) * 1e3, 2),
              "bytes_per_step": int(bytes_step), "n_active_mean": mean_act}
 
-    # ---- sweep: MoE block and layer step at b = 4, 8, 16, 32 (uniform) and 64 (Zipf
-    # bias); chain b = 1..64
+    # the other configurations, for comparison (graph-timed like the step);
+    # both use a second stream, so a counter run (--eager-only) skips them
+    if not args.eager_only:
+        def step_alt(i):
+            lay = layers[i % len(layers)]
+            return lay.step(pool[i % NX]["x"][:b], pool[i % NX]["r"][:b], prefetch=not prefetch)
+
+        step_alt(0)
+        g = capture(torch, step_alt, K)
+        alt_ms, _ = replay_timed(torch, g, K)
+        del g
+
+        def block_streams(i, bb=b):
+            lay = layers[i % len(layers)]
+            return lay.moe_block_streams(pool[i % NX]["x"][:bb])
+
+        block_streams(0)
+        g = capture(torch, block_streams, K)
+        streams_ms, _ = replay_timed(torch, g, K)
+        del g
+        log(f"step with prefetch {'off' if prefetch else 'on'}: {alt_ms * 1e3:.1f} us; "
+            f"MoE block as two-stream composition: {streams_ms * 1e3:.1f} us")
+        extra[("step_us_prefetch_off" if prefetch else "step_us_prefetch_on")] = \
+            round(alt_ms * 1e3, 2)
+        extra["moe_block_two_stream_us"] = round(streams_ms * 1e3, 2)
+
+    # ---- the tiny workload (d = 256, E = 8, top-2, I = 128): launch-bound, its
+    # weights sit in the caches; us only
+    if not args.no_sweep:
+        tcfg = synth.MOE_CONFIGS["tiny"]
+        tw = synth.make_moe_weights(tcfg, device=dev)
+        tl = DecodeLayer(tw, tcfg.k, b_max=1)
+        tx = [synth.make_tokens(tcfg, device=dev, index=i, b=1) for i in range(NX)]
+        tl.moe_block(tx[0])
+        g = capture(torch, lambda i: tl.moe_block(tx[i % NX]), K)
+        tiny_ms, _ = replay_timed(torch, g, K)
+        del g
+        extra["tiny"] = {"what": "moe_block", "b": 1, "d": tcfg.d, "E": tcfg.E,
+                         "top_k": tcfg.k, "I": tcfg.I, "us": round(tiny_ms * 1e3, 2),
+                         "note": "launch-bound (about 725 KB of weights, cache-resident); "
+                                 "no GB/s claim"}
+        log(f"tiny MoE block b=1: {tiny_ms * 1e3:.2f} us")
+
+    # ---- sweep: MoE block and layer step at b = 2, 4 and the verify batches
+    # 8 r (r = 1..8) with uniform routing, b = 64 with the Zipf(1.1) router
+    # bias; chain b = 1..64. The oracle runs beside some of them on the host.
+    oracle_runs = []
+    hw = None if args.no_cpu_baseline else HostWeights(layers[0])
+    main_bias = layers[0].moe["bias"]
     if not args.no_sweep:
         sweep = []
         S = 40
-        bias = synth.zipf_router_bias(cfg.E, 1.1, cfg.seed).to(dev)
-        for bb, zipf in ((4, False), (8, False), (16, False), (32, False), (64, True)):
+        zbias64 = synth.zipf_router_bias(cfg.E, 1.1, cfg.seed).to(dev)
+        cases = [(bb, False) for bb in SWEEP_UNIFORM] + [(64, True)]
+        if not args.no_cpu_baseline:
+            # host copies first (no copies while the GPU is timed); the
+            # single-thread oracle steps then run in host threads beside the
+            # GPU sweep
+            log("oracle: preparing host copies for the sweep batches")
+            oracle_runs = [OracleStep(hw, cfg.k, cc, pool[0], bb, zbias64 if zipf else None,
+                                      synth.MOE_CONFIGS["b64zipf" if zipf else "b16"])
+                           for bb, zipf in ORACLE_CASES]
+            threads = start_single_thread_runs(oracle_runs, reps=3)
+        for bb, zipf in cases:
             for lay in layers:
-                lay.moe["bias"] = bias if zipf else None
-            acts = []
+                lay.moe["bias"] = zbias64 if zipf else None
+            cfg_b = synth.MOE_CONFIGS["b64zipf" if zipf else "b16"]
+            acts, hist = [], {}
             for i in range(NX):
                 block(i, bb)
-                acts.append(int(torch.unique(layers[i % len(layers)].ids[:bb]).numel()))
+                ids_i = layers[i % len(layers)].ids[:bb]
+                acts.append(int(torch.unique(ids_i).numel()))
+                cnt = torch.bincount(ids_i.reshape(-1).long(), minlength=cfg.E)
+                for c, nexp in zip(*torch.unique(cnt[cnt > 0], return_counts=True)):
+                    hist[int(c)] = hist.get(int(c), 0) + int(nexp)
             g = capture(torch, lambda i: block(i, bb), S)
             ts, _ = replay_timed(torch, g, S)
             del g
             us = ts * 1e3
             na = sum(acts[i % NX] for i in range(S)) / S
-            by = moe_bytes(synth.MOE_CONFIGS["b64zipf" if zipf else "b16"], bb, na)
-            sweep.append({"what": "moe_block", "b": bb, "routing": "zipf1.1" if zipf else "uniform",
-                          "us": round(us, 1), "n_active_mean": na,
-                          "GBps": round(by / us / 1e3, 1),
-                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
-                          "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4)})
-            log(f"MoE block b={bb} {'zipf' if zipf else 'uniform'}: {us:.1f} us, "
-                f"n_active {na:.1f}, {by / us / 1e3:.0f} GB/s")
+            by = moe_bytes(cfg_b, bb, na)
+            routing = "zipf1.1" if zipf else "uniform"
+            entry = {"what": "moe_block", "b": bb, "routing": routing, "us": round(us, 1),
+                     "n_active_mean": na, "GBps": round(by / us / 1e3, 1),
+                     "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
+                     "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4),
+                     "tokens_per_expert_hist": {str(c): round(n / NX, 2)
+                                                for c, n in sorted(hist.items())}}
+            if bb % 8 == 0 and not zipf:
+                entry["verify_requests"] = bb // 8
+            sweep.append(entry)
+            log(f"MoE block b={bb} {routing}: {us:.1f} us, n_active {na:.1f}, "
+                f"{by / us / 1e3:.0f} GB/s")
             # the whole layer step at this batch: chain, then the block on its output
             acts = []
             for i in range(NX):
@@ -509,25 +696,15 @@ def main() -> int:
             del g
             us = ts * 1e3
             na = sum(acts[i % NX] for i in range(S)) / S
-            by = moe_bytes(synth.MOE_CONFIGS["b64zipf" if zipf else "b16"], bb, na) + \
-                chain_bytes(cc, bb)
-            entry = {"what": "layer_step", "b": bb,
-                     "routing": "zipf1.1" if zipf else "uniform", "us": round(us, 1),
-                     "n_active_mean": na, "GBps": round(by / us / 1e3, 1),
-                     "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
-                     "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4)}
-            if not args.no_cpu_baseline:
-                # the oracle beside it: one layer step at this batch on the host cores
-                cfg_b = synth.MOE_CONFIGS["b64zipf" if zipf else "b16"]
-                oms, othr, oby = oracle_step(layers[0], cfg_b, cc, pool[0], bb)
-                entry["oracle"] = {"ms_per_step": round(oms, 1), "cores": othr,
-                                   "GBps": round(oby / oms / 1e6, 3), "steps": 1}
-                log(f"oracle layer step b={bb}: {oms:.0f} ms on {othr} threads")
-            sweep.append(entry)
-            log(f"layer step b={bb} {'zipf' if zipf else 'uniform'}: {us:.1f} us, "
-                f"n_active {na:.1f}, {by / us / 1e3:.0f} GB/s")
+            by = moe_bytes(cfg_b, bb, na) + chain_bytes(cc, bb)
+            sweep.append({"what": "layer_step", "b": bb, "routing": routing, "us": round(us, 1),
+                          "n_active_mean": na, "GBps": round(by / us / 1e3, 1),
+                          "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
+                          "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4)})
+            log(f"layer step b={bb} {routing}: {us:.1f} us, n_active {na:.1f}, "
+                f"{by / us / 1e3:.0f} GB/s")
         for lay in layers:
-            lay.moe["bias"] = None
+            lay.moe["bias"] = main_bias
 
         def chain(i, bb):
             lay = layers[i % len(layers)]
@@ -546,13 +723,27 @@ def main() -> int:
                           "frac_of_peak": round(by / us / 1e3 / PEAK_GBS, 4),
                           "frac_of_read_ceiling": round(by / us / 1e3 / ceiling, 4)})
             log(f"chain b={bb}: {us:.1f} us, {by / us / 1e3:.0f} GB/s")
+        if oracle_runs:
+            for t in threads:
+                t.join()
+            # all host cores, once the single-thread runs are done
+            for o in oracle_runs:
+                o.time_all_cores(reps=3)
+            for o in oracle_runs:
+                for e in sweep:
+                    if (e["what"] == "layer_step" and e["b"] == o.b
+                            and (e["routing"] == "zipf1.1") == (o.bias is not None)):
+                        e["oracle"] = o.report()
+                        log(f"oracle layer step b={o.b}: {o.report()}")
         extra["sweep"] = sweep
 
     # ---- CPU baseline: the oracle, timed on this host's cores
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(torch, layers[0], cfg, cc, pool, b, args.cpu_seconds)
+        cpu = cpu_baseline(torch, hw, cfg, cc, pool, b, args.cpu_seconds,
+                           tiny=extra.get("tiny"))
 
+    rocprof_us = trace_in_graph() if b == 1 and not args.zipf else None
     out = {
         "metric": "MoE decode layer us/step and achieved HBM GB/s (% of peak), batch 1-64",
         "value": round(gbs, 1),
@@ -592,9 +783,16 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(gu_gbs / PEAK_GBS, 4),
             "frac_of_read_ceiling": round(gu_gbs / ceiling, 4),
-            "traffic": traffic_per_launch() if b == 1 else None,
+            "traffic": traffic_per_launch() if b == 1 and not args.zipf else None,
             "bytes_per_launch": int(gu_bytes),
             "avg_launch_us": round(kern_avg * 1e3, 2),
+            "avg_launch_us_source": "HIP events on the kernel's stream around each of the "
+                                    f"{K} eager launches of this run (frac uses this)",
+            "avg_launch_us_in_graph_rocprof": rocprof_us,
+            "frac_in_graph_rocprof": (round(gu_bytes / (rocprof_us * 1e-6) / 1e9 / PEAK_GBS, 4)
+                                      if rocprof_us else None),
+            "in_graph_rocprof_source": "profiles/layer_step_b1_kernel_trace.json: rocprofv3 "
+                                       "kernel trace, the dispatches of the timed graph replay",
         },
         "cpu_baseline": cpu,
     }
@@ -603,75 +801,165 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(torch, layer, cfg, cc, pool, b, seconds):
-    """Time the oracle (plain fp64 C, all host cores) on whole layer steps at
-    batch b, as many as fit in about `seconds` (at least one)."""
+# sweep batches with uniform routing: 2, 4 and the verify batches 8 r (a
+# speculative-decoding step verifies 8 tokens per request, r = 1..8)
+SWEEP_UNIFORM = (2, 4, 8, 16, 24, 32, 40, 48, 56, 64)
+# where the oracle is timed beside the sweep (batch, Zipf bias)
+ORACLE_CASES = ((2, False), (4, False), (8, False), (16, False), (32, False), (64, True))
+
+
+class HostWeights:
+    """Host copies of one layer's weights for the oracle; experts are copied
+    the first time one is named."""
+
+    def __init__(self, layer):
+        self.layer = layer
+        self.dense = {k: v.cpu() for k, v in layer.moe.items()
+                      if k not in ("w13", "w2", "bias") and v is not None}
+        self.chain = {k: v.cpu() for k, v in layer.chain_w.items()}
+        self.experts = {}
+
+    def expert(self, e):
+        if e not in self.experts:
+            self.experts[e] = (self.layer.moe["w13"][e].cpu(), self.layer.moe["w2"][e].cpu())
+        return self.experts[e]
+
+
+class OracleStep:
+    """One whole layer step of the oracle (plain fp64 C) at batch b: the
+    chain, then the MoE block on its output. Everything it reads is on the
+    host before any clock starts (the experts its own routing picks)."""
+
+    def __init__(self, hw, k, cc, inp, b, bias, cfg_b):
+        import numpy as np
+
+        import oracle
+        self.hw, self.k, self.cc, self.b, self.cfg_b = hw, k, cc, b, cfg_b
+        self.bias = None if bias is None else bias.cpu()
+        self.x, self.r = inp["x"][:b].cpu(), inp["r"][:b].cpu()
+        ch = hw.chain
+        hm = oracle.chain(self.x, self.r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)["y"]
+        ids, _ = oracle.topk_softmax(
+            oracle.router_logits(hm, hw.dense["w_router"], self.bias), k)
+        self.act = [int(e) for e in np.unique(ids)]
+        for e in self.act:
+            hw.expert(e)
+        self.nbytes = moe_bytes(cfg_b, b, len(self.act)) + chain_bytes(cc, b)
+        self.single, self.multi, self.threads = [], [], None
+
+    def run(self) -> float:
+        import oracle
+        ch, host = self.hw.chain, dict(self.hw.dense)
+        host["bias"] = self.bias
+        t0 = time.perf_counter()
+        c = oracle.chain(self.x, self.r, ch["w_in"], ch["w_o"], ch["gamma"], self.cc.eps)
+        oracle.moe_block(c["y"], host, self.k, expert_weights=self.hw.expert)
+        return time.perf_counter() - t0
+
+    def time_all_cores(self, reps):
+        import oracle
+        self.threads = oracle.threads()
+        self.multi = [self.run() for _ in range(reps)]
+
+    def report(self) -> dict:
+        import statistics as st
+        out = {"bytes": int(self.nbytes), "n_active": len(self.act)}
+        if self.multi:
+            ms = st.median(self.multi) * 1e3
+            out.update({"ms_per_step": round(ms, 1), "cores": self.threads,
+                        "GBps": round(self.nbytes / ms / 1e6, 3), "runs": len(self.multi)})
+        if self.single:
+            ms1 = st.median(self.single) * 1e3
+            out.update({"ms_per_step_1thread": round(ms1, 1),
+                        "GBps_1thread": round(self.nbytes / ms1 / 1e6, 3),
+                        "runs_1thread": len(self.single)})
+        out["note"] = ("median of the runs; the single-thread runs of all sweep batches ran "
+                       "concurrently, one host thread each, beside the GPU sweep")
+        return out
+
+
+def start_single_thread_runs(runs, reps):
+    """One host thread per oracle step, each timing it reps times on one core."""
+    import threading
+
+    import oracle
+
+    def work(o):
+        oracle.set_threads(1)
+        o.single = [o.run() for _ in range(reps)]
+
+    ts = [threading.Thread(target=work, args=(o,), daemon=True) for o in runs]
+    for t in ts:
+        t.start()
+    return ts
+
+
+def cpu_baseline(torch, hw, cfg, cc, pool, b, seconds, tiny=None):
+    """Time the oracle (plain fp64 C) on whole layer steps at batch b: as many
+    as fit in about `seconds` on all host cores, and the median of three on
+    one core (also for the tiny workload's MoE block when it was timed)."""
+    import statistics as st
+    import threading
+
     import numpy as np
 
     import oracle
 
-    L = oracle.lib()
     threads = oracle.threads()
-    host = {k: (v.cpu() if v is not None else None) for k, v in layer.moe.items()
-            if k not in ("w13", "w2")}
-    ch = {k: v.cpu() for k, v in layer.chain_w.items()}
-    experts = {}
-
-    def fetch(e):
-        if e not in experts:
-            experts[e] = (layer.moe["w13"][e].cpu(), layer.moe["w2"][e].cpu())
-        return experts[e]
-
-    done, spent, i, nbytes = 0, 0.0, 0, 0
+    steps = [OracleStep(hw, cfg.k, cc, pool[i], b, hw.layer.moe.get("bias"), cfg)
+             for i in range(NX)]
+    done, spent, nbytes = 0, 0.0, 0
     while done < 2000 and (done == 0 or spent < seconds):
-        inp = pool[i % len(pool)]
-        x, r = inp["x"][:b].cpu(), inp["r"][:b].cpu()
-        # host copies of what this step reads (outside the timed part)
-        hm = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)["y"]
-        ids, _ = oracle.topk_softmax(oracle.router_logits(hm, host["w_router"]), cfg.k)
-        for e in np.unique(ids):
-            fetch(int(e))
-        t0 = time.perf_counter()
-        c = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)
-        oracle.moe_block(c["y"], host, cfg.k, expert_weights=fetch)
-        dt = time.perf_counter() - t0
-        nbytes += moe_bytes(cfg, b, len(np.unique(ids))) + chain_bytes(cc, b)
-        spent += dt
+        o = steps[done % NX]
+        spent += o.run()
+        nbytes += o.nbytes
         done += 1
-        i += 1
     sec = spent / done
     log(f"oracle: {done} steps, {sec * 1e3:.1f} ms/step on {threads} threads")
-    del L
-    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "ms_per_step": round(sec * 1e3, 2),
-            "sample": f"{done} whole layer steps at batch {b} (chain + MoE block, "
-                      f"{cfg.k} routed experts each), fp64 C oracle with OpenMP"}
+    single = []
 
+    def one():
+        oracle.set_threads(1)
+        single.extend(steps[i].run() for i in range(3))
 
-def oracle_step(layer, cfg, cc, inp, b):
-    """One whole layer step of the oracle (plain fp64 C, all host cores) at
-    batch b: (ms, threads, bytes of the step). The experts it reads are copied
-    to the host before the clock starts."""
-    import numpy as np
+    t = threading.Thread(target=one)
+    t.start()
+    t.join()
+    sec1 = st.median(single)
+    out = {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "ms_per_step": round(sec * 1e3, 2),
+           "ms_per_step_1thread": round(sec1 * 1e3, 2),
+           "GBps_1thread": round(float(np.mean([s.nbytes for s in steps[:3]])) / sec1 / 1e9, 3),
+           "host": host_info(),
+           "sample": f"{done} whole layer steps at batch {b} (chain + MoE block, "
+                     f"{cfg.k} routed experts each) on all {threads} threads, and the median "
+                     "of 3 on one thread; fp64 C oracle with OpenMP, a plain-loop "
+                     "reference, not a tuned CPU implementation"}
+    if tiny is not None:
+        import synth
+        tcfg = synth.MOE_CONFIGS["tiny"]
+        tw = {k: (v.cpu() if v is not None else None)
+              for k, v in synth.make_moe_weights(tcfg, device="cuda").items()}
+        tx = synth.make_tokens(tcfg, device="cuda", index=0, b=1).cpu()
 
-    import oracle
+        def tiny_run():
+            t0 = time.perf_counter()
+            oracle.moe_block(tx, tw, tcfg.k)
+            return time.perf_counter() - t0
 
-    threads = oracle.threads()
-    host = {k: (v.cpu() if v is not None else None) for k, v in layer.moe.items()
-            if k not in ("w13", "w2")}
-    ch = {k: v.cpu() for k, v in layer.chain_w.items()}
-    x, r = inp["x"][:b].cpu(), inp["r"][:b].cpu()
-    hm = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)["y"]
-    ids, _ = oracle.topk_softmax(oracle.router_logits(hm, host["w_router"], host["bias"]),
-                                 cfg.k)
-    experts = {int(e): (layer.moe["w13"][int(e)].cpu(), layer.moe["w2"][int(e)].cpu())
-               for e in np.unique(ids)}
-    t0 = time.perf_counter()
-    c = oracle.chain(x, r, ch["w_in"], ch["w_o"], ch["gamma"], cc.eps)
-    oracle.moe_block(c["y"], host, cfg.k, expert_weights=lambda e: experts[e])
-    dt = time.perf_counter() - t0
-    nbytes = moe_bytes(cfg, b, len(experts)) + chain_bytes(cc, b)
-    return dt * 1e3, threads, nbytes
+        multi = [tiny_run() for _ in range(3)]
+        one_t = []
+
+        def tiny_one():
+            oracle.set_threads(1)
+            one_t.extend(tiny_run() for _ in range(3))
+
+        t = threading.Thread(target=tiny_one)
+        t.start()
+        t.join()
+        tiny["oracle"] = {"ms": round(st.median(multi) * 1e3, 3), "cores": threads,
+                          "ms_1thread": round(st.median(one_t) * 1e3, 3), "runs": 3}
+    return out
 
 
 if __name__ == "__main__":

@@ -75,6 +75,15 @@ int k3_version(void);
 #define K3_OP_PREFETCH 5
 #define K3_OP_ROUTER_LATENT 6
 #define K3_OP_MOE_BLOCK 7
+/* Not an entry point: the engine the routed experts' gate/up and down
+ * products ran on in the last successful k3_moe_experts or k3_moe_block
+ * call -- K3_VARIANT_DOT2 (VALU dot2 row engines: every expert holds at most
+ * four tokens of the call) or K3_VARIANT_MFMA (every expert's tokens on bf16
+ * MFMA 16x16x32 tiles). The automatic choice is DOT2 for b <= 4 and MFMA
+ * above. k3_force_variant(K3_OP_EXPERT_ENGINE, K3_VARIANT_MFMA) runs
+ * batches 2-4 on the MFMA tiles too (batch 1 and DOT2 above batch 4 are not
+ * available and fail with K3_ERR_UNSUPPORTED). */
+#define K3_OP_EXPERT_ENGINE 8
 
 #define K3_VARIANT_NONE 0
 #define K3_VARIANT_DOT2 1    /* VALU dot2 GEMV: whole weight rows per wave */

@@ -30,7 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libk3dec.so")
 _lib = None
 
 OP = {"router_topk": 0, "proj_skinny": 1, "moe_experts": 2, "shared_expert": 3,
-      "oproj_residual": 4, "prefetch": 5, "router_latent": 6, "moe_block": 7}
+      "oproj_residual": 4, "prefetch": 5, "router_latent": 6, "moe_block": 7,
+      "expert_engine": 8}
 VARIANT = {"none": 0, "dot2": 1, "mfma": 2, "grouped": 3, "stream": 4}
 VARIANT_NAME = {v: k for k, v in VARIANT.items()}
 

@@ -8,10 +8,11 @@
 namespace k3 {
 
 namespace {
-std::atomic<int> g_last_variant[8];
-std::atomic<int> g_forced_variant[8];
-std::atomic<void *> g_trace_begin[8];
-std::atomic<void *> g_trace_end[8];
+constexpr int kOps = K3_OP_EXPERT_ENGINE + 1;  // op slots of the dispatch record
+std::atomic<int> g_last_variant[kOps];
+std::atomic<int> g_forced_variant[kOps];
+std::atomic<void *> g_trace_begin[kOps];
+std::atomic<void *> g_trace_end[kOps];
 std::mutex g_cu_mutex;
 int g_cu_count[64];
 int g_max_lds[64];
@@ -58,12 +59,12 @@ int budget_grid(int want, int cu_budget, int per_cu) {
 }
 
 void record_dispatch(int op, int variant) {
-    if (op >= 0 && op < 8)
+    if (op >= 0 && op < kOps)
         g_last_variant[op].store(variant);
 }
 
 void trace_begin(int op, hipStream_t s) {
-    if (op < 0 || op >= 8)
+    if (op < 0 || op >= kOps)
         return;
     void *ev = g_trace_begin[op].load();
     if (ev)
@@ -71,7 +72,7 @@ void trace_begin(int op, hipStream_t s) {
 }
 
 void trace_end(int op, hipStream_t s) {
-    if (op < 0 || op >= 8)
+    if (op < 0 || op >= kOps)
         return;
     void *ev = g_trace_end[op].load();
     if (ev)
@@ -79,7 +80,7 @@ void trace_end(int op, hipStream_t s) {
 }
 
 int forced_variant(int op) {
-    return (op >= 0 && op < 8) ? g_forced_variant[op].load() : K3_VARIANT_NONE;
+    return (op >= 0 && op < kOps) ? g_forced_variant[op].load() : K3_VARIANT_NONE;
 }
 
 }  // namespace k3
@@ -100,11 +101,11 @@ const char *k3_status_string(int status) {
 int k3_version(void) { return 10000; }
 
 int k3_get_last_dispatch(int op) {
-    return (op >= 0 && op < 8) ? k3::g_last_variant[op].load() : K3_VARIANT_NONE;
+    return (op >= 0 && op < k3::kOps) ? k3::g_last_variant[op].load() : K3_VARIANT_NONE;
 }
 
 int k3_force_variant(int op, int variant) {
-    if (op < 0 || op > K3_OP_MOE_BLOCK || variant < K3_VARIANT_NONE ||
+    if (op < 0 || op >= k3::kOps || variant < K3_VARIANT_NONE ||
         variant > K3_VARIANT_STREAM)
         return K3_ERR_INVALID_ARG;
     k3::g_forced_variant[op].store(variant);
@@ -112,7 +113,7 @@ int k3_force_variant(int op, int variant) {
 }
 
 int k3_trace_events(int op, void *begin, void *end) {
-    if (op < 0 || op > K3_OP_MOE_BLOCK || (!begin) != (!end))
+    if (op < 0 || op >= k3::kOps || (!begin) != (!end))
         return K3_ERR_INVALID_ARG;
     k3::g_trace_begin[op].store(begin);
     k3::g_trace_end[op].store(end);

@@ -672,10 +672,26 @@ PermuteOut permute_out(const MoeWorkspace &L, char *ws) {
                       (int *)(ws + L.sorted_token), (int *)(ws + L.slot_pos)};
 }
 
+// The engine of the expert products of a b-token call: dot2 rows while every
+// expert holds at most kDot2MaxTokens tokens (b < kAllMfmaMin), MFMA tiles
+// above; a forced K3_OP_EXPERT_ENGINE variant overrides it. 0 when the
+// forced engine cannot run b tokens (MFMA needs b >= 2: batch 1 has no
+// permutation; dot2 holds at most kDot2MaxTokens tokens per expert).
+int expert_engine(int b) {
+    const int fv = forced_variant(K3_OP_EXPERT_ENGINE);
+    if (fv == K3_VARIANT_NONE)
+        return b >= kAllMfmaMin ? K3_VARIANT_MFMA : K3_VARIANT_DOT2;
+    if (fv == K3_VARIANT_MFMA)
+        return b >= 2 ? fv : 0;
+    if (fv == K3_VARIANT_DOT2)
+        return b < kAllMfmaMin ? fv : 0;
+    return 0;
+}
+
 void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int32_t *topk_ids,
                      const float *topk_w, int k, const uint16_t *w13, const uint16_t *w2, int E,
                      int I, int d_out, const float *y_add, hipEvent_t y_add_ready, uint16_t *y,
-                     int cu_budget, char *ws, int trace_op, hipStream_t s,
+                     int cu_budget, char *ws, int trace_op, hipStream_t s, int engine,
                      const DownExtra *extra = nullptr, bool permuted = false) {
     const MoeWorkspace L = moe_workspace_layout(b, E, k, I, d_out);
     uint16_t *hbuf = (uint16_t *)(ws + L.hbuf);
@@ -713,23 +729,17 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
         // selection kernel before this call (permuted)
         if (!permuted)
             k_moe_permute<<<1, kBlock, 0, s>>>(topk_ids, b, k, E, permute_out(L, ws));
-        // Above kAllMfmaMin tokens every expert runs in the MFMA launches
-        // (heavy list first, then the light one); below, light experts run
-        // on dot2 rows.
-        const bool all_mfma = b >= kAllMfmaMin;
-        const ExpertList none{nullptr, nullptr, nullptr, nullptr, nullptr};
+        // On the MFMA engine every expert runs in the MFMA launches (heavy
+        // list first, then the light one); on the dot2 engine every expert is
+        // light (at most kDot2MaxTokens tokens) and runs on dot2 rows.
+        const bool all_mfma = engine == K3_VARIANT_MFMA;
         if (!all_mfma)
             launch_gateup_dot2(kDot2MaxTokens, z, ldz, d_in, w13, I, light, hbuf, cu_budget, s);
-        const bool any_heavy = b > kDot2MaxTokens;
-        const int pairs = b * k < E ? b * k : E;
-        const int max_heavy = all_mfma ? pairs
-                                       : ((b * k) / (kDot2MaxTokens + 1) < E
-                                              ? (b * k) / (kDot2MaxTokens + 1)
-                                              : E);
-        if (any_heavy) {
+        const int max_jobs = b * k < E ? b * k : E;
+        if (all_mfma) {
             SkExperts J{};
             J.L = heavy;
-            J.L2 = all_mfma ? light : none;
+            J.L2 = light;
             J.w = w13;
             J.w_stride = (int64_t)2 * I * d_in;
             J.K = d_in;
@@ -739,14 +749,15 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
             J.ldx = ldz;
             J.gather = true;
             J.h = hbuf;
-            launch_sk_experts(J, b, max_heavy, cu_budget, s);
+            launch_sk_experts(J, b, max_jobs, cu_budget, s);
         }
         trace_end(trace_op, s);
         if (!all_mfma)
             launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
-        if (any_heavy || extra) {
+        if (all_mfma || extra) {
+            const ExpertList none{nullptr, nullptr, nullptr, nullptr, nullptr};
             SkExperts J{};
-            J.L = heavy;
+            J.L = heavy;  // empty on the dot2 engine (every expert is light)
             J.L2 = all_mfma ? light : none;
             J.w = w2;
             J.w_stride = (int64_t)d_out * I;
@@ -762,7 +773,7 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
                 J.xT = extra->xT;
                 J.out_x = extra->out_x;
             }
-            const int jobs = (any_heavy ? max_heavy : 0) + (extra ? 1 : 0);
+            const int jobs = (all_mfma ? max_jobs : 0) + (extra ? 1 : 0);
             launch_sk_experts(J, b, jobs, cu_budget, s);
         }
         if (y_add_ready)
@@ -832,16 +843,21 @@ extern "C" int k3_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in,
     const int fv = forced_variant(K3_OP_MOE_EXPERTS);
     if (fv != K3_VARIANT_NONE && fv != K3_VARIANT_GROUPED)
         return K3_ERR_UNSUPPORTED;
+    const int engine = expert_engine(b);
+    if (!engine)
+        return K3_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < moe_workspace_layout(b, E, k, I, d_out).total ||
         !aligned16(workspace))
         return K3_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     run_moe_experts(z, ldz, b, d_in, topk_ids, topk_w, k, w13, w2, E, I, d_out, y_add,
                     (hipEvent_t)y_add_ready, y, cu_budget, (char *)workspace, K3_OP_MOE_EXPERTS,
-                    s);
+                    s, engine);
     const int st = launch_status();
-    if (st == K3_OK)
+    if (st == K3_OK) {
         record_dispatch(K3_OP_MOE_EXPERTS, K3_VARIANT_GROUPED);
+        record_dispatch(K3_OP_EXPERT_ENGINE, engine);
+    }
     return st;
 }
 
@@ -903,6 +919,9 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
     const size_t need = L.total + (nin ? align_up((size_t)b * d * sizeof(uint16_t), 256) : 0);
     if (!workspace || ws_bytes < need || !aligned16(workspace))
         return K3_ERR_WORKSPACE;
+    const int engine = expert_engine(b);
+    if (!engine)
+        return K3_ERR_UNSUPPORTED;
     int variant = forced_variant(K3_OP_MOE_BLOCK);
     const bool fits = b <= kDot2MaxTokens && rls_fits(b, d, E) &&
                       (size_t)b * I_s * 2 <= 65536;
@@ -939,8 +958,10 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
         trace_end(K3_OP_MOE_EXPERTS, s);
         launch_down_b1(hbuf, I, w2, d, topk_ids, topk_w, k, E, nullptr, hs, w2_s, y_s, y, 0, s);
         const int st = launch_status();
-        if (st == K3_OK)
+        if (st == K3_OK) {
             record_dispatch(K3_OP_MOE_BLOCK, variant);
+            record_dispatch(K3_OP_EXPERT_ENGINE, engine);
+        }
         return st;
     }
     bool permuted = false;  // the selection kernel wrote the expert lists too
@@ -984,20 +1005,24 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
         if (b > kDot2MaxTokens && I_s == I) {
             const DownExtra ex{w2_s, hs, I_s, b, y_s};
             run_moe_experts(z, ldz, b, d_lat, topk_ids, topk_w, k, w13, w2, E, I, d, y_s, nullptr,
-                            y, 0, ws + L.moe, K3_OP_MOE_EXPERTS, s, &ex);
+                            y, 0, ws + L.moe, K3_OP_MOE_EXPERTS, s, engine, &ex);
             const int st = launch_status();
-            if (st == K3_OK)
+            if (st == K3_OK) {
                 record_dispatch(K3_OP_MOE_BLOCK, variant);
+                record_dispatch(K3_OP_EXPERT_ENGINE, engine);
+            }
             return st;
         }
         sk_proj_f32_direct(hs, I_s, b, w2_s, d, I_s, y_s, d, 0, s);
     }
     // 3-4. routed gate/up, down and combine with the shared output added
     run_moe_experts(z, ldz, b, d_lat, topk_ids, topk_w, k, w13, w2, E, I, d, y_s, nullptr, y, 0,
-                    ws + L.moe, K3_OP_MOE_EXPERTS, s, nullptr, permuted);
+                    ws + L.moe, K3_OP_MOE_EXPERTS, s, engine, nullptr, permuted);
     const int st = launch_status();
-    if (st == K3_OK)
+    if (st == K3_OK) {
         record_dispatch(K3_OP_MOE_BLOCK, variant);
+        record_dispatch(K3_OP_EXPERT_ENGINE, engine);
+    }
     return st;
 }
 

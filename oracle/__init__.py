@@ -67,6 +67,7 @@ def _load(path: str):
     L.orc_oproj_residual_rmsnorm.argtypes = [_f64p, _i64, _int, _int, _u16p, _int, _f64p,
                                              _f64p, ctypes.c_double, _f64p, _f64p]
     L.orc_max_threads.restype = _int
+    L.orc_set_threads.argtypes = [_int]
     return L
 
 
@@ -94,8 +95,15 @@ def use_library(path: str):
 
 
 def threads() -> int:
-    """Threads the oracle's parallel loops use (OMP_NUM_THREADS or all cores)."""
+    """Threads the oracle's parallel loops use on this thread (OMP_NUM_THREADS
+    or all cores, unless set_threads changed it)."""
     return lib().orc_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads this calling thread's oracle calls use from now on (timing
+    only; every result is the same for any thread count)."""
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- marshalling

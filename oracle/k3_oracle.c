@@ -268,3 +268,16 @@ int orc_max_threads(void)
     return 1;
 #endif
 }
+
+/* Threads the calling thread's later parallel loops use (n >= 1); each
+ * caller thread keeps its own setting. Timing only: results do not depend
+ * on it. */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

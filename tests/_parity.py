@@ -59,3 +59,26 @@ def check_ids(gpu_ids, ref_ids, ref_logits, k):
         lg = ref_logits[t][g[t]].astype(np.float64)
         assert (np.diff(lg) <= GAP).all(), f"token {t}: ids not in descending logit order"
     return differ
+
+
+def ref_selection(gpu_ids, logits, k):
+    """Oracle ids and weights for every token, after the gap rule.
+
+    Where the GPU's set differs from the oracle's (only inside the tie band,
+    which check_ids verifies), the reference continues from the GPU's choice:
+    the oracle's top-k softmax run on that token's logits with every expert
+    outside the GPU's set masked to -inf, i.e. the renormalised softmax over
+    exactly the GPU's experts. Returns (ids, w, tokens that differed)."""
+    import oracle
+    ref_ids, ref_w = oracle.topk_softmax(logits, k)
+    differ = check_ids(gpu_ids, ref_ids, logits, k)
+    if differ:
+        g = np.asarray(gpu_ids.cpu() if torch.is_tensor(gpu_ids) else gpu_ids)
+        masked = np.full((len(differ), logits.shape[1]), -np.inf, dtype=np.float32)
+        for i, t in enumerate(differ):
+            masked[i, g[t]] = logits[t, g[t]]
+        ids2, w2 = oracle.topk_softmax(masked, k)
+        for i, t in enumerate(differ):
+            assert set(ids2[i].tolist()) == set(g[t].tolist())
+            ref_ids[t], ref_w[t] = ids2[i], w2[i]
+    return ref_ids, ref_w, differ

@@ -68,8 +68,22 @@ def test_force_variant_validation(L):
     assert L.k3_force_variant(7, 0) == K3_OK
     assert L.k3_force_variant(6, 1) == K3_OK
     assert L.k3_force_variant(6, 0) == K3_OK
+    assert L.k3_force_variant(8, 2) == K3_OK  # the expert engine
+    assert L.k3_force_variant(8, 0) == K3_OK
     assert L.k3_force_variant(9, 0) == INVALID
     assert L.k3_force_variant(1, 17) == INVALID
+
+
+def test_op_and_variant_codes_match_header():
+    """The binding's op and variant tables carry the header's values."""
+    import moe_router_topk_amd as k3
+    text = open(HEADER).read()
+    ops = {m.group(1).lower(): int(m.group(2))
+           for m in re.finditer(r"#define K3_OP_(\w+) (\d+)", text)}
+    variants = {m.group(1).lower(): int(m.group(2))
+                for m in re.finditer(r"#define K3_VARIANT_(\w+) (\d+)", text)}
+    assert ops == k3.OP
+    assert variants == k3.VARIANT
 
 
 def test_workspace_sizes(L):

@@ -89,8 +89,9 @@ def test_counter_summary_empty(tmp_path):
 
 @pytest.mark.parametrize("b", [1, 4, 64])
 def test_oracle_step_counts_what_it_reads(b):
-    """bench.oracle_step on the tiny layer: its byte count matches moe_bytes +
-    chain_bytes for the experts its own routing picked."""
+    """bench.OracleStep on the tiny layer: its byte count matches moe_bytes +
+    chain_bytes for the experts its own routing picked, and it reports a
+    median time on all cores and on one."""
     import types
 
     import numpy as np
@@ -102,10 +103,45 @@ def test_oracle_step_counts_what_it_reads(b):
     cc = synth.ChainConfig("t", d=256, n_in=384, k_o=256)
     lay = types.SimpleNamespace(moe=w, chain_w=synth.make_chain_weights(cc))
     inp = synth.make_chain_inputs(cc, b)
-    ms, threads, nbytes = bench.oracle_step(lay, cfg, cc, inp, b)
-    assert ms > 0 and threads >= 1
+    o = bench.OracleStep(bench.HostWeights(lay), cfg.k, cc, inp, b, None, cfg)
+    for t in bench.start_single_thread_runs([o], reps=3):
+        t.join()
+    o.time_all_cores(reps=3)
+    rep = o.report()
+    assert rep["ms_per_step"] > 0 and rep["ms_per_step_1thread"] > 0
+    assert rep["runs"] == rep["runs_1thread"] == 3 and rep["cores"] >= 1
     hm = oracle.chain(inp["x"], inp["r"], lay.chain_w["w_in"], lay.chain_w["w_o"],
                       lay.chain_w["gamma"], cc.eps)["y"]
     ids, _ = oracle.topk_softmax(oracle.router_logits(hm, w["w_router"]), cfg.k)
     n_act = len(np.unique(ids))
-    assert nbytes == bench.moe_bytes(cfg, b, n_act) + bench.chain_bytes(cc, b)
+    assert o.nbytes == bench.moe_bytes(cfg, b, n_act) + bench.chain_bytes(cc, b)
+    assert rep["n_active"] == n_act
+
+
+def test_trace_summary_takes_the_timed_replay(tmp_path):
+    """The kernel-trace reducer picks dispatches [W + NX + K, W + NX + 2K) of
+    each batch-1 step kernel as the timed region."""
+    import json
+    W, K = 2, 3
+    names = ["void k3::k_gemv<7, 1, k3::EpiBf16>(x)", "void k3::k_oproj_gemv<8, 1>(x)",
+             "void k3::k_rls_gemv<7, 1, true>(x)", "void k3::k_moe_up_b1<true, 7>(x)",
+             "void k3::k_down_b1<8>(x)"]
+    n_steps = W + bench.NX + 2 * K + 4  # eager, replay, then a few later steps
+    t = 0
+    lines = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    for i in range(n_steps):
+        timed = W + bench.NX + K <= i < W + bench.NX + 2 * K
+        for j, n in enumerate(names):
+            d = (70_000 if timed else 90_000) if j == 3 else 10_000
+            lines.append(f'"{n}",{t},{t + d}')
+            t += d + 1000
+    (tmp_path / "run").mkdir()
+    (tmp_path / "run" / "kt_kernel_trace.csv").write_text("\n".join(lines) + "\n")
+    js, md = tmp_path / "t.json", tmp_path / "t.md"
+    assert bench.write_trace_summary(str(tmp_path), W, K, str(js), str(md)) == 0
+    out = json.loads(js.read_text())
+    assert out["dominant_timed_region_avg_us"] == 70.0
+    assert out["dominant_all_dispatches_avg_us"] > 70.0
+    # a step every 4 x (10 + 1) + (70 + 1) us; the span ends with the last kernel
+    assert abs(out["timed_region_us_per_step"] - (K * 115.0 - 1.0) / K) < 0.01
+    assert "k_moe_up_b1<true, 7>" in md.read_text()
