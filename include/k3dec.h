@@ -50,6 +50,7 @@ extern "C" {
 #define K3_ERR_UNSUPPORTED (-2)  /* shape outside the supported range, or misaligned */
 #define K3_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than the size query says */
 #define K3_ERR_HIP (-4)          /* the HIP runtime reported an error at launch */
+#define K3_ERR_SCRATCH (-5)      /* the shape needs more than K3_NOALLOC_SCRATCH_BYTES of scratch */
 
 /* Limits of the library (argument checks return K3_ERR_UNSUPPORTED beyond them). */
 #define K3_MAX_BATCH 64      /* tokens per call */
@@ -298,6 +299,33 @@ int k3_moe_block_rmsnorm(const float *h32, int b, int d, const uint16_t *gamma, 
                          int I_s, int32_t *topk_ids, float *topk_w, uint16_t *z, int64_t ldz,
                          float *y_s, uint16_t *y, void *workspace, size_t ws_bytes,
                          void *stream);
+
+/* The MoE block without a workspace argument, for callers that cannot
+ * allocate device memory: code under stream (graph) capture, serving loops
+ * and harnesses that forbid allocation. It runs exactly k3_moe_block (same
+ * kernels, same outputs bit for bit) with the scratch memory in a static
+ * device array of K3_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on, until the process ends. The first call on a device
+ * looks that array's address up once; no call allocates or frees anything.
+ *
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (two streams, or two host threads) race on it and give
+ * undefined results. Serialise them, or use k3_moe_block with a workspace
+ * each. The array keeps the last call's contents; no call needs it cleared.
+ *
+ * Arguments and limits are k3_moe_block's without workspace and ws_bytes.
+ * Shapes whose k3_moe_block_workspace_size exceeds K3_NOALLOC_SCRATCH_BYTES
+ * fail with K3_ERR_SCRATCH before anything is launched (the full-size layer,
+ * d = d_lat = 7168, E = 384, k = 8, I = I_s = 2048, needs 27.7 MiB at
+ * b = 64, so every batch 1..64 fits).
+ */
+#define K3_NOALLOC_SCRATCH_BYTES (32u << 20)
+int k3_moe_block_noalloc(const uint16_t *x, int64_t ldx, int b, int d,
+                         const uint16_t *w_router, const float *bias, int E, int k,
+                         const uint16_t *w_lat, int d_lat, const uint16_t *w13,
+                         const uint16_t *w2, int I, const uint16_t *w13_s,
+                         const uint16_t *w2_s, int I_s, int32_t *topk_ids, float *topk_w,
+                         uint16_t *z, int64_t ldz, float *y_s, uint16_t *y, void *stream);
 
 /* Attention output projection with residual add and RMSNorm (Part 1
  * section 2, "Overlap computation and communication": the output

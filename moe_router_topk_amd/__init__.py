@@ -18,7 +18,7 @@ __all__ = [
     "K3Error", "lib", "library_path",
     "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
     "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_stream_read", "k3_moe_block",
-    "k3_moe_block_rmsnorm", "oproj_h32_view",
+    "k3_moe_block_rmsnorm", "k3_moe_block_noalloc", "oproj_h32_view",
     "k3_get_last_dispatch", "k3_force_variant",
     "k3_trace_events", "HipEvent",
     "k3_status_string", "k3_version", "workspace_size",
@@ -44,7 +44,7 @@ EXPORTED_SYMBOLS = [
     "k3_moe_block_rmsnorm_workspace_size",
     "k3_router_topk", "k3_router_topk_latent", "k3_proj_skinny", "k3_moe_experts",
     "k3_shared_expert", "k3_oproj_residual", "k3_prefetch", "k3_moe_block",
-    "k3_moe_block_rmsnorm", "k3_oproj_residual_h32", "k3_stream_read",
+    "k3_moe_block_rmsnorm", "k3_oproj_residual_h32", "k3_stream_read", "k3_moe_block_noalloc",
 ]
 
 _vp = ctypes.c_void_p
@@ -107,6 +107,10 @@ def lib():
     L.k3_moe_block.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp,
                                _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]
     L.k3_moe_block.restype = _i32
+    L.k3_moe_block_noalloc.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32,
+                                       _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp,
+                                       _vp, _vp]
+    L.k3_moe_block_noalloc.restype = _i32
     L.k3_router_topk.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                  _sz, _vp]
     L.k3_router_topk_latent.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32,
@@ -404,6 +408,34 @@ def k3_moe_block(x, w_router, bias, k, w_lat, w13, w2, w13_s, w2_s, topk_ids=Non
         _ptr(x), _ld(x), b, d, _ptr(w_router), _ptr(bias), E, k, _ptr(w_lat), d_lat, _ptr(w13),
         _ptr(w2), I, _ptr(w13_s), _ptr(w2_s), I_s, _ptr(topk_ids), _ptr(topk_w), _ptr(z), _ld(z),
         _ptr(y_s), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+    return y, topk_ids, topk_w, z, y_s
+
+
+def k3_moe_block_noalloc(x, w_router, bias, k, w_lat, w13, w2, w13_s, w2_s, topk_ids=None,
+                         topk_w=None, z=None, y_s=None, y=None, stream=None):
+    """k3_moe_block with the library's static scratch instead of a workspace
+    (the library allocates nothing; outputs are allocated here when not
+    passed): returns (y, topk_ids, topk_w, z, y_s)."""
+    dev = _dev(x)
+    b, d = x.shape
+    E = w_router.shape[0]
+    d_lat = w_lat.shape[0]
+    I = w13.shape[1] // 2
+    I_s = w13_s.shape[0] // 2
+    if topk_ids is None:
+        topk_ids = torch.empty((b, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((b, k), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((b, d_lat), dtype=torch.bfloat16, device=dev)
+    if y_s is None:
+        y_s = torch.empty((b, d), dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((b, d), dtype=torch.bfloat16, device=dev)
+    _check("k3_moe_block_noalloc", lib().k3_moe_block_noalloc(
+        _ptr(x), _ld(x), b, d, _ptr(w_router), _ptr(bias), E, k, _ptr(w_lat), d_lat, _ptr(w13),
+        _ptr(w2), I, _ptr(w13_s), _ptr(w2_s), I_s, _ptr(topk_ids), _ptr(topk_w), _ptr(z), _ld(z),
+        _ptr(y_s), _ptr(y), _stream(stream)))
     return y, topk_ids, topk_w, z, y_s
 
 

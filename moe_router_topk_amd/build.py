@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libk3dec.so")
-SOURCES = ["api.cpp", "dense.hip", "experts.hip", "moe_b1.hip", "prefetch.hip", "skinny.hip"]
+SOURCES = ["api.cpp", "dense.hip", "experts.hip", "moe_b1.hip", "noalloc.hip", "prefetch.hip",
+           "skinny.hip"]
 ARCH = os.environ.get("K3_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -94,6 +94,7 @@ const char *k3_status_string(int status) {
     case K3_ERR_UNSUPPORTED: return "K3_ERR_UNSUPPORTED: shape outside the supported range, misaligned pointer, or forced variant that cannot run the shape";
     case K3_ERR_WORKSPACE: return "K3_ERR_WORKSPACE: workspace NULL or smaller than the size query requires";
     case K3_ERR_HIP: return "K3_ERR_HIP: the HIP runtime reported an error at launch";
+    case K3_ERR_SCRATCH: return "K3_ERR_SCRATCH: the shape needs more scratch than the no-alloc entry point holds (K3_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown k3 status";
     }
 }

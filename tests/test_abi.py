@@ -54,7 +54,7 @@ def test_exports_no_cxx_or_torch_types():
 
 def test_status_strings(L):
     L.k3_status_string.restype = ctypes.c_char_p
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         s = L.k3_status_string(code).decode()
         assert s.startswith("K3_"), s
     assert L.k3_status_string(-99).decode() == "unknown k3 status"
@@ -278,3 +278,24 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(k3, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         k3.lib()
+
+
+def test_noalloc_argument_checks(L):
+    """k3_moe_block_noalloc rejects a NULL input and shapes beyond its static
+    scratch before it touches the device (fake pointers are never used)."""
+    f = L.k3_moe_block_noalloc
+    f.restype = ctypes.c_int
+    v, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [v, i64, ctypes.c_int, ctypes.c_int, v, v, ctypes.c_int, ctypes.c_int, v,
+                  ctypes.c_int, v, v, ctypes.c_int, v, v, ctypes.c_int, v, v, v, i64, v, v, v]
+
+    def call(x, b, d, E, k, d_lat, I, I_s):
+        return f(x, d, b, d, P, None, E, k, P, d_lat, P, P, I, P, P, I_s, P, P, P, d_lat, P, P,
+                 None)
+
+    assert call(None, 1, 7168, 384, 8, 7168, 2048, 2048) == INVALID
+    assert call(P, 0, 7168, 384, 8, 7168, 2048, 2048) == INVALID
+    # 64 tokens at E = 1024, top-32, d = I = 8192 need about 122 MiB of scratch
+    assert call(P, 64, 8192, 1024, 32, 8192, 8192, 8192) == -5
+    L.k3_status_string.restype = ctypes.c_char_p
+    assert b"K3_NOALLOC_SCRATCH_BYTES" in L.k3_status_string(-5)
