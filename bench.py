@@ -110,18 +110,17 @@ def sources_digest(paths) -> str:
     return h.hexdigest()
 
 
-def trace_in_graph():
-    """The dominant kernel's average duration inside the graph-replayed timed
-    region, from the committed rocprofv3 kernel-trace summary, or None when it
-    is missing or the kernel changed since."""
+def committed_trace():
+    """The committed rocprofv3 kernel-trace summary of the default step, or
+    {} when it is missing or the dominant kernel's sources changed since."""
     try:
         with open(TRACE_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("source_sha256") != sources_digest(DOMINANT_SOURCES):
-        return None
-    return t.get("dominant_timed_region_avg_us")
+        return {}
+    return t
 
 
 # the kernels of one batch-1 layer step, once each, in launch order
@@ -743,7 +742,8 @@ def main() -> int:
         cpu = cpu_baseline(torch, hw, cfg, cc, pool, b, args.cpu_seconds,
                            tiny=extra.get("tiny"))
 
-    rocprof_us = trace_in_graph() if b == 1 and not args.zipf else None
+    tr = committed_trace() if b == 1 and not args.zipf else {}
+    rocprof_us = tr.get("dominant_timed_region_avg_us")
     out = {
         "metric": "MoE decode layer us/step and achieved HBM GB/s (% of peak), batch 1-64",
         "value": round(gbs, 1),
@@ -788,11 +788,13 @@ def main() -> int:
             "avg_launch_us": round(kern_avg * 1e3, 2),
             "avg_launch_us_source": "HIP events on the kernel's stream around each of the "
                                     f"{K} eager launches of this run (frac uses this)",
+            "avg_launch_us_rocprof_all_dispatches": tr.get("dominant_all_dispatches_avg_us"),
             "avg_launch_us_in_graph_rocprof": rocprof_us,
             "frac_in_graph_rocprof": (round(gu_bytes / (rocprof_us * 1e-6) / 1e9 / PEAK_GBS, 4)
                                       if rocprof_us else None),
-            "in_graph_rocprof_source": "profiles/layer_step_b1_kernel_trace.json: rocprofv3 "
-                                       "kernel trace, the dispatches of the timed graph replay",
+            "rocprof_source": "profiles/layer_step_b1_kernel_trace.json: rocprofv3 kernel "
+                              "trace of this command without the sweep; all dispatches of the "
+                              "kernel, and those of the timed graph replay",
         },
         "cpu_baseline": cpu,
     }
