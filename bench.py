@@ -451,6 +451,9 @@ def main() -> int:
     ap.add_argument("--counter-summary", metavar="DIR", default="",
                     help="no GPU work: per-kernel means of every counter in the rocprofv3 "
                          "--pmc csv files under DIR, as a markdown table")
+    ap.add_argument("--mall-probe", action="store_true",
+                    help="only time the o-projection cold, after k3_prefetch of its weights "
+                         "and warm (what the prefetch leaves in the MALL)")
     ap.add_argument("--trace-summary", metavar="DIR", default="",
                     help="no GPU work: reduce the rocprofv3 kernel trace of a default run "
                          "(same --steps/--warmup) to per-kernel statistics of its timed "
@@ -486,6 +489,10 @@ def main() -> int:
     k3.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.mall_probe:
+        print(json.dumps(mall_probe(torch, k3, synth)), flush=True)
+        return 0
 
     if args.copy_mb:
         n = args.copy_mb * (1 << 20)
@@ -801,6 +808,72 @@ def main() -> int:
     out.update(extra)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def mall_probe(torch, k3, synth, reps=7) -> dict:
+    """What k3_prefetch leaves in the MALL for the operator that follows. The
+    o-projection (W_o, 117 MB) is timed with HIP events: cold (after 1 GiB of
+    allocating reads of other memory), after k3_prefetch of all or the first
+    half of W_o, and warm (right after itself); then 117 MB reads of W_o
+    themselves, allocating (k3_prefetch) and non-temporal (k3_stream_read),
+    cold and after an allocating read. Medians of reps, in us."""
+    import statistics as st
+    dev = "cuda:0"
+    cc = synth.CHAIN_CONFIG
+    cw = synth.make_chain_weights(cc, device=dev)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    wo_bytes = cw["w_o"].numel() * 2
+    out = {"what": "o-projection W_o [7168 x 8192] bf16 (117.4 MB) after MALL preparation",
+           "flush": "k3_prefetch over 1 GiB of other memory before every mode"}
+
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    for b in (1, 16):
+        a = synth.randn_bf16((b, cc.k_o), 1.0, 0, "pf_a", b, device=dev)
+        r = synth.randn_bf16((b, cc.d), 1.0, 0, "pf_r", b, device=dev)
+        ws = torch.empty(k3.workspace_size("oproj_residual", b=b, K=cc.k_o, d=cc.d),
+                         dtype=torch.uint8, device=dev)
+        yn = torch.empty((b, cc.d), dtype=torch.bfloat16, device=dev)
+
+        def oproj():
+            k3.k3_oproj_residual(a, cw["w_o"], r, cw["gamma"], cc.eps, y_norm=yn, workspace=ws)
+
+        res = {}
+        for _ in range(reps):
+            for mode in ("cold", "prefetched", "prefetched_half", "warm"):
+                k3.k3_prefetch(flush)
+                if mode == "prefetched":
+                    k3.k3_prefetch(cw["w_o"])
+                elif mode == "prefetched_half":
+                    k3.k3_prefetch(cw["w_o"], nbytes=wo_bytes // 2)
+                elif mode == "warm":
+                    oproj()
+                torch.cuda.synchronize()
+                res.setdefault(mode, []).append(timed(oproj))
+        out[f"oproj_b{b}_us"] = {m: round(st.median(v), 1) for m, v in res.items()}
+        log(f"o-proj b={b}: {out[f'oproj_b{b}_us']}")
+    t = {"prefetch_cold": [], "prefetch_after_prefetch": [], "stream_read_cold": [],
+         "stream_read_after_prefetch": []}
+    for _ in range(reps):
+        for mode in t:
+            k3.k3_prefetch(flush)
+            if mode.endswith("after_prefetch"):
+                k3.k3_prefetch(cw["w_o"])
+            torch.cuda.synchronize()
+            if mode.startswith("prefetch"):
+                t[mode].append(timed(lambda: k3.k3_prefetch(cw["w_o"])))
+            else:
+                t[mode].append(timed(lambda: k3.k3_stream_read(cw["w_o"])))
+    out["w_o_read_us"] = {m: round(st.median(v), 1) for m, v in t.items()}
+    log(f"117 MB reads of W_o: {out['w_o_read_us']}")
+    return out
 
 
 # sweep batches with uniform routing: 2, 4 and the verify batches 8 r (a

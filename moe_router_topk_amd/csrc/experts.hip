@@ -19,6 +19,7 @@
 #include <math.h>
 
 #include "k3_device.h"
+#include "k3_gemv.h"
 #include "k3_internal.h"
 #include "k3_skinny.h"
 
@@ -231,6 +232,221 @@ k_gateup_dot2(const uint16_t *__restrict__ z, int64_t ldz, int d,
                 });
         }
         s0 = s1;
+    }
+}
+
+// ------------------------------------------------------------------ 8-row gate/up
+// Routed gate/up at 2-4 tokens on the 8-row engine (k3_gemv.h): every active
+// expert is on the light list, holding at most NT = b tokens. All b token
+// rows are staged in LDS; as at batch 1 a group is (list entry a, columns
+// 4c .. 4c + 3) -- gate rows 4c .. 4c + 3 and up rows I + 4c .. I + 4c + 3 of
+// w13[e_a] -- and workgroup w takes the same column blocks (an even share of
+// the I / 4) of every entry, so its stream runs on across the experts. A
+// group's sums are taken for its entry's tokens only (the entry's count is
+// wave-uniform). h of position p = start_a + t, column j goes to hbuf[p][j].
+template <int U, int NT>
+__global__ void __launch_bounds__(kBlock)
+k_gateup_rows8(const uint16_t *__restrict__ z, int64_t ldz, int d,
+               const uint16_t *__restrict__ w13, int I, ExpertList L,
+               uint16_t *__restrict__ hbuf, int ps_stride) {
+    extern __shared__ u32x4 zs[];  // NT token rows (d / 8 vectors each), then ps[4][NT][ps_stride]
+    const int nv = d >> 3;
+    float *ps = reinterpret_cast<float *>(zs + NT * nv);
+    int c0, c1;
+    split_range(I >> 2, gridDim.x, blockIdx.x, c0, c1);
+    const int cps = c1 - c0;  // this workgroup's column blocks per entry
+    const int n = L.count();
+    struct Slot {
+        int nt;
+        int off[NT];  // the entry's token rows in zs (vectors), unused ones repeat the last
+    };
+    GvStage<4> st[NT];  // d <= 8192
+    gemv8_stream_slots<U, NT>(
+        n * cps, d,
+        [&](int g, const uint16_t *&base, int &nr, int &skip) {
+            const int a = g / cps, c = c0 + (g - a * cps);
+            int e, p0, na;
+            L.get(a, e, p0, na);
+            base = w13 + ((int64_t)e * 2 * I + 4 * c) * d;
+            nr = 8;
+            skip = I - 4;
+        },
+        [&](int g) {
+            Slot cx;
+            int e, p0, na;
+            L.get(g / cps, e, p0, na);
+            cx.nt = na;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                cx.off[t] = ld_scalar(L.sorted_token + p0 + min(t, na - 1)) * nv;
+            return cx;
+        },
+        [&](const Slot &cx, int kv, int t) { return zs[cx.off[t] + kv]; }, ps, ps_stride,
+        [&]() {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                st[t].load(z + (int64_t)t * ldz, nv);
+        },
+        [&]() {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                st[t].store(zs + t * nv, nv);
+            __syncthreads();
+        });
+    const int nrow = 8 * n * cps;
+    for (int q = threadIdx.x; q < NT * nrow; q += kBlock) {
+        const int t = q / nrow, i = q - t * nrow, r = i & 7;
+        const int g = i >> 3, a = g / cps;
+        if (r < 4 && t < L.ntok[a])
+            hbuf[(int64_t)(L.start[a] + t) * I + 4 * (c0 + g - a * cps) + r] =
+                f32_to_bf16(silu(gv_total(ps, ps_stride, i, NT, t)) *
+                            gv_total(ps, ps_stride, i + 4, NT, t));
+    }
+}
+
+// ------------------------------------------------------------------ 8-row down + combine
+// Routed down projection at 2-4 tokens on the 8-row engine, with the
+// weighted combine in its epilogue: y[t][r] = bf16(y_add[t][r] + sum_j
+// w[t][j] o[slot_pos[t][j]][r]), slots in order j = 0..k-1 (as k_combine
+// adds them). Workgroup w owns rows [rb0, rb1) of the output (at most 8 GPS)
+// for every entry of the light list; its units are (entry a, 8-row group
+// rg), entry-major, one unit per group: wave wq streams K-quarter wq (U
+// pieces of 64, I = 256 U) of the group's rows of w2[e_a]. A wave needs only
+// its own quarter of the entry's h rows, so it stages them itself into a
+// two-slot ring in LDS: at the start of entry a it stores entry a + 1's
+// quarter rows (loaded one entry earlier, so the weight loads issued since
+// then keep streaming) and issues the loads of entry a + 2's. With GPS
+// groups per entry the staging falls on fixed steps of the unit pairs, so
+// every load is issued on every path.
+template <int NT, int GPS>
+__global__ void __launch_bounds__(kBlock)
+k_down_rows8(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict__ w2, int d_out,
+             ExpertList L, const int *__restrict__ slot_pos, const float *__restrict__ topk_w,
+             int k, const float *__restrict__ y_add, uint16_t *__restrict__ y, int ps_stride) {
+    constexpr int U = 8;            // pieces per wave quarter: I = 256 U = 2048
+    constexpr int QV = U * 8;       // 16-byte vectors in a quarter row (one per lane)
+    __shared__ u32x4 hq[4][2][NT][QV];  // [wave][ring slot][token][vector]
+    __shared__ int s_entry[NT * K3_MAX_TOPK], s_pos[NT * K3_MAX_TOPK];
+    __shared__ float s_w[NT * K3_MAX_TOPK], s_ya[NT * 8 * GPS];
+    extern __shared__ float ps[];   // [4][NT][ps_stride]
+    const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
+    int rb0, rb1;
+    split_range(d_out, gridDim.x, blockIdx.x, rb0, rb1);
+    const int rows = rb1 - rb0;
+    const int n = L.count();
+    const int nunits = n * GPS;
+    const int P = NT * k;  // (token, slot) pairs; NT is the batch
+    // h quarter rows of entry a into registers: token t's vector `lane`
+    // (tokens past the entry's count, and entries past the list, read zeros)
+    auto hload = [&](u32x4 (&hr)[NT], int a) {
+        const int ac = min(a, n - 1);
+        int e, p0, na;
+        L.get(ac < 0 ? 0 : ac, e, p0, na);
+        na = a < n ? na : 0;
+        const rsrc_t r = act_range(hbuf);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            hr[t] = ld_act16(r, t < na ? ((uint32_t)(p0 + t) * (uint32_t)I +
+                                          (uint32_t)(wq * QV + lane) * 8u) * 2u
+                                       : kOffNone);
+    };
+    auto hstore = [&](const u32x4 (&hr)[NT], int slot) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            hq[wq][slot][t][lane] = hr[t];
+    };
+    const int rl = lane >> 3, el = (lane & 7) * 8;
+    auto load = [&](u32x4 (&b)[U], int u) {
+        const int a = u / GPS, rg = u - a * GPS;
+        int e, p0, na;
+        L.get(u < nunits ? a : 0, e, p0, na);
+        const int nr = max(0, min(8, rows - 8 * rg));
+        const uint32_t bytes = u < nunits ? (uint32_t)nr * (uint32_t)I * 2u : 0u;
+        const rsrc_t r = weight_range(
+            uniform_ptr(w2 + (int64_t)e * d_out * I + (int64_t)(rb0 + 8 * rg) * I), bytes);
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+            b[i] = ld_weight16(r, ((uint32_t)(rl * I + (wq * U + i) * 64 + el)) * 2u);
+    };
+    float acc[NT];
+    auto fin = [&](const u32x4 (&b)[U], int u) {
+        const int a = u / GPS, rg = u - a * GPS;
+        int e, p0, na;
+        L.get(u < nunits ? a : 0, e, p0, na);
+        const int slot = a & 1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            acc[t] = 0.0f;
+            if (t < na) {
+#pragma unroll
+                for (int i = 0; i < U; ++i)
+                    acc[t] = dot8(b[i], hq[wq][slot][t][i * 8 + (lane & 7)], acc[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float sum = gv_red8(acc[t]);
+            if (u < nunits && (lane & 7) == 0)
+                ps[(wq * NT + t) * ps_stride + 8 * (a * GPS + rg) + rl] = sum;
+        }
+    };
+    // the combine's inputs and the list's entries, loaded before any weights
+    const int q = threadIdx.x;
+    const int pq = min(q, P - 1), yq = min(q, NT * rows - 1);
+    const int sp = slot_pos[pq];
+    const float sw = topk_w[pq];
+    const float ya = y_add ? y_add[(int64_t)(yq / rows) * d_out + rb0 + yq % rows] : 0.0f;
+    const int qa = min(q, max(n - 1, 0));
+    const int q_start = L.start[qa], q_ntok = q < n ? L.ntok[qa] : 0;
+    u32x4 h0[NT], hr[NT];
+    hload(h0, 0);
+    hload(hr, 1);
+    u32x4 A[U], B[U];
+    load(A, 0);
+    hstore(h0, 0);
+    if (q < P) {
+        s_pos[q] = sp;
+        s_w[q] = sw;
+    }
+    if (q < NT * rows)
+        s_ya[q] = ya;
+    for (int t = 0; t < q_ntok; ++t)
+        s_entry[q_start + t] = q;
+    __syncthreads();
+    // entry a starts at unit GPS a: store entry a + 1's quarter rows (slot
+    // (a + 1) & 1, which entry a - 1 used), then issue entry a + 2's. Units
+    // run in pairs, so with GPS = 2 every pair starts one entry and with
+    // GPS = 1 each unit does.
+    auto stage = [&](int a) {
+        hstore(hr, (a + 1) & 1);
+        hload(hr, a + 2);
+    };
+    static_assert(GPS == 1 || GPS == 2, "one or two row groups per entry");
+    for (int u = 0; u < nunits; u += 2) {
+        load(B, u + 1);
+        stage(u / GPS);
+        __builtin_amdgcn_sched_barrier(0);
+        fin(A, u);
+        load(A, u + 2);
+        if constexpr (GPS == 1)
+            stage(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fin(B, u + 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < NT * rows; i += kBlock) {
+        const int t = i / rows, rr = i - t * rows;
+        float sum = s_ya[i];
+        for (int j = 0; j < k; ++j) {
+            const int pos = s_pos[t * k + j];
+            if (pos >= 0) {
+                const int a = s_entry[pos];
+                const int tt = pos - L.start[a];
+                sum += s_w[t * k + j] *
+                       gv_total(ps, ps_stride, 8 * (a * GPS + (rr >> 3)) + (rr & 7), NT, tt);
+            }
+        }
+        y[(int64_t)t * d_out + rb0 + rr] = f32_to_bf16(sum);
     }
 }
 
@@ -595,6 +811,100 @@ void launch_gateup_dot2(int tm, const uint16_t *z, int64_t ldz, int d, const uin
         k_gateup_dot2<kDot2MaxTokens, List><<<grid, kBlock, lds, s>>>(z, ldz, d, w13, I, L, hbuf);
 }
 
+// The 8-row gate/up at 2 <= b <= 4: one workgroup per column block of I / 4
+// at most, two per compute unit; LDS holds the b token rows and the partial
+// sums of every entry of the share.
+int rows8_grid(int I, int cu_budget) { return budget_grid(I / 4, cu_budget, 2); }
+
+size_t rows8_lds(int b, int d, int k, int E, int I, int grid, int &ps_stride) {
+    const int entries = b * k < E ? b * k : E;
+    ps_stride = 8 * entries * ((I / 4 + grid - 1) / grid);
+    return (size_t)b * d * sizeof(uint16_t) + (size_t)4 * b * ps_stride * sizeof(float);
+}
+
+bool rows8_fits(int b, int d, int k, int E, int I, int cu_budget) {
+    int ps_stride;
+    const size_t cap = device_max_lds() < 81920 ? device_max_lds() : 81920;
+    return b >= 2 && b <= kDot2MaxTokens && d % 64 == 0 && d <= 8192 && I % 4 == 0 &&
+           rows8_lds(b, d, k, E, I, rows8_grid(I, cu_budget), ps_stride) <= cap;
+}
+
+void launch_gateup_rows8(int b, const uint16_t *z, int64_t ldz, int d, const uint16_t *w13, int I,
+                         int k, int E, ExpertList L, uint16_t *hbuf, int cu_budget,
+                         hipStream_t s) {
+    const int grid = rows8_grid(I, cu_budget);
+    int ps_stride;
+    const size_t lds = rows8_lds(b, d, k, E, I, grid, ps_stride);
+#define K3_R8(U_, T_) \
+    k_gateup_rows8<U_, T_><<<grid, kBlock, lds, s>>>(z, ldz, d, w13, I, L, hbuf, ps_stride)
+    const bool u7 = gv_unit_pieces(d) == 7;
+    if (b == 2) {
+        if (u7)
+            K3_R8(7, 2);
+        else
+            K3_R8(8, 2);
+    } else if (b == 3) {
+        if (u7)
+            K3_R8(7, 3);
+        else
+            K3_R8(8, 3);
+    } else {
+        if (u7)
+            K3_R8(7, 4);
+        else
+            K3_R8(8, 4);
+    }
+#undef K3_R8
+}
+
+// The 8-row down + combine at 2 <= b <= 4: two workgroups per compute unit,
+// each owning at most 16 output rows (one or two 8-row groups per entry).
+int down_rows8_grid(int d_out, int cu_budget) { return budget_grid(d_out, cu_budget, 2); }
+
+bool down_rows8_fits(int b, int I, int d_out, int k, int E, int cu_budget, int &ps_stride,
+                     size_t &lds) {
+    if (b < 2 || b > kDot2MaxTokens || I != 2048 || k > K3_MAX_TOPK)
+        return false;
+    const int grid = down_rows8_grid(d_out, cu_budget);
+    const int rows = (d_out + grid - 1) / grid;
+    const int gps = (rows + 7) / 8;
+    const int entries = b * k < E ? b * k : E;
+    ps_stride = 8 * entries * gps;
+    lds = (size_t)4 * b * ps_stride * sizeof(float);
+    // static LDS: the h ring (8 KB per token) and the combine's tables
+    const size_t fixed = (size_t)b * 8192 + 4096;
+    const size_t cap = device_max_lds() < 81920 ? device_max_lds() : 81920;
+    return gps <= 2 && lds + fixed <= cap;
+}
+
+void launch_down_rows8(int b, const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
+                       ExpertList L, const int *slot_pos, const float *topk_w, int k,
+                       const float *y_add, uint16_t *y, int cu_budget, int ps_stride, size_t lds,
+                       hipStream_t s) {
+    const int grid = down_rows8_grid(d_out, cu_budget);
+    const int gps = ((d_out + grid - 1) / grid + 7) / 8;
+#define K3_D8(T_, G_)                                                                       \
+    k_down_rows8<T_, G_><<<grid, kBlock, lds, s>>>(hbuf, I, w2, d_out, L, slot_pos, topk_w, \
+                                                   k, y_add, y, ps_stride)
+    if (b == 2) {
+        if (gps == 1)
+            K3_D8(2, 1);
+        else
+            K3_D8(2, 2);
+    } else if (b == 3) {
+        if (gps == 1)
+            K3_D8(3, 1);
+        else
+            K3_D8(3, 2);
+    } else {
+        if (gps == 1)
+            K3_D8(4, 1);
+        else
+            K3_D8(4, 2);
+    }
+#undef K3_D8
+}
+
 template <class List, class Out>
 void launch_down_dot2(int tm, const uint16_t *hbuf, int I, const uint16_t *w2, int d_out, List L,
                       Out out, int cu_budget, hipStream_t s) {
@@ -733,7 +1043,9 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
         // list first, then the light one); on the dot2 engine every expert is
         // light (at most kDot2MaxTokens tokens) and runs on dot2 rows.
         const bool all_mfma = engine == K3_VARIANT_MFMA;
-        if (!all_mfma)
+        if (!all_mfma && rows8_fits(b, d_in, k, E, I, cu_budget))
+            launch_gateup_rows8(b, z, ldz, d_in, w13, I, k, E, light, hbuf, cu_budget, s);
+        else if (!all_mfma)
             launch_gateup_dot2(kDot2MaxTokens, z, ldz, d_in, w13, I, light, hbuf, cu_budget, s);
         const int max_jobs = b * k < E ? b * k : E;
         if (all_mfma) {
@@ -752,6 +1064,17 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
             launch_sk_experts(J, b, max_jobs, cu_budget, s);
         }
         trace_end(trace_op, s);
+        int ps_stride = 0;
+        size_t lds = 0;
+        if (!all_mfma && !extra &&
+            down_rows8_fits(b, I, d_out, k, E, cu_budget, ps_stride, lds)) {
+            // down projection and combine in one kernel, which reads y_add
+            if (y_add_ready)
+                (void)hipStreamWaitEvent(s, y_add_ready, 0);
+            launch_down_rows8(b, hbuf, I, w2, d_out, light, slot_pos, topk_w, k, y_add, y,
+                              cu_budget, ps_stride, lds, s);
+            return;
+        }
         if (!all_mfma)
             launch_down_dot2(kDot2MaxTokens, hbuf, I, w2, d_out, light, out, cu_budget, s);
         if (all_mfma || extra) {

@@ -161,6 +161,96 @@ __device__ __forceinline__ void gemv8_stream(int ngroups, int K, Grp grp, XV xv,
     __syncthreads();  // every quarter's partials are in ps
 }
 
+// gemv8_stream for groups that each serve their own tokens (the routed
+// experts at batches 2-4: a group belongs to one expert, whose few tokens are
+// some of the NT token rows in LDS). slot(g) returns the group's context, with
+// a member nt (<= NT, the same in every lane): tokens t < nt are multiplied,
+// the others skipped (their partial sums are written as zeros). xv(cx, kv, t)
+// gives token t's activation vector kv for that context. Every other argument
+// is gemv8_stream's, and so is every summation order.
+template <int U, int NT, class Grp, class Slot, class XV, class First, class Pre>
+__device__ __forceinline__ void gemv8_stream_slots(int ngroups, int K, Grp grp, Slot slot, XV xv,
+                                                   float *ps, int ps_stride, First first,
+                                                   Pre pre) {
+    const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
+    int p0, p1;
+    split_range(K >> 6, kBlock / kWave, wq, p0, p1);
+    const int upg = max(1, (p1 - p0 + U - 1) / U);
+    const int nunits = ngroups * upg;
+    const int rl = lane >> 3, el = (lane & 7) * 8;
+    auto load = [&](u32x4 (&b)[U], int u) {
+        const int g = u / upg, c = u - g * upg;
+        const uint16_t *base;
+        int nr, skip;
+        grp(g < ngroups ? g : 0, base, nr, skip);
+        skip = __builtin_amdgcn_readfirstlane(skip);
+        const uint32_t bytes =
+            u < nunits ? (uint32_t)__builtin_amdgcn_readfirstlane(nr + (nr > 4 ? skip : 0)) *
+                             (uint32_t)K * 2u
+                       : 0u;
+        const rsrc_t r = weight_range(uniform_ptr(base), bytes);
+        const int row = rl + (rl >= 4 ? skip : 0);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int p = p0 + c * U + i;
+            const uint32_t past = (uint32_t)(p1 - 1 - p) & 0x80000000u;
+            b[i] = ld_weight16(r, ((uint32_t)(row * K + p * 64 + el) * 2u) | past);
+        }
+    };
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        acc[t] = 0.0f;
+    const bool exact = p1 > p0 && (p1 - p0) % U == 0;
+    auto fin = [&](u32x4 (&b)[U], int u) {
+        const int g = u / upg, c = u - g * upg;
+        const auto cx = slot(g < ngroups ? g : 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < cx.nt) {
+                if (exact) {
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+                        const int kv = (p0 + c * U + i) * 8 + (lane & 7);
+                        acc[t] = dot8(b[i], xv(cx, kv, t), acc[t]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+                        const int p = p0 + c * U + i;
+                        const uint32_t m = (p < p1 && u < nunits) ? 0xffffffffu : 0u;
+                        const int kv = min(p, p1 - 1) * 8 + (lane & 7);
+                        const u32x4 xa = xv(cx, kv, t);
+                        acc[t] = dot8(b[i], u32x4{xa.x & m, xa.y & m, xa.z & m, xa.w & m}, acc[t]);
+                    }
+                }
+            }
+        }
+        if (c == upg - 1) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float s = gv_red8(acc[t]);
+                acc[t] = 0.0f;
+                if (g < ngroups && (lane & 7) == 0)
+                    ps[(wq * NT + t) * ps_stride + 8 * g + rl] = s;
+            }
+        }
+    };
+    u32x4 A[U], B[U];
+    first();
+    load(A, 0);
+    pre();
+    for (int u = 0; u < nunits; u += 2) {
+        load(B, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fin(A, u);
+        load(A, u + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        fin(B, u + 1);
+    }
+    __syncthreads();
+}
+
 // The four quarter sums of row i of the share, in wave order (token t of NT).
 __device__ __forceinline__ float gv_total(const float *ps, int ps_stride, int i, int NT = 1,
                                           int t = 0) {
