@@ -267,7 +267,10 @@ k_oproj_finish_rmsnorm(const float *__restrict__ part, int ks, int T, int d, uin
     uint2 *r = reinterpret_cast<uint2 *>(res + (int64_t)t * d);
     f32x4 *h = reinterpret_cast<f32x4 *>(h32 + (int64_t)t * d);
     RmsRow rr;
-    f32x4 pv[kNormVec][kSkMaxSplit];
+    // the K ranges in two halves of kSkMaxSplit / 2 (every load of a half in
+    // flight at once), added in range order
+    constexpr int HS = kSkMaxSplit / 2;
+    f32x4 pv[kNormVec][HS], acc[kNormVec];
     uint2 rv[kNormVec];
 #pragma unroll
     for (int j = 0; j < kNormVec; ++j) {
@@ -275,17 +278,37 @@ k_oproj_finish_rmsnorm(const float *__restrict__ part, int ks, int T, int d, uin
         const int ic = i < n4 ? i : 0;
         rv[j] = r[ic];
 #pragma unroll
-        for (int q = 0; q < kSkMaxSplit; ++q)
+        for (int q = 0; q < HS; ++q)
             pv[j][q] = p[ic + (q < ks ? q : 0) * stride];
     }
     rr.load_gamma(d, gamma);
 #pragma unroll
     for (int j = 0; j < kNormVec; ++j) {
-        f32x4 v = pv[j][0];
+        acc[j] = pv[j][0];
 #pragma unroll
-        for (int q = 1; q < kSkMaxSplit; ++q)
+        for (int q = 1; q < HS; ++q)
             if (q < ks)
-                v += pv[j][q];
+                acc[j] += pv[j][q];
+    }
+    if (ks > HS) {
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j) {
+            const int i = threadIdx.x + j * kBlock;
+            const int ic = i < n4 ? i : 0;
+#pragma unroll
+            for (int q = 0; q < HS; ++q)
+                pv[j][q] = p[ic + (HS + q < ks ? HS + q : 0) * stride];
+        }
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j)
+#pragma unroll
+            for (int q = 0; q < HS; ++q)
+                if (HS + q < ks)
+                    acc[j] += pv[j][q];
+    }
+#pragma unroll
+    for (int j = 0; j < kNormVec; ++j) {
+        f32x4 v = acc[j];
         const uint32_t lo = rv[j].x, hi = rv[j].y;
         v.x += bf16_to_f32((uint16_t)(lo & 0xffffu));
         v.y += bf16_to_f32((uint16_t)(lo >> 16));

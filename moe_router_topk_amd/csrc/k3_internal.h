@@ -71,7 +71,7 @@ void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *
 // sums of its K ranges into `part` (sk_partial_bytes(T, rows) bytes, rows
 // = all output rows of the call) and a small kernel finishes them.
 size_t sk_partial_bytes(int T, int rows);
-int sk_ksplit(int K);
+int sk_ksplit(int K, int T);
 int sk_mt(int T);
 void sk_proj_bf16(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
                   uint16_t *y, int64_t ldy, float *part, hipStream_t s);

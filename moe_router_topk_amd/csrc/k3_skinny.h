@@ -19,7 +19,7 @@ constexpr int kSkRows = 64;           // weight rows per workgroup tile (16 per 
 constexpr int kSkKc = 256;            // K per chunk
 constexpr int kSkKq = kSkKc / 8;      // 16-byte vectors per token row of a chunk
 constexpr int kSkKb = kSkKc / 32;     // MFMA k-steps per chunk
-constexpr int kSkMaxSplit = 4;        // most K ranges a projection is split into
+constexpr int kSkMaxSplit = 8;        // most K ranges a projection is split into
 constexpr int kSkMaxTokens = 64;
 
 // Weight operand loads. One load instruction covers 8 rows x 128 bytes: lane
@@ -500,5 +500,145 @@ struct SkDense {
             }
     }
 };
+
+// ------------------------------------------------------------------ token-resident dense pass
+// For dense projections (every row against the same tokens): workgroup b owns
+// K range ks = b % ksplit, [ks kr, ks kr + kr), and stages the tokens of that
+// range into LDS once; then each of its WPB waves streams its own 16-row
+// tiles of the projection through the range, with two register buffers in
+// flight and no barrier, from one tile to the next without draining. The
+// rows are numbered over the segments of J (16-row tiles, a segment's last one
+// may be partial); the workgroups of one K range take tiles wave by wave in
+// turn. The epilogue writes each tile's fp32 partial sums for its K range
+// (summed in range order by the finishing kernels), as SkDense::store does.
+// K-steps within a range run in order, so the sums are a function of K, kr
+// and the tokens alone.
+constexpr int kResKc = 256;         // K per chunk (one register buffer: 16 rows x 512 bytes)
+constexpr int kResMaxRange = 1024;  // widest K range (its tokens sit in LDS)
+
+template <int MT, int WPB>
+__global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ksplit, int kr) {
+    extern __shared__ u32x4 xr[];  // [MT * 16][KQ + 1]: the range's tokens, zero past T and K
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wq = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int nch = (kr + kResKc - 1) / kResKc;
+    const int KQ = nch * (kResKc / 8);  // staged vectors per token row
+    const int ks = blockIdx.x % ksplit;
+    const int k0 = ks * kr, k1 = min(K, k0 + kr);
+    const int T = J.T;
+    // tiles of the segments
+    int st[4];
+    st[0] = 0;
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+        st[s + 1] = st[s] + (J.N[s] + 15) / 16;
+    const int ntiles = st[3];
+    const int wpk = (gridDim.x / ksplit) * WPB;  // waves of this K range
+    const int w0 = (blockIdx.x / ksplit) * WPB + wq;
+    const int nitems = w0 < ntiles ? (ntiles - 1 - w0) / wpk + 1 : 0;
+    const int nunits = nitems * nch;
+    // token staging: issued first, stored after the first weight loads
+    constexpr int SMAX = MT * 16 * (kResMaxRange / 8) / (WPB * kWave);  // vectors per thread
+    const int nvec = MT * 16 * KQ;
+    const rsrc_t rx = act_range(J.x);
+    u32x4 sv[SMAX];
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const int i = threadIdx.x + j * WPB * kWave;
+        const int t = i / KQ, v = i - t * KQ;
+        const int k = k0 + 8 * v;
+        const bool ok = i < nvec && t < T && k < k1;
+        sv[j] = ld_act16(rx, ok ? ((uint32_t)t * (uint32_t)J.ldx + (uint32_t)k) * 2u : kOffNone);
+    }
+    // the unit u = (item u / nch, chunk u % nch) of this wave: its tile's rows
+    auto rows_of = [&](int u, const uint16_t *&wr, int &nvalid, int &n0, int &nseg) {
+        const int g = w0 + (u / nch) * wpk;  // tile
+        const int s = g >= st[2] ? 2 : (g >= st[1] ? 1 : 0);
+        const int r0 = (g - st[s]) * 16;
+        nvalid = max(0, min(16, J.N[s] - r0));
+        wr = J.W[s] + (int64_t)(nvalid > 0 ? r0 : 0) * K;
+        n0 = J.rows_before[s] + r0;
+        nseg = J.N[s] - r0;
+    };
+    auto load = [&](u32x4 (&buf)[kSkKb], int u) {
+        const uint16_t *wr;
+        int nvalid, n0, nseg;
+        rows_of(u < nunits ? u : 0, wr, nvalid, n0, nseg);
+        const uint32_t wbytes =
+            u < nunits ? (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u : 0u;
+        const rsrc_t rw = weight_range(uniform_ptr(wr), wbytes);
+        const int cc = u - (u / nch) * nch;
+        const int r8 = lane & 7, q = lane >> 3;
+#pragma unroll
+        for (int e = 0; e < kSkKb; ++e) {
+            const int row = 8 * (e & 1) + r8;
+            const int k = k0 + cc * kResKc + 64 * (e >> 1) + 8 * q;
+            const uint32_t past = (uint32_t)(k1 - 1 - k) & 0x80000000u;
+            buf[e] = ld_weight16(rw, ((uint32_t)(row * K + k) * 2u) | past);
+        }
+    };
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int g4 = lane >> 4, rl = lane & 15;
+    auto fin = [&](const u32x4 (&buf)[kSkKb], int u) {
+        const int cc = u - (u / nch) * nch;
+        const u32x4 *xb = xr + cc * (kResKc / 8);
+#pragma unroll
+        for (int p = 0; p < kSkKb / 2; ++p) {
+            u32x4 b0, b1;
+            sk_pair(buf[2 * p], buf[2 * p + 1], b0, b1);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const u32x4 *xrow = xb + (mt * 16 + rl) * (KQ + 1);
+                acc[mt] = mfma16x16x32(xrow[8 * p + 2 * g4], b0, acc[mt]);
+                acc[mt] = mfma16x16x32(xrow[8 * p + 2 * g4 + 1], b1, acc[mt]);
+            }
+        }
+        if (cc == nch - 1 && u < nunits) {
+            // acc[mt][i] = out[token 16 mt + 4 g4 + i][row rl of the tile]
+            const uint16_t *wr;
+            int nvalid, n0, nseg;
+            rows_of(u, wr, nvalid, n0, nseg);
+            if (rl < nseg) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = mt * 16 + 4 * g4 + i;
+                        if (t < T)
+                            J.part[((int64_t)ks * T + t) * J.ldp + n0 + rl] = acc[mt][i];
+                    }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    u32x4 A[kSkKb], B[kSkKb];
+    load(A, 0);
+    load(B, 1);
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const int i = threadIdx.x + j * WPB * kWave;
+        if (i < nvec) {
+            const int t = i / KQ;
+            xr[t * (KQ + 1) + (i - t * KQ)] = sv[j];
+        }
+    }
+    __syncthreads();
+    // units run in pairs; an odd count ends with an empty unit (no weights,
+    // no store), so the loop has one exit and every load is issued on every
+    // path
+    for (int u = 0; u < nunits; u += 2) {
+        sk_keep_order();
+        fin(A, u);
+        load(A, u + 2);
+        sk_keep_order();
+        fin(B, u + 1);
+        load(B, u + 3);
+    }
+}
 
 }  // namespace k3

@@ -125,20 +125,33 @@ k_sk_finish_topk(const float *__restrict__ part, int ks, int T, int64_t ldp, SkO
 }
 
 // ------------------------------------------------------------------ launchers
-// K ranges of a K-wide projection: a function of K alone (about four chunks
-// per range, at most kSkMaxSplit ranges), so every call that streams the
-// same rows against the same tokens sums them in the same order, whichever
-// other rows share its launch.
-int sk_ksplit(int K) {
-    const int nchunks = (K + kSkKc - 1) / kSkKc;
-    const int ks = nchunks / 4;
-    return ks < 1 ? 1 : (ks > kSkMaxSplit ? kSkMaxSplit : ks);
-}
-
 int sk_mt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 
+// The dense passes at 5-32 tokens run token-resident (k_sk_res); at 33-64
+// tokens, whose range tokens would fill the LDS, the per-chunk staging
+// kernel (k_sk_gemm). Measured on the chain (in-process A/B): the resident
+// pass 2-5% faster at 8-32 tokens, 1% slower at 64.
+static bool sk_resident(int T) { return sk_mt(T) <= 2; }
+
+// K ranges of a K-wide dense pass over T tokens: a function of K and T alone,
+// so every call that streams the same rows against the same tokens sums them
+// in the same order, whichever other rows share its launch. Token-resident:
+// kSkMaxSplit ranges of K / kSkMaxSplit (ranges of 128 when K is narrower);
+// K % 128 == 0 and K <= 8192, so a range is a multiple of 16 and at most
+// kResMaxRange wide. Per-chunk staging: about four 256-wide chunks per range,
+// at most four ranges.
+int sk_ksplit(int K, int T) {
+    if (sk_resident(T)) {
+        const int ks = K / 128;
+        return ks < 1 ? 1 : (ks > kSkMaxSplit ? kSkMaxSplit : ks);
+    }
+    const int ks = ((K + kSkKc - 1) / kSkKc) / 4;
+    return ks < 1 ? 1 : (ks > 4 ? 4 : ks);
+}
+
 size_t sk_partial_bytes(int T, int rows) {
-    return align_up((size_t)kSkMaxSplit * T * rows * sizeof(float), 256);
+    const size_t ks = sk_resident(T) ? kSkMaxSplit : 4;
+    return align_up(ks * T * rows * sizeof(float), 256);
 }
 
 // Partial sums of up to three row segments against the same tokens:
@@ -171,7 +184,21 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
     J.T = T;
     J.part = part;
     J.ldp = ldp_force > 0 ? ldp_force : rows;
-    const int ks = ks_force > 0 ? ks_force : sk_ksplit(K);
+    if (ks_force <= 0 && sk_resident(T)) {
+        // the token-resident pass: each workgroup stages its K range's tokens
+        // once (at most 66 KB); four waves per workgroup, two per compute unit
+        const int ks = sk_ksplit(K, T), kr = K / ks;
+        int grid = budget_grid(1 << 30, cu_budget, 2);
+        grid = grid < ks ? ks : grid / ks * ks;
+        const int kq = (kr + kResKc - 1) / kResKc * (kResKc / 8);
+        const size_t lds = (size_t)mt * 16 * (kq + 1) * sizeof(u32x4);
+        if (mt == 1)
+            k_sk_res<1, 4><<<grid, kBlock, lds, s>>>(J, K, ks, kr);
+        else
+            k_sk_res<2, 4><<<grid, kBlock, lds, s>>>(J, K, ks, kr);
+        return ks;
+    }
+    const int ks = ks_force > 0 ? ks_force : sk_ksplit(K, T);
     const int grid = budget_grid(tiles * ks, cu_budget, 2);
     switch (mt) {
     case 1:
