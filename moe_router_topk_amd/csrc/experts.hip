@@ -542,9 +542,12 @@ struct SkExperts {
         return n1() + (L2.n ? __builtin_amdgcn_readfirstlane(L2.count()) : 0);
     }
     __device__ int count() const { return nlist() + (w_x ? 1 : 0); }
-    // Down launches group each XCD's items (measured: 16-token down 480-486
-    // against 502-508 us, no change at 8 or 64 tokens); gate/up launches keep
-    // the plain interleave, which was faster for them at 8-64 tokens.
+    // Down launches group each XCD's items; gate/up launches keep the plain
+    // interleave, which was faster for them at 8-64 tokens. Measured on the
+    // whole MoE block, grouped against plain down launches in one process
+    // (medians of six graph replays of 30 blocks): 821.5 against 829.4 us at
+    // 8 tokens, 1525.5 against 1534.5 us at 16, 2595 against 2601 us at 32,
+    // equal (859.3 us) at 64 with the Zipf bias.
     __device__ bool xcd_grouped() const { return !pair; }
     __device__ int tiles() const {
         return pair ? I / (32 * tpw) : (rows + 64 * tpw - 1) / (64 * tpw);

@@ -292,6 +292,16 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     const int items = J.count() * per_job;
     const int vq = threadIdx.x % KQ;
 
+    // Workgroups are dispatched to the 8 XCDs in turn, so consecutive items
+    // (the tiles of one expert) normally run on 8 XCDs. Grouped, workgroup b
+    // takes, in every full round of G items, the item of virtual index
+    // (b % 8) G / 8 + b / 8: each XCD takes a consecutive block of the round
+    // and one expert's token rows stay in one L2. A partial last round keeps
+    // the plain interleave, so its items spread over every XCD. Either way
+    // every item has exactly one workgroup. u.it is the round of the item.
+    const int G = gridDim.x, bx = blockIdx.x;
+    const int vb = (J.xcd_grouped() && G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx;
+    const int nfull = items / G;
     auto open = [&](Cur &u, int from) {
         u.valid = false;
         u.c = 0;
@@ -299,12 +309,15 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
         u.tile = 0;
         u.ks = 0;
         u.jb = Job{};
-        for (int it = from; it < items; it += gridDim.x) {
+        for (int r = from; r * (int)gridDim.x < items; ++r) {
+            const int it = r * (int)gridDim.x + (r < nfull ? vb : (int)blockIdx.x);
+            if (it >= items)
+                break;
             const int a = it / per_job, rem = it - a * per_job;
             const Job jb = J.job(a);
             if (jb.T <= 0)
                 continue;  // uniform over the workgroup
-            u.it = it;
+            u.it = r;
             u.jb = jb;
             u.tile = rem / ksplit;
             u.ks = rem - u.tile * ksplit;
@@ -317,7 +330,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     };
     auto next = [&](Cur &u) {
         if (u.valid && ++u.c >= u.c1)
-            open(u, u.it + gridDim.x);
+            open(u, u.it + 1);
     };
 
     // token cursor: this thread stages vectors q = tid + j * 256 of each
@@ -374,13 +387,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
             acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Cur C, W, A;  // multiply, weights (one ahead), tokens (two ahead)
-    // Workgroups are dispatched to the 8 XCDs in turn, so consecutive items
-    // (the tiles of one expert) normally run on 8 XCDs. Grouped, workgroup b
-    // takes the items of virtual index (b % 8) G / 8 + b / 8: each XCD takes a
-    // consecutive block of every round, and one expert's token rows stay in
-    // one L2. Either way every item has exactly one workgroup.
-    const int G = gridDim.x, bx = blockIdx.x;
-    open(C, (J.xcd_grouped() && G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx);
+    open(C, 0);
     if (!C.valid)
         return;
     W = C;
