@@ -1003,8 +1003,15 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         trace_end(K3_OP_OPROJ_RESIDUAL, s);
         if (y_norm)
             k_rmsnorm<<<b, kBlock, 0, s>>>(h32, d, gamma, eps, y_norm);
-    } else if (y_norm && d % 4 == 0 && d <= 4 * kNormVec * kBlock) {
-        // partial sums, then the finish and the norm in one kernel
+    } else if (y_norm && d % 4 == 0 && d <= 4 * kNormVec * kBlock &&
+               sk_ksplit(K, b) <= kSkMaxSplit / 2) {
+        // partial sums, then the finish and the norm in one kernel. That
+        // kernel gives each token one workgroup, which reads all the token's
+        // K-range partials; with more than four ranges the finish spread over
+        // every compute unit plus the norm kernel is faster (the chain of
+        // projections at 8, 16, 32 tokens: 63.5 -> 61.1, 68.2 -> 66.1,
+        // 73.9 -> 72.5 us; at 64 tokens, four ranges, the fused kernel is
+        // 1.8 us faster)
         float *part = (float *)((char *)workspace + oproj_part_offset(b, d));
         const int ks = sk_oproj_partials(a, lda, b, K, w_o, d, part, s);
         k_oproj_finish_rmsnorm<<<b, kBlock, 0, s>>>(part, ks, b, d, residual, h32, gamma, eps,

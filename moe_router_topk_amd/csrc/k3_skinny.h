@@ -17,23 +17,42 @@ namespace k3 {
 
 constexpr int kSkRows = 64;           // weight rows per workgroup tile (16 per wave)
 constexpr int kSkKc = 256;            // K per chunk
-constexpr int kSkKq = kSkKc / 8;      // 16-byte vectors per token row of a chunk
 constexpr int kSkKb = kSkKc / 32;     // MFMA k-steps per chunk
 constexpr int kSkMaxSplit = 8;        // most K ranges a projection is split into
-constexpr int kSkMaxTokens = 64;
 
-// Weight operand loads. One load instruction covers 8 rows x 128 bytes: lane
-// l reads row 8h + l % 8 (h the instruction's half of the wave's 16 rows) at
-// bytes 16 (l / 8) of a 128-byte piece, so each row is fetched in whole
-// 128-byte lines. (Loading the MFMA operand order directly, 16 rows x 64
-// bytes per instruction, streams about a quarter slower.) Load 2p + h of a
-// chunk holds piece p of the rows of half h.
-__device__ __forceinline__ void sk_wload(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K, int lane) {
-    const int r8 = lane & 7, q = lane >> 3;
+// Weight operand loads. One load instruction covers 8 rows x 128 bytes of the
+// wave's 16-row tile (h the instruction's half), so each row is fetched in
+// whole 128-byte lines, in one of two lane layouts:
+//   interleaved (RC = false): lane l reads row 8h + l % 8 at bytes 16 (l / 8)
+//     of the piece; one DPP exchange per vector turns a pair of halves into
+//     MFMA operands;
+//   row-contiguous (RC = true): lane l reads row 8h + l / 8 at bytes
+//     16 (l % 8), so each group of four lanes covers 64 contiguous bytes of
+//     one row; the operands then also need a cross-lane permutation
+//     (ds_bpermute, four per vector).
+// Per load instruction the interleaved layout makes the L1 cache handle
+// four times the accesses (hardware counters: 44 against 15 per
+// instruction); at 33-64 tokens, where each operand feeds four MFMAs, the
+// row-contiguous layout is faster (chain of projections at 64 tokens 85.0
+// -> 82.1 us, 64-token Zipf MoE block 847 -> 835 us), and at 5-32 tokens the
+// permutation costs more than it saves (expert stream 2-3% slower), so
+// those keep the interleaved layout. (Loading the MFMA operand order
+// directly, 16 rows x 64 bytes per instruction, streams about a quarter
+// slower than either.) With TPW 16-row tiles per wave (the wave's 16 TPW
+// contiguous rows) over a K chunk of kSkKc / TPW, load u holds tile
+// u / (8 / TPW), piece (u / 2) % (4 / TPW), half u % 2. With TPW = 2 a
+// staged token chunk and each token operand read from LDS serve twice the
+// weight rows.
+template <int TPW, bool RC>
+__device__ __forceinline__ void sk_wload_t(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K,
+                                           int lane) {
+    constexpr int KC = kSkKc / TPW, PP = KC / 64;
+    const int r8 = RC ? lane >> 3 : lane & 7, q = RC ? lane & 7 : lane >> 3;
 #pragma unroll
     for (int u = 0; u < kSkKb; ++u) {
-        const int row = 8 * (u & 1) + r8;
-        const int k = c * kSkKc + 64 * (u >> 1) + 8 * q;
+        const int tt = u / (2 * PP), p = (u / 2) % PP;
+        const int row = 16 * tt + 8 * (u & 1) + r8;
+        const int k = c * KC + 64 * p + 8 * q;
         // past K: the sign bit of K - 1 - k moves the offset out of the range
         // (reads zero); arithmetic rather than a select, which the compiler
         // would turn into a branch and a wait around the load
@@ -43,16 +62,45 @@ __device__ __forceinline__ void sk_wload(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, 
 }
 
 // The two loads of one piece (x: rows 0-7, y: rows 8-15) -> the B operands of
-// its two MFMA k-steps, row l % 16 in lane l: lanes l and l ^ 8 trade one
-// vector (row_ror:8 within each 16-lane row, written into half the banks).
-// Step 0 then holds elements 16g .. 16g + 7 of the piece in lane group
-// g = l / 16, step 1 elements 16g + 8 .. 16g + 15.
+// its two MFMA k-steps, row l % 16 in lane l (lane group g = l / 16 holds
+// eight consecutive elements of the piece).
+//   interleaved: lanes l and l ^ 8 trade one vector (row_ror:8 within each
+//     16-lane row, written into half the banks); step 0 then holds elements
+//     16g .. 16g + 7, step 1 elements 16g + 8 .. 16g + 15;
+//   row-contiguous: within each 16-lane row the lanes of quads 1 and 3 take
+//     y's vector from four lanes down (p0) and those of quads 0 and 2 x's
+//     from four lanes up (p1), so lane 8m + 4b + j of p0 holds row 8b + m,
+//     elements 8j .. 8j + 7 (p1: 32 + 8j ..); then lane 16g + n reads lane
+//     8 (n % 8) + 4 (n / 8) + g: step 0 holds elements 8g .. 8g + 7, step 1
+//     elements 32 + 8g .. 32 + 8g + 7.
+// sk_a_vec gives the matching token operand: the 16-byte vector of the piece
+// that lane group g multiplies in step s.
+template <bool RC>
 __device__ __forceinline__ void sk_pair(const u32x4 &x, const u32x4 &y, u32x4 &s0, u32x4 &s1) {
+    if (!RC) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s0[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)x[i], (int)y[i], 0x128, 0xf, 0xc,
+                                                          false);
+            s1[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)y[i], (int)x[i], 0x128, 0xf, 0x3,
+                                                          false);
+        }
+        return;
+    }
+    const int lane = threadIdx.x & (kWave - 1), n = lane & 15;
+    const int src = 4 * (8 * (n & 7) + 4 * (n >> 3) + (lane >> 4));  // byte address of the lane
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        s0[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)x[i], (int)y[i], 0x128, 0xf, 0xc, false);
-        s1[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)y[i], (int)x[i], 0x128, 0xf, 0x3, false);
+        const int p0 = __builtin_amdgcn_update_dpp((int)x[i], (int)y[i], 0x114, 0xf, 0xa, false);
+        const int p1 = __builtin_amdgcn_update_dpp((int)y[i], (int)x[i], 0x104, 0xf, 0x5, false);
+        s0[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, p0);
+        s1[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, p1);
     }
+}
+
+template <bool RC>
+__device__ __forceinline__ int sk_a_vec(int p, int g, int s) {
+    return RC ? 8 * p + 4 * s + g : 8 * p + 2 * g + s;
 }
 
 // The compiler may not move instructions across this point: it keeps a
@@ -61,46 +109,9 @@ __device__ __forceinline__ void sk_pair(const u32x4 &x, const u32x4 &y, u32x4 &s
 // in flight instead of two).
 __device__ __forceinline__ void sk_keep_order() { __builtin_amdgcn_sched_barrier(0); }
 
-// acc[mt] += tokens 16 mt .. 16 mt + 15 (staged chunk xs) x the wave's 16
-// rows (loads buf of the same chunk).
-template <int MT>
-__device__ __forceinline__ void sk_mfma_chunk(f32x4 (&acc)[MT], const u32x4 (&buf)[kSkKb],
-                                              const u32x4 (&xs)[MT * 16][kSkKq + 1], int mt_n,
-                                              int lane) {
-    const int g = lane >> 4, rl = lane & 15;
-#pragma unroll
-    for (int p = 0; p < kSkKb / 2; ++p) {
-        u32x4 b0, b1;
-        sk_pair(buf[2 * p], buf[2 * p + 1], b0, b1);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            if (mt < mt_n) {
-                acc[mt] = mfma16x16x32(xs[mt * 16 + rl][8 * p + 2 * g], b0, acc[mt]);
-                acc[mt] = mfma16x16x32(xs[mt * 16 + rl][8 * p + 2 * g + 1], b1, acc[mt]);
-            }
-    }
-}
-
-// The same with TPW 16-row tiles per wave (the wave's 16 TPW contiguous
-// rows) over a K chunk of kSkKc / TPW: load u holds tile u / (8 / TPW),
-// piece (u / 2) % (4 / TPW), half u % 2. With TPW = 2 a staged token chunk
-// and each token operand read from LDS serve twice the weight rows.
-template <int TPW>
-__device__ __forceinline__ void sk_wload_t(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K,
-                                           int lane) {
-    constexpr int KC = kSkKc / TPW, PP = KC / 64;
-    const int r8 = lane & 7, q = lane >> 3;
-#pragma unroll
-    for (int u = 0; u < kSkKb; ++u) {
-        const int tt = u / (2 * PP), p = (u / 2) % PP;
-        const int row = 16 * tt + 8 * (u & 1) + r8;
-        const int k = c * KC + 64 * p + 8 * q;
-        const uint32_t past = (uint32_t)(K - 1 - k) & 0x80000000u;
-        buf[u] = ld_weight16(rw, ((uint32_t)(row * K + k) * 2u) | past);
-    }
-}
-
-template <int MT, int TPW>
+// acc[tt][mt] += tokens 16 mt .. 16 mt + 15 (staged chunk xs) x tile tt of
+// the wave's rows (loads buf of the same chunk).
+template <int MT, int TPW, bool RC>
 __device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32x4 (&buf)[kSkKb],
                                                 const u32x4 (&xs)[MT * 16][kSkKc / TPW / 8 + 1],
                                                 int mt_n, int lane) {
@@ -111,12 +122,12 @@ __device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32
         u32x4 b0[TPW], b1[TPW];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
-            sk_pair(buf[tt * 2 * PP + 2 * p], buf[tt * 2 * PP + 2 * p + 1], b0[tt], b1[tt]);
+            sk_pair<RC>(buf[tt * 2 * PP + 2 * p], buf[tt * 2 * PP + 2 * p + 1], b0[tt], b1[tt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             if (mt < mt_n) {
-                const u32x4 a0 = xs[mt * 16 + rl][8 * p + 2 * g];
-                const u32x4 a1 = xs[mt * 16 + rl][8 * p + 2 * g + 1];
+                const u32x4 a0 = xs[mt * 16 + rl][sk_a_vec<RC>(p, g, 0)];
+                const u32x4 a1 = xs[mt * 16 + rl][sk_a_vec<RC>(p, g, 1)];
 #pragma unroll
                 for (int tt = 0; tt < TPW; ++tt) {
                     acc[tt][mt] = mfma16x16x32(a0, b0[tt], acc[tt][mt]);
@@ -192,7 +203,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         // range, offsets out of range): every load is issued on every path,
         // so the waits for a buffer count exactly the loads issued after it.
         auto wload = [&](u32x4 (&buf)[kSkKb], int c) {
-            sk_wload_t<TPW>(buf, weight_range(wbase, c < c1 ? wbytes : 0u), c, K, lane);
+            sk_wload_t<TPW, MT == 4>(buf, weight_range(wbase, c < c1 ? wbytes : 0u), c, K, lane);
         };
         auto aload = [&](u32x4 (&st)[SQ], int c) {
             const rsrc_t rx = act_range(xb);
@@ -216,7 +227,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
             for (int mt = 0; mt < MT; ++mt)
                 acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto compute = [&](u32x4 (&buf)[kSkKb], int b) {
-            sk_mfma_chunk_t<MT, TPW>(acc, buf, xs[b], mt_n, lane);
+            sk_mfma_chunk_t<MT, TPW, MT == 4>(acc, buf, xs[b], mt_n, lane);
         };
         // Chunk c (the item's chunks alternate between token buffers 0 and 1):
         // the weights of chunk c + 1 go out, chunk c is multiplied, the tokens
@@ -361,7 +372,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
         // turns every load into a loop over lanes
         const uint32_t wbytes =
             u.valid ? (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u : 0u;
-        sk_wload_t<TPW>(buf, weight_range(uniform_ptr(wr), wbytes), u.c, K, lane);
+        sk_wload_t<TPW, MT == 4>(buf, weight_range(uniform_ptr(wr), wbytes), u.c, K, lane);
     };
     auto aload = [&](u32x4 (&st)[SQ], const Cur &u) {
         const rsrc_t rx = act_range(uniform_ptr(xb));
@@ -420,7 +431,7 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
         wload(nbuf, W);
         sk_keep_order();
         const int mt_n = C.valid ? min((C.jb.T + 15) >> 4, MT) : 0;
-        sk_mfma_chunk_t<MT, TPW>(acc, buf, xs[b], mt_n, lane);
+        sk_mfma_chunk_t<MT, TPW, MT == 4>(acc, buf, xs[b], mt_n, lane);
         if (C.valid && C.c + 1 >= C.c1) {
             // acc[tt][mt][i] = out[token 16 mt + 4 g + i][row rl of the
             // wave's tile tt]
@@ -575,7 +586,7 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
             u < nunits ? (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u : 0u;
         const rsrc_t rw = weight_range(uniform_ptr(wr), wbytes);
         const int cc = u - (u / nch) * nch;
-        const int r8 = lane & 7, q = lane >> 3;
+        const int r8 = lane & 7, q = lane >> 3;  // the interleaved layout (see sk_wload_t)
 #pragma unroll
         for (int e = 0; e < kSkKb; ++e) {
             const int row = 8 * (e & 1) + r8;
@@ -595,12 +606,12 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
 #pragma unroll
         for (int p = 0; p < kSkKb / 2; ++p) {
             u32x4 b0, b1;
-            sk_pair(buf[2 * p], buf[2 * p + 1], b0, b1);
+            sk_pair<false>(buf[2 * p], buf[2 * p + 1], b0, b1);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const u32x4 *xrow = xb + (mt * 16 + rl) * (KQ + 1);
-                acc[mt] = mfma16x16x32(xrow[8 * p + 2 * g4], b0, acc[mt]);
-                acc[mt] = mfma16x16x32(xrow[8 * p + 2 * g4 + 1], b1, acc[mt]);
+                acc[mt] = mfma16x16x32(xrow[sk_a_vec<false>(p, g4, 0)], b0, acc[mt]);
+                acc[mt] = mfma16x16x32(xrow[sk_a_vec<false>(p, g4, 1)], b1, acc[mt]);
             }
         }
         if (cc == nch - 1 && u < nunits) {
