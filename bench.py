@@ -454,6 +454,9 @@ def main() -> int:
     ap.add_argument("--mall-probe", action="store_true",
                     help="only time the o-projection cold, after k3_prefetch of its weights "
                          "and warm (what the prefetch leaves in the MALL)")
+    ap.add_argument("--router-fusion", action="store_true",
+                    help="only time the batch-1 router + top-k as two kernels (default) and "
+                         "as one kernel whose last workgroup selects (K3_VARIANT_LASTWG)")
     ap.add_argument("--trace-summary", metavar="DIR", default="",
                     help="no GPU work: reduce the rocprofv3 kernel trace of a default run "
                          "(same --steps/--warmup) to per-kernel statistics of its timed "
@@ -492,6 +495,9 @@ def main() -> int:
 
     if args.mall_probe:
         print(json.dumps(mall_probe(torch, k3, synth)), flush=True)
+        return 0
+    if args.router_fusion:
+        print(json.dumps(router_fusion(torch, k3, synth)), flush=True)
         return 0
 
     if args.copy_mb:
@@ -873,6 +879,46 @@ def mall_probe(torch, k3, synth, reps=7) -> dict:
                 t[mode].append(timed(lambda: k3.k3_stream_read(cw["w_o"])))
     out["w_o_read_us"] = {m: round(st.median(v), 1) for m, v in t.items()}
     log(f"117 MB reads of W_o: {out['w_o_read_us']}")
+    return out
+
+
+def router_fusion(torch, k3, synth, n=100, reps=7) -> dict:
+    """The batch-1 router scores + top-k (384 experts x 7168, top-8) two ways:
+    the default projection kernel followed by the top-k kernel, and the forced
+    last-workgroup variant (one kernel: every workgroup publishes its logits
+    with a release fence and takes a ticket; the last one acquires and
+    selects). Each is captured as n calls (two weight copies alternating, so
+    the 5.5 MB of router rows are not cache-resident) and replayed reps times,
+    alternating; medians in us per call."""
+    import statistics as st
+    dev = "cuda:0"
+    cfg = synth.MOE_CONFIGS["b1"]
+    ws_ = [synth.make_moe_weights(cfg, device=dev, layer=li) for li in range(2)]
+    xs = [synth.make_tokens(cfg, device=dev, index=i, b=1) for i in range(4)]
+    nbytes = k3.workspace_size("router_topk", b=1, E=cfg.E)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    ids = torch.empty((1, cfg.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, cfg.k), dtype=torch.float32, device=dev)
+
+    def call(i):
+        k3.k3_router_topk(xs[i % 4], ws_[i % 2]["w_router"], None, cfg.k, topk_ids=ids,
+                          topk_w=wts, workspace=ws)
+
+    graphs = {}
+    for name in ("two_kernels", "last_workgroup"):
+        k3.k3_force_variant("router_topk", "lastwg" if name == "last_workgroup" else "none")
+        for i in range(8):
+            call(i)
+        graphs[name] = capture(torch, call, n)
+    k3.k3_force_variant("router_topk", "none")
+    t = {name: [] for name in graphs}
+    for _ in range(reps):
+        for name, g in graphs.items():
+            t[name].append(replay_timed(torch, g, n)[0] * 1e3)
+    out = {"what": "batch-1 router (384 x 7168 bf16) + top-8 selection, graph-replayed",
+           "calls_per_replay": n,
+           "us_per_call": {name: round(st.median(v), 2) for name, v in t.items()}}
+    log(f"router + top-k at b=1: {out['us_per_call']}")
     return out
 
 

@@ -91,6 +91,16 @@ int k3_version(void);
 #define K3_VARIANT_MFMA 2    /* bf16 MFMA 16x16x32 tiles, K split inside the workgroup */
 #define K3_VARIANT_GROUPED 3 /* permutation + grouped expert tiles */
 #define K3_VARIANT_STREAM 4  /* plain streaming kernel */
+/* k3_router_topk at batch 1 only: the router projection's last workgroup
+ * selects the experts (one kernel instead of the projection and a top-k
+ * kernel). Each workgroup publishes its logits with an agent-scope release
+ * fence and takes a ticket from a counter in bytes 0-3 of the workspace; the
+ * holder of the last ticket acquires, resets the counter and runs the top-k.
+ * Those bytes must be zero before the first call on a workspace; each call
+ * leaves them zero. Measured slower on gfx950 than the two-kernel default
+ * (the fences write back and invalidate the L2 of every workgroup's XCD);
+ * kept so that the comparison can be repeated. */
+#define K3_VARIANT_LASTWG 5
 
 /* Variant the last successful call of `op` on this process launched. */
 int k3_get_last_dispatch(int op);
@@ -146,7 +156,8 @@ size_t k3_moe_block_rmsnorm_workspace_size(int b, int d, int E, int k, int d_lat
  * bias     device, [E] fp32, or NULL for none
  * topk_ids device, [b x k] int32 (output)
  * topk_w   device, [b x k] fp32 (output)
- * workspace device, >= k3_router_topk_workspace_size(b, E) bytes
+ * workspace device, >= k3_router_topk_workspace_size(b, E) bytes (with the forced
+ *          K3_VARIANT_LASTWG its first 4 bytes zero on the first call)
  * Limits: 1 <= b <= 64, 1 <= k <= min(E, 32), E <= 1024.
  */
 int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,

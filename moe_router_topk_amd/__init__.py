@@ -32,7 +32,7 @@ _lib = None
 OP = {"router_topk": 0, "proj_skinny": 1, "moe_experts": 2, "shared_expert": 3,
       "oproj_residual": 4, "prefetch": 5, "router_latent": 6, "moe_block": 7,
       "expert_engine": 8}
-VARIANT = {"none": 0, "dot2": 1, "mfma": 2, "grouped": 3, "stream": 4}
+VARIANT = {"none": 0, "dot2": 1, "mfma": 2, "grouped": 3, "stream": 4, "lastwg": 5}
 VARIANT_NAME = {v: k for k, v in VARIANT.items()}
 
 EXPORTED_SYMBOLS = [
@@ -239,7 +239,9 @@ def _workspace(device, nbytes: int, tag: str):
     key = (device.index if device.index is not None else torch.cuda.current_device(), tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        # zeroed once: the forced last-workgroup router keeps its counter in
+        # the workspace head, which must start at zero (and stays zero)
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -271,7 +273,8 @@ def workspace_size(op: str, **kw) -> int:
 # ------------------------------------------------------------------ entry points
 def k3_router_topk(x, w_router, bias, k, topk_ids=None, topk_w=None, workspace=None,
                    stream=None):
-    """(topk_ids [b x k] int32, topk_w [b x k] fp32) for x [b x d] bf16."""
+    """(topk_ids [b x k] int32, topk_w [b x k] fp32) for x [b x d] bf16. A caller's
+    workspace must start with 4 zero bytes for the forced "lastwg" variant."""
     dev = _dev(x)
     b, d = x.shape
     E = w_router.shape[0]

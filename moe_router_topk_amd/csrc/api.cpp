@@ -107,7 +107,7 @@ int k3_get_last_dispatch(int op) {
 
 int k3_force_variant(int op, int variant) {
     if (op < 0 || op >= k3::kOps || variant < K3_VARIANT_NONE ||
-        variant > K3_VARIANT_STREAM)
+        variant > K3_VARIANT_LASTWG)
         return K3_ERR_INVALID_ARG;
     k3::g_forced_variant[op].store(variant);
     return K3_OK;

@@ -443,14 +443,46 @@ k_oproj_gemv(const uint16_t *__restrict__ a, int64_t lda, const uint16_t *__rest
 // With NORM (one token) the input is x = RMSNorm(h32) * gamma (as k_rmsnorm
 // computes it), normalised by every workgroup while its first weights load;
 // workgroup 0 also writes x to x_out when that is not null.
-template <int U, int NT, bool NORM>
+// After the outputs: nothing (NoFinish), or LastTopk.
+struct NoFinish {
+    __device__ void operator()(const float *, int) const {}
+};
+
+// The forced K3_VARIANT_LASTWG of the one-token router: every workgroup
+// publishes its logits (agent-scope release fence) and takes a ticket from
+// the counter; the holder of the last ticket acquires, resets the counter for
+// the next call and selects the token's experts from all E logits, as
+// k_topk_softmax does.
+struct LastTopk {
+    int *counter;  // zero before the launch, zero after it
+    int k;
+    int32_t *ids;
+    float *wts;
+    __device__ void operator()(const float *logits, int E) const {
+        __shared__ int last;
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            last = atomicAdd(counter, 1) == (int)gridDim.x - 1;
+        __syncthreads();
+        if (!last)
+            return;
+        __threadfence();
+        if (threadIdx.x == 0)
+            *counter = 0;
+        if (threadIdx.x < kWave)
+            topk_wave(logits, E, k, ids, wts);
+    }
+};
+
+template <int U, int NT, bool NORM, class Fin = NoFinish>
 __global__ void __launch_bounds__(kBlock)
 k_rls_gemv(const uint16_t *__restrict__ x, int64_t ldx, int d, const uint16_t *__restrict__ Wr,
             const float *__restrict__ bias, int E, float *__restrict__ logits,
             const uint16_t *__restrict__ Wl, int NL, uint16_t *__restrict__ z,
             const uint16_t *__restrict__ W13s, int Is, uint16_t *__restrict__ hs,
             int ps_stride, const float *__restrict__ h32, const uint16_t *__restrict__ gamma,
-            float eps, uint16_t *__restrict__ x_out, int64_t ldz) {
+            float eps, uint16_t *__restrict__ x_out, int64_t ldz, Fin fin = Fin{}) {
     extern __shared__ u32x4 xs[];  // NT token rows, then ps[4][NT][ps_stride], then bias
     const int nv = d >> 3;
     float *ps = reinterpret_cast<float *>(xs + NT * nv);
@@ -534,6 +566,7 @@ k_rls_gemv(const uint16_t *__restrict__ x, int64_t ldx, int d, const uint16_t *_
                             gv_total(ps, ps_stride, i + 4, NT, t));
         }
     }
+    fin(logits, E);
 }
 
 static int rls_gemv_ps_stride(int E, int NL, int Is, int grid) {
@@ -811,6 +844,28 @@ void launch_rls(const uint16_t *x, int64_t ldx, int b, int d, const uint16_t *w_
 #undef K3_RLS
 }
 
+// One token's router logits and top-k in one kernel (K3_VARIANT_LASTWG);
+// false when the row engine cannot run the shape.
+bool launch_router_last(const uint16_t *x, int64_t ldx, int d, const uint16_t *w_router,
+                        const float *bias, int E, float *logits, int k, int32_t *ids, float *wts,
+                        int *counter, hipStream_t s) {
+    if (!rls_gemv_fits(1, d, E, 0, 0))
+        return false;
+    const int grid = rls_gemv_grid(E, 0, 0, 0);
+    int ps_stride;
+    const size_t lds = rls_gemv_lds(1, d, E, 0, 0, grid, ps_stride);
+    const LastTopk fin{counter, k, ids, wts};
+    if (gv_unit_pieces(d) == 7)
+        k_rls_gemv<7, 1, false, LastTopk><<<grid, kBlock, lds, s>>>(
+            x, ldx, d, w_router, bias, E, logits, nullptr, 0, nullptr, nullptr, 0, nullptr,
+            ps_stride, nullptr, nullptr, 0.0f, nullptr, 0, fin);
+    else
+        k_rls_gemv<8, 1, false, LastTopk><<<grid, kBlock, lds, s>>>(
+            x, ldx, d, w_router, bias, E, logits, nullptr, 0, nullptr, nullptr, 0, nullptr,
+            ps_stride, nullptr, nullptr, 0.0f, nullptr, 0, fin);
+    return true;
+}
+
 void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *wts,
                  hipStream_t s) {
     k_topk_softmax<<<b, kWave, 0, s>>>(logits, E, k, ids, wts);
@@ -885,12 +940,26 @@ extern "C" int k3_router_topk(const uint16_t *x, int64_t ldx, int b, int d,
                                       ws_bytes, k3_router_topk_workspace_size(b, E));
     if (chk != K3_OK)
         return chk;
-    const int variant = pick_router_variant(K3_OP_ROUTER_TOPK, b, d, E);
-    if (variant < 0)
-        return K3_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     float *logits = (float *)((char *)workspace + router_logits_offset());
     float *part = (float *)((char *)workspace + router_partial_offset(b, E));
+    if (forced_variant(K3_OP_ROUTER_TOPK) == K3_VARIANT_LASTWG) {
+        // the counter sits in the workspace head, which no other kernel touches
+        if (b != 1)
+            return K3_ERR_UNSUPPORTED;
+        trace_begin(K3_OP_ROUTER_TOPK, s);
+        if (!launch_router_last(x, ldx, d, w_router, bias, E, logits, k, topk_ids, topk_w,
+                                (int *)workspace, s))
+            return K3_ERR_UNSUPPORTED;
+        trace_end(K3_OP_ROUTER_TOPK, s);
+        const int st = launch_status();
+        if (st == K3_OK)
+            record_dispatch(K3_OP_ROUTER_TOPK, K3_VARIANT_LASTWG);
+        return st;
+    }
+    const int variant = pick_router_variant(K3_OP_ROUTER_TOPK, b, d, E);
+    if (variant < 0)
+        return K3_ERR_UNSUPPORTED;
     trace_begin(K3_OP_ROUTER_TOPK, s);
     if (variant == K3_VARIANT_DOT2) {
         launch_rls(x, ldx, b, d, w_router, bias, E, logits, nullptr, 0, nullptr, 0, nullptr, 0,

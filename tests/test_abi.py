@@ -72,6 +72,22 @@ def test_force_variant_validation(L):
     assert L.k3_force_variant(8, 0) == K3_OK
     assert L.k3_force_variant(9, 0) == INVALID
     assert L.k3_force_variant(1, 17) == INVALID
+    assert L.k3_force_variant(0, 6) == INVALID
+
+
+def test_router_last_workgroup_variant_is_batch_one_only(L):
+    """The forced last-workgroup router runs one token only; other batches
+    and other ops refuse it before launching anything."""
+    assert L.k3_force_variant(0, 5) == K3_OK
+    try:
+        assert _router(L, b=2) == UNSUP
+    finally:
+        assert L.k3_force_variant(0, 0) == K3_OK
+    assert L.k3_force_variant(1, 5) == K3_OK
+    try:
+        assert L.k3_proj_skinny(P, 256, 1, 256, P, 256, P, 256, P, 1 << 20, None) == UNSUP
+    finally:
+        assert L.k3_force_variant(1, 0) == K3_OK
 
 
 def test_op_and_variant_codes_match_header():

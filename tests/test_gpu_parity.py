@@ -102,6 +102,51 @@ def test_router_topk_full(k3, full, host, b, zipf):
     assert k3.k3_get_last_dispatch("router_topk") == want
 
 
+@pytest.mark.parametrize("zipf", [0.0, 1.1])
+def test_router_topk_last_workgroup_variant(k3, full, host, zipf):
+    """The forced last-workgroup router (one kernel: the projection's last
+    workgroup selects) gives the default two-kernel path's bits, matches the
+    oracle, and leaves its counter at zero: five calls in a row on one
+    workspace, on different tokens, all agree."""
+    cfg, w = full
+    bias = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
+    nbytes = k3.workspace_size("router_topk", b=1, E=cfg.E)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    for i in range(5):
+        x = synth.make_tokens(cfg, device=DEV, index=140 + i, b=1)
+        ids0, wts0 = k3.k3_router_topk(x, w["w_router"], bias, cfg.k)
+        k3.k3_force_variant("router_topk", "lastwg")
+        try:
+            ids, wts = k3.k3_router_topk(x, w["w_router"], bias, cfg.k, workspace=ws)
+            torch.cuda.synchronize()
+            assert k3.k3_get_last_dispatch("router_topk") == "lastwg"
+        finally:
+            k3.k3_force_variant("router_topk", "none")
+        assert torch.equal(ids, ids0) and torch.equal(wts, wts0), f"call {i}"
+        assert int(ws[:4].view(torch.int32).item()) == 0, "the counter was not reset"
+        logits = oracle.router_logits(x.cpu(), host[0]["w_router"],
+                                      bias.cpu() if bias is not None else None)
+        _, ref_w, _ = ref_selection(ids, logits, cfg.k)
+        assert_rel_close(wts.cpu().numpy().astype(np.float64), ref_w, "topk_w")
+
+
+def test_router_topk_last_workgroup_variant_tiny(k3):
+    """The same at the tiny workload (E = 8, one workgroup: it is its own
+    last)."""
+    cfg = synth.MOE_CONFIGS["tiny"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    x = synth.make_tokens(cfg, device=DEV, index=3, b=1)
+    ids0, wts0 = k3.k3_router_topk(x, w["w_router"], None, cfg.k)
+    k3.k3_force_variant("router_topk", "lastwg")
+    try:
+        for _ in range(3):
+            ids, wts = k3.k3_router_topk(x, w["w_router"], None, cfg.k)
+            torch.cuda.synchronize()
+            assert torch.equal(ids, ids0) and torch.equal(wts, wts0)
+    finally:
+        k3.k3_force_variant("router_topk", "none")
+
+
 @pytest.mark.parametrize("b", [2, 8])
 def test_router_topk_ties(k3, b):
     """x = 0 makes every logit 0: ids 0..k-1 and weights 1/k (row engine at
