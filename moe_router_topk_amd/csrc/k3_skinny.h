@@ -527,7 +527,9 @@ struct SkDense {
 // flight and no barrier, from one tile to the next without draining. The
 // rows are numbered over the segments of J (16-row tiles, a segment's last one
 // may be partial); the workgroups of one K range take tiles wave by wave in
-// turn. The epilogue writes each tile's fp32 partial sums for its K range
+// turn, and the tiles of a last, partial round go to waves in an order that
+// visits every compute unit before any twice (below). The epilogue writes
+// each tile's fp32 partial sums for its K range
 // (summed in range order by the finishing kernels), as SkDense::store does.
 // K-steps within a range run in order, so the sums are a function of K, kr
 // and the tokens alone.
@@ -551,9 +553,21 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
     for (int s = 0; s < 3; ++s)
         st[s + 1] = st[s] + (J.N[s] + 15) / 16;
     const int ntiles = st[3];
-    const int wpk = (gridDim.x / ksplit) * WPB;  // waves of this K range
-    const int w0 = (blockIdx.x / ksplit) * WPB + wq;
-    const int nitems = w0 < ntiles ? (ntiles - 1 - w0) / wpk + 1 : 0;
+    const int nb = gridDim.x / ksplit;  // workgroups of this K range
+    const int bw = blockIdx.x / ksplit;
+    const int wpk = nb * WPB;           // waves of this K range
+    const int w0 = bw * WPB + wq;
+    // Full rounds: wave w0 takes tiles w0, w0 + wpk, ... The R tiles of the
+    // partial last round go to the waves of rank < R, where rank counts the
+    // range's H = nb / 2 compute units first: workgroups are dispatched to the
+    // XCDs in turn and fill one slot on every compute unit before the second,
+    // so with two per compute unit workgroups bw and bw + H share one. (The
+    // plain order gave the o-projection's compute units 16 or 12 tiles at
+    // 5-32 tokens.) Which wave takes a tile does not change its sums.
+    const int nfull = ntiles / wpk, rlast = ntiles - nfull * wpk;
+    const int H = nb / 2;
+    const int rank = nb % 2 == 0 ? (wq * 2 + bw / H) * H + bw % H : w0;
+    const int nitems = nfull + (rank < rlast ? 1 : 0);
     const int nunits = nitems * nch;
     // token staging: issued first, stored after the first weight loads
     constexpr int SMAX = MT * 16 * (kResMaxRange / 8) / (WPB * kWave);  // vectors per thread
@@ -570,7 +584,8 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
     }
     // the unit u = (item u / nch, chunk u % nch) of this wave: its tile's rows
     auto rows_of = [&](int u, const uint16_t *&wr, int &nvalid, int &n0, int &nseg) {
-        const int g = w0 + (u / nch) * wpk;  // tile
+        const int it = u / nch;
+        const int g = it < nfull ? w0 + it * wpk : nfull * wpk + rank;  // tile
         const int s = g >= st[2] ? 2 : (g >= st[1] ? 1 : 0);
         const int r0 = (g - st[s]) * 16;
         nvalid = max(0, min(16, J.N[s] - r0));
