@@ -2,14 +2,16 @@
 //
 // "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 1 ("Tune shapes for
 // the workload"): above batch 2 the projections switch to split-K kernels.
-// Here a workgroup owns a tile of 64 weight rows (16 per wave) and one of
-// `ksplit` K ranges; its four waves share each 256-wide K chunk of the
-// token rows, staged in LDS, while each wave streams its own 16 rows with
-// two register buffers in flight. The product runs on
-// v_mfma_f32_16x16x32_bf16 with the tokens as the A operand (up to four
-// 16-token tiles) and the weight rows as B. A job's epilogue either writes
-// fp32 partial sums per K range (summed in a fixed order by a small reduce
-// kernel), or, with one K range, finishes the outputs directly.
+// Here a workgroup owns a tile of 64 TPW weight rows (16 TPW per wave, TPW =
+// 2 at 33-64 tokens, else 1) and one of `ksplit` K ranges; its four waves
+// share each K chunk of the token rows, staged in LDS, while each wave
+// streams its own rows with two register buffers in flight. The product
+// runs on v_mfma_f32_16x16x32_bf16 with the tokens as the A operand (up to
+// four 16-token tiles) and the weight rows as B. A job's epilogue either
+// writes fp32 partial sums per K range (summed in a fixed order by a small
+// reduce kernel), or, with one K range, finishes the outputs directly. The
+// token-resident pass at the end of the file stages a whole K range once
+// instead (dense projections at 5-32 tokens).
 #pragma once
 #include "k3_device.h"
 
