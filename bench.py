@@ -457,6 +457,10 @@ def main() -> int:
     ap.add_argument("--router-fusion", action="store_true",
                     help="only time the batch-1 router + top-k as two kernels (default) and "
                          "as one kernel whose last workgroup selects (K3_VARIANT_LASTWG)")
+    ap.add_argument("--shard-probe", action="store_true",
+                    help="only time the kernels at one GPU's share under tensor parallelism "
+                         "over 8 GPUs (experts I = 256, input projection 1536 rows, "
+                         "o-projection K = 1024)")
     ap.add_argument("--trace-summary", metavar="DIR", default="",
                     help="no GPU work: reduce the rocprofv3 kernel trace of a default run "
                          "(same --steps/--warmup) to per-kernel statistics of its timed "
@@ -498,6 +502,9 @@ def main() -> int:
         return 0
     if args.router_fusion:
         print(json.dumps(router_fusion(torch, k3, synth)), flush=True)
+        return 0
+    if args.shard_probe:
+        print(json.dumps(shard_probe(torch, k3, synth)), flush=True)
         return 0
 
     if args.copy_mb:
@@ -919,6 +926,85 @@ def router_fusion(torch, k3, synth, n=100, reps=7) -> dict:
            "calls_per_replay": n,
            "us_per_call": {name: round(st.median(v), 2) for name, v in t.items()}}
     log(f"router + top-k at b=1: {out['us_per_call']}")
+    return out
+
+
+def shard_probe(torch, k3, synth, n=50, reps=5) -> dict:
+    """One GPU's share of the layer under tensor parallelism over 8 GPUs, as
+    the kernels would run it before their collectives (not run here): the
+    routed experts and the shared expert at I = I_s = 256, the input
+    projection's 1536 of 12288 rows, the o-projection's 1024 of 8192 K
+    columns (+ residual + norm). Graph-replayed calls; weight copies rotate
+    so that each call reads its weights from HBM (the dense shares: 20
+    copies, 440 and 294 MB; the experts: two layers, tokens rotating).
+    Medians in us per call, GB/s of algorithmic bytes."""
+    import statistics as st
+    dev = "cuda:0"
+    cfg = synth.MOE_CONFIGS["tp8_shard"]
+    cc = synth.CHAIN_CONFIG
+    mw = [synth.make_moe_weights(cfg, device=dev, layer=li) for li in range(2)]
+    cw = synth.make_chain_weights(cc, device=dev)
+    w_in = [cw["w_in"][:1536].clone() for _ in range(20)]
+    w_o = [cw["w_o"][:, :1024].contiguous() for _ in range(20)]
+    del cw["w_in"], cw["w_o"]
+    xs = [synth.make_tokens(cfg, device=dev, index=i, b=64) for i in range(8)]
+    bias = synth.zipf_router_bias(cfg.E, 1.1, cfg.seed).to(dev)
+    out = {"what": "kernels at one GPU's TP8 share, before their collectives",
+           "calls_per_replay": n}
+
+    def timed(fn):
+        for i in range(4):
+            fn(i)
+        g = capture(torch, fn, n)
+        return st.median(replay_timed(torch, g, n)[0] * 1e3 for _ in range(reps))
+
+    expert_bytes = 2 * (2 * cfg.I * cfg.d + cfg.d * cfg.I)
+    for b, zipf in ((1, False), (16, False), (64, True)):
+        ids_all, wts_all, zs = [], [], []
+        for i in range(8):
+            x = xs[i][:b]
+            ids, wts = k3.k3_router_topk(x, mw[i % 2]["w_router"], bias if zipf else None, cfg.k)
+            ids_all.append(ids)
+            wts_all.append(wts)
+            zs.append(k3.k3_proj_skinny(x, mw[i % 2]["w_lat"]))
+        torch.cuda.synchronize()
+        n_act = st.mean(int(torch.unique(t).numel()) for t in ids_all)
+        y = torch.empty((b, cfg.d), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(k3.workspace_size("moe_experts", b=b, d_in=cfg.d, E=cfg.E, k=cfg.k,
+                                           I=cfg.I, d_out=cfg.d), dtype=torch.uint8, device=dev)
+        us = timed(lambda i: k3.k3_moe_experts(zs[i % 8], ids_all[i % 8], wts_all[i % 8],
+                                               mw[i % 2]["w13"], mw[i % 2]["w2"], y=y,
+                                               workspace=ws))
+        by = n_act * expert_bytes
+        key = f"routed_experts_b{b}" + ("_zipf" if zipf else "")
+        out[key] = {"us": round(us, 2), "n_active": round(n_act, 1),
+                    "GBps": round(by / us / 1e3, 1)}
+        log(f"TP8 share, routed experts b={b}: {out[key]}")
+    for b in (1, 16, 64):
+        y_s = torch.empty((b, cfg.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(k3.workspace_size("shared_expert", b=b, d=cfg.d, I=cfg.I_s),
+                         dtype=torch.uint8, device=dev)
+        us = timed(lambda i: k3.k3_shared_expert(xs[i % 8][:b], mw[i % 2]["w13_s"],
+                                                 mw[i % 2]["w2_s"], y_s=y_s, workspace=ws))
+        out[f"shared_expert_b{b}"] = {"us": round(us, 2),
+                                      "GBps": round(expert_bytes / us / 1e3, 1)}
+        q = torch.empty((b, 1536), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(k3.workspace_size("proj_skinny", b=b, K=cc.d, N=1536),
+                          dtype=torch.uint8, device=dev)
+        us = timed(lambda i: k3.k3_proj_skinny(xs[i % 8][:b], w_in[i % 20], y=q, workspace=wsp))
+        out[f"in_proj_1536_b{b}"] = {"us": round(us, 2),
+                                     "GBps": round(2 * 1536 * cc.d / us / 1e3, 1)}
+        a = synth.randn_bf16((b, 1024), 1.0, 0, "shard_a", b, device=dev)
+        r = synth.randn_bf16((b, cc.d), 1.0, 0, "shard_r", b, device=dev)
+        yn = torch.empty((b, cc.d), dtype=torch.bfloat16, device=dev)
+        wso = torch.empty(k3.workspace_size("oproj_residual", b=b, K=1024, d=cc.d),
+                          dtype=torch.uint8, device=dev)
+        us = timed(lambda i: k3.k3_oproj_residual(a, w_o[i % 20], r, cw["gamma"], cc.eps,
+                                                  y_norm=yn, workspace=wso))
+        out[f"o_proj_k1024_b{b}"] = {"us": round(us, 2),
+                                     "GBps": round(2 * cc.d * 1024 / us / 1e3, 1)}
+        log(f"TP8 share b={b}: shared {out[f'shared_expert_b{b}']}, in-proj "
+            f"{out[f'in_proj_1536_b{b}']}, o-proj {out[f'o_proj_k1024_b{b}']}")
     return out
 
 

@@ -74,6 +74,9 @@ MOE_CONFIGS = {
     "b16": MoEConfig("b16", b=16, d=7168, E=384, k=8, I=2048, I_s=2048, d_lat=7168),
     "b64zipf": MoEConfig("b64zipf", b=64, d=7168, E=384, k=8, I=2048, I_s=2048, d_lat=7168,
                          zipf_bias=1.1),
+    # one GPU's share of the experts under tensor parallelism over 8 GPUs
+    # (I = I_s = 2048 / 8); router and latent rows whole
+    "tp8_shard": MoEConfig("tp8_shard", b=1, d=7168, E=384, k=8, I=256, I_s=256, d_lat=7168),
 }
 CHAIN_CONFIG = ChainConfig("chain")
 CHAIN_BATCHES = (1, 2, 4, 8, 16, 32, 64)

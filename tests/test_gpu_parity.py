@@ -312,6 +312,61 @@ def test_proj_skinny_strided_output(k3, chain_w, chain_host, b):
     assert (yb[:, 12288:] == 0).all()
 
 
+# ---------------------------------------------------------------- per-GPU TP8 shares
+@pytest.fixture(scope="module")
+def shard(k3):
+    """One GPU's share of the experts under tensor parallelism over 8 GPUs
+    (I = I_s = 256), with the router and latent rows whole."""
+    cfg = synth.MOE_CONFIGS["tp8_shard"]
+    w = synth.make_moe_weights(cfg, device=DEV)
+    torch.cuda.synchronize()
+    return cfg, w, _experts_on_host(w)
+
+
+@pytest.mark.parametrize("b,zipf", [(1, 0.0), (3, 0.0), (16, 0.0), (64, 1.1)])
+def test_moe_experts_tp8_shard(k3, shard, b, zipf):
+    """Routed experts at one GPU's TP8 share (gate/up [512 x 7168], down
+    [7168 x 256] per expert; the all-reduce of y is not run): every token
+    against the oracle, on the engine the batch calls for."""
+    cfg, w, fetch = shard
+    x, z, ids, wts, y_add, y = _routed_case(k3, cfg, w, b, zipf, 600 + b)
+    assert k3.k3_get_last_dispatch("expert_engine") == _engine(b)
+    ref = oracle.moe_experts(z.cpu(), ids.cpu().numpy(), wts.cpu().numpy(), fetch, cfg.E,
+                             y_add=y_add.cpu())
+    assert_rel_close(y.cpu(), ref, "y")
+
+
+@pytest.mark.parametrize("b", [1, 4, 16, 64])
+def test_shared_expert_tp8_shard(k3, shard, b):
+    cfg, w, _ = shard
+    x = synth.make_tokens(cfg, device=DEV, index=620 + b, b=b)
+    y_s = k3.k3_shared_expert(x, w["w13_s"], w["w2_s"])
+    torch.cuda.synchronize()
+    ref = oracle.shared_expert(x.cpu(), w["w13_s"].cpu(), w["w2_s"].cpu())
+    assert_rel_close(y_s.cpu(), ref, "y_s")
+
+
+@pytest.mark.parametrize("b", [1, 8, 64])
+def test_chain_projections_tp8_shard(k3, chain_w, chain_host, b):
+    """The chain's projections at one GPU's TP8 share: the input projection's
+    rows split (1536 x 7168) and the o-projection's K split (7168 x 1024;
+    the all-reduce that would precede the norm is not run): every output."""
+    cc = synth.CHAIN_CONFIG
+    inp = synth.make_chain_inputs(cc, b, device=DEV, index=640 + b)
+    q = k3.k3_proj_skinny(inp["x"], chain_w["w_in"][:1536])
+    w_o = chain_w["w_o"][:, :1024].contiguous()
+    a = synth.randn_bf16((b, 1024), 1.0, 0, "tp8_a", b, device=DEV)
+    r = synth.randn_bf16((b, cc.d), 1.0, 0, "tp8_r", b, device=DEV)
+    r_in = r.clone()
+    y = k3.k3_oproj_residual(a, w_o, r, chain_w["gamma"], cc.eps)
+    torch.cuda.synchronize()
+    assert_rel_close(q.cpu(), oracle.linear(inp["x"].cpu(), chain_host["w_in"][:1536]), "q")
+    h_ref, y_ref = oracle.oproj_residual_rmsnorm(a.cpu(), w_o.cpu(), r_in.cpu(),
+                                                 chain_host["gamma"], cc.eps)
+    assert_rel_close(r.cpu(), h_ref, "h")
+    assert_rel_close(y.cpu(), y_ref, "y_norm")
+
+
 # ---------------------------------------------------------------- shared expert
 @pytest.mark.parametrize("b", [1, 2, 4, 16, 40, 64])
 def test_shared_expert_full(k3, full, host, b):
