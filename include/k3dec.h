@@ -124,9 +124,11 @@ int k3_trace_events(int op, void *begin, void *end);
 
 /* ------------------------------------------------------------ workspace sizes
  * Bytes of device workspace each entry point needs for the given shape
- * (16-byte aligned, caller-owned). Workspaces need no initialisation and
- * keep no state between calls. A workspace serves one call at a time: calls
- * that may overlap need workspaces of their own.
+ * (16-byte aligned, caller-owned; 0 for a non-positive size argument).
+ * Workspaces need no initialisation and keep no state between calls. A
+ * workspace serves one call at a time: calls that may overlap need
+ * workspaces of their own. The router queries, which are not given the
+ * reduction width, return the bound over every width.
  */
 size_t k3_router_topk_workspace_size(int b, int E);
 size_t k3_router_topk_latent_workspace_size(int b, int E, int d_lat);

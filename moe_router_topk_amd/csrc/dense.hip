@@ -730,13 +730,13 @@ size_t oproj_h32_offset() { return kHeadBytes; }
 extern "C" size_t k3_router_topk_workspace_size(int b, int E) {
     if (b <= 0 || E <= 0)
         return 0;
-    return router_partial_offset(b, E) + sk_partial_bytes(b, E);
+    return router_partial_offset(b, E) + sk_partial_bytes(b, E, 0);
 }
 
 extern "C" size_t k3_router_topk_latent_workspace_size(int b, int E, int d_lat) {
     if (b <= 0 || E <= 0 || d_lat <= 0)
         return 0;
-    return router_partial_offset(b, E) + sk_partial_bytes(b, E + d_lat);
+    return router_partial_offset(b, E) + sk_partial_bytes(b, E + d_lat, 0);
 }
 
 static size_t oproj_part_offset(int b, int d) {
@@ -748,17 +748,15 @@ extern "C" const float *k3_oproj_residual_h32(const void *workspace) {
 }
 
 extern "C" size_t k3_oproj_residual_workspace_size(int b, int K, int d) {
-    (void)K;
-    if (b <= 0 || d <= 0)
+    if (b <= 0 || d <= 0 || K <= 0)
         return 0;
-    return oproj_part_offset(b, d) + sk_partial_bytes(b, d);
+    return oproj_part_offset(b, d) + sk_partial_bytes(b, d, K);
 }
 
 extern "C" size_t k3_proj_skinny_workspace_size(int b, int K, int N) {
-    (void)K;
-    if (b <= 0 || N <= 0)
+    if (b <= 0 || N <= 0 || K <= 0)
         return 0;
-    return kHeadBytes + sk_partial_bytes(b, N);
+    return kHeadBytes + sk_partial_bytes(b, N, K);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1079,8 +1077,9 @@ extern "C" int k3_oproj_residual(const uint16_t *a, int64_t lda, int b, int K,
         // K-range partials; with more than four ranges the finish spread over
         // every compute unit plus the norm kernel is faster (the chain of
         // projections at 8, 16, 32 tokens: 63.5 -> 61.1, 68.2 -> 66.1,
-        // 73.9 -> 72.5 us; at 64 tokens, four ranges, the fused kernel is
-        // 1.8 us faster)
+        // 73.9 -> 72.5 us; with four ranges at 64 tokens the fused kernel
+        // was 1.8 us faster). The 8192-wide o-projection of the chain has
+        // eight ranges at every token count.
         float *part = (float *)((char *)workspace + oproj_part_offset(b, d));
         const int ks = sk_oproj_partials(a, lda, b, K, w_o, d, part, s);
         k_oproj_finish_rmsnorm<<<b, kBlock, 0, s>>>(part, ks, b, d, residual, h32, gamma, eps,

@@ -768,8 +768,8 @@ BlockWorkspace block_workspace_layout(int b, int E, int k, int I, int d, int d_l
     w.hs = w.logits + align_up((size_t)b * E * sizeof(float), 256);
     w.moe = w.hs + align_up((size_t)b * I_s * sizeof(uint16_t), 256);
     w.part = w.moe + moe_workspace_layout(b, E, k, I, d).total;
-    const int rows1 = E + d_lat + 2 * I_s;
-    w.total = w.part + sk_partial_bytes(b, rows1 > d ? rows1 : d);
+    // the partials of the router + latent + shared gate/up pass (K = d)
+    w.total = w.part + sk_partial_bytes(b, E + d_lat + 2 * I_s, d);
     return w;
 }
 }  // namespace
@@ -788,7 +788,9 @@ size_t shared_part_offset(int b, int I) { return align_up((size_t)b * I * sizeof
 extern "C" size_t k3_shared_expert_workspace_size(int b, int d, int I) {
     if (b <= 0 || I <= 0 || d <= 0)
         return 0;
-    return shared_part_offset(b, I) + sk_partial_bytes(b, 2 * I > d ? 2 * I : d);
+    // gate/up: 2I rows over K = d; down: d rows over K = I
+    const size_t g = sk_partial_bytes(b, 2 * I, d), dn = sk_partial_bytes(b, d, I);
+    return shared_part_offset(b, I) + (g > dn ? g : dn);
 }
 
 extern "C" size_t k3_moe_block_workspace_size(int b, int d, int E, int k, int d_lat, int I,
@@ -1111,7 +1113,8 @@ void run_moe_experts(const uint16_t *z, int64_t ldz, int b, int d_in, const int3
 }
 
 // The shared expert; the MFMA variant keeps the partial sums of its K
-// ranges in `part` (sk_partial_bytes(b, max(2I, d)) bytes).
+// ranges in `part` (the larger of sk_partial_bytes(b, 2I, d) and
+// sk_partial_bytes(b, d, I) bytes).
 void run_shared_expert(int variant, const uint16_t *x, int64_t ldx, int b, int d,
                        const uint16_t *w13, const uint16_t *w2, int I, float *y_s, int cu_budget,
                        uint16_t *hbuf, float *part, int trace_op, hipStream_t s) {

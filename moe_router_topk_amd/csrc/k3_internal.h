@@ -68,9 +68,10 @@ void launch_topk(const float *logits, int b, int E, int k, int32_t *ids, float *
                  hipStream_t s);
 
 // The split-K MFMA engine (skinny.hip). Each projection writes fp32 partial
-// sums of its K ranges into `part` (sk_partial_bytes(T, rows) bytes, rows
-// = all output rows of the call) and a small kernel finishes them.
-size_t sk_partial_bytes(int T, int rows);
+// sums of its K ranges into `part` (sk_partial_bytes(T, rows, K) bytes, rows
+// = all output rows of the call) and a small kernel finishes them. K = 0
+// gives the bound over every K (for size queries that are not given K).
+size_t sk_partial_bytes(int T, int rows, int K);
 int sk_ksplit(int K, int T);
 int sk_mt(int T);
 void sk_proj_bf16(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,

@@ -2,8 +2,9 @@
 //
 // "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 1 ("Tune shapes for
 // the workload"): above batch 2 the projections switch to split-K kernels.
-// Here a workgroup owns a tile of 64 TPW weight rows (16 TPW per wave, TPW =
-// 2 at 33-64 tokens, else 1) and one of `ksplit` K ranges; its four waves
+// Here a workgroup owns a tile of 16 TPW WPB weight rows (WPB waves of 16 TPW
+// rows; TPW = 2 at 33-64 tokens, else 1; WPB = 4, or 6-7 for the dense
+// projections at 33-64 tokens) and one of `ksplit` K ranges; its waves
 // share each K chunk of the token rows, staged in LDS, while each wave
 // streams its own rows with two register buffers in flight. The product
 // runs on v_mfma_f32_16x16x32_bf16 with the tokens as the A operand (up to
@@ -17,7 +18,6 @@
 
 namespace k3 {
 
-constexpr int kSkRows = 64;           // weight rows per workgroup tile (16 per wave)
 constexpr int kSkKc = 256;            // K per chunk
 constexpr int kSkKb = kSkKc / 32;     // MFMA k-steps per chunk
 constexpr int kSkMaxSplit = 8;        // most K ranges a projection is split into
@@ -45,22 +45,33 @@ constexpr int kSkMaxSplit = 8;        // most K ranges a projection is split int
 // u / (8 / TPW), piece (u / 2) % (4 / TPW), half u % 2. With TPW = 2 a
 // staged token chunk and each token operand read from LDS serve twice the
 // weight rows.
+// sk_wload_p issues the loads of piece p (every tile, both halves);
+// sk_wload_t the whole chunk.
 template <int TPW, bool RC>
-__device__ __forceinline__ void sk_wload_t(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K,
-                                           int lane) {
+__device__ __forceinline__ void sk_wload_p(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K, int lane,
+                                           int p) {
     constexpr int KC = kSkKc / TPW, PP = KC / 64;
     const int r8 = RC ? lane >> 3 : lane & 7, q = RC ? lane & 7 : lane >> 3;
 #pragma unroll
-    for (int u = 0; u < kSkKb; ++u) {
-        const int tt = u / (2 * PP), p = (u / 2) % PP;
-        const int row = 16 * tt + 8 * (u & 1) + r8;
-        const int k = c * KC + 64 * p + 8 * q;
-        // past K: the sign bit of K - 1 - k moves the offset out of the range
-        // (reads zero); arithmetic rather than a select, which the compiler
-        // would turn into a branch and a wait around the load
-        const uint32_t past = (uint32_t)(K - 1 - k) & 0x80000000u;
-        buf[u] = ld_weight16(rw, ((uint32_t)(row * K + k) * 2u) | past);
-    }
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int u = tt * 2 * PP + 2 * p + h;
+            const int row = 16 * tt + 8 * h + r8;
+            const int k = c * KC + 64 * p + 8 * q;
+            // past K: the sign bit of K - 1 - k moves the offset out of the
+            // range (reads zero); arithmetic rather than a select, which the
+            // compiler would turn into a branch and a wait around the load
+            const uint32_t past = (uint32_t)(K - 1 - k) & 0x80000000u;
+            buf[u] = ld_weight16(rw, ((uint32_t)(row * K + k) * 2u) | past);
+        }
+}
+template <int TPW, bool RC>
+__device__ __forceinline__ void sk_wload_t(u32x4 (&buf)[kSkKb], rsrc_t rw, int c, int K,
+                                           int lane) {
+#pragma unroll
+    for (int p = 0; p < kSkKc / TPW / 64; ++p)
+        sk_wload_p<TPW, RC>(buf, rw, c, K, lane, p);
 }
 
 // The two loads of one piece (x: rows 0-7, y: rows 8-15) -> the B operands of
@@ -112,15 +123,21 @@ __device__ __forceinline__ int sk_a_vec(int p, int g, int s) {
 __device__ __forceinline__ void sk_keep_order() { __builtin_amdgcn_sched_barrier(0); }
 
 // acc[tt][mt] += tokens 16 mt .. 16 mt + 15 (staged chunk xs) x tile tt of
-// the wave's rows (loads buf of the same chunk).
-template <int MT, int TPW, bool RC>
-__device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32x4 (&buf)[kSkKb],
-                                                const u32x4 (&xs)[MT * 16][kSkKc / TPW / 8 + 1],
-                                                int mt_n, int lane) {
+// the wave's rows (loads buf of the same chunk). ld(p) issues piece p of the
+// next chunk's weight loads just before piece p is multiplied, so a step's
+// loads go out spread over its multiplies rather than in one burst ahead of
+// them (chain of projections at 64 tokens 84.1 -> 83.3 us, 64-token Zipf
+// MoE block 830 -> 825 us, 8-16 tokens unchanged; in-process A/B).
+template <int MT, int TPW, bool RC, class Ld>
+__device__ __forceinline__ void sk_mfma_chunk(f32x4 (&acc)[TPW][MT], const u32x4 (&buf)[kSkKb],
+                                              const u32x4 (&xs)[MT * 16][kSkKc / TPW / 8 + 1],
+                                              int mt_n, int lane, Ld ld) {
     constexpr int PP = kSkKc / TPW / 64;
     const int g = lane >> 4, rl = lane & 15;
 #pragma unroll
     for (int p = 0; p < PP; ++p) {
+        ld(p);
+        sk_keep_order();
         u32x4 b0[TPW], b1[TPW];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
@@ -136,6 +153,7 @@ __device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32
                     acc[tt][mt] = mfma16x16x32(a1, b1[tt], acc[tt][mt]);
                 }
             }
+        sk_keep_order();
     }
 }
 
@@ -156,15 +174,21 @@ __device__ __forceinline__ void sk_mfma_chunk_t(f32x4 (&acc)[TPW][MT], const u32
 // token chunk serves twice the weight rows, which halves the token staging
 // per weight byte (at 64 tokens it would otherwise equal the weight bytes).
 // The K-steps run in the same order for either TPW, so the sums are the same.
-template <int MT, class Jobs, int TPW = 1>
-__global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
+// WPB waves per workgroup (J.wpb must equal it); the token buffers are the
+// launch's dynamic LDS, 2 MT 16 (kSkKc / TPW / 8 + 1) 16-byte vectors.
+template <int MT, class Jobs, int TPW = 1, int WPB = 4>
+__global__ void __launch_bounds__(WPB * kWave) k_sk_gemm(Jobs J, int K, int ksplit) {
     constexpr int KC = kSkKc / TPW;  // K per chunk
     constexpr int KQ = KC / 8;       // 16-byte vectors per token row of a chunk
+    constexpr int NT = WPB * kWave;
     // two token buffers (chunks alternate); +1 vector per row keeps the MFMA
     // reads conflict-free
-    __shared__ u32x4 xs[2][MT * 16][KQ + 1];
-    __shared__ float xch[2][MT][4][kWave];     // epilogue exchange between waves
-    constexpr int SQ = MT * 16 * KQ / kBlock;  // staged vectors per thread per chunk
+    extern __shared__ u32x4 xs_lds[];
+    auto &xs = *reinterpret_cast<u32x4 (*)[2][MT * 16][KQ + 1]>(xs_lds);
+    __shared__ float xch[2][MT][4][kWave];  // epilogue exchange between waves
+    constexpr int NV = MT * 16 * KQ;        // staged vectors per chunk
+    constexpr int SQ = (NV + NT - 1) / NT;  // per thread (the last may be empty)
+    static_assert(NT % KQ == 0, "each thread stages one vector column");
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
     const int nchunks = (K + KC - 1) / KC;
     const int per_job = J.tiles() * ksplit;
@@ -185,17 +209,18 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         const uint16_t *wbase = uniform_ptr(wr);
         const uint32_t wbytes =
             (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u;
-        // This thread stages vectors q = tid + j * 256 of each chunk: token
-        // q / KQ, vector q % KQ. Rows past T read zeros through the buffer
-        // range (no branch, no memory access).
+        // This thread stages vectors q = tid + j NT of each chunk: token
+        // q / KQ, vector q % KQ. Rows past T (and vectors past NV) read zeros
+        // through the buffer range (no branch, no memory access).
         const uint16_t *xb = uniform_ptr(J.xbase(jb));
         const uint32_t xld = (uint32_t)J.xld(jb);
         uint32_t xo[SQ];
         bool xv[SQ];
 #pragma unroll
         for (int j = 0; j < SQ; ++j) {
-            const int t = (threadIdx.x + j * kBlock) / KQ;
-            xv[j] = t < T;
+            const int q = threadIdx.x + j * NT;
+            const int t = q / KQ;
+            xv[j] = t < T && q < NV;
             xo[j] = (uint32_t)J.xrow(jb, xv[j] ? t : 0) * xld;
         }
         const int vq = threadIdx.x % KQ;
@@ -218,8 +243,9 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         auto astore = [&](u32x4 (&st)[SQ], int b) {
 #pragma unroll
             for (int j = 0; j < SQ; ++j) {
-                const int q = threadIdx.x + j * kBlock;
-                xs[b][q / KQ][q % KQ] = st[j];
+                const int q = threadIdx.x + j * NT;
+                if (NV % NT == 0 || q < NV)
+                    xs[b][q / KQ][q % KQ] = st[j];
             }
         };
         f32x4 acc[TPW][MT];
@@ -228,11 +254,16 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](u32x4 (&buf)[kSkKb], int b) {
-            sk_mfma_chunk_t<MT, TPW, MT == 4>(acc, buf, xs[b], mt_n, lane);
+        // multiply chunk buffer buf (token buffer b) while chunk cn's weights
+        // go out into nb
+        auto compute = [&](u32x4 (&buf)[kSkKb], int b, u32x4 (&nb)[kSkKb], int cn) {
+            const rsrc_t rw = weight_range(wbase, cn < c1 ? wbytes : 0u);
+            sk_mfma_chunk<MT, TPW, MT == 4>(acc, buf, xs[b], mt_n, lane, [&](int p) {
+                sk_wload_p<TPW, MT == 4>(nb, rw, cn, K, lane, p);
+            });
         };
         // Chunk c (the item's chunks alternate between token buffers 0 and 1):
-        // the weights of chunk c + 1 go out, chunk c is multiplied, the tokens
+        // chunk c is multiplied while the weights of chunk c + 1 go out, the tokens
         // of chunk c + 1 (loaded one step earlier) go to the other buffer and
         // the tokens of chunk c + 2 go out; one barrier per chunk. A token
         // load thus has a whole step to arrive, and each wait is for loads
@@ -246,15 +277,11 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm(Jobs J, int K, int ksplit) {
         aload(st, c0 + 1);
         __syncthreads();
         for (int c = c0; c < c1; c += 2) {
-            wload(B, c + 1);
-            sk_keep_order();
-            compute(A, 0);
+            compute(A, 0, B, c + 1);
             astore(st, 1);
             aload(st, c + 2);
             __syncthreads();
-            wload(A, c + 2);
-            sk_keep_order();
-            compute(B, 1);
+            compute(B, 1, A, c + 2);
             astore(st, 0);
             aload(st, c + 3);
             __syncthreads();
@@ -430,10 +457,17 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     // nbuf, A's tokens (already staged in st for unit C + 1) go to buffer
     // b ^ 1 and the tokens of the unit after go out
     auto step = [&](u32x4 (&buf)[kSkKb], u32x4 (&nbuf)[kSkKb], int b) {
-        wload(nbuf, W);
-        sk_keep_order();
+        const uint16_t *wr;
+        int nvalid;
+        J.wave_rows(W.jb, W.tile, wq, wr, nvalid);
+        const uint32_t wbytes =
+            W.valid ? (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u : 0u;
+        const rsrc_t rw = weight_range(uniform_ptr(wr), wbytes);
+        const int wc = W.c;
         const int mt_n = C.valid ? min((C.jb.T + 15) >> 4, MT) : 0;
-        sk_mfma_chunk_t<MT, TPW, MT == 4>(acc, buf, xs[b], mt_n, lane);
+        sk_mfma_chunk<MT, TPW, MT == 4>(acc, buf, xs[b], mt_n, lane, [&](int p) {
+            sk_wload_p<TPW, MT == 4>(nbuf, rw, wc, K, lane, p);
+        });
         if (C.valid && C.c + 1 >= C.c1) {
             // acc[tt][mt][i] = out[token 16 mt + 4 g + i][row rl of the
             // wave's tile tt]
@@ -480,6 +514,7 @@ struct SkDense {
     float *part;
     int64_t ldp;
     int tpw;  // 16-row tiles per wave
+    int wpb;  // waves per workgroup: a tile is 16 tpw wpb rows
 
     struct Job {
         int T;
@@ -492,7 +527,7 @@ struct SkDense {
     }
     __device__ void wave_rows(const Job &, int tile, int wq, const uint16_t *&w, int &n) const {
         const int s = seg(tile);
-        const int r0 = (tile - tiles_before[s]) * kSkRows * tpw + wq * 16 * tpw;
+        const int r0 = (tile - tiles_before[s]) * 16 * wpb * tpw + wq * 16 * tpw;
         n = max(0, min(16 * tpw, N[s] - r0));
         w = W[s] + (int64_t)(n > 0 ? r0 : 0) * K;
     }
@@ -506,7 +541,7 @@ struct SkDense {
         const int lane = threadIdx.x & (kWave - 1);
         const int s = seg(tile);
         const int r =
-            (tile - tiles_before[s]) * kSkRows * tpw + wq * 16 * tpw + 16 * tt + (lane & 15);
+            (tile - tiles_before[s]) * 16 * wpb * tpw + wq * 16 * tpw + 16 * tt + (lane & 15);
         if (r >= N[s])
             return;
         const int n = rows_before[s] + r;

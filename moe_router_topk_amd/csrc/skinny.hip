@@ -139,20 +139,59 @@ static bool sk_resident(int T) { return sk_mt(T) <= 2; }
 // kSkMaxSplit ranges of K / kSkMaxSplit (ranges of 128 when K is narrower);
 // K % 128 == 0 and K <= 8192, so a range is a multiple of 16 and at most
 // kResMaxRange wide. Per-chunk staging: about four 256-wide chunks per range,
-// at most four ranges.
+// at most four ranges, except eight for K = 8192 (the o-projection): its
+// 7168 rows then make exactly one 224-row tile per compute unit (below), which
+// streams faster than four ranges of 112-row tiles (26.7 against 28.7 us at
+// 64 tokens) by more than the finish + norm costs over the fused one-pass
+// finish (9.4 against 7.2 us).
 int sk_ksplit(int K, int T) {
     if (sk_resident(T)) {
         const int ks = K / 128;
         return ks < 1 ? 1 : (ks > kSkMaxSplit ? kSkMaxSplit : ks);
     }
+    if (K >= 8192)
+        return kSkMaxSplit;
     const int ks = ((K + kSkKc - 1) / kSkKc) / 4;
     return ks < 1 ? 1 : (ks > 4 ? 4 : ks);
 }
 
-size_t sk_partial_bytes(int T, int rows) {
-    const size_t ks = sk_resident(T) ? kSkMaxSplit : 4;
+size_t sk_partial_bytes(int T, int rows, int K) {
+    const size_t ks = K > 0 ? sk_ksplit(K, T) : kSkMaxSplit;
     return align_up(ks * T * rows * sizeof(float), 256);
 }
+
+// Tile shape of a per-chunk dense pass at 33-64 tokens. With four waves per
+// workgroup and 128-row tiles the launches do not divide over the compute
+// units: 384 items for the 12288-row input projection (some compute units
+// run two workgroups, some one) and 224 for the o-projection (32 idle). A
+// workgroup of WPB waves with one tile of 16 TPW WPB rows per compute unit
+// balances them: where some shape gives between 15/16 of the compute units
+// and all of them items, one workgroup runs per compute unit. Measured on the
+// chain of projections at 64 tokens (in-process A/B): input projection 41.6
+// -> 33.2 us with six waves of two tiles (192 rows), chain 83.7 -> 72.4 us
+// with the o-projection at seven waves of one tile; twelve waves of one tile
+// (three waves per SIMD) ran the input projection at 39.5 us.
+namespace {
+struct SkShape {
+    int wpb, tpw;
+};
+SkShape sk_dense_shape(const int *N, int nseg, int ks, int cu_budget) {
+    int cus = device_cu_count();
+    if (cu_budget > 0 && cu_budget < cus)
+        cus = cu_budget;
+    const SkShape cand[] = {{6, 2}, {7, 2}, {7, 1}};
+    for (const SkShape &c : cand) {
+        const int rows = 16 * c.wpb * c.tpw;
+        int tiles = 0;
+        for (int i = 0; i < nseg; ++i)
+            tiles += (N[i] + rows - 1) / rows;
+        const int items = tiles * ks;
+        if (items <= cus && 16 * items >= 15 * cus)
+            return c;
+    }
+    return SkShape{4, 2};
+}
+}  // namespace
 
 // Partial sums of up to three row segments against the same tokens:
 // part[(ks * T + t) * rows_total + n]. Returns the number of K ranges used.
@@ -166,6 +205,13 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
     // staging per weight byte); below, one
     const int mt = sk_mt(T);
     J.tpw = mt == 4 ? 2 : 1;
+    J.wpb = 4;
+    if (mt == 4 && ks_force <= 0) {
+        const SkShape sh = sk_dense_shape(N, nseg, sk_ksplit(K, T), cu_budget);
+        J.wpb = sh.wpb;
+        J.tpw = sh.tpw;
+    }
+    const int tile_rows = 16 * J.wpb * J.tpw;
     int tiles = 0, rows = 0;
     for (int i = 0; i < 3; ++i) {
         J.W[i] = i < nseg ? W[i] : W[0];
@@ -173,7 +219,7 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
         J.tiles_before[i] = tiles;
         J.rows_before[i] = rows;
         if (i < nseg) {
-            tiles += (N[i] + kSkRows * J.tpw - 1) / (kSkRows * J.tpw);
+            tiles += (N[i] + tile_rows - 1) / tile_rows;
             rows += N[i];
         }
     }
@@ -199,16 +245,27 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
         return ks;
     }
     const int ks = ks_force > 0 ? ks_force : sk_ksplit(K, T);
-    const int grid = budget_grid(tiles * ks, cu_budget, 2);
+    const int grid = budget_grid(tiles * ks, cu_budget, J.wpb == 4 ? 2 : 1);
+    // dynamic LDS: two token buffers of 16 MT rows x (kSkKc / TPW / 8 + 1) vectors
+    auto lds = [](int m, int tpw) {
+        return (size_t)2 * 16 * m * (kSkKc / tpw / 8 + 1) * sizeof(u32x4);
+    };
     switch (mt) {
     case 1:
-        k_sk_gemm<1, SkDense, 1><<<grid, kBlock, 0, s>>>(J, K, ks);
+        k_sk_gemm<1, SkDense, 1><<<grid, kBlock, lds(1, 1), s>>>(J, K, ks);
         break;
     case 2:
-        k_sk_gemm<2, SkDense, 1><<<grid, kBlock, 0, s>>>(J, K, ks);
+        k_sk_gemm<2, SkDense, 1><<<grid, kBlock, lds(2, 1), s>>>(J, K, ks);
         break;
     default:
-        k_sk_gemm<4, SkDense, 2><<<grid, kBlock, 0, s>>>(J, K, ks);
+        if (J.wpb == 6)
+            k_sk_gemm<4, SkDense, 2, 6><<<grid, 6 * kWave, lds(4, 2), s>>>(J, K, ks);
+        else if (J.wpb == 7 && J.tpw == 2)
+            k_sk_gemm<4, SkDense, 2, 7><<<grid, 7 * kWave, lds(4, 2), s>>>(J, K, ks);
+        else if (J.wpb == 7)
+            k_sk_gemm<4, SkDense, 1, 7><<<grid, 7 * kWave, lds(4, 1), s>>>(J, K, ks);
+        else
+            k_sk_gemm<4, SkDense, 2><<<grid, kBlock, lds(4, 2), s>>>(J, K, ks);
         break;
     }
     return ks;
