@@ -599,8 +599,9 @@ struct SkExperts {
     __device__ int xld(const Job &jb) const { return (int)(jb.extra ? ldx_x : ldx); }
     // Epilogue of tile tt of the wave's tpw tiles.
     template <int MT>
-    __device__ void store(const Job &jb, int tile, int, int wq, int tt, const f32x4 (&acc)[MT],
-                          float (*xch)[MT][4][kWave]) const {
+    __device__ __forceinline__ void store(const Job &jb, int tile, int, int wq, int tt,
+                                          const f32x4 (&acc)[MT],
+                                          float (*xch)[MT][4][kWave]) const {
         const int lane = threadIdx.x & (kWave - 1);
         const int g = lane >> 4, rl = lane & 15;
         const int T = jb.T;

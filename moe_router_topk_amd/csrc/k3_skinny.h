@@ -536,8 +536,9 @@ struct SkDense {
     __device__ int xld(const Job &) const { return (int)ldx; }
     // Epilogue of tile tt of the wave's tpw tiles.
     template <int MT>
-    __device__ void store(const Job &, int tile, int ks, int wq, int tt, const f32x4 (&acc)[MT],
-                          float (*)[MT][4][kWave]) const {
+    __device__ __forceinline__ void store(const Job &, int tile, int ks, int wq, int tt,
+                                          const f32x4 (&acc)[MT],
+                                          float (*)[MT][4][kWave]) const {
         const int lane = threadIdx.x & (kWave - 1);
         const int s = seg(tile);
         const int r =
@@ -607,7 +608,8 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
     const int nitems = nfull + (rank < rlast ? 1 : 0);
     const int nunits = nitems * nch;
     // token staging: issued first, stored after the first weight loads
-    constexpr int SMAX = MT * 16 * (kResMaxRange / 8) / (WPB * kWave);  // vectors per thread
+    constexpr int SMAX =  // vectors per thread
+        (MT * 16 * (kResMaxRange / 8) + WPB * kWave - 1) / (WPB * kWave);
     const int nvec = MT * 16 * KQ;
     const rsrc_t rx = act_range(J.x);
     u32x4 sv[SMAX];

@@ -232,13 +232,31 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
     J.ldp = ldp_force > 0 ? ldp_force : rows;
     if (ks_force <= 0 && sk_resident(T)) {
         // the token-resident pass: each workgroup stages its K range's tokens
-        // once (at most 66 KB); four waves per workgroup, two per compute unit
+        // once (at most 66 KB), then its waves stream 16-row tiles. Four
+        // waves per workgroup and two workgroups per compute unit, or seven
+        // waves and one where that gives every wave the same number of tiles
+        // and four waves do not (the 7168-row o-projection: 448 tiles per
+        // range, 1.75 per wave against 2)
         const int ks = sk_ksplit(K, T), kr = K / ks;
-        int grid = budget_grid(1 << 30, cu_budget, 2);
+        int tiles16 = 0;
+        for (int i = 0; i < nseg; ++i)
+            tiles16 += (N[i] + 15) / 16;
+        auto waves_per_range = [&](int wpb, int per_cu) {
+            int g = budget_grid(1 << 30, cu_budget, per_cu);
+            g = g < ks ? ks : g / ks * ks;
+            return g / ks * wpb;
+        };
+        const int w4 = waves_per_range(4, 2), w7 = waves_per_range(7, 1);
+        const bool seven = tiles16 % w4 != 0 && tiles16 % w7 == 0;
+        int grid = budget_grid(1 << 30, cu_budget, seven ? 1 : 2);
         grid = grid < ks ? ks : grid / ks * ks;
         const int kq = (kr + kResKc - 1) / kResKc * (kResKc / 8);
         const size_t lds = (size_t)mt * 16 * (kq + 1) * sizeof(u32x4);
-        if (mt == 1)
+        if (seven && mt == 1)
+            k_sk_res<1, 7><<<grid, 7 * kWave, lds, s>>>(J, K, ks, kr);
+        else if (seven)
+            k_sk_res<2, 7><<<grid, 7 * kWave, lds, s>>>(J, K, ks, kr);
+        else if (mt == 1)
             k_sk_res<1, 4><<<grid, kBlock, lds, s>>>(J, K, ks, kr);
         else
             k_sk_res<2, 4><<<grid, kBlock, lds, s>>>(J, K, ks, kr);
