@@ -356,38 +356,68 @@ __device__ __forceinline__ void topk_keys(const float (&lv)[kTopkPer], int E,
 // the softmax over the k picked logits (the full softmax renormalised over
 // the selection), written by lanes j < k to ids[j], wts[j]. Only the first
 // ceil(E / 64) keys of a lane can be non-empty; the rest are skipped (a
-// wave-uniform bound: E is the same in every lane).
+// wave-uniform bound: E is the same in every lane). Each lane keeps its
+// largest remaining key and that key's slot (the first such slot), so a
+// pick costs the two wave reductions and a rescan of the winning lane's
+// slots only (about 200 instructions per pick when every lane rescanned
+// every slot, and most of the selection's time).
 struct TopkPicker {
     uint32_t key[kTopkPer];
     int per;  // key slots that can hold logits
     int n;    // picks so far
     uint32_t sel_key, top_key;
     int sel_e;
+    uint32_t hk;     // this lane's largest remaining key (0: none left)
+    int hs;          // its slot
+    uint32_t taken;  // this lane's slots already picked (bit i: slot i)
     __device__ __forceinline__ void init(int E) {
         per = __builtin_amdgcn_readfirstlane((E + kWave - 1) / kWave);
         n = 0;
         sel_key = top_key = 0u;
         sel_e = 0;
+        hk = 0u;
+        hs = 0;
+        taken = 0u;
+    }
+    // hk, hs from this lane's slots not yet taken. Slots go in groups of
+    // four behind a wave-uniform test against per (slots past E hold key 0,
+    // so a group's tail needs no test). Each group is its own instantiation
+    // and a taken slot is a bit of `taken`, not a cleared key, so every
+    // index is a constant and the keys stay in registers.
+    static_assert(kTopkPer == 16, "four groups of four key slots");
+    template <int G>
+    __device__ __forceinline__ void head_group(uint32_t &bk, int &bs) const {
+        if (4 * G < per)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!((taken >> (4 * G + j)) & 1u) && key[4 * G + j] > bk) {
+                    bk = key[4 * G + j];
+                    bs = 4 * G + j;
+                }
+    }
+    __device__ __forceinline__ void head() {
+        uint32_t bk = 0u;
+        int bs = 0;
+        head_group<0>(bk, bs);
+        head_group<1>(bk, bs);
+        head_group<2>(bk, bs);
+        head_group<3>(bk, bs);
+        hk = bk;
+        hs = bs;
     }
     // The next pick's expert (the same in every lane).
     __device__ __forceinline__ int next() {
         const int lane = threadIdx.x & (kWave - 1);
-        uint32_t bk = 0u;
-        int bi = 0;
-#pragma unroll
-        for (int i = 0; i < kTopkPer; ++i) {
-            if (i < per && key[i] > bk) {
-                bk = key[i];
-                bi = i;
-            }
+        if (n == 0)
+            head();  // the keys are complete by the first pick
+        const uint32_t m = wave_max_u32(hk);
+        const uint32_t w = wave_min_u32(hk == m ? (uint32_t)(hs * kWave + lane) : 0xffffffffu);
+        if ((int)(w & (kWave - 1)) == lane) {
+            // the winning lane gives up the slot (its head) and finds its
+            // next head
+            taken |= 1u << hs;
+            head();
         }
-        const uint32_t m = wave_max_u32(bk);
-        const uint32_t w = wave_min_u32(bk == m ? (uint32_t)(bi * kWave + lane) : 0xffffffffu);
-        const int wi = (int)(w >> 6);
-#pragma unroll
-        for (int i = 0; i < kTopkPer; ++i)
-            if (i < per && wi == i && (int)(w & (kWave - 1)) == lane)
-                key[i] = 0u;
         if (lane == n) {
             sel_key = m;
             sel_e = (int)w;

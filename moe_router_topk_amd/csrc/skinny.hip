@@ -49,16 +49,42 @@ __device__ __forceinline__ float sk_sum(const float *part, int ks, int64_t strid
     return v;
 }
 
+// Segment s's descriptor, s differing between lanes. Each field is chosen
+// among the three segments' copies, which are uniform (scalar loads of the
+// kernel arguments): indexing O.s[s] directly made the compiler read the
+// descriptor with vector loads from the argument buffer, one dependent
+// memory round trip per field, before the partials' loads could go out.
+__device__ __forceinline__ SkOutSeg sk_seg(const SkOuts &O, int s) {
+    // readfirstlane keeps each copy a scalar value, so the compiler cannot
+    // fold the choice back into a per-lane index into the arguments
+    auto u32 = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    auto u64 = [](int64_t v) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    SkOutSeg q;
+    q.mode = s == 0 ? u32(O.s[0].mode) : (s == 1 ? u32(O.s[1].mode) : u32(O.s[2].mode));
+    q.cols = s == 0 ? u32(O.s[0].cols) : (s == 1 ? u32(O.s[1].cols) : u32(O.s[2].cols));
+    q.rows_before = s == 0 ? u32(O.s[0].rows_before)
+                           : (s == 1 ? u32(O.s[1].rows_before) : u32(O.s[2].rows_before));
+    q.y = s == 0 ? uniform_ptr(O.s[0].y) : (s == 1 ? uniform_ptr(O.s[1].y) : uniform_ptr(O.s[2].y));
+    q.ldy = s == 0 ? u64(O.s[0].ldy) : (s == 1 ? u64(O.s[1].ldy) : u64(O.s[2].ldy));
+    q.bias = s == 0 ? uniform_ptr(O.s[0].bias)
+                    : (s == 1 ? uniform_ptr(O.s[1].bias) : uniform_ptr(O.s[2].bias));
+    q.h32 = s == 0 ? uniform_ptr(O.s[0].h32)
+                   : (s == 1 ? uniform_ptr(O.s[1].h32) : uniform_ptr(O.s[2].h32));
+    return q;
+}
+
 __device__ __forceinline__ void sk_finish_one(const float *__restrict__ part, int ks, int T,
                                               int64_t ldp, const SkOuts &O, int64_t i) {
     const int t = (int)(i / O.cols_total);
     int c = (int)(i - (int64_t)t * O.cols_total);
-    int s = 0;
-    while (s < O.nseg - 1 && c >= O.s[s].cols) {
-        c -= O.s[s].cols;
-        ++s;
-    }
-    const SkOutSeg &q = O.s[s];
+    const int c0 = O.s[0].cols, c1 = O.s[1].cols;
+    const int s = (O.nseg > 1 && c >= c0) ? ((O.nseg > 2 && c >= c0 + c1) ? 2 : 1) : 0;
+    c -= (s >= 1 ? c0 : 0) + (s >= 2 ? c1 : 0);
+    const SkOutSeg q = sk_seg(O, s);
     const int64_t stride = (int64_t)T * ldp;
     const int64_t base = (int64_t)t * ldp + q.rows_before;
     if (q.mode == 2) {
@@ -104,11 +130,25 @@ k_sk_finish_topk(const float *__restrict__ part, int ks, int T, int64_t ldp, SkO
         __shared__ float lg[K3_MAX_EXPERTS];
         const int t = blockIdx.x;
         const int64_t stride = (int64_t)T * ldp;
-        for (int c = threadIdx.x; c < E; c += kBlock) {
-            const float v = sk_sum(part, ks, stride, (int64_t)t * ldp + c);
-            const float l = r.bias ? v + r.bias[c] : v;
-            ((float *)r.y)[(int64_t)t * r.ldy + c] = l;
-            lg[c] = l;
+        // every load of the token's logits (partials and bias) goes out
+        // before the first sum, so the row waits for one memory latency
+        constexpr int PER = K3_MAX_EXPERTS / kBlock;
+        float v[PER], bv[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = threadIdx.x + j * kBlock;
+            const int cc = c < E ? c : 0;
+            v[j] = sk_sum(part, ks, stride, (int64_t)t * ldp + cc);
+            bv[j] = r.bias ? r.bias[cc] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = threadIdx.x + j * kBlock;
+            if (c < E) {
+                const float l = r.bias ? v[j] + bv[j] : v[j];
+                ((float *)r.y)[(int64_t)t * r.ldy + c] = l;
+                lg[c] = l;
+            }
         }
         __syncthreads();
         if (threadIdx.x < kWave)
