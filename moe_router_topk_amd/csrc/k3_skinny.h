@@ -714,3 +714,150 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
 }
 
 }  // namespace k3
+
+// ------------------------------------------------------------------ whole-K pass (5-8 tokens)
+namespace k3 {
+
+// Dense projections over at most kKwMaxTokens tokens with final outputs and
+// no partial sums: workgroup g owns rows [g R, g R + R) (NT 16-row tiles,
+// the last ones possibly short) over the whole K, and its NW waves split K
+// into slices of kKwSlice (NW = K / kKwSlice). Wave w stages its slice of the
+// tokens in its own LDS region (no other wave reads it) and
+// streams that slice of every tile of the workgroup with two 8 KB register
+// buffers in flight; at the end the NW slice sums of each output are added
+// in wave order through LDS and written as bf16 (mode 0) or added to the
+// residual (mode 1: h32 = bf16 residual + sum, residual = bf16(h32)). So an
+// output's summation order is a function of K alone, and no finishing kernel
+// follows. The tokens' slices take (kKwMaxTokens + 1) rows of LDS per wave
+// (the extra row is zeros, which token rows of the MFMA tile past T read).
+constexpr int kKwMaxTokens = 8;
+constexpr int kKwSlice = 1024;  // K per wave
+
+struct KwJob {
+    const uint16_t *W;  // [N][K]
+    int N, K;
+    const uint16_t *x;  // [T][ldx]
+    int64_t ldx;
+    int T;
+    int R;     // rows per workgroup (at most 16 NT)
+    int mode;  // 0: y = bf16(x . W^T); 1: residual add
+    uint16_t *y;  // mode 0: y [T][ldy]; mode 1: the residual [T][ldy], updated in place
+    int64_t ldy;
+    float *h32;  // mode 1: [T][ldy]
+};
+
+// LDS bytes of k_sk_kw<NW, NT>: the token slices, later reused for the sums
+constexpr size_t kw_lds_bytes(int nw, int nt) {
+    const size_t tok = (size_t)nw * (kKwMaxTokens + 1) * (kKwSlice / 8 + 1) * 16;
+    const size_t red = (size_t)nw * nt * 4 * kWave * 4;
+    return tok > red ? tok : red;
+}
+
+template <int NW, int NT>
+__global__ void __launch_bounds__(NW * kWave) k_sk_kw(KwJob J) {
+    extern __shared__ u32x4 kw_lds[];
+    constexpr int KQ = kKwSlice / 8;  // 16-byte vectors per token row of a slice
+    constexpr int RS = KQ + 1;        // row stride (+1 keeps the MFMA reads conflict-free)
+    constexpr int ROWS = kKwMaxTokens + 1;
+    constexpr int NCH = kKwSlice / kSkKc;  // 256-wide chunks per slice
+    constexpr int NU = NT * NCH;           // units (tile, chunk) per wave
+    constexpr int SV = ROWS * KQ / kWave;  // staged vectors per lane
+    static_assert(ROWS * KQ % kWave == 0, "whole vectors per lane");
+    const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
+    const int T = J.T, K = J.K;
+    const int k0 = wq * kKwSlice;
+    const int r0 = blockIdx.x * J.R;
+    const int r1 = min(J.N, r0 + J.R);
+    u32x4 *xw = kw_lds + wq * ROWS * RS;
+    // the wave's token slice: row t < T from x, rows T.. zeros
+    u32x4 sv[SV];
+    {
+        const rsrc_t rx = act_range(uniform_ptr(J.x));
+#pragma unroll
+        for (int j = 0; j < SV; ++j) {
+            const int q = lane + j * kWave;
+            const int t = q / KQ, v = q - t * KQ;
+            sv[j] = ld_act16(rx, t < T ? ((uint32_t)t * (uint32_t)J.ldx + (uint32_t)(k0 + 8 * v)) * 2u
+                                       : kOffNone);
+        }
+    }
+    // unit u: tile u / NCH, chunk u % NCH of the slice (tile-major, so each
+    // row's slice streams in order)
+    auto load = [&](u32x4 (&buf)[kSkKb], int u) {
+        const int t = u / NCH, c = u - t * NCH;
+        const int rt = r0 + 16 * t;
+        const int nvalid = u < NU ? max(0, min(16, r1 - rt)) : 0;
+        const rsrc_t rw =
+            weight_range(uniform_ptr(J.W + (int64_t)(nvalid > 0 ? rt : 0) * K),
+                         (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u);
+        sk_wload_t<1, false>(buf, rw, k0 / kSkKc + c, K, lane);
+    };
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int g = lane >> 4, rl = lane & 15;
+    const u32x4 *xa = xw + (rl < T ? rl : T) * RS;  // this lane's token row
+    auto compute = [&](const u32x4 (&buf)[kSkKb], int u) {
+        const int t = u / NCH, c = u - t * NCH;
+#pragma unroll
+        for (int p = 0; p < kSkKb / 2; ++p) {
+            u32x4 b0, b1;
+            sk_pair<false>(buf[2 * p], buf[2 * p + 1], b0, b1);
+            const u32x4 *xc = xa + c * (kSkKc / 8);
+            acc[t] = mfma16x16x32(xc[sk_a_vec<false>(p, g, 0)], b0, acc[t]);
+            acc[t] = mfma16x16x32(xc[sk_a_vec<false>(p, g, 1)], b1, acc[t]);
+        }
+    };
+    u32x4 A[kSkKb], B[kSkKb];
+    load(A, 0);
+    load(B, 1);
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+        const int q = lane + j * kWave;
+        const int t = q / KQ;
+        xw[t * RS + (q - t * KQ)] = sv[j];
+    }
+    // other lanes of the wave read these vectors: one barrier (once per
+    // launch) orders the writes before them
+    __syncthreads();
+    // units in pairs (NU is even: NCH is); every load is issued on every path
+#pragma unroll
+    for (int u = 0; u < NU; u += 2) {
+        sk_keep_order();
+        compute(A, u);
+        load(A, u + 2);
+        sk_keep_order();
+        compute(B, u + 1);
+        load(B, u + 3);
+    }
+    __syncthreads();  // every wave is done with its token slice: reuse the LDS
+    float *red = reinterpret_cast<float *>(kw_lds);  // [NW][NT][4][64]
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            red[((wq * NT + t) * 4 + i) * kWave + lane] = acc[t][i];
+    __syncthreads();
+    // acc[t][i] of lane l = out[token 4 (l / 16) + i][row r0 + 16 t + l % 16]
+    for (int e = threadIdx.x; e < NT * 4 * kWave; e += NW * kWave) {
+        const int t = e / (4 * kWave), i = (e / kWave) & 3, ln = e & (kWave - 1);
+        float v = red[e];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            v += red[w * NT * 4 * kWave + e];
+        const int tok = 4 * (ln >> 4) + i, n = r0 + 16 * t + (ln & 15);
+        if (tok < T && n < r1) {
+            const int64_t o = (int64_t)tok * J.ldy + n;
+            if (J.mode == 0) {
+                J.y[o] = f32_to_bf16(v);
+            } else {
+                const float h = bf16_to_f32(J.y[o]) + v;
+                J.y[o] = f32_to_bf16(h);
+                J.h32[o] = h;
+            }
+        }
+    }
+}
+
+}  // namespace k3

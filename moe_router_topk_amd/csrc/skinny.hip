@@ -356,9 +356,38 @@ SkOuts sk_outs1(int mode, int cols, void *y, int64_t ldy, const float *bias) {
     return O;
 }
 
-// y[t][n] = bf16(x . W^T) through partials.
+// The whole-K pass (k_sk_kw) for 5..kKwMaxTokens tokens: K a multiple of
+// kKwSlice with seven or eight slices (one wave each), at most four 16-row
+// tiles per workgroup on one workgroup per compute unit. Returns false (and
+// launches nothing) for other shapes.
+static bool sk_kw_launch(KwJob J, hipStream_t s) {
+    if (J.T < 5 || J.T > kKwMaxTokens || J.K % kKwSlice)
+        return false;
+    const int nw = J.K / kKwSlice;
+    if (nw != 7 && nw != 8)
+        return false;
+    const int cus = device_cu_count();
+    J.R = (J.N + cus - 1) / cus;
+    const int nt = (J.R + 15) / 16;
+    if (nt < 2 || nt > 4)
+        return false;
+    const int grid = (J.N + J.R - 1) / J.R;
+#define K3_KW(NW_, NT_)                                                                  \
+    k_sk_kw<NW_, NT_><<<grid, NW_ * kWave, kw_lds_bytes(NW_, NT_), s>>>(J)
+    if (nw == 7)
+        nt == 2 ? K3_KW(7, 2) : nt == 3 ? K3_KW(7, 3) : K3_KW(7, 4);
+    else
+        nt == 2 ? K3_KW(8, 2) : nt == 3 ? K3_KW(8, 3) : K3_KW(8, 4);
+#undef K3_KW
+    return true;
+}
+
+// y[t][n] = bf16(x . W^T): whole-K pass where it applies, else partials and
+// the finishing kernel.
 void sk_proj_bf16(const uint16_t *x, int64_t ldx, int T, const uint16_t *W, int N, int K,
                   uint16_t *y, int64_t ldy, float *part, hipStream_t s) {
+    if (sk_kw_launch(KwJob{W, N, K, x, ldx, T, 0, 0, y, ldy, nullptr}, s))
+        return;
     const int ks = sk_dense_partials(&W, &N, 1, K, x, ldx, T, part, 0, s);
     sk_finish(part, ks, T, N, sk_outs1(0, N, y, ldy, nullptr), 0, s);
 }
@@ -439,6 +468,8 @@ int sk_oproj_partials(const uint16_t *a, int64_t lda, int T, int K, const uint16
 
 void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint16_t *W_o, int d,
                        uint16_t *residual, float *h32, float *part, hipStream_t s) {
+    if (sk_kw_launch(KwJob{W_o, d, K, a, lda, T, 0, 1, residual, d, h32}, s))
+        return;
     const int ks = sk_dense_partials(&W_o, &d, 1, K, a, lda, T, part, 0, s);
     SkOuts O{};
     O.s[0] = SkOutSeg{3, d, 0, residual, d, nullptr, h32};

@@ -286,10 +286,11 @@ def test_row_engine_short_and_uneven_rows(k3, K, N, b):
         assert_rel_close(yn.cpu(), y_ref, "y_norm")
 
 
-@pytest.mark.parametrize("b", sorted(set(synth.CHAIN_BATCHES) | {24, 40, 48, 56}))
+@pytest.mark.parametrize("b", sorted(set(synth.CHAIN_BATCHES) | {5, 6, 7, 24, 40, 48, 56}))
 def test_proj_skinny_chain_in(k3, chain_w, chain_host, b):
     """The attention input projection 7168 -> 12288 at every chain batch the
-    benchmark times and the verify batches 8 r; every output."""
+    benchmark times, the verify batches 8 r and 5-7 tokens (the whole-K pass
+    covers 5-8); every output."""
     inp = synth.make_chain_inputs(synth.CHAIN_CONFIG, b, device=DEV, index=300 + b)
     q = k3.k3_proj_skinny(inp["x"], chain_w["w_in"])
     torch.cuda.synchronize()
@@ -583,7 +584,7 @@ def test_moe_experts_invalid_ids_dropped(k3):
 
 
 # ---------------------------------------------------------------- o-proj + residual + norm
-@pytest.mark.parametrize("b", [1, 2, 3, 4, 8, 16, 24, 32, 40, 48, 56, 64])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 24, 32, 40, 48, 56, 64])
 def test_oproj_residual_full(k3, chain_w, chain_host, b):
     w = chain_w
     cc = synth.CHAIN_CONFIG
