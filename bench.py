@@ -124,7 +124,7 @@ def committed_trace():
 
 
 # the kernels of one batch-1 layer step, once each, in launch order
-STEP_B1_KERNELS = ["k_gemv<7, 1,", "k_oproj_gemv<", "k_rls_gemv<7, 1, true>",
+STEP_B1_KERNELS = ["k_gemv<7, 1,", "k_oproj_gemv<", "k_rls_gemv<7, 1, true",
                    "k_moe_up_b1<true", "k_down_b1<"]
 
 
