@@ -85,6 +85,15 @@ int k3_version(void);
  * batches 2-4 on the MFMA tiles too (batch 1 and DOT2 above batch 4 are not
  * available and fail with K3_ERR_UNSUPPORTED). */
 #define K3_OP_EXPERT_ENGINE 8
+/* Not an entry point: the MFMA pass of the last dense projection above four
+ * tokens -- K3_VARIANT_WHOLEK (5-8 tokens, K a multiple of 1024 with seven or
+ * eight 1024-wide slices: whole-K workgroups, no partial sums),
+ * K3_VARIANT_RESIDENT (token-resident split-K pass, up to 32 tokens) or
+ * K3_VARIANT_SPLITK (per-chunk split-K pass, 33-64 tokens). Recorded by
+ * k3_proj_skinny, k3_oproj_residual and the router passes of
+ * k3_router_topk(_latent), k3_shared_expert and the MoE block above four
+ * tokens. It cannot be forced. */
+#define K3_OP_DENSE_PASS 9
 
 #define K3_VARIANT_NONE 0
 #define K3_VARIANT_DOT2 1    /* VALU dot2 GEMV: whole weight rows per wave */
@@ -101,6 +110,9 @@ int k3_version(void);
  * (the fences write back and invalidate the L2 of every workgroup's XCD);
  * kept so that the comparison can be repeated. */
 #define K3_VARIANT_LASTWG 5
+#define K3_VARIANT_WHOLEK 6   /* K3_OP_DENSE_PASS only */
+#define K3_VARIANT_RESIDENT 7 /* K3_OP_DENSE_PASS only */
+#define K3_VARIANT_SPLITK 8   /* K3_OP_DENSE_PASS only */
 
 /* Variant the last successful call of `op` on this process launched. */
 int k3_get_last_dispatch(int op);

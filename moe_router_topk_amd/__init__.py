@@ -31,8 +31,9 @@ _lib = None
 
 OP = {"router_topk": 0, "proj_skinny": 1, "moe_experts": 2, "shared_expert": 3,
       "oproj_residual": 4, "prefetch": 5, "router_latent": 6, "moe_block": 7,
-      "expert_engine": 8}
-VARIANT = {"none": 0, "dot2": 1, "mfma": 2, "grouped": 3, "stream": 4, "lastwg": 5}
+      "expert_engine": 8, "dense_pass": 9}
+VARIANT = {"none": 0, "dot2": 1, "mfma": 2, "grouped": 3, "stream": 4, "lastwg": 5,
+           "wholek": 6, "resident": 7, "splitk": 8}
 VARIANT_NAME = {v: k for k, v in VARIANT.items()}
 
 EXPORTED_SYMBOLS = [

@@ -8,7 +8,7 @@
 namespace k3 {
 
 namespace {
-constexpr int kOps = K3_OP_EXPERT_ENGINE + 1;  // op slots of the dispatch record
+constexpr int kOps = K3_OP_DENSE_PASS + 1;  // op slots of the dispatch record
 std::atomic<int> g_last_variant[kOps];
 std::atomic<int> g_forced_variant[kOps];
 std::atomic<void *> g_trace_begin[kOps];
@@ -106,7 +106,7 @@ int k3_get_last_dispatch(int op) {
 }
 
 int k3_force_variant(int op, int variant) {
-    if (op < 0 || op >= k3::kOps || variant < K3_VARIANT_NONE ||
+    if (op < 0 || op >= k3::kOps || op == K3_OP_DENSE_PASS || variant < K3_VARIANT_NONE ||
         variant > K3_VARIANT_LASTWG)
         return K3_ERR_INVALID_ARG;
     k3::g_forced_variant[op].store(variant);

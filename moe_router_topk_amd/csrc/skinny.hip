@@ -300,6 +300,7 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
             k_sk_res<1, 4><<<grid, kBlock, lds, s>>>(J, K, ks, kr);
         else
             k_sk_res<2, 4><<<grid, kBlock, lds, s>>>(J, K, ks, kr);
+        record_dispatch(K3_OP_DENSE_PASS, K3_VARIANT_RESIDENT);
         return ks;
     }
     const int ks = ks_force > 0 ? ks_force : sk_ksplit(K, T);
@@ -326,6 +327,7 @@ int sk_dense_partials(const uint16_t *const *W, const int *N, int nseg, int K, c
             k_sk_gemm<4, SkDense, 2><<<grid, kBlock, lds(4, 2), s>>>(J, K, ks);
         break;
     }
+    record_dispatch(K3_OP_DENSE_PASS, K3_VARIANT_SPLITK);
     return ks;
 }
 
@@ -379,6 +381,7 @@ static bool sk_kw_launch(KwJob J, hipStream_t s) {
     else
         nt == 2 ? K3_KW(8, 2) : nt == 3 ? K3_KW(8, 3) : K3_KW(8, 4);
 #undef K3_KW
+    record_dispatch(K3_OP_DENSE_PASS, K3_VARIANT_WHOLEK);
     return true;
 }
 

@@ -70,8 +70,10 @@ def test_force_variant_validation(L):
     assert L.k3_force_variant(6, 0) == K3_OK
     assert L.k3_force_variant(8, 2) == K3_OK  # the expert engine
     assert L.k3_force_variant(8, 0) == K3_OK
-    assert L.k3_force_variant(9, 0) == INVALID
+    assert L.k3_force_variant(9, 0) == INVALID  # the dense pass record cannot be forced
+    assert L.k3_force_variant(10, 0) == INVALID
     assert L.k3_force_variant(1, 17) == INVALID
+    assert L.k3_force_variant(1, 6) == INVALID  # record-only variants
     assert L.k3_force_variant(0, 6) == INVALID
 
 

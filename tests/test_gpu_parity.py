@@ -227,6 +227,13 @@ def test_router_topk_latent_tiny_repeated(k3):
 
 
 # ---------------------------------------------------------------- skinny projection
+def dense_pass_for(b, K):
+    """The MFMA pass a single dense projection takes above four tokens."""
+    if 5 <= b <= 8 and K % 1024 == 0 and K // 1024 in (7, 8):
+        return "wholek"
+    return "resident" if b <= 32 else "splitk"
+
+
 @pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 8, 9, 16, 17, 24, 32, 33, 40, 48, 56, 64])
 def test_proj_skinny_latent(k3, full, host, b):
     cfg, w = full
@@ -235,6 +242,8 @@ def test_proj_skinny_latent(k3, full, host, b):
     torch.cuda.synchronize()
     assert_rel_close(y.cpu(), oracle.linear(x.cpu(), host[0]["w_lat"]), "z")
     assert k3.k3_get_last_dispatch("proj_skinny") == ("dot2" if b <= 4 else "mfma")
+    if b > 4:
+        assert k3.k3_get_last_dispatch("dense_pass") == dense_pass_for(b, cfg.d)
 
 
 @pytest.mark.parametrize("variant", ["dot2", "mfma"])
@@ -296,6 +305,8 @@ def test_proj_skinny_chain_in(k3, chain_w, chain_host, b):
     torch.cuda.synchronize()
     assert_rel_close(q.cpu(), oracle.linear(inp["x"].cpu(), chain_host["w_in"]), "q")
     assert k3.k3_get_last_dispatch("proj_skinny") == ("dot2" if b <= 4 else "mfma")
+    if b > 4:
+        assert k3.k3_get_last_dispatch("dense_pass") == dense_pass_for(b, synth.CHAIN_CONFIG.d)
 
 
 @pytest.mark.parametrize("b", [3, 20])
@@ -599,6 +610,8 @@ def test_oproj_residual_full(k3, chain_w, chain_host, b):
     assert_rel_close(r.cpu(), h_ref, "h")
     assert_rel_close(y.cpu(), y_ref, "y_norm")
     assert k3.k3_get_last_dispatch("oproj_residual") == ("dot2" if b <= 4 else "mfma")
+    if b > 4:
+        assert k3.k3_get_last_dispatch("dense_pass") == dense_pass_for(b, cc.k_o)
 
 
 def test_oproj_residual_identity_norm(k3):
