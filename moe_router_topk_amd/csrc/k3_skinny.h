@@ -722,15 +722,19 @@ namespace k3 {
 // no partial sums: workgroup g owns rows [g R, g R + R) (NT 16-row tiles,
 // the last ones possibly short) over the whole K, and its NW waves split K
 // into slices of kKwSlice (NW = K / kKwSlice). Wave w stages its slice of the
-// tokens in its own LDS region (no other wave reads it) and
-// streams that slice of every tile of the workgroup with two 8 KB register
-// buffers in flight; at the end the NW slice sums of each output are added
-// in wave order through LDS and written as bf16 (mode 0) or added to the
-// residual (mode 1: h32 = bf16 residual + sum, residual = bf16(h32)). So an
-// output's summation order is a function of K alone, and no finishing kernel
-// follows. The tokens' slices take (kKwMaxTokens + 1) rows of LDS per wave
-// (the extra row is zeros, which token rows of the MFMA tile past T read).
-constexpr int kKwMaxTokens = 8;
+// tokens in its own LDS region (no other wave reads it) and streams that
+// slice of every tile of the workgroup with two 8 KB register buffers in
+// flight; at the end the NW slice sums of each output are added in wave
+// order through LDS and written as bf16 (mode 0) or added to the residual
+// (mode 1: h32 = bf16 residual + sum, residual = bf16(h32)). So an output's
+// summation order is a function of K alone, and no finishing kernel follows.
+// Up to 8 tokens a wave stages its whole slice at once (PH = 1); up to 16 it
+// stages it in two halves (PH = 2): the second half's tokens are loaded into
+// registers at the start and written over the first half once the first
+// half's chunks of every tile are multiplied. A region holds 8 PH + 1 token
+// rows (the extra row is zeros, which token rows of the MFMA tile past T
+// read).
+constexpr int kKwMaxTokens = 16;
 constexpr int kKwSlice = 1024;  // K per wave
 
 struct KwJob {
@@ -746,51 +750,65 @@ struct KwJob {
     float *h32;  // mode 1: [T][ldy]
 };
 
-// LDS bytes of k_sk_kw<NW, NT>: the token slices, later reused for the sums
-constexpr size_t kw_lds_bytes(int nw, int nt) {
-    const size_t tok = (size_t)nw * (kKwMaxTokens + 1) * (kKwSlice / 8 + 1) * 16;
+// LDS bytes of k_sk_kw<NW, NT, PH>: the token slices, later reused for the sums
+constexpr size_t kw_lds_bytes(int nw, int nt, int ph) {
+    const size_t tok = (size_t)nw * (8 * ph + 1) * (kKwSlice / ph / 8 + 1) * 16;
     const size_t red = (size_t)nw * nt * 4 * kWave * 4;
     return tok > red ? tok : red;
 }
 
-template <int NW, int NT>
+template <int NW, int NT, int PH>
 __global__ void __launch_bounds__(NW * kWave) k_sk_kw(KwJob J) {
     extern __shared__ u32x4 kw_lds[];
-    constexpr int KQ = kKwSlice / 8;  // 16-byte vectors per token row of a slice
-    constexpr int RS = KQ + 1;        // row stride (+1 keeps the MFMA reads conflict-free)
-    constexpr int ROWS = kKwMaxTokens + 1;
-    constexpr int NCH = kKwSlice / kSkKc;  // 256-wide chunks per slice
-    constexpr int NU = NT * NCH;           // units (tile, chunk) per wave
-    constexpr int SV = ROWS * KQ / kWave;  // staged vectors per lane
+    constexpr int SL = kKwSlice / PH;  // K of the slice staged at once
+    constexpr int KQ = SL / 8;         // 16-byte vectors per token row of it
+    constexpr int RS = KQ + 1;         // row stride (+1 keeps the MFMA reads conflict-free)
+    constexpr int ROWS = 8 * PH + 1;
+    constexpr int NCH = SL / kSkKc;  // 256-wide chunks per staged part
+    constexpr int NUP = NT * NCH;    // units (tile, chunk) per part
+    constexpr int NU = PH * NUP;
+    constexpr int SV = ROWS * KQ / kWave;  // staged vectors per lane per part
     static_assert(ROWS * KQ % kWave == 0, "whole vectors per lane");
+    static_assert(NUP % 2 == 0, "units run in pairs within a part");
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
     const int T = J.T, K = J.K;
     const int k0 = wq * kKwSlice;
     const int r0 = blockIdx.x * J.R;
     const int r1 = min(J.N, r0 + J.R);
     u32x4 *xw = kw_lds + wq * ROWS * RS;
-    // the wave's token slice: row t < T from x, rows T.. zeros
-    u32x4 sv[SV];
+    // every part's token vectors: row t < T from x, the others zeros
+    u32x4 sv[PH][SV];
     {
         const rsrc_t rx = act_range(uniform_ptr(J.x));
 #pragma unroll
+        for (int h = 0; h < PH; ++h)
+#pragma unroll
+            for (int j = 0; j < SV; ++j) {
+                const int q = lane + j * kWave;
+                const int t = q / KQ, v = q - t * KQ;
+                const int k = k0 + h * SL + 8 * v;
+                sv[h][j] = ld_act16(
+                    rx, t < T ? ((uint32_t)t * (uint32_t)J.ldx + (uint32_t)k) * 2u : kOffNone);
+            }
+    }
+    auto stage = [&](int h) {
+#pragma unroll
         for (int j = 0; j < SV; ++j) {
             const int q = lane + j * kWave;
-            const int t = q / KQ, v = q - t * KQ;
-            sv[j] = ld_act16(rx, t < T ? ((uint32_t)t * (uint32_t)J.ldx + (uint32_t)(k0 + 8 * v)) * 2u
-                                       : kOffNone);
+            const int t = q / KQ;
+            xw[t * RS + (q - t * KQ)] = sv[h][j];
         }
-    }
-    // unit u: tile u / NCH, chunk u % NCH of the slice (tile-major, so each
-    // row's slice streams in order)
+    };
+    // unit u: part u / NUP; within it tile (u % NUP) / NCH, chunk u % NCH
+    // (tile-major, so each row's part streams in order)
     auto load = [&](u32x4 (&buf)[kSkKb], int u) {
-        const int t = u / NCH, c = u - t * NCH;
+        const int h = u / NUP, t = (u % NUP) / NCH, c = u % NCH;
         const int rt = r0 + 16 * t;
         const int nvalid = u < NU ? max(0, min(16, r1 - rt)) : 0;
         const rsrc_t rw =
             weight_range(uniform_ptr(J.W + (int64_t)(nvalid > 0 ? rt : 0) * K),
                          (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u);
-        sk_wload_t<1, false>(buf, rw, k0 / kSkKc + c, K, lane);
+        sk_wload_t<1, false>(buf, rw, (k0 + h * SL) / kSkKc + c, K, lane);
     };
     f32x4 acc[NT];
 #pragma unroll
@@ -799,7 +817,7 @@ __global__ void __launch_bounds__(NW * kWave) k_sk_kw(KwJob J) {
     const int g = lane >> 4, rl = lane & 15;
     const u32x4 *xa = xw + (rl < T ? rl : T) * RS;  // this lane's token row
     auto compute = [&](const u32x4 (&buf)[kSkKb], int u) {
-        const int t = u / NCH, c = u - t * NCH;
+        const int t = (u % NUP) / NCH, c = u % NCH;
 #pragma unroll
         for (int p = 0; p < kSkKb / 2; ++p) {
             u32x4 b0, b1;
@@ -812,18 +830,19 @@ __global__ void __launch_bounds__(NW * kWave) k_sk_kw(KwJob J) {
     u32x4 A[kSkKb], B[kSkKb];
     load(A, 0);
     load(B, 1);
-#pragma unroll
-    for (int j = 0; j < SV; ++j) {
-        const int q = lane + j * kWave;
-        const int t = q / KQ;
-        xw[t * RS + (q - t * KQ)] = sv[j];
-    }
-    // other lanes of the wave read these vectors: one barrier (once per
-    // launch) orders the writes before them
+    stage(0);
+    // other lanes of the wave read these vectors: a barrier orders the
+    // writes before them (once per part)
     __syncthreads();
-    // units in pairs (NU is even: NCH is); every load is issued on every path
+    // units in pairs; every load is issued on every path
 #pragma unroll
     for (int u = 0; u < NU; u += 2) {
+        if (u > 0 && u % NUP == 0) {
+            // the previous part's multiplies are done: its region takes the
+            // next part's tokens
+            stage(u / NUP);
+            __syncthreads();
+        }
         sk_keep_order();
         compute(A, u);
         load(A, u + 2);

@@ -360,8 +360,9 @@ SkOuts sk_outs1(int mode, int cols, void *y, int64_t ldy, const float *bias) {
 
 // The whole-K pass (k_sk_kw) for 5..kKwMaxTokens tokens: K a multiple of
 // kKwSlice with seven or eight slices (one wave each), at most four 16-row
-// tiles per workgroup on one workgroup per compute unit. Returns false (and
-// launches nothing) for other shapes.
+// tiles per workgroup on one workgroup per compute unit; token slices staged
+// whole up to 8 tokens, in two halves up to 16. Returns false (and launches
+// nothing) for other shapes.
 static bool sk_kw_launch(KwJob J, hipStream_t s) {
     if (J.T < 5 || J.T > kKwMaxTokens || J.K % kKwSlice)
         return false;
@@ -374,12 +375,16 @@ static bool sk_kw_launch(KwJob J, hipStream_t s) {
     if (nt < 2 || nt > 4)
         return false;
     const int grid = (J.N + J.R - 1) / J.R;
-#define K3_KW(NW_, NT_)                                                                  \
-    k_sk_kw<NW_, NT_><<<grid, NW_ * kWave, kw_lds_bytes(NW_, NT_), s>>>(J)
+    const int ph = J.T <= 8 ? 1 : 2;
+#define K3_KW(NW_, NT_, PH_)                                                             \
+    k_sk_kw<NW_, NT_, PH_><<<grid, NW_ * kWave, kw_lds_bytes(NW_, NT_, PH_), s>>>(J)
+#define K3_KW_NT(NW_, PH_)                                                               \
+    (nt == 2 ? K3_KW(NW_, 2, PH_) : nt == 3 ? K3_KW(NW_, 3, PH_) : K3_KW(NW_, 4, PH_))
     if (nw == 7)
-        nt == 2 ? K3_KW(7, 2) : nt == 3 ? K3_KW(7, 3) : K3_KW(7, 4);
+        ph == 1 ? K3_KW_NT(7, 1) : K3_KW_NT(7, 2);
     else
-        nt == 2 ? K3_KW(8, 2) : nt == 3 ? K3_KW(8, 3) : K3_KW(8, 4);
+        ph == 1 ? K3_KW_NT(8, 1) : K3_KW_NT(8, 2);
+#undef K3_KW_NT
 #undef K3_KW
     record_dispatch(K3_OP_DENSE_PASS, K3_VARIANT_WHOLEK);
     return true;

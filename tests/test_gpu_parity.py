@@ -229,7 +229,7 @@ def test_router_topk_latent_tiny_repeated(k3):
 # ---------------------------------------------------------------- skinny projection
 def dense_pass_for(b, K):
     """The MFMA pass a single dense projection takes above four tokens."""
-    if 5 <= b <= 8 and K % 1024 == 0 and K // 1024 in (7, 8):
+    if 5 <= b <= 16 and K % 1024 == 0 and K // 1024 in (7, 8):
         return "wholek"
     return "resident" if b <= 32 else "splitk"
 
@@ -295,11 +295,11 @@ def test_row_engine_short_and_uneven_rows(k3, K, N, b):
         assert_rel_close(yn.cpu(), y_ref, "y_norm")
 
 
-@pytest.mark.parametrize("b", sorted(set(synth.CHAIN_BATCHES) | {5, 6, 7, 24, 40, 48, 56}))
+@pytest.mark.parametrize("b", sorted(set(synth.CHAIN_BATCHES) | {5, 6, 7, 9, 12, 15, 24, 40, 48, 56}))
 def test_proj_skinny_chain_in(k3, chain_w, chain_host, b):
     """The attention input projection 7168 -> 12288 at every chain batch the
-    benchmark times, the verify batches 8 r and 5-7 tokens (the whole-K pass
-    covers 5-8); every output."""
+    benchmark times, the verify batches 8 r and 5-7, 9, 12, 15 tokens (the
+    whole-K pass covers 5-16, in two staged halves above 8); every output."""
     inp = synth.make_chain_inputs(synth.CHAIN_CONFIG, b, device=DEV, index=300 + b)
     q = k3.k3_proj_skinny(inp["x"], chain_w["w_in"])
     torch.cuda.synchronize()
@@ -595,7 +595,7 @@ def test_moe_experts_invalid_ids_dropped(k3):
 
 
 # ---------------------------------------------------------------- o-proj + residual + norm
-@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 24, 32, 40, 48, 56, 64])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8, 9, 13, 16, 17, 24, 32, 40, 48, 56, 64])
 def test_oproj_residual_full(k3, chain_w, chain_host, b):
     w = chain_w
     cc = synth.CHAIN_CONFIG
