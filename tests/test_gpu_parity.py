@@ -187,11 +187,14 @@ def test_router_topk_many_experts(k3, b):
     assert_rel_close(wts.cpu().numpy(), ref_w, "topk_w")
 
 
-@pytest.mark.parametrize("b,zipf", [(1, 0.0), (2, 0.0), (4, 1.1), (16, 0.0), (40, 0.0),
-                                    (64, 1.1)])
+@pytest.mark.parametrize("b,zipf", [(1, 0.0), (2, 0.0), (4, 1.1), (8, 0.0), (16, 0.0),
+                                    (24, 0.0), (40, 0.0), (64, 1.1)])
 def test_router_topk_latent_full(k3, full, host, b, zipf):
     """The fused router + latent pass: ids and weights as k3_router_topk, z as
-    k3_proj_skinny, at full size (dot2 up to 4 tokens, MFMA above)."""
+    k3_proj_skinny, at full size (dot2 up to 4 tokens, MFMA above). Bit for
+    bit where the separate latent projection takes the fused pass's summation
+    order; at 5-16 tokens it takes the whole-K pass (1024-wide K slices
+    instead of K ranges), and the two z agree to rounding."""
     cfg, w = full
     bias = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
     x = synth.make_tokens(cfg, device=DEV, index=150 + b, b=b)
@@ -207,7 +210,13 @@ def test_router_topk_latent_full(k3, full, host, b, zipf):
     ids2, wts2 = k3.k3_router_topk(x, w["w_router"], bias, cfg.k)
     z2 = k3.k3_proj_skinny(x, w["w_lat"])
     torch.cuda.synchronize()
-    assert torch.equal(ids, ids2) and torch.equal(wts, wts2) and torch.equal(z, z2)
+    assert torch.equal(ids, ids2) and torch.equal(wts, wts2)
+    if b > 4 and k3.k3_get_last_dispatch("dense_pass") == "wholek":
+        # fp32 sums in two orders, each rounded to bf16: at most a couple of
+        # bf16 units apart (2^-8 relative each)
+        assert_rel_close(z2.cpu(), z.float().cpu(), "z, separate against fused", tol=8e-3)
+    else:
+        assert torch.equal(z, z2)
 
 
 def test_router_topk_latent_tiny_repeated(k3):
