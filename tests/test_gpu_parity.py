@@ -318,6 +318,37 @@ def test_proj_skinny_chain_in(k3, chain_w, chain_host, b):
         assert k3.k3_get_last_dispatch("dense_pass") == dense_pass_for(b, synth.CHAIN_CONFIG.d)
 
 
+@pytest.mark.parametrize("b,K,N", [(5, 7168, 12248), (11, 8192, 5000), (16, 7168, 16384),
+                                   (9, 8192, 4104), (13, 7168, 4100), (8, 8192, 7168)])
+def test_whole_k_pass_shapes(k3, b, K, N):
+    """The whole-K pass at the edges of its shapes: rows per workgroup from
+    17 to 64 (two to four 16-row tiles, the last short), N not a multiple of
+    16 (the last workgroup's rows partial), seven and eight K slices, one and
+    two staged halves, x and y as column slices of wider buffers; then the
+    o-projection form (residual add) on the same shape."""
+    xb = synth.randn_bf16((b, K + 32), 1.0, 11, "wk_x", K * 100 + N + b, device=DEV)
+    x = xb[:, 32:]
+    W = synth.randn_bf16((N, K), 1 / math.sqrt(K), 11, "wk_w", K * 100 + N, device=DEV)
+    yb = torch.zeros((b, N + 24), dtype=torch.bfloat16, device=DEV)
+    y = yb[:, :N]
+    k3.k3_proj_skinny(x, W, y=y)
+    torch.cuda.synchronize()
+    assert k3.k3_get_last_dispatch("dense_pass") == "wholek"
+    assert_rel_close(y.cpu(), oracle.linear(x.cpu(), W.cpu()), "y")
+    assert (yb[:, N:] == 0).all()
+    if N % 8 == 0 and N <= 8192:  # the o-projection's width limits
+        r = synth.randn_bf16((b, N), 1.0, 11, "wk_r", K * 100 + N + b, device=DEV)
+        g = (synth.randn_bf16((N,), 0.1, 11, "wk_g", N, device=DEV).float() + 1).to(
+            torch.bfloat16)
+        r0 = r.clone()
+        yn = k3.k3_oproj_residual(x, W, r, g, 1e-6)
+        torch.cuda.synchronize()
+        assert k3.k3_get_last_dispatch("dense_pass") == "wholek"
+        h_ref, y_ref = oracle.oproj_residual_rmsnorm(x.cpu(), W.cpu(), r0.cpu(), g.cpu(), 1e-6)
+        assert_rel_close(r.cpu(), h_ref, "h")
+        assert_rel_close(yn.cpu(), y_ref, "y_norm")
+
+
 @pytest.mark.parametrize("b", [3, 20])
 def test_proj_skinny_strided_output(k3, chain_w, chain_host, b):
     """x and y as column slices of wider buffers (row strides > width), on
