@@ -11,8 +11,10 @@
 // four 16-token tiles) and the weight rows as B. A job's epilogue either
 // writes fp32 partial sums per K range (summed in a fixed order by a small
 // reduce kernel), or, with one K range, finishes the outputs directly. The
-// token-resident pass at the end of the file stages a whole K range once
-// instead (dense projections at 5-32 tokens).
+// token-resident pass after it stages a whole K range once instead (dense
+// projections at 5-32 tokens), and the whole-K pass at the end of the file
+// gives each workgroup whole rows and no partial sums (single dense
+// projections at 5-16 tokens).
 #pragma once
 #include "k3_device.h"
 
@@ -715,7 +717,7 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
 
 }  // namespace k3
 
-// ------------------------------------------------------------------ whole-K pass (5-8 tokens)
+// ------------------------------------------------------------------ whole-K pass (5-16 tokens)
 namespace k3 {
 
 // Dense projections over at most kKwMaxTokens tokens with final outputs and

@@ -167,10 +167,11 @@ k_sk_finish_topk(const float *__restrict__ part, int ks, int T, int64_t ldp, SkO
 // ------------------------------------------------------------------ launchers
 int sk_mt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 
-// The dense passes at 5-32 tokens run token-resident (k_sk_res); at 33-64
-// tokens, whose range tokens would fill the LDS, the per-chunk staging
+// The split-K dense passes at 5-32 tokens run token-resident (k_sk_res); at
+// 33-64 tokens, whose range tokens would fill the LDS, the per-chunk staging
 // kernel (k_sk_gemm). Measured on the chain (in-process A/B): the resident
-// pass 2-5% faster at 8-32 tokens, 1% slower at 64.
+// pass 2-5% faster at 8-32 tokens, 1% slower at 64. (Single projections at
+// 5-16 tokens take the whole-K pass first: sk_kw_launch.)
 static bool sk_resident(int T) { return sk_mt(T) <= 2; }
 
 // K ranges of a K-wide dense pass over T tokens: a function of K and T alone,
