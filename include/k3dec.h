@@ -86,7 +86,7 @@ int k3_version(void);
  * available and fail with K3_ERR_UNSUPPORTED). */
 #define K3_OP_EXPERT_ENGINE 8
 /* Not an entry point: the MFMA pass of the last dense projection above four
- * tokens -- K3_VARIANT_WHOLEK (5-16 tokens, K a multiple of 1024 with seven
+ * tokens -- K3_VARIANT_WHOLEK (5-32 tokens, K a multiple of 1024 with seven
  * or eight 1024-wide slices: whole-K workgroups, no partial sums),
  * K3_VARIANT_RESIDENT (token-resident split-K pass, up to 32 tokens) or
  * K3_VARIANT_SPLITK (per-chunk split-K pass, 33-64 tokens). Recorded by

@@ -14,7 +14,7 @@
 // token-resident pass after it stages a whole K range once instead (dense
 // projections at 5-32 tokens), and the whole-K pass at the end of the file
 // gives each workgroup whole rows and no partial sums (single dense
-// projections at 5-16 tokens).
+// projections at 5-32 tokens).
 #pragma once
 #include "k3_device.h"
 
@@ -717,7 +717,7 @@ __global__ void __launch_bounds__(WPB * kWave) k_sk_res(SkDense J, int K, int ks
 
 }  // namespace k3
 
-// ------------------------------------------------------------------ whole-K pass (5-16 tokens)
+// ------------------------------------------------------------------ whole-K pass (5-32 tokens)
 namespace k3 {
 
 // Dense projections over at most kKwMaxTokens tokens with final outputs and
@@ -730,13 +730,15 @@ namespace k3 {
 // order through LDS and written as bf16 (mode 0) or added to the residual
 // (mode 1: h32 = bf16 residual + sum, residual = bf16(h32)). So an output's
 // summation order is a function of K alone, and no finishing kernel follows.
-// Up to 8 tokens a wave stages its whole slice at once (PH = 1); up to 16 it
-// stages it in two halves (PH = 2): the second half's tokens are loaded into
-// registers at the start and written over the first half once the first
-// half's chunks of every tile are multiplied. A region holds 8 PH + 1 token
-// rows (the extra row is zeros, which token rows of the MFMA tile past T
-// read).
-constexpr int kKwMaxTokens = 16;
+// The slice is staged in PH parts, one part at a time: the whole slice up
+// to 8 tokens (PH = 1), halves up to 16 (PH = 2), quarters up to 32 (PH = 4).
+// A part's tokens are loaded into registers ahead of it (every part at the
+// start for PH <= 2, the next one while the current one is multiplied for
+// PH = 4) and written over the previous part once its chunks of every tile
+// are multiplied. Each weight fragment meets TB 16-token blocks (TB = 2 above
+// 16 tokens). A region holds 8 PH + 1 token rows (34 for TB = 2); the rows
+// past T are zeros, which token rows of the MFMA tile past T read.
+constexpr int kKwMaxTokens = 32;
 constexpr int kKwSlice = 1024;  // K per wave
 
 struct KwJob {
@@ -752,53 +754,55 @@ struct KwJob {
     float *h32;  // mode 1: [T][ldy]
 };
 
-// LDS bytes of k_sk_kw<NW, NT, PH>: the token slices, later reused for the sums
-constexpr size_t kw_lds_bytes(int nw, int nt, int ph) {
-    const size_t tok = (size_t)nw * (8 * ph + 1) * (kKwSlice / ph / 8 + 1) * 16;
-    const size_t red = (size_t)nw * nt * 4 * kWave * 4;
+constexpr int kw_rows(int ph, int tb) { return tb == 1 ? 8 * ph + 1 : 16 * tb + 2; }
+
+// LDS bytes of k_sk_kw<NW, NT, PH, TB>: the token slices, later reused for the sums
+constexpr size_t kw_lds_bytes(int nw, int nt, int ph, int tb) {
+    const size_t tok = (size_t)nw * kw_rows(ph, tb) * (kKwSlice / ph / 8 + 1) * 16;
+    const size_t red = (size_t)nw * nt * tb * 4 * kWave * 4;
     return tok > red ? tok : red;
 }
 
-template <int NW, int NT, int PH>
+template <int NW, int NT, int PH, int TB>
 __global__ void __launch_bounds__(NW * kWave) k_sk_kw(KwJob J) {
     extern __shared__ u32x4 kw_lds[];
     constexpr int SL = kKwSlice / PH;  // K of the slice staged at once
     constexpr int KQ = SL / 8;         // 16-byte vectors per token row of it
     constexpr int RS = KQ + 1;         // row stride (+1 keeps the MFMA reads conflict-free)
-    constexpr int ROWS = 8 * PH + 1;
+    constexpr int ROWS = kw_rows(PH, TB);
     constexpr int NCH = SL / kSkKc;  // 256-wide chunks per staged part
     constexpr int NUP = NT * NCH;    // units (tile, chunk) per part
     constexpr int NU = PH * NUP;
     constexpr int SV = ROWS * KQ / kWave;  // staged vectors per lane per part
+    constexpr int NS = PH <= 2 ? PH : 1;   // parts held in registers at once
     static_assert(ROWS * KQ % kWave == 0, "whole vectors per lane");
-    static_assert(NUP % 2 == 0, "units run in pairs within a part");
+    static_assert(NU % 2 == 0, "units run in pairs");
+    static_assert((TB == 1 ? 8 * PH : 16 * TB) < ROWS, "a zero row past the most tokens");
     const int lane = threadIdx.x & (kWave - 1), wq = wave_in_block();
     const int T = J.T, K = J.K;
     const int k0 = wq * kKwSlice;
     const int r0 = blockIdx.x * J.R;
     const int r1 = min(J.N, r0 + J.R);
     u32x4 *xw = kw_lds + wq * ROWS * RS;
-    // every part's token vectors: row t < T from x, the others zeros
-    u32x4 sv[PH][SV];
-    {
-        const rsrc_t rx = act_range(uniform_ptr(J.x));
+    // part h's token vectors (row t < T from x, the others zeros) into set h % NS
+    u32x4 sv[NS][SV];
+    const rsrc_t rx = act_range(uniform_ptr(J.x));
+    auto fetch = [&](int h) {
 #pragma unroll
-        for (int h = 0; h < PH; ++h)
-#pragma unroll
-            for (int j = 0; j < SV; ++j) {
-                const int q = lane + j * kWave;
-                const int t = q / KQ, v = q - t * KQ;
-                const int k = k0 + h * SL + 8 * v;
-                sv[h][j] = ld_act16(
-                    rx, t < T ? ((uint32_t)t * (uint32_t)J.ldx + (uint32_t)k) * 2u : kOffNone);
-            }
-    }
+        for (int j = 0; j < SV; ++j) {
+            const int q = lane + j * kWave;
+            const int t = q / KQ, v = q - t * KQ;
+            const int k = k0 + h * SL + 8 * v;
+            sv[h % NS][j] = ld_act16(
+                rx, t < T ? ((uint32_t)t * (uint32_t)J.ldx + (uint32_t)k) * 2u : kOffNone);
+        }
+    };
     auto stage = [&](int h) {
 #pragma unroll
         for (int j = 0; j < SV; ++j) {
             const int q = lane + j * kWave;
             const int t = q / KQ;
-            xw[t * RS + (q - t * KQ)] = sv[h][j];
+            xw[t * RS + (q - t * KQ)] = sv[h % NS][j];
         }
     };
     // unit u: part u / NUP; within it tile (u % NUP) / NCH, chunk u % NCH
@@ -812,62 +816,82 @@ __global__ void __launch_bounds__(NW * kWave) k_sk_kw(KwJob J) {
                          (uint32_t)__builtin_amdgcn_readfirstlane(nvalid) * (uint32_t)K * 2u);
         sk_wload_t<1, false>(buf, rw, (k0 + h * SL) / kSkKc + c, K, lane);
     };
-    f32x4 acc[NT];
+    f32x4 acc[NT][TB];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+            acc[t][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int g = lane >> 4, rl = lane & 15;
-    const u32x4 *xa = xw + (rl < T ? rl : T) * RS;  // this lane's token row
+    const u32x4 *xa[TB];  // this lane's token row in each 16-token block
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+        xa[tb] = xw + (16 * tb + rl < T ? 16 * tb + rl : T) * RS;
     auto compute = [&](const u32x4 (&buf)[kSkKb], int u) {
         const int t = (u % NUP) / NCH, c = u % NCH;
 #pragma unroll
         for (int p = 0; p < kSkKb / 2; ++p) {
             u32x4 b0, b1;
             sk_pair<false>(buf[2 * p], buf[2 * p + 1], b0, b1);
-            const u32x4 *xc = xa + c * (kSkKc / 8);
-            acc[t] = mfma16x16x32(xc[sk_a_vec<false>(p, g, 0)], b0, acc[t]);
-            acc[t] = mfma16x16x32(xc[sk_a_vec<false>(p, g, 1)], b1, acc[t]);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const u32x4 *xc = xa[tb] + c * (kSkKc / 8);
+                acc[t][tb] = mfma16x16x32(xc[sk_a_vec<false>(p, g, 0)], b0, acc[t][tb]);
+                acc[t][tb] = mfma16x16x32(xc[sk_a_vec<false>(p, g, 1)], b1, acc[t][tb]);
+            }
         }
     };
+    // at a part boundary the previous part's multiplies are done: its region
+    // takes the next part's tokens (other lanes of the wave read them, so a
+    // barrier orders the writes before the reads), and with one register set
+    // the part after that is fetched
+    auto next_part = [&](int h) {
+        stage(h);
+        __syncthreads();
+        if (NS == 1 && h + 1 < PH)
+            fetch(h + 1);
+    };
     u32x4 A[kSkKb], B[kSkKb];
+#pragma unroll
+    for (int h = 0; h < NS; ++h)
+        fetch(h);
     load(A, 0);
     load(B, 1);
-    stage(0);
-    // other lanes of the wave read these vectors: a barrier orders the
-    // writes before them (once per part)
-    __syncthreads();
+    next_part(0);
     // units in pairs; every load is issued on every path
 #pragma unroll
     for (int u = 0; u < NU; u += 2) {
-        if (u > 0 && u % NUP == 0) {
-            // the previous part's multiplies are done: its region takes the
-            // next part's tokens
-            stage(u / NUP);
-            __syncthreads();
-        }
+        if (u > 0 && u % NUP == 0)
+            next_part(u / NUP);
         sk_keep_order();
         compute(A, u);
         load(A, u + 2);
+        if ((u + 1) % NUP == 0)  // only with NUP odd (three tiles in quarters)
+            next_part((u + 1) / NUP);
         sk_keep_order();
         compute(B, u + 1);
         load(B, u + 3);
     }
     __syncthreads();  // every wave is done with its token slice: reuse the LDS
-    float *red = reinterpret_cast<float *>(kw_lds);  // [NW][NT][4][64]
+    constexpr int NB = NT * TB;                      // 16x16 output blocks per wave
+    float *red = reinterpret_cast<float *>(kw_lds);  // [NW][NB][4][64]
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            red[((wq * NT + t) * 4 + i) * kWave + lane] = acc[t][i];
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red[((wq * NB + t * TB + tb) * 4 + i) * kWave + lane] = acc[t][tb][i];
     __syncthreads();
-    // acc[t][i] of lane l = out[token 4 (l / 16) + i][row r0 + 16 t + l % 16]
-    for (int e = threadIdx.x; e < NT * 4 * kWave; e += NW * kWave) {
-        const int t = e / (4 * kWave), i = (e / kWave) & 3, ln = e & (kWave - 1);
+    // acc[t][tb][i] of lane l = out[token 16 tb + 4 (l / 16) + i][row r0 + 16 t + l % 16]
+    for (int e = threadIdx.x; e < NB * 4 * kWave; e += NW * kWave) {
+        const int q = e / (4 * kWave), i = (e / kWave) & 3, ln = e & (kWave - 1);
+        const int t = q / TB, tb = q - t * TB;
         float v = red[e];
 #pragma unroll
         for (int w = 1; w < NW; ++w)
-            v += red[w * NT * 4 * kWave + e];
-        const int tok = 4 * (ln >> 4) + i, n = r0 + 16 * t + (ln & 15);
+            v += red[w * NB * 4 * kWave + e];
+        const int tok = 16 * tb + 4 * (ln >> 4) + i, n = r0 + 16 * t + (ln & 15);
         if (tok < T && n < r1) {
             const int64_t o = (int64_t)tok * J.ldy + n;
             if (J.mode == 0) {

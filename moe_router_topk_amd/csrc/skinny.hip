@@ -171,7 +171,7 @@ int sk_mt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 // 33-64 tokens, whose range tokens would fill the LDS, the per-chunk staging
 // kernel (k_sk_gemm). Measured on the chain (in-process A/B): the resident
 // pass 2-5% faster at 8-32 tokens, 1% slower at 64. (Single projections at
-// 5-16 tokens take the whole-K pass first: sk_kw_launch.)
+// 5-32 tokens take the whole-K pass first: sk_kw_launch.)
 static bool sk_resident(int T) { return sk_mt(T) <= 2; }
 
 // K ranges of a K-wide dense pass over T tokens: a function of K and T alone,
@@ -360,10 +360,10 @@ SkOuts sk_outs1(int mode, int cols, void *y, int64_t ldy, const float *bias) {
 }
 
 // The whole-K pass (k_sk_kw) for 5..kKwMaxTokens tokens: K a multiple of
-// kKwSlice with seven or eight slices (one wave each), at most four 16-row
+// kKwSlice with seven or eight slices (one wave each), two to four 16-row
 // tiles per workgroup on one workgroup per compute unit; token slices staged
-// whole up to 8 tokens, in two halves up to 16. Returns false (and launches
-// nothing) for other shapes.
+// whole up to 8 tokens, in halves up to 16, in quarters (two token blocks)
+// up to 32. Returns false (and launches nothing) for other shapes.
 static bool sk_kw_launch(KwJob J, hipStream_t s) {
     if (J.T < 5 || J.T > kKwMaxTokens || J.K % kKwSlice)
         return false;
@@ -376,15 +376,20 @@ static bool sk_kw_launch(KwJob J, hipStream_t s) {
     if (nt < 2 || nt > 4)
         return false;
     const int grid = (J.N + J.R - 1) / J.R;
-    const int ph = J.T <= 8 ? 1 : 2;
-#define K3_KW(NW_, NT_, PH_)                                                             \
-    k_sk_kw<NW_, NT_, PH_><<<grid, NW_ * kWave, kw_lds_bytes(NW_, NT_, PH_), s>>>(J)
-#define K3_KW_NT(NW_, PH_)                                                               \
-    (nt == 2 ? K3_KW(NW_, 2, PH_) : nt == 3 ? K3_KW(NW_, 3, PH_) : K3_KW(NW_, 4, PH_))
+    const int ph = J.T <= 8 ? 1 : J.T <= 16 ? 2 : 4;
+#define K3_KW(NW_, NT_, PH_, TB_)                                                        \
+    k_sk_kw<NW_, NT_, PH_, TB_>                                                          \
+        <<<grid, NW_ * kWave, kw_lds_bytes(NW_, NT_, PH_, TB_), s>>>(J)
+#define K3_KW_NT(NW_, PH_, TB_)                                                          \
+    (nt == 2 ? K3_KW(NW_, 2, PH_, TB_)                                                   \
+             : nt == 3 ? K3_KW(NW_, 3, PH_, TB_) : K3_KW(NW_, 4, PH_, TB_))
+#define K3_KW_PH(NW_)                                                                    \
+    (ph == 1 ? K3_KW_NT(NW_, 1, 1) : ph == 2 ? K3_KW_NT(NW_, 2, 1) : K3_KW_NT(NW_, 4, 2))
     if (nw == 7)
-        ph == 1 ? K3_KW_NT(7, 1) : K3_KW_NT(7, 2);
+        K3_KW_PH(7);
     else
-        ph == 1 ? K3_KW_NT(8, 1) : K3_KW_NT(8, 2);
+        K3_KW_PH(8);
+#undef K3_KW_PH
 #undef K3_KW_NT
 #undef K3_KW
     record_dispatch(K3_OP_DENSE_PASS, K3_VARIANT_WHOLEK);

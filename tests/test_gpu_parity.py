@@ -193,7 +193,7 @@ def test_router_topk_latent_full(k3, full, host, b, zipf):
     """The fused router + latent pass: ids and weights as k3_router_topk, z as
     k3_proj_skinny, at full size (dot2 up to 4 tokens, MFMA above). Bit for
     bit where the separate latent projection takes the fused pass's summation
-    order; at 5-16 tokens it takes the whole-K pass (1024-wide K slices
+    order; at 5-32 tokens it takes the whole-K pass (1024-wide K slices
     instead of K ranges), and the two z agree to rounding."""
     cfg, w = full
     bias = synth.zipf_router_bias(cfg.E, zipf, cfg.seed).to(DEV) if zipf else None
@@ -238,7 +238,7 @@ def test_router_topk_latent_tiny_repeated(k3):
 # ---------------------------------------------------------------- skinny projection
 def dense_pass_for(b, K):
     """The MFMA pass a single dense projection takes above four tokens."""
-    if 5 <= b <= 16 and K % 1024 == 0 and K // 1024 in (7, 8):
+    if 5 <= b <= 32 and K % 1024 == 0 and K // 1024 in (7, 8):
         return "wholek"
     return "resident" if b <= 32 else "splitk"
 
@@ -304,11 +304,14 @@ def test_row_engine_short_and_uneven_rows(k3, K, N, b):
         assert_rel_close(yn.cpu(), y_ref, "y_norm")
 
 
-@pytest.mark.parametrize("b", sorted(set(synth.CHAIN_BATCHES) | {5, 6, 7, 9, 12, 15, 24, 40, 48, 56}))
+@pytest.mark.parametrize("b", sorted(set(synth.CHAIN_BATCHES)
+                                    | {5, 6, 7, 9, 12, 15, 17, 20, 24, 31, 33, 40, 48, 56}))
 def test_proj_skinny_chain_in(k3, chain_w, chain_host, b):
     """The attention input projection 7168 -> 12288 at every chain batch the
-    benchmark times, the verify batches 8 r and 5-7, 9, 12, 15 tokens (the
-    whole-K pass covers 5-16, in two staged halves above 8); every output."""
+    benchmark times, the verify batches 8 r and 5-7, 9, 12, 15, 17, 20, 31 and
+    33 tokens (the whole-K pass covers 5-32: the slice staged whole up to 8
+    tokens, in halves up to 16, in quarters with two token blocks up to 32);
+    every output."""
     inp = synth.make_chain_inputs(synth.CHAIN_CONFIG, b, device=DEV, index=300 + b)
     q = k3.k3_proj_skinny(inp["x"], chain_w["w_in"])
     torch.cuda.synchronize()
@@ -319,13 +322,16 @@ def test_proj_skinny_chain_in(k3, chain_w, chain_host, b):
 
 
 @pytest.mark.parametrize("b,K,N", [(5, 7168, 12248), (11, 8192, 5000), (16, 7168, 16384),
-                                   (9, 8192, 4104), (13, 7168, 4100), (8, 8192, 7168)])
+                                   (9, 8192, 4104), (13, 7168, 4100), (8, 8192, 7168),
+                                   (17, 8192, 7168), (23, 7168, 12248), (29, 8192, 5000),
+                                   (32, 7168, 16384), (19, 7168, 4100), (32, 8192, 4104)])
 def test_whole_k_pass_shapes(k3, b, K, N):
     """The whole-K pass at the edges of its shapes: rows per workgroup from
     17 to 64 (two to four 16-row tiles, the last short), N not a multiple of
-    16 (the last workgroup's rows partial), seven and eight K slices, one and
-    two staged halves, x and y as column slices of wider buffers; then the
-    o-projection form (residual add) on the same shape."""
+    16 (the last workgroup's rows partial), seven and eight K slices, the
+    slice staged whole, in halves and in quarters (17-32 tokens: two token
+    blocks, the second partial below 32), x and y as column slices of wider
+    buffers; then the o-projection form (residual add) on the same shape."""
     xb = synth.randn_bf16((b, K + 32), 1.0, 11, "wk_x", K * 100 + N + b, device=DEV)
     x = xb[:, 32:]
     W = synth.randn_bf16((N, K), 1 / math.sqrt(K), 11, "wk_w", K * 100 + N, device=DEV)
