@@ -754,6 +754,9 @@ struct KwJob {
     float *h32;  // mode 1: [T][ldy]
 };
 
+// Token rows of a wave's LDS region: the form's most tokens (8 PH, or 16 TB
+// with two token blocks) plus zero rows: one, or two where that keeps each
+// lane's share of a staged part a whole number of vectors.
 constexpr int kw_rows(int ph, int tb) { return tb == 1 ? 8 * ph + 1 : 16 * tb + 2; }
 
 // LDS bytes of k_sk_kw<NW, NT, PH, TB>: the token slices, later reused for the sums
