@@ -85,18 +85,21 @@ def chain_bytes(cc, b: int) -> int:
 def gateup_bytes(cfg, b: int, n_active: int) -> int:
     """Per launch of the kernel traced as the routed experts' gate/up pass:
     n_active experts' [2I x d_lat] weights, the z rows it reads and the h rows
-    it writes. At batch 1 that kernel (k_moe_up_b1) also selects the experts:
-    + the logits it reads, the ids and weights it writes."""
+    it writes. At batch 1 that kernel (k_moe_up_b1) also selects the experts
+    and, ahead of the routed rows, streams the shared expert's gate/up rows:
+    + the logits it reads, the ids and weights it writes, the shared
+    [2 I_s x d] weights, the x row it reads and the h_s row it writes."""
     dl, I, E, k = cfg.d_lat, cfg.I, cfg.E, cfg.k
     n = 2 * n_active * 2 * I * dl + 2 * b * dl + 2 * b * k * I
     if b == 1:
         n += 4 * E + 8 * k
+        n += 2 * 2 * cfg.I_s * cfg.d + 2 * cfg.d + 2 * cfg.I_s
     return n
 
 
 def gateup_kernel_name(b: int) -> str:
     if b == 1:
-        return "k_moe_up_b1<true> (expert selection + routed gate/up + SwiGLU)"
+        return "k_moe_up_b1<true> (shared gate/up, expert selection, routed gate/up + SwiGLU)"
     if b <= 4:
         return "routed gate/up + SwiGLU (dot2 rows for light experts, MFMA tiles for heavy)"
     return "routed gate/up + SwiGLU, every expert on MFMA tiles (k_sk_gemm_stream)"
@@ -300,7 +303,7 @@ def write_traffic_summary(pmc_dir: str) -> int:
     traffic = int(round(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale))
     algo = gateup_bytes(synth.MOE_CONFIGS["b1"], 1, synth.MOE_CONFIGS["b1"].k)
     out = {
-        "kernel": "k3::k_moe_up_b1<true> (expert selection + routed gate/up + SwiGLU), "
+        "kernel": "k3::k_moe_up_b1<true> (shared gate/up, expert selection, routed gate/up + SwiGLU), "
                   "batch 1, d=7168, E=384, k=8, I=2048",
         "commands": [
             f"rocprofv3 --pmc {ctr} --output-format csv -d {pmc_dir}/pmc_{key} -o c -- "

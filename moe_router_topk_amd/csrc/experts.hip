@@ -1266,7 +1266,12 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
     uint16_t *hs = (uint16_t *)(ws + L.hs);
     const bool fast = variant == K3_VARIANT_DOT2 && b == 1 && I_s == I &&
                       up_b1_fits(d_lat, k, I, 0) && down_b1_fits(k, I, d, true, 0);
-    const bool norm_in_pass = nin && fast && rls_gemv_fits(1, d, E, d_lat, I_s);
+    // the shared gate/up rows ride at the head of the routed gate/up kernel
+    // (they stream while its selection waits for the logits) where x and z
+    // are equally wide; else in the router pass
+    const bool sh_up = fast && d_lat == d && up_b1_fits(d_lat, k, I, 0, true);
+    const bool norm_in_pass =
+        nin && fast && rls_gemv_fits(1, d, E, d_lat, sh_up ? 0 : I_s);
     if (nin && !norm_in_pass) {
         // the norm as its own kernel, into x_out or the workspace
         uint16_t *xb = nin->x_out ? nin->x_out : (uint16_t *)(ws + L.total);
@@ -1275,16 +1280,27 @@ static int moe_block_run(const uint16_t *x, int64_t ldx, const NormIn *nin, int 
     }
     trace_begin(K3_OP_MOE_BLOCK, s);
     if (fast) {
-        // 1. router, latent and shared gate/up rows in one pass over x (with
-        //    the norm of its input folded in when it comes as h32);
-        // 2. expert selection and routed gate/up;
+        // 1. router and latent rows (and the shared gate/up rows unless step
+        //    2 takes them) in one pass over x, with the norm of its input
+        //    folded in when it comes as h32 (the pass then publishes x);
+        // 2. [shared gate/up,] expert selection and routed gate/up;
         // 3. routed and shared down rows with the combine
-        launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz, w13_s, I_s, hs,
-                   s, 0, norm_in_pass ? nin : nullptr);
+        NormIn nin2{};
+        const uint16_t *xs = x;
+        if (norm_in_pass) {
+            nin2 = *nin;
+            if (sh_up && !nin2.x_out)
+                nin2.x_out = (uint16_t *)(ws + L.total);
+            xs = nin2.x_out;
+        }
+        launch_rls(x, ldx, b, d, w_router, bias, E, logits, w_lat, d_lat, z, ldz,
+                   sh_up ? nullptr : w13_s, sh_up ? 0 : I_s, sh_up ? nullptr : hs, s, 0,
+                   norm_in_pass ? &nin2 : nullptr);
         trace_end(K3_OP_MOE_BLOCK, s);
         uint16_t *hbuf = (uint16_t *)(ws + L.moe + moe_workspace_layout(b, E, k, I, d).hbuf);
         trace_begin(K3_OP_MOE_EXPERTS, s);
-        launch_up_b1(true, z, d_lat, w13, I, E, k, nullptr, logits, topk_ids, topk_w, hbuf, 0, s);
+        launch_up_b1(true, z, d_lat, w13, I, E, k, nullptr, logits, topk_ids, topk_w, hbuf, 0, s,
+                     sh_up ? xs : nullptr, sh_up ? w13_s : nullptr, sh_up ? hs : nullptr);
         trace_end(K3_OP_MOE_EXPERTS, s);
         launch_down_b1(hbuf, I, w2, d, topk_ids, topk_w, k, E, nullptr, hs, w2_s, y_s, y, 0, s);
         const int st = launch_status();

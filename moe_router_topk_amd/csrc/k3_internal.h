@@ -102,13 +102,16 @@ void sk_oproj_residual(const uint16_t *a, int64_t lda, int T, int K, const uint1
 // Batch-1 routed experts (moe_b1.hip). up_b1: routed gate/up + SwiGLU into
 // hbuf, k x I values in the pair's own layout ([I / 4][k][4], read only by
 // down_b1: launch both or neither); with `topk` the selection from logits
-// happens in the kernel (ids/weights written out). down_b1: y = bf16(base +
+// happens in the kernel (ids/weights written out); with w13s (`shared` in
+// up_b1_fits) the shared expert's gate/up rows on xs (d wide) stream first,
+// into hs. down_b1: y = bf16(base +
 // sum_j w_j w2[ids[j]] . h_j) with base = y_add, or, with w2s, the shared
 // expert's down projection of hs (also written to y_s).
-bool up_b1_fits(int d, int k, int I, int cu_budget);
+bool up_b1_fits(int d, int k, int I, int cu_budget, bool shared = false);
 void launch_up_b1(bool topk, const uint16_t *z, int d, const uint16_t *w13, int I, int E, int k,
                   const int32_t *ids_in, const float *logits, int32_t *ids_out, float *w_out,
-                  uint16_t *hbuf, int cu_budget, hipStream_t s);
+                  uint16_t *hbuf, int cu_budget, hipStream_t s, const uint16_t *xs = nullptr,
+                  const uint16_t *w13s = nullptr, uint16_t *hs = nullptr);
 bool down_b1_fits(int k, int I, int d_out, bool shared, int cu_budget);
 void launch_down_b1(const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
                     const int32_t *ids, const float *wts, int k, int E, const float *y_add,

@@ -4,10 +4,11 @@
 // "Hyper Optimizing Kimi K3 in vLLM", Part 1 section 3 ("Improve MoE
 // scheduling and overlap"): the routed experts follow the router and the
 // latent projection; the shared expert's work fills the gap the routing
-// leaves. Here the shared expert's rows ride in the passes around the
-// routed ones (gate/up with the router and latent rows, down as one more
-// slot of the routed down kernel), and the expert selection itself runs
-// while the routed weights stream: each pick is made just before its
+// leaves. Here the shared expert's rows ride in the passes of the routed
+// ones (its gate/up rows at the head of the routed gate/up kernel, streaming
+// while the selection waits for the router's logits; its down rows as one
+// more slot of the routed down kernel), and the expert selection itself
+// runs while the routed weights stream: each pick is made just before its
 // expert's rows are needed.
 #include <math.h>
 
@@ -39,20 +40,26 @@ __device__ __forceinline__ int64_t hb1_index(int a, int j, int k) {
 // expert: the first weight loads wait for one pick only, and the later picks
 // run while earlier loads are in flight (workgroup 0 publishes ids and
 // weights). Without TOPK the ids come from ids_in and slots outside [0, E)
-// are skipped.
+// are skipped. With w13s the shared expert's gate/up rows (input xs, the
+// block's x, d wide like z) come first as one more slot: its rows stream
+// while the selection waits for the logits, and hs[j] = bf16(silu(gate) *
+// up) in the router pass's order and rounding.
 template <bool TOPK, int U>
 __global__ void __launch_bounds__(kBlock)
 k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ w13, int I,
             int E, int k, const int32_t *__restrict__ ids_in, const float *__restrict__ logits,
             int32_t *__restrict__ ids_out, float *__restrict__ w_out,
-            uint16_t *__restrict__ hbuf, int ps_stride) {
-    extern __shared__ u32x4 zs[];  // z (d / 8 vectors), then ps[4][ps_stride]
+            uint16_t *__restrict__ hbuf, int ps_stride, const uint16_t *__restrict__ xs,
+            const uint16_t *__restrict__ w13s, uint16_t *__restrict__ hs) {
+    extern __shared__ u32x4 zs[];  // z (d / 8 vectors), x with w13s, then ps[4][ps_stride]
     const int nv = d >> 3;
-    float *ps = reinterpret_cast<float *>(zs + nv);
+    const int sh = w13s ? 1 : 0;  // the shared slot comes first
+    float *ps = reinterpret_cast<float *>(zs + (1 + sh) * nv);
     const int gpe = I >> 2;  // column blocks (groups) per slot
     int c0, c1;
     split_range(gpe, gridDim.x, blockIdx.x, c0, c1);
     const int cps = c1 - c0;  // this workgroup's groups per slot
+    const int gsh = sh * cps;  // the shared slot's groups
     // the expert of the slot the stream is on (slots come in order)
     TopkPicker pk;
     float lv[kTopkPer];
@@ -69,17 +76,22 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
         }
         return cur_e;
     };
-    GvStage<4> zst;  // d <= 8192
+    GvStage<4> zst, xst;  // d <= 8192
     gemv8_stream<U>(
-        k * cps, d,
+        gsh + k * cps, d,
         [&](int g, const uint16_t *&base, int &nr, int &skip) {
-            const int a = g / cps, c = c0 + (g - a * cps);
+            skip = I - 4;
+            if (g < gsh) {
+                base = w13s + (int64_t)(4 * (c0 + g)) * d;
+                nr = 8;
+                return;
+            }
+            const int gr = g - gsh, a = gr / cps, c = c0 + (gr - a * cps);
             const int e = slot_expert(a);
             base = w13 + ((int64_t)(e < 0 ? 0 : e) * 2 * I + 4 * c) * d;
             nr = e >= 0 ? 8 : 0;
-            skip = I - 4;
         },
-        [&](int, int kv, int) { return zs[kv]; }, ps, ps_stride,
+        [&](int g, int kv, int) { return zs[(g < gsh ? nv : 0) + kv]; }, ps, ps_stride,
         [&]() {
             // the logits first: the first pick waits for them, not for z
             if (TOPK) {
@@ -87,15 +99,30 @@ k_moe_up_b1(const uint16_t *__restrict__ z, int d, const uint16_t *__restrict__ 
                 pk.init(E);
             }
             zst.load(z, nv);
-            if (TOPK)
+            if (sh) {
+                xst.load(xs, nv);
+            } else if (TOPK) {
                 topk_keys(lv, E, pk.key);
+            }
         },
         [&]() {
+            // with the shared slot first the first weight loads are out
+            // before the selection waits for the logits
+            if (TOPK && sh)
+                topk_keys(lv, E, pk.key);
             zst.store(zs, nv);
+            if (sh)
+                xst.store(zs + nv, nv);
             __syncthreads();
         });
-    for (int i = threadIdx.x; i < 8 * k * cps; i += kBlock) {
-        const int r = i & 7, g = i >> 3, a = g / cps, j = 4 * (c0 + g - a * cps) + r;
+    for (int i = threadIdx.x; i < 8 * gsh; i += kBlock) {
+        const int r = i & 7, j = 4 * (c0 + (i >> 3)) + r;
+        if (r < 4)
+            hs[j] = f32_to_bf16(silu(gv_total(ps, ps_stride, i)) * gv_total(ps, ps_stride, i + 4));
+    }
+    for (int q = threadIdx.x; q < 8 * k * cps; q += kBlock) {
+        const int i = 8 * gsh + q;
+        const int r = q & 7, g = q >> 3, a = g / cps, j = 4 * (c0 + g - a * cps) + r;
         bool ok = true;
         if (!TOPK) {
             const int e = ids_in[a];
@@ -265,31 +292,33 @@ void launch_down_b1(const uint16_t *hbuf, int I, const uint16_t *w2, int d_out,
                                               y_s, y, ps_stride);
 }
 
-// LDS of the gate/up kernel: z, then the partial sums of the share (k
-// slots x the workgroup's column blocks).
-static size_t up_b1_lds(int d, int k, int I, int grid, int &ps_stride) {
-    ps_stride = 8 * k * ((I / 4 + grid - 1) / grid);
-    return (size_t)d * sizeof(uint16_t) + (size_t)4 * ps_stride * sizeof(float);
+// LDS of the gate/up kernel: z (and x with the shared slot), then the
+// partial sums of the share (the slots x the workgroup's column blocks).
+static size_t up_b1_lds(int d, int k, int I, int grid, int &ps_stride, bool shared) {
+    const int ns = k + (shared ? 1 : 0);
+    ps_stride = 8 * ns * ((I / 4 + grid - 1) / grid);
+    return (size_t)(shared ? 2 : 1) * d * sizeof(uint16_t) + (size_t)4 * ps_stride * sizeof(float);
 }
 
 // One workgroup per column block of I / 4 at most, two per compute unit.
 static int up_b1_grid(int I, int cu_budget) { return budget_grid(I / 4, cu_budget, 2); }
 
-bool up_b1_fits(int d, int k, int I, int cu_budget) {
+bool up_b1_fits(int d, int k, int I, int cu_budget, bool shared) {
     int ps_stride;
     return d % 64 == 0 && d <= 8192 && I % 4 == 0 && I >= 4 &&
-           up_b1_lds(d, k, I, up_b1_grid(I, cu_budget), ps_stride) <= 65536;
+           up_b1_lds(d, k, I, up_b1_grid(I, cu_budget), ps_stride, shared) <= 65536;
 }
 
 void launch_up_b1(bool topk, const uint16_t *z, int d, const uint16_t *w13, int I, int E, int k,
                   const int32_t *ids_in, const float *logits, int32_t *ids_out, float *w_out,
-                  uint16_t *hbuf, int cu_budget, hipStream_t s) {
+                  uint16_t *hbuf, int cu_budget, hipStream_t s, const uint16_t *xs,
+                  const uint16_t *w13s, uint16_t *hs) {
     const int grid = up_b1_grid(I, cu_budget);
     int ps_stride;
-    const size_t lds = up_b1_lds(d, k, I, grid, ps_stride);
+    const size_t lds = up_b1_lds(d, k, I, grid, ps_stride, w13s != nullptr);
 #define K3_UP(T_, U_)                                                                          \
     k_moe_up_b1<T_, U_><<<grid, kBlock, lds, s>>>(z, d, w13, I, E, k, ids_in, logits, ids_out, \
-                                                 w_out, hbuf, ps_stride)
+                                                 w_out, hbuf, ps_stride, xs, w13s, hs)
     if (topk && gv_unit_pieces(d) == 7)
         K3_UP(true, 7);
     else if (topk)

@@ -49,10 +49,11 @@ def test_chain_bytes_weights():
         assert acts == b * (2 * D + 2 * 12288 + 2 * 8192 + 4 * D + 8 * D + 2 * D)
 
 
-def test_gateup_bytes_batch1_includes_selection():
+def test_gateup_bytes_batch1_includes_selection_and_shared_rows():
     cfg = synth.MOE_CONFIGS["b1"]
     w = 2 * K * 2 * I * D
-    assert bench.gateup_bytes(cfg, 1, K) == w + 2 * D + 2 * K * I + 4 * E + 8 * K
+    shared = 2 * 2 * cfg.I_s * D + 2 * D + 2 * cfg.I_s
+    assert bench.gateup_bytes(cfg, 1, K) == w + 2 * D + 2 * K * I + 4 * E + 8 * K + shared
     assert bench.gateup_bytes(cfg, 16, 100) == 2 * 100 * 2 * I * D + 2 * 16 * D + 2 * 16 * K * I
 
 
