@@ -509,6 +509,7 @@ k_down_dot2(const uint16_t *__restrict__ hbuf, int I, const uint16_t *__restrict
 // job after the list: the shared expert's down projection into y_s.
 struct SkExperts {
     int tpw = 1;  // 16-row tiles per wave of the launch (a wave streams 16 tpw rows)
+    int sa = 0, sp = 0;  // slot shares of the stream kernel (0: none)
     ExpertList L;
     ExpertList L2;  // a second list after L (its n may be null: none)
     const uint16_t *w;  // expert e: w + e * w_stride, [rows][K] (gate/up: [2I][K])
@@ -549,6 +550,8 @@ struct SkExperts {
     // 8 tokens, 1525.5 against 1534.5 us at 16, 2595 against 2601 us at 32,
     // equal (859.3 us) at 64 with the Zipf bias.
     __device__ bool xcd_grouped() const { return !pair; }
+    __device__ int share_p() const { return sp; }
+    __device__ int share_a() const { return sa; }
     __device__ int tiles() const {
         return pair ? I / (32 * tpw) : (rows + 64 * tpw - 1) / (64 * tpw);
     }
@@ -953,6 +956,16 @@ void launch_sk_experts(SkExperts J, int b, int max_jobs, int cu_budget, hipStrea
     const int items = max_jobs * tiles;
     // two workgroups per compute unit, each streaming its items back to back
     const int grid = budget_grid(items < 1 ? 1 : items, cu_budget, 2);
+    // At 33-64 tokens the first workgroup of each compute unit takes 4 of
+    // every 7 rounds (slot shares): measured on the MoE block in one process,
+    // uniform routing, 33 tokens 2640 -> 2619 us, 40 2941 -> 2898, 48 3276
+    // -> 3227, 56 3562 -> 3518, 64 3791 -> 3729; 64 with the Zipf bias
+    // unchanged (826 -> 827). Below 33 tokens it did not pay (16 tokens
+    // +0.3%, 8 tokens even); 7:12 and 5:9 shares gained less at 64 tokens.
+    if (mt == 4 && cu_budget == 0 && grid == 2 * device_cu_count()) {
+        J.sa = 4;
+        J.sp = 7;
+    }
     switch (mt) {
     case 1:
         k_sk_gemm_stream<1, SkExperts, 1><<<grid, kBlock, 0, s>>>(J, J.K, 1);

@@ -170,6 +170,7 @@ __device__ __forceinline__ void sk_mfma_chunk(f32x4 (&acc)[TPW][MT], const u32x4
 //   int  xld(jb)                          its row stride in elements
 //   void store(jb, tile, ks, wq, acc, xch)   epilogue (may hold a block barrier)
 //   bool xcd_grouped()                    (stream kernel) give each XCD consecutive items
+//   int  share_a(), share_p()             (stream kernel) slot shares, 0 for none (below)
 // One item per loop iteration (the pipeline is filled per item): for dense
 // projections, whose items are many and uniform. TPW 16-row tiles per wave
 // (J.tpw must equal it) over K chunks of kSkKc / TPW: with TPW = 2 a staged
@@ -344,6 +345,18 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     const int G = gridDim.x, bx = blockIdx.x;
     const int vb = (J.xcd_grouped() && G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx;
     const int nfull = items / G;
+    // Slot shares (share_p > 0, G = 2 workgroups per compute unit): workgroups
+    // b and b + G / 2 share compute unit b, and the first-dispatched one is
+    // served faster. The items then come in rounds of G / 2, item cu of a
+    // round (XCD-grouped as above in full rounds) to compute unit cu, and of
+    // every share_p rounds the unit's first workgroup takes the first
+    // share_a, its second the others. Every item still has exactly one
+    // workgroup; u.it is then the round of G / 2.
+    const int sp = J.share_p(), sa = J.share_a();
+    const bool shares = sp > 0 && G % 16 == 0;
+    const int ncu = G / 2, slot = bx / ncu, cu = bx - slot * ncu;
+    const int vcu = J.xcd_grouped() ? (cu % 8) * (ncu / 8) + cu / 8 : cu;
+    const int nfullq = ncu > 0 ? items / ncu : 0;
     auto open = [&](Cur &u, int from) {
         u.valid = false;
         u.c = 0;
@@ -351,8 +364,16 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
         u.tile = 0;
         u.ks = 0;
         u.jb = Job{};
-        for (int r = from; r * (int)gridDim.x < items; ++r) {
-            const int it = r * (int)gridDim.x + (r < nfull ? vb : (int)blockIdx.x);
+        const int rstep = shares ? ncu : (int)gridDim.x;
+        for (int r = from; r * rstep < items; ++r) {
+            int it;
+            if (shares) {
+                if ((slot == 0) != (r % sp < sa))
+                    continue;  // the other workgroup's round
+                it = r * ncu + (r < nfullq ? vcu : cu);
+            } else {
+                it = r * (int)gridDim.x + (r < nfull ? vb : (int)blockIdx.x);
+            }
             if (it >= items)
                 break;
             const int a = it / per_job, rem = it - a * per_job;
