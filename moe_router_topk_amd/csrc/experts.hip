@@ -956,15 +956,16 @@ void launch_sk_experts(SkExperts J, int b, int max_jobs, int cu_budget, hipStrea
     const int items = max_jobs * tiles;
     // two workgroups per compute unit, each streaming its items back to back
     const int grid = budget_grid(items < 1 ? 1 : items, cu_budget, 2);
-    // At 33-64 tokens the first workgroup of each compute unit takes 4 of
-    // every 7 rounds (slot shares): measured on the MoE block in one process,
-    // uniform routing, 33 tokens 2640 -> 2619 us, 40 2941 -> 2898, 48 3276
-    // -> 3227, 56 3562 -> 3518, 64 3791 -> 3729; 64 with the Zipf bias
-    // unchanged (826 -> 827). Below 33 tokens it did not pay (16 tokens
-    // +0.3%, 8 tokens even); 7:12 and 5:9 shares gained less at 64 tokens.
-    if (mt == 4 && cu_budget == 0 && grid == 2 * device_cu_count()) {
-        J.sa = 4;
-        J.sp = 7;
+    // Slot shares: the first workgroup of each compute unit takes 4 of every
+    // 7 rounds at 33-64 tokens, 7 of every 12 at 17-32. Measured on the MoE
+    // block in one process, uniform routing: 33 tokens 2640 -> 2619 us, 40
+    // 2941 -> 2898, 48 3276 -> 3227, 56 3562 -> 3518, 64 3791 -> 3729 (64
+    // with the Zipf bias unchanged, 826 -> 827; 7:12 and 5:9 gained less at
+    // 64); 17 tokens 1562 -> 1560, 24 2056 -> 2039, 32 2522 -> 2510 (4:7
+    // gained less there). At 5-16 tokens no ratio paid (16 tokens +0.3%).
+    if (mt >= 2 && cu_budget == 0 && grid == 2 * device_cu_count()) {
+        J.sa = mt == 4 ? 4 : 7;
+        J.sp = mt == 4 ? 7 : 12;
     }
     switch (mt) {
     case 1:
