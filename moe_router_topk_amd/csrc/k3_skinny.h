@@ -345,9 +345,9 @@ __global__ void __launch_bounds__(kBlock) k_sk_gemm_stream(Jobs J, int K, int ks
     const int G = gridDim.x, bx = blockIdx.x;
     const int vb = (J.xcd_grouped() && G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx;
     const int nfull = items / G;
-    // Slot shares (share_p > 0, G = 2 workgroups per compute unit): workgroups
-    // b and b + G / 2 share compute unit b, and the first-dispatched one is
-    // served faster. The items then come in rounds of G / 2, item cu of a
+    // Slot shares (share_p > 0, set only for a grid of two workgroups per
+    // compute unit): workgroups b and b + G / 2 share a compute unit, and the
+    // first-dispatched one is served faster. The items then come in rounds of G / 2, item cu of a
     // round (XCD-grouped as above in full rounds) to compute unit cu, and of
     // every share_p rounds the unit's first workgroup takes the first
     // share_a, its second the others. Every item still has exactly one
