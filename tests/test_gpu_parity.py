@@ -539,6 +539,20 @@ def test_moe_experts_deterministic(k3, full):
     assert torch.equal(a, bb)
 
 
+@pytest.mark.parametrize("b,zipf", [(24, 0.0), (48, 0.0), (64, 1.1)])
+def test_moe_experts_schedule_does_not_change_bits(k3, full, b, zipf):
+    """Which workgroup takes which expert item does not change any output:
+    the full-device launch (two workgroups per compute unit, slot shares and
+    XCD-grouped rounds above 16 tokens) against a budget of all but one
+    compute unit (an odd grid: plain round-robin items), bit for bit."""
+    cfg, w = full
+    _, z, ids, wts, y_add, y = _routed_case(k3, cfg, w, b, zipf, 650 + b)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    y2 = k3.k3_moe_experts(z, ids, wts, w["w13"], w["w2"], y_add=y_add, cu_budget=cus - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
 def test_moe_experts_b1_invalid_id_dropped(k3):
     """Batch 1 (slots are experts, no permutation): an id outside [0, E)
     contributes nothing."""
